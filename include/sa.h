@@ -1,0 +1,163 @@
+/*
+ * sa.h — C interface of the Sketch Attention (SA) library for MI355X (gfx950).
+ *
+ * Sketch Attention compresses one user's history X (n events x d) into a fixed
+ * k x d sketch against k prototypes P that every user shares:
+ *
+ *   Z[j,i]  = p_j . x_i / sqrt(d)                    affinities
+ *   A[j,i]  = exp Z[j,i] / sum_j' exp Z[j',i]        softmax over the k
+ *                                                     prototypes, per token
+ *   S[j]    = sum_i A[j,i] x_i                       plain-sum sketch, or
+ *   S[j]    = sum_i A[j,i] x_i / mu[j],  mu[j] = sum_i A[j,i]
+ *                                                     (mass normalisation)
+ *
+ * Sources: "SequenceO1: End-to-End Ultra-Long (100K) Sequence Modeling in
+ * Recommendation with Low-Rank Caching" — reading-notes page, section 3.1,
+ * Eq. (5)-(9) (prototypes, affinities, prototype-wise softmax, sketch), and the
+ * paper's HTML page, FlashSA paragraph of the system-design section (fused,
+ * streaming computation of affinities, max / log-sum-exp statistics and the
+ * aggregation, with no k x n matrix in memory, over ragged batches).  The
+ * W_Q, W_K projections of Eq. (6) are folded into P by the caller
+ * (P_eff = P W_Q W_K^T gives the same affinities).  Mass normalisation and the
+ * backward pass are not printed on the pages: the first is the weighted mean
+ * of the tokens a prototype receives, the second is the chain rule of the
+ * lines above.
+ *
+ * Batches are CSR-ragged: users' histories are concatenated along the token
+ * axis, and offsets[u] .. offsets[u+1] are user u's rows.  No padding.
+ *
+ * General conventions
+ *  - All tensors are dense, row-major, contiguous, in device memory, and
+ *    16-byte aligned.  The caller owns every buffer, including the workspace;
+ *    the library allocates nothing and keeps no mutable global state, so calls
+ *    on different streams with different workspaces may run concurrently.
+ *  - GPU work is enqueued on `stream` and calls return without waiting.
+ *    Argument errors are reported synchronously by the return value and
+ *    nothing is enqueued.  Inconsistent device-side offsets are detected on
+ *    the device, recorded in the workspace and read back by
+ *    sa_get_device_status(); kernels clamp every index, so bad offsets give
+ *    wrong numbers, never an out-of-bounds access.
+ *  - Outputs are float32.  X and P are float32 (SA_F32, float32 arithmetic
+ *    throughout) or bfloat16 (SA_BF16, bf16 matrix-core products with float32
+ *    accumulation; the softmax weights enter the second product as bf16).
+ *  - Results are bitwise reproducible for identical inputs, device and
+ *    problem: every reduction runs in a fixed order and no floating-point
+ *    atomics are used.
+ *  - Shape limits: d in {32, 64, 128}; 1 <= k <= 2048; batch >= 1;
+ *    0 <= total_tokens < 2^36.  Users may be empty (n_u = 0 gives S = 0 and
+ *    mass = 0).
+ */
+#ifndef SKETCH_ATTENTION_SA_H
+#define SKETCH_ATTENTION_SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL_ARG = 1,            /* a required pointer is NULL              */
+  SA_ERR_BAD_SHAPE = 2,           /* k, d, batch or total_tokens out of range */
+  SA_ERR_BAD_DTYPE = 3,           /* dtype is not SA_F32 / SA_BF16           */
+  SA_ERR_UNSUPPORTED = 4,         /* flags or op not supported               */
+  SA_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes < sa_workspace_size()          */
+  SA_ERR_BAD_OFFSETS = 6,         /* host-checked or device-detected offsets */
+  SA_ERR_MISALIGNED = 7,          /* a pointer is not 16-byte aligned        */
+  SA_ERR_HIP = 8                  /* a HIP runtime call failed               */
+} sa_status;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* Problem flags. */
+enum { SA_FLAG_MASS_NORM = 1u };
+
+/* Operation selector for sa_workspace_size. */
+enum { SA_OP_FORWARD = 0, SA_OP_BACKWARD = 1 };
+
+typedef struct {
+  int32_t batch;         /* B, number of users (>= 1)                    */
+  int32_t k;             /* prototypes                                   */
+  int32_t d;             /* width of X rows and prototypes               */
+  int64_t total_tokens;  /* T = offsets[B]                               */
+  sa_dtype dtype;        /* dtype of X and P                             */
+  uint32_t flags;        /* SA_FLAG_*                                    */
+} sa_problem;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int sa_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sa_status_string(sa_status status);
+
+/* Host-only validation of a problem description; makes no HIP call.
+ * offsets_host (nullable): a host copy of the B+1 offsets; when given, it
+ * must start at 0, be non-decreasing and end at total_tokens, else
+ * SA_ERR_BAD_OFFSETS. */
+sa_status sa_validate(const sa_problem* problem, const int64_t* offsets_host);
+
+/* Bytes of workspace that sa_forward (op = SA_OP_FORWARD) or sa_backward
+ * (op = SA_OP_BACKWARD) need for this problem.  Returns 0 for an invalid
+ * problem or op.  Pure host arithmetic; makes no HIP call. */
+size_t sa_workspace_size(const sa_problem* problem, int op);
+
+/*
+ * Forward.  Computes, for every user u, the sketch S[u] (k x d) and the
+ * prototype masses mass[u] (k), plus the per-token log-sum-exp of the
+ * affinities, lse[i] = log sum_j exp Z[j,i] (natural log), which the
+ * FlashSA paragraph names as the softmax statistic and the backward reuses.
+ *
+ *  offsets_dev : int64 [B+1] device; offsets[0] = 0, non-decreasing,
+ *                offsets[B] = total_tokens.
+ *  X           : [T, d] (dtype) device.
+ *  P           : [k, d] (dtype) device, shared by all users.
+ *  S           : float [B, k, d] device, written.
+ *  lse         : float [T] device, written; may be NULL (kept in workspace).
+ *  mass        : float [B, k] device, written; may be NULL.
+ *  ws, ws_bytes: device workspace of at least
+ *                sa_workspace_size(problem, SA_OP_FORWARD) bytes; its
+ *                contents on entry are ignored.
+ *  stream      : HIP stream (hipStream_t) the work is enqueued on.
+ * Errors: SA_ERR_NULL_ARG, SA_ERR_BAD_SHAPE, SA_ERR_BAD_DTYPE,
+ * SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE_TOO_SMALL, SA_ERR_MISALIGNED
+ * (nothing enqueued); SA_ERR_HIP if a launch fails.
+ */
+sa_status sa_forward(const sa_problem* problem, const int64_t* offsets_dev,
+                     const void* X, const void* P, float* S, float* lse,
+                     float* mass, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward.  Given dS = dL/dS (float [B, k, d]), writes
+ *   dX = dL/dX  (float [T, d], overwritten) and
+ *   dP = dL/dP  (float [k, d], overwritten; summed over all users because
+ *                the prototypes are shared).
+ * The softmax weights are recomputed tile by tile from X, P and lse; lse is
+ * the forward's output (float [T]) or NULL, in which case it is recomputed.
+ * With SA_FLAG_MASS_NORM, S and mass from the forward are required (float
+ * [B, k, d] and [B, k]); without it they are ignored and may be NULL.
+ * Formulas (chain rule, one user, c = 1/sqrt(d)):
+ *   G = dS, cv = 0                     (plain sum)
+ *   G[j] = dS[j] / mu[j], cv[j] = G[j] . S[j]   (mass norm; mu[j] = 0 -> 0)
+ *   g_i = sum_j A[j,i] G[j];  delta_i = x_i . g_i - sum_j A[j,i] cv[j]
+ *   dZ[j,i] = A[j,i] (G[j] . x_i - cv[j] - delta_i)
+ *   dX_i = g_i + c sum_j dZ[j,i] p_j;   dP = c sum_u sum_i dZ[j,i] x_i
+ * Same error behaviour as sa_forward.
+ */
+sa_status sa_backward(const sa_problem* problem, const int64_t* offsets_dev,
+                      const void* X, const void* P, const float* dS,
+                      const float* lse, const float* S, const float* mass,
+                      float* dX, float* dP, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Waits for `stream`, then reports whether a kernel of the last call that
+ * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS) or not
+ * (SA_OK).  SA_ERR_HIP if the wait or the read fails. */
+sa_status sa_get_device_status(const void* ws, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKETCH_ATTENTION_SA_H */

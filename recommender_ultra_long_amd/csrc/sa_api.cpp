@@ -1,0 +1,190 @@
+// sa_api.cpp — the C-ABI of include/sa.h: validation, work plan, workspace
+// layout and kernel dispatch.  Host code only; kernels live in the .hip files.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/sa.h"
+#include "sa_kernels.h"
+
+namespace sa {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* p) {
+  if (B < 1 || k < 1 || k > 2048 || !(d == 32 || d == 64 || d == 128)) return false;
+  if (T < 0 || T >= ((int64_t)1 << 36)) return false;
+  if (dtype != 0 && dtype != 1) return false;
+  memset(p, 0, sizeof(*p));
+  p->B = B; p->k = k; p->d = d; p->T = T; p->dtype = dtype; p->mass_norm = mass_norm;
+  p->chunk = dtype == 1 ? kChunkBf16 : kChunkF32;
+  p->nchunks = (k + p->chunk - 1) / p->chunk;
+  int G = kTargetWorkgroups / p->nchunks;
+  if (G < 1) G = 1;
+  if ((int64_t)G > T) G = (int)(T > 0 ? T : 1);   // every segment non-empty
+  p->G = G;
+  p->nslots = (int64_t)G + B - 1;
+
+  const size_t Tn = (size_t)T;
+  size_t off = 0;
+  p->off_status = off; off += 256;
+  p->off_lse = off; off = align256(off + Tn * 4);
+  p->off_part = off; off = align256(off + (size_t)p->nslots * k * d * 4);
+  p->off_pmass = off; off = align256(off + (size_t)p->nslots * k * 4);
+  p->fwd_bytes = off;
+
+  const size_t esz = dtype == 1 ? 2 : 4;
+  off = 0;
+  p->off_status = 0; off += 256;
+  p->off_G = off; off = align256(off + (size_t)B * k * d * esz);
+  p->off_cv = off; off = align256(off + (size_t)B * k * 4);
+  p->off_g = off; off = align256(off + Tn * d * 4);
+  p->off_delta = off; off = align256(off + Tn * 4);
+  p->off_dxp = off; off = align256(off + (size_t)p->nchunks * Tn * d * 4);
+  p->off_dpp = off; off = align256(off + (size_t)G * k * d * 4);
+  p->off_blse = off; off = align256(off + Tn * 4);
+  p->bwd_bytes = off;
+  return true;
+}
+
+}  // namespace sa
+
+using namespace sa;
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" {
+
+int sa_version(void) { return 10000; }
+
+const char* sa_status_string(sa_status s) {
+  switch (s) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_NULL_ARG: return "SA_ERR_NULL_ARG: a required pointer is NULL";
+    case SA_ERR_BAD_SHAPE: return "SA_ERR_BAD_SHAPE: batch, k, d or total_tokens out of range";
+    case SA_ERR_BAD_DTYPE: return "SA_ERR_BAD_DTYPE: dtype must be SA_F32 or SA_BF16";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: unsupported flags or operation";
+    case SA_ERR_WORKSPACE_TOO_SMALL: return "SA_ERR_WORKSPACE_TOO_SMALL: workspace smaller than sa_workspace_size()";
+    case SA_ERR_BAD_OFFSETS: return "SA_ERR_BAD_OFFSETS: offsets not 0-based, non-decreasing and ending at total_tokens";
+    case SA_ERR_MISALIGNED: return "SA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+    case SA_ERR_HIP: return "SA_ERR_HIP: a HIP runtime call failed";
+  }
+  return "SA_ERR_UNKNOWN";
+}
+
+sa_status sa_validate(const sa_problem* pr, const int64_t* offsets_host) {
+  if (pr == nullptr) return SA_ERR_NULL_ARG;
+  if (pr->dtype != SA_F32 && pr->dtype != SA_BF16) return SA_ERR_BAD_DTYPE;
+  if ((pr->flags & ~(uint32_t)SA_FLAG_MASS_NORM) != 0u) return SA_ERR_UNSUPPORTED;
+  if (pr->batch < 1 || pr->k < 1 || pr->k > 2048) return SA_ERR_BAD_SHAPE;
+  if (!(pr->d == 32 || pr->d == 64 || pr->d == 128)) return SA_ERR_BAD_SHAPE;
+  if (pr->total_tokens < 0 || pr->total_tokens >= ((int64_t)1 << 36)) return SA_ERR_BAD_SHAPE;
+  if (offsets_host != nullptr) {
+    if (offsets_host[0] != 0 || offsets_host[pr->batch] != pr->total_tokens) return SA_ERR_BAD_OFFSETS;
+    for (int32_t u = 0; u < pr->batch; ++u)
+      if (offsets_host[u + 1] < offsets_host[u]) return SA_ERR_BAD_OFFSETS;
+  }
+  return SA_OK;
+}
+
+size_t sa_workspace_size(const sa_problem* pr, int op) {
+  if (sa_validate(pr, nullptr) != SA_OK) return 0;
+  Plan p;
+  if (!make_plan(pr->batch, pr->k, pr->d, pr->total_tokens, (int)pr->dtype,
+                 (pr->flags & SA_FLAG_MASS_NORM) != 0u, &p))
+    return 0;
+  if (op == SA_OP_FORWARD) return p.fwd_bytes;
+  if (op == SA_OP_BACKWARD) return p.bwd_bytes;
+  return 0;
+}
+
+sa_status sa_forward(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                     const void* P, float* S, float* lse, float* mass, void* ws,
+                     size_t ws_bytes, void* stream) {
+  sa_status v = sa_validate(pr, nullptr);
+  if (v != SA_OK) return v;
+  if (offsets_dev == nullptr || P == nullptr || S == nullptr || ws == nullptr) return SA_ERR_NULL_ARG;
+  if (X == nullptr && pr->total_tokens > 0) return SA_ERR_NULL_ARG;
+  if (((uintptr_t)offsets_dev & 7u) != 0u) return SA_ERR_MISALIGNED;
+  if ((X && !aligned16(X)) || !aligned16(P) || !aligned16(S) || !aligned16(ws) ||
+      (lse && !aligned16(lse)) || (mass && !aligned16(mass)))
+    return SA_ERR_MISALIGNED;
+  Plan p;
+  const bool mn = (pr->flags & SA_FLAG_MASS_NORM) != 0u;
+  if (!make_plan(pr->batch, pr->k, pr->d, pr->total_tokens, (int)pr->dtype, mn, &p))
+    return SA_ERR_BAD_SHAPE;
+  if (ws_bytes < p.fwd_bytes) return SA_ERR_WORKSPACE_TOO_SMALL;
+
+  char* w = (char*)ws;
+  FwdArgs a;
+  a.offsets = offsets_dev;
+  a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
+  a.X = X; a.P = P;
+  a.lse = lse ? lse : (float*)(w + p.off_lse);
+  a.S = S; a.mass = mass;
+  a.part = (float*)(w + p.off_part);
+  a.pmass = (float*)(w + p.off_pmass);
+  a.status = (uint32_t*)(w + p.off_status);
+  a.G = p.G; a.nchunks = p.nchunks;
+  a.mass_norm = mn ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = pr->dtype == SA_BF16 ? launch_fwd_bf16(a, st) : launch_fwd_f32(a, st);
+  return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+sa_status sa_backward(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                      const void* P, const float* dS, const float* lse, const float* S,
+                      const float* mass, float* dX, float* dP, void* ws, size_t ws_bytes,
+                      void* stream) {
+  sa_status v = sa_validate(pr, nullptr);
+  if (v != SA_OK) return v;
+  const bool mn = (pr->flags & SA_FLAG_MASS_NORM) != 0u;
+  if (offsets_dev == nullptr || P == nullptr || dS == nullptr || dP == nullptr || ws == nullptr)
+    return SA_ERR_NULL_ARG;
+  if ((X == nullptr || dX == nullptr) && pr->total_tokens > 0) return SA_ERR_NULL_ARG;
+  if (mn && (S == nullptr || mass == nullptr)) return SA_ERR_NULL_ARG;
+  if (((uintptr_t)offsets_dev & 7u) != 0u) return SA_ERR_MISALIGNED;
+  if ((X && !aligned16(X)) || !aligned16(P) || !aligned16(dS) || !aligned16(dP) ||
+      (dX && !aligned16(dX)) || !aligned16(ws) || (lse && !aligned16(lse)) ||
+      (S && !aligned16(S)) || (mass && !aligned16(mass)))
+    return SA_ERR_MISALIGNED;
+  Plan p;
+  if (!make_plan(pr->batch, pr->k, pr->d, pr->total_tokens, (int)pr->dtype, mn, &p))
+    return SA_ERR_BAD_SHAPE;
+  if (ws_bytes < p.bwd_bytes) return SA_ERR_WORKSPACE_TOO_SMALL;
+
+  char* w = (char*)ws;
+  BwdArgs a;
+  a.offsets = offsets_dev;
+  a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
+  a.X = X; a.P = P; a.dS = dS;
+  a.lse_ws = (float*)(w + p.off_blse);
+  a.recompute_lse = lse == nullptr ? 1 : 0;
+  a.lse = lse ? lse : a.lse_ws;
+  a.S = S; a.mass = mass;
+  a.dX = dX; a.dP = dP;
+  a.Gq = (void*)(w + p.off_G);
+  a.cv = (float*)(w + p.off_cv);
+  a.g = (float*)(w + p.off_g);
+  a.delta = (float*)(w + p.off_delta);
+  a.dxp = (float*)(w + p.off_dxp);
+  a.dpp = (float*)(w + p.off_dpp);
+  a.status = (uint32_t*)(w + p.off_status);
+  a.G = p.G; a.nchunks = p.nchunks;
+  a.mass_norm = mn ? 1 : 0;
+  hipError_t e = launch_bwd(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return SA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+sa_status sa_get_device_status(const void* ws, void* stream) {
+  if (ws == nullptr) return SA_ERR_NULL_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return SA_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return SA_ERR_HIP;
+  return word == kStatusOk ? SA_OK : SA_ERR_BAD_OFFSETS;
+}
+
+}  // extern "C"

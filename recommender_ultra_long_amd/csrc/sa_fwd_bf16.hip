@@ -1,0 +1,346 @@
+// sa_fwd_bf16.hip — Sketch Attention forward, bf16 inputs, fp32 accumulation,
+// matrix cores (v_mfma_f32_32x32x16_bf16) for both contractions.
+//
+// Method: SequenceO1 reading notes, section 3.1, Eq. (6)-(9); FlashSA
+// paragraph of the paper's HTML page (streamed affinities, per-token max and
+// log-sum-exp, aggregation, no k x n matrix in memory).
+//
+// Two passes over the history, because the softmax normalises over all k
+// prototypes of a token while one compute unit cannot hold the k x d fp32
+// accumulator for k = 1024 (512 KiB, the whole register file):
+//
+//  1. sa_stats_bf16: token-stationary.  Each wave keeps 64 tokens' rows in
+//     registers as MFMA B operands, streams every prototype through LDS, and
+//     reduces the per-token max and sum of exponentials inside each lane
+//     (orientation Z = P X^T puts a token in each lane and prototypes in the
+//     registers).  Writes lse (natural log) per token.
+//  2. sa_agg_bf16: prototype-stationary.  A workgroup owns 256 prototypes
+//     (4 waves x 64, B operands in registers, fp32 accumulators in AGPRs) and a
+//     contiguous segment of tokens.  Per 32-token tile: Z^T = X P_w^T on the
+//     matrix cores, A = exp2(Z alpha - lse2) in registers, then
+//     U^T += X^T A^T, whose B operand is the first product's C fragment as is
+//     (prototype per lane, tokens per register) and whose A operand (X^T) is
+//     read from the LDS tile with the gfx950 transpose read.  Partial sketches
+//     go to a workspace slot per (segment, user) piece; sa_reduce sums them
+//     in segment order.
+#include "sa_device.h"
+#include "sa_kernels.h"
+
+namespace sa {
+
+// ----------------------------------------------------------------------------
+// Pass 1: per-token log-sum-exp over all k prototypes.
+// Block: 256 threads = 4 waves; wave w handles tokens blk*256 + 64w .. +63 as
+// two 32-token MFMA tiles.  Prototypes are streamed in chunks of 64 rows
+// through LDS in fragment order, double buffered via registers.
+template <int D>
+__global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
+                                                     const bf16* __restrict__ P, int k,
+                                                     int64_t T, float alpha, float scale,
+                                                     float* __restrict__ lse_out) {
+  constexpr int KS = D / 16;            // 16-wide reduction steps over d
+  constexpr int PCH = 64;               // prototypes per LDS chunk
+  constexpr int NPIECE = PCH * D / 8;   // 16-byte pieces per chunk
+  constexpr int PPT = NPIECE / 256;     // pieces per thread
+  static_assert(PPT >= 1, "");
+  __shared__ bf16x8 sP[2][NPIECE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int64_t tok0 = (int64_t)blockIdx.x * 256 + wave * 64;
+
+  // This lane's token rows as B operands: xb[tt][ks] = X[tok][16 ks + 8h .. +7].
+  bf16x8 xb[2][KS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int64_t tok = tok0 + tt * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (tok < T) xb[tt][ks] = *(const bf16x8*)(X + tok * D + 16 * ks + 8 * h);
+      else xb[tt][ks] = bf16x8{};
+    }
+  }
+
+  // Piece q of a chunk: prototype row r = q / (D/8), 16-byte column piece
+  // cp = q % (D/8).  Fragment-order slot: tile r/32, step cp/2,
+  // lane (r % 32) + 32 (cp % 2).
+  auto load_chunk = [&](int p0, bf16x8 (&reg)[PPT]) {
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      const int q = tid + 256 * e;
+      const int r = q / (D / 8), cp = q % (D / 8);
+      const int row = p0 + r;
+      if (row < k) reg[e] = *(const bf16x8*)(P + (int64_t)row * D + 8 * cp);
+      else reg[e] = bf16x8{};
+    }
+  };
+  auto store_chunk = [&](int buf, const bf16x8 (&reg)[PPT]) {
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      const int q = tid + 256 * e;
+      const int r = q / (D / 8), cp = q % (D / 8);
+      const int slot = ((r >> 5) * KS + (cp >> 1)) * 64 + (r & 31) + 32 * (cp & 1);
+      sP[buf][slot] = reg[e];
+    }
+  };
+
+  float m[2] = {-INFINITY, -INFINITY};   // running max of raw dot products
+  float l[2] = {0.f, 0.f};               // running sum of exp2((z - m) alpha)
+
+  bf16x8 pre[PPT];
+  load_chunk(0, pre);
+  store_chunk(0, pre);
+  __syncthreads();
+  const int nch = (k + PCH - 1) / PCH;
+  for (int ci = 0; ci < nch; ++ci) {
+    const int p0 = ci * PCH;
+    if (ci + 1 < nch) load_chunk(p0 + PCH, pre);
+    const int buf = ci & 1;
+#pragma unroll
+    for (int pt = 0; pt < PCH / 32; ++pt) {
+      const int pbase = p0 + pt * 32;
+      if (pbase >= k) break;             // uniform across the block
+      f32x16 c0 = {}, c1 = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = sP[buf][(pt * KS + ks) * 64 + lane];
+        c0 = mfma32(a, xb[0][ks], c0);
+        c1 = mfma32(a, xb[1][ks], c1);
+      }
+      const bool partial = pbase + 32 > k;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x16 v = tt == 0 ? c0 : c1;
+        if (partial) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (pbase + crow(i, h) >= k) v[i] = -INFINITY;
+        }
+        float tmax = v[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, v[i]);
+        const float mnew = fmaxf(m[tt], tmax);
+        // A lane whose prototypes are all padding so far keeps m = -inf; a
+        // zero shift then keeps every term at exp2(-inf) = 0 instead of NaN.
+        const float ma = mnew == -INFINITY ? 0.f : mnew * alpha;
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += exp2_fast(fmaf(v[i], alpha, -ma));
+        l[tt] = fmaf(l[tt], exp2_fast(fmaf(m[tt], alpha, -ma)), s);
+        m[tt] = mnew;
+      }
+    }
+    if (ci + 1 < nch) store_chunk(buf ^ 1, pre);
+    __syncthreads();
+  }
+
+  // Lanes l and l ^ 32 saw disjoint halves of the prototypes of one token.
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const float mo = shfl_xor32(m[tt]), lo = shfl_xor32(l[tt]);
+    const float M = fmaxf(m[tt], mo);
+    const float Ma = M * alpha;
+    const float L = l[tt] * exp2_fast(fmaf(m[tt], alpha, -Ma)) + lo * exp2_fast(fmaf(mo, alpha, -Ma));
+    const int64_t tok = tok0 + tt * 32 + l32;
+    if (h == 0 && tok < T) lse_out[tok] = M * scale + __logf(L);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Pass 2: partial sketches per (segment, user) piece for one 256-prototype
+// chunk.  grid = (G segments, nchunks); block = 256 threads (4 waves).
+template <int D>
+__global__ __launch_bounds__(256, 1) void sa_agg_bf16(
+    const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
+    const bf16* __restrict__ P, int k, int64_t T, int G, float alpha,
+    const float* __restrict__ lse, float* __restrict__ part, float* __restrict__ pmass) {
+  constexpr int KS = D / 16;             // reduction steps of the affinity product
+  constexpr int DB = D / 32;             // 32-row blocks of the transposed sketch
+  constexpr int PT = 2;                  // 32-prototype tiles per wave
+  constexpr int KC = 4 * PT * 32;        // prototypes per workgroup
+  constexpr int TILE = 32;               // tokens per step
+  constexpr int ROW = D + 8;             // LDS row pitch in elements (16 B pad)
+  constexpr int PIECES = TILE * D / 8;   // 16-byte pieces per tile
+  constexpr int PPT = (PIECES + 255) / 256;
+
+  __shared__ __attribute__((aligned(16))) bf16 sX[2][TILE * ROW];
+  __shared__ __attribute__((aligned(16))) float sL[2][TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int s = blockIdx.x, chunk = blockIdx.y;
+  const int pw0 = chunk * KC + wave * PT * 32;   // first prototype of this wave
+
+  // Prototype rows as B operands of Z^T = X P^T: pw[pt][ks] holds
+  // P[pw0 + 32 pt + l32][16 ks + 8h .. +7].
+  bf16x8 pw[PT][KS];
+#pragma unroll
+  for (int pt = 0; pt < PT; ++pt) {
+    const int row = pw0 + pt * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      pw[pt][ks] = row < k ? *(const bf16x8*)(P + (int64_t)row * D + 16 * ks + 8 * h) : bf16x8{};
+  }
+
+  const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
+  TileWalker<TILE> cur;
+  cur.start(offsets, B, lo, hi);
+  if (!cur.valid) return;
+
+  // Staging of one tile: rows [t0, t1) of X and lse * log2(e); rows past t1
+  // are zero with lse = +inf, so they contribute exactly nothing.
+  bf16x8 xr[PPT];
+  float lr = 0.f;
+  auto load_tile = [&](int64_t t0, int64_t t1) {
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      const int q = tid + 256 * e;
+      const int r = q / (D / 8), cp = q % (D / 8);
+      xr[e] = (q < PIECES && t0 + r < t1) ? *(const bf16x8*)(X + (t0 + r) * D + 8 * cp) : bf16x8{};
+    }
+    if (tid < TILE) lr = (t0 + tid < t1) ? lse[t0 + tid] * kLog2e : INFINITY;
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+      const int q = tid + 256 * e;
+      if (q < PIECES) {
+        const int r = q / (D / 8), cp = q % (D / 8);
+        *(bf16x8*)(&sX[buf][r * ROW + 8 * cp]) = xr[e];
+      }
+    }
+    if (tid < TILE) sL[buf][tid] = lr;
+  };
+
+  f32x16 acc[PT][DB];
+#pragma unroll
+  for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[pt][db] = f32x16{};
+  float mass[PT] = {0.f, 0.f};
+
+  load_tile(cur.t0, cur.t1);
+  store_tile(0);
+  __syncthreads();
+
+  // transpose-read geometry (see lds_read_tr16): 16-lane group g = lane / 16
+  const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
+
+  int buf = 0;
+  while (cur.valid) {
+    TileWalker<TILE> nxt = cur;
+    nxt.advance();
+    if (nxt.valid) load_tile(nxt.t0, nxt.t1);
+
+    const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
+
+    // Z^T tile (32 tokens x 32 prototypes per pt): A = X rows, B = P rows.
+    f32x16 z[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) z[pt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *(const SA_LDS bf16x8*)(xs + l32 * ROW + 16 * ks + 8 * h);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) z[pt] = mfma32(a, pw[pt][ks], z[pt]);
+    }
+
+    // Softmax weights.  Register i of a lane is token crow(i, h) of the tile.
+    const SA_LDS float* ls = (const SA_LDS float*)&sL[buf][0];
+    f32x4 lq[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) lq[g] = *(const SA_LDS f32x4*)(ls + 8 * g + 4 * h);
+    bf16x8 abf[PT][2];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      float ms = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float a = exp2_fast(fmaf(z[pt][i], alpha, -lq[i >> 2][i & 3]));
+        ms += a;
+        abf[pt][i >> 3][i & 7] = (bf16)a;
+      }
+      mass[pt] += ms;
+    }
+
+    // U^T (d x prototypes) += X^T (d x tokens) A^T (tokens x prototypes).
+    // K slot j of half h in block kb is token 16 kb + 8 (j / 4) + 4h + (j % 4),
+    // matching the C fragment rows above.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row0 = 16 * kb + 4 * h + tr_r;
+        const int col = 32 * db + 16 * tr_half + 4 * tr_c;
+        const bf16x4 v0 = lds_read_tr16(xs + row0 * ROW + col);
+        const bf16x4 v1 = lds_read_tr16(xs + (row0 + 8) * ROW + col);
+        const bf16x8 a = concat4(v0, v1);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt][db] = mfma32(a, abf[pt][kb], acc[pt][db]);
+      }
+    }
+
+    if (cur.last_in_piece()) {
+      // Flush the piece to slot s + user.  acc[pt][db] register i holds
+      // U[proto = pw0 + 32 pt + l32][d = 32 db + crow(i, h)].
+      const int64_t slot = (int64_t)s + cur.user;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const int proto = pw0 + pt * 32 + l32;
+        const float mo = shfl_xor32(mass[pt]);
+        if (proto < k) {
+          float* dst = part + (slot * k + proto) * D;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4 v = {acc[pt][db][4 * g], acc[pt][db][4 * g + 1], acc[pt][db][4 * g + 2],
+                         acc[pt][db][4 * g + 3]};
+              *(f32x4*)(dst + 32 * db + 8 * g + 4 * h) = v;
+            }
+          if (h == 0) pmass[slot * k + proto] = mass[pt] + mo;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[pt][db] = f32x16{};
+        mass[pt] = 0.f;
+      }
+    }
+
+    if (nxt.valid) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    cur = nxt;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host-side launchers.
+template <int D>
+static hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const float alpha = scale * kLog2e;
+  if (a.T > 0) {
+    const unsigned nb = (unsigned)((a.T + 255) / 256);
+    hipLaunchKernelGGL(sa_stats_bf16<D>, dim3(nb), dim3(256), 0, st, (const bf16*)a.X,
+                       (const bf16*)a.P, a.k, a.T, alpha, scale, a.lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sa_agg_bf16<D>, dim3(a.G, a.nchunks), dim3(256), 0, st, a.offsets, a.B,
+                       (const bf16*)a.X, (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part,
+                       a.pmass);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_reduce(a, st);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_fwd_bf16_t<32>(a, st);
+    case 64: return launch_fwd_bf16_t<64>(a, st);
+    case 128: return launch_fwd_bf16_t<128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

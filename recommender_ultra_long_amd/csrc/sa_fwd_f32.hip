@@ -1,0 +1,163 @@
+// sa_fwd_f32.hip — Sketch Attention forward with float32 inputs and float32
+// arithmetic throughout (vector ALU; there is no reduced-precision step).
+//
+// Method: SequenceO1 reading notes, section 3.1, Eq. (6)-(9).  Same two-pass
+// structure as the bf16 path: per-token log-sum-exp over all prototypes, then
+// prototype-chunk aggregation per (segment, user) piece, then sa_reduce.
+#include "sa_device.h"
+#include "sa_kernels.h"
+
+namespace sa {
+
+// Pass 1: one token per thread, prototypes streamed through LDS 32 at a time.
+template <int D>
+__global__ __launch_bounds__(256) void sa_stats_f32(const float* __restrict__ X,
+                                                    const float* __restrict__ P, int k, int64_t T,
+                                                    float alpha, float scale,
+                                                    float* __restrict__ lse_out) {
+  constexpr int PC = 32;
+  __shared__ float sP[PC][D];
+  const int tid = threadIdx.x;
+  const int64_t tok = (int64_t)blockIdx.x * 256 + tid;
+  float x[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) x[e] = tok < T ? X[tok * D + e] : 0.f;
+  float m = -INFINITY, l = 0.f;
+  for (int p0 = 0; p0 < k; p0 += PC) {
+    __syncthreads();
+    for (int q = tid; q < PC * D; q += 256) {
+      const int r = q / D, c = q % D;
+      sP[r][c] = (p0 + r < k) ? P[(int64_t)(p0 + r) * D + c] : 0.f;
+    }
+    __syncthreads();
+    const int np = k - p0 < PC ? k - p0 : PC;
+    float z[PC];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PC; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc = fmaf(sP[j][e], x[e], acc);
+      z[j] = j < np ? acc : -INFINITY;
+      tmax = fmaxf(tmax, z[j]);
+    }
+    const float mnew = fmaxf(m, tmax);
+    const float ma = mnew * alpha;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < PC; ++j) s += exp2_fast(fmaf(z[j], alpha, -ma));
+    l = fmaf(l, exp2_fast(fmaf(m, alpha, -ma)), s);
+    m = mnew;
+  }
+  if (tok < T) lse_out[tok] = m * scale + __logf(l);
+}
+
+// Pass 2: grid = (G, nchunks), block 256.  Workgroup owns 64 prototypes;
+// thread t owns prototype t / 4 and columns (t % 4) D/4 .. +D/4 of U.
+template <int D>
+__global__ __launch_bounds__(256) void sa_agg_f32(const int64_t* __restrict__ offsets, int B,
+                                                  const float* __restrict__ X,
+                                                  const float* __restrict__ P, int k, int64_t T,
+                                                  int G, float alpha,
+                                                  const float* __restrict__ lse,
+                                                  float* __restrict__ part,
+                                                  float* __restrict__ pmass) {
+  constexpr int PC = kChunkF32;   // 64
+  constexpr int TILE = 32;
+  constexpr int DQ = D / 4;
+  __shared__ float sP[PC][D + 1];
+  __shared__ float sX[TILE][D + 1];
+  __shared__ float sA[PC][TILE + 1];
+  __shared__ float sL[TILE];
+  const int tid = threadIdx.x;
+  const int j = tid >> 2, q = tid & 3;
+  const int s = blockIdx.x;
+  const int p0 = blockIdx.y * PC;
+
+  for (int i = tid; i < PC * D; i += 256) {
+    const int r = i / D, c = i % D;
+    sP[r][c] = (p0 + r < k) ? P[(int64_t)(p0 + r) * D + c] : 0.f;
+  }
+
+  const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
+  TileWalker<TILE> cur;
+  cur.start(offsets, B, lo, hi);
+
+  float acc[DQ];
+#pragma unroll
+  for (int e = 0; e < DQ; ++e) acc[e] = 0.f;
+  float ms = 0.f;
+
+  while (cur.valid) {
+    __syncthreads();
+    for (int i = tid; i < TILE * D; i += 256) {
+      const int r = i / D, c = i % D;
+      sX[r][c] = (cur.t0 + r < cur.t1) ? X[(cur.t0 + r) * D + c] : 0.f;
+    }
+    if (tid < TILE) sL[tid] = (cur.t0 + tid < cur.t1) ? lse[cur.t0 + tid] * kLog2e : INFINITY;
+    __syncthreads();
+    // 8 softmax weights per thread: prototype j, tokens 8q .. 8q+7.
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int tt = 8 * q + t;
+      float z = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) z = fmaf(sP[j][e], sX[tt][e], z);
+      const float a = exp2_fast(fmaf(z, alpha, -sL[tt]));
+      sA[j][tt] = a;
+      ms += a;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int tt = 0; tt < TILE; ++tt) {
+      const float a = sA[j][tt];
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) acc[e] = fmaf(a, sX[tt][q * DQ + e], acc[e]);
+    }
+    if (cur.last_in_piece()) {
+      const int64_t slot = (int64_t)s + cur.user;
+      float mt = ms + __shfl_xor(ms, 1, 64);
+      mt += __shfl_xor(mt, 2, 64);
+      if (p0 + j < k) {
+        float* dst = part + (slot * k + p0 + j) * D + q * DQ;
+#pragma unroll
+        for (int e = 0; e < DQ; ++e) dst[e] = acc[e];
+        if (q == 0) pmass[slot * k + p0 + j] = mt;
+      }
+#pragma unroll
+      for (int e = 0; e < DQ; ++e) acc[e] = 0.f;
+      ms = 0.f;
+    }
+    cur.advance();
+  }
+}
+
+template <int D>
+static hipError_t launch_fwd_f32_t(const FwdArgs& a, hipStream_t st) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const float alpha = scale * kLog2e;
+  if (a.T > 0) {
+    const unsigned nb = (unsigned)((a.T + 255) / 256);
+    hipLaunchKernelGGL(sa_stats_f32<D>, dim3(nb), dim3(256), 0, st, (const float*)a.X,
+                       (const float*)a.P, a.k, a.T, alpha, scale, a.lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sa_agg_f32<D>, dim3(a.G, a.nchunks), dim3(256), 0, st, a.offsets, a.B,
+                       (const float*)a.X, (const float*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part,
+                       a.pmass);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_reduce(a, st);
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_fwd_f32_t<32>(a, st);
+    case 64: return launch_fwd_f32_t<64>(a, st);
+    case 128: return launch_fwd_f32_t<128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

@@ -1,0 +1,210 @@
+"""ctypes binding of libsa.so (include/sa.h).
+
+Argument marshalling only: every step of Sketch Attention runs in the HIP
+kernels of the library.  PyTorch provides device memory (outputs and the
+workspace are torch tensors) and the stream (the current torch stream unless
+one is given).  The library must have been built (``__graft_entry__.build()``
+or ``python recommender_ultra_long_amd/build.py``); loading fails loudly
+otherwise — there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsa.so")
+_lib = None
+
+SA_OK = 0
+SA_ERR_NULL_ARG = 1
+SA_ERR_BAD_SHAPE = 2
+SA_ERR_BAD_DTYPE = 3
+SA_ERR_UNSUPPORTED = 4
+SA_ERR_WORKSPACE_TOO_SMALL = 5
+SA_ERR_BAD_OFFSETS = 6
+SA_ERR_MISALIGNED = 7
+SA_ERR_HIP = 8
+
+SA_F32 = 0
+SA_BF16 = 1
+SA_FLAG_MASS_NORM = 1
+SA_OP_FORWARD = 0
+SA_OP_BACKWARD = 1
+
+EXPORTED = ("sa_version", "sa_status_string", "sa_validate", "sa_workspace_size",
+            "sa_forward", "sa_backward", "sa_get_device_status")
+
+
+class SaProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("k", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+class SAError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def load():
+    """Loads libsa.so once.  torch is imported first so that the library binds
+    to the HIP runtime torch already loaded (same SONAME)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, sz, i32, i64p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)
+    pp = ctypes.POINTER(SaProblem)
+    lib.sa_version.restype = i32
+    lib.sa_version.argtypes = []
+    lib.sa_status_string.restype = ctypes.c_char_p
+    lib.sa_status_string.argtypes = [i32]
+    lib.sa_validate.restype = i32
+    lib.sa_validate.argtypes = [pp, i64p]
+    lib.sa_workspace_size.restype = sz
+    lib.sa_workspace_size.argtypes = [pp, i32]
+    lib.sa_forward.restype = i32
+    lib.sa_forward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sa_backward.restype = i32
+    lib.sa_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sa_get_device_status.restype = i32
+    lib.sa_get_device_status.argtypes = [vp, vp]
+    _lib = lib
+    return lib
+
+
+def version():
+    return load().sa_version()
+
+
+def status_string(status):
+    return load().sa_status_string(int(status)).decode()
+
+
+def make_problem(batch, k, d, total_tokens, dtype, mass_norm=False):
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}.get(dtype, 99)
+    return SaProblem(int(batch), int(k), int(d), int(total_tokens), int(dtype),
+                     SA_FLAG_MASS_NORM if mass_norm else 0)
+
+
+def validate(problem, offsets_host=None):
+    lib = load()
+    ptr = None
+    if offsets_host is not None:
+        arr = np.ascontiguousarray(offsets_host, dtype=np.int64)
+        ptr = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    return lib.sa_validate(ctypes.byref(problem), ptr)
+
+
+def workspace_size(problem, op=SA_OP_FORWARD):
+    return int(load().sa_workspace_size(ctypes.byref(problem), int(op)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _device_offsets(offsets, device):
+    if isinstance(offsets, torch.Tensor):
+        return offsets.to(device=device, dtype=torch.int64).contiguous()
+    return torch.as_tensor(np.asarray(offsets, dtype=np.int64), device=device)
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, workspace=None,
+               stream=None, want_lse=True, want_mass=True):
+    """Calls sa_forward.  offsets: int64 [B+1] (device tensor, or host array
+    copied to X's device); X [T, d] and P [k, d] float32 or bfloat16 on the
+    GPU.  Returns (S [B, k, d] f32, lse [T] f32 or None, mass [B, k] f32 or
+    None)."""
+    lib = load()
+    dev = P.device
+    off = _device_offsets(offsets, dev)
+    B = off.numel() - 1
+    T, d = X.shape
+    k = P.shape[0]
+    pr = make_problem(B, k, d, T, X.dtype, mass_norm)
+    if S is None:
+        S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((T,), dtype=torch.float32, device=dev)
+    if mass is None and want_mass:
+        mass = torch.empty((B, k), dtype=torch.float32, device=dev)
+    ws_bytes = workspace_size(pr, SA_OP_FORWARD)
+    ws = _workspace(ws_bytes, dev, workspace)
+    st = lib.sa_forward(ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(S), _ptr(lse),
+                        _ptr(mass), _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
+                        _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_forward")
+    return S, lse, mass
+
+
+def sa_backward(offsets, X, P, dS, lse=None, S=None, mass=None, mass_norm=False, dX=None,
+                dP=None, workspace=None, stream=None):
+    """Calls sa_backward.  Returns (dX [T, d] f32, dP [k, d] f32)."""
+    lib = load()
+    dev = P.device
+    off = _device_offsets(offsets, dev)
+    B = off.numel() - 1
+    T, d = X.shape
+    k = P.shape[0]
+    pr = make_problem(B, k, d, T, X.dtype, mass_norm)
+    if dX is None:
+        dX = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if dP is None:
+        dP = torch.empty((k, d), dtype=torch.float32, device=dev)
+    ws_bytes = workspace_size(pr, SA_OP_BACKWARD)
+    ws = _workspace(ws_bytes, dev, workspace)
+    st = lib.sa_backward(ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(dS), _ptr(lse),
+                         _ptr(S), _ptr(mass), _ptr(dX), _ptr(dP), _ptr(ws),
+                         ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_backward")
+    return dX, dP
+
+
+def sa_get_device_status(workspace, stream=None):
+    return load().sa_get_device_status(_ptr(workspace), _stream_handle(stream))
+
+
+class SketchAttention(torch.autograd.Function):
+    """Autograd wrapper: S = SA(X, P) over a CSR-ragged batch.  Gradients flow
+    to X and P through sa_backward."""
+
+    @staticmethod
+    def forward(ctx, X, P, offsets, mass_norm=False):
+        off = _device_offsets(offsets, P.device)
+        S, lse, mass = sa_forward(off, X, P, mass_norm)
+        ctx.save_for_backward(X, P, off, S, lse, mass)
+        ctx.mass_norm = mass_norm
+        return S
+
+    @staticmethod
+    def backward(ctx, dS):
+        X, P, off, S, lse, mass = ctx.saved_tensors
+        dX, dP = sa_backward(off, X, P, dS.contiguous().float(), lse, S, mass, ctx.mass_norm)
+        return dX.to(X.dtype), dP.to(P.dtype), None, None

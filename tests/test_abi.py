@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/sa.h, and host-side validation returns the documented
+status codes synchronously (no kernel is launched on any error path)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from recommender_ultra_long_amd import sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "sa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = sa.load()
+    names = _declared_functions()
+    assert set(names) == set(sa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    assert sa.version() == 10000
+    for code in range(9):
+        s = sa.status_string(code)
+        assert s.startswith("SA_")
+    assert sa.status_string(123) == "SA_ERR_UNKNOWN"
+
+
+def _p(**kw):
+    base = dict(batch=2, k=64, d=32, total_tokens=100, dtype=sa.SA_F32, mass_norm=False)
+    base.update(kw)
+    return sa.make_problem(base["batch"], base["k"], base["d"], base["total_tokens"], base["dtype"],
+                           base["mass_norm"])
+
+
+def test_validate_shapes_and_dtypes():
+    assert sa.validate(_p()) == sa.SA_OK
+    assert sa.validate(_p(dtype=sa.SA_BF16, d=128, k=1024)) == sa.SA_OK
+    assert sa.validate(_p(k=2048)) == sa.SA_OK
+    assert sa.validate(_p(k=0)) == sa.SA_ERR_BAD_SHAPE
+    assert sa.validate(_p(k=2049)) == sa.SA_ERR_BAD_SHAPE
+    assert sa.validate(_p(d=48)) == sa.SA_ERR_BAD_SHAPE
+    assert sa.validate(_p(d=256)) == sa.SA_ERR_BAD_SHAPE
+    assert sa.validate(_p(batch=0)) == sa.SA_ERR_BAD_SHAPE
+    assert sa.validate(_p(total_tokens=-1)) == sa.SA_ERR_BAD_SHAPE
+    assert sa.validate(_p(total_tokens=1 << 36)) == sa.SA_ERR_BAD_SHAPE
+    assert sa.validate(_p(dtype=7)) == sa.SA_ERR_BAD_DTYPE
+    pr = _p()
+    pr.flags = 2
+    assert sa.validate(pr) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_validate_host_offsets():
+    assert sa.validate(_p(), np.array([0, 40, 100])) == sa.SA_OK
+    assert sa.validate(_p(), np.array([0, 0, 100])) == sa.SA_OK
+    assert sa.validate(_p(), np.array([1, 40, 100])) == sa.SA_ERR_BAD_OFFSETS
+    assert sa.validate(_p(), np.array([0, 40, 99])) == sa.SA_ERR_BAD_OFFSETS
+    assert sa.validate(_p(), np.array([0, 60, 40])) == sa.SA_ERR_BAD_OFFSETS
+
+
+def test_workspace_size():
+    f = sa.workspace_size(_p(), sa.SA_OP_FORWARD)
+    b = sa.workspace_size(_p(), sa.SA_OP_BACKWARD)
+    assert f > 0 and b > 0 and f % 256 == 0 and b % 256 == 0
+    assert sa.workspace_size(_p(k=0), sa.SA_OP_FORWARD) == 0
+    assert sa.workspace_size(_p(), 5) == 0
+    # grows with the token count (the per-token lse and backward buffers)
+    assert sa.workspace_size(_p(total_tokens=10000), 0) > f
+    assert sa.workspace_size(_p(total_tokens=10000), 1) > b
+
+
+def _call_forward(pr, off=1, X=1, P=1, S=1, lse=0, mass=0, ws=1, ws_bytes=1 << 30):
+    # Fake but 256-aligned addresses: every call below must fail validation
+    # before any pointer is dereferenced or any kernel enqueued.
+    lib = sa.load()
+    a = lambda v: ctypes.c_void_p(v * 4096) if v else None
+    return lib.sa_forward(ctypes.byref(pr), a(off), a(X), a(P), a(S), a(lse), a(mass), a(ws),
+                          ctypes.c_size_t(ws_bytes), None)
+
+
+def _call_backward(pr, off=1, X=1, P=1, dS=1, lse=0, S=0, mass=0, dX=1, dP=1, ws=1,
+                   ws_bytes=1 << 30):
+    lib = sa.load()
+    a = lambda v: ctypes.c_void_p(v * 4096) if v else None
+    return lib.sa_backward(ctypes.byref(pr), a(off), a(X), a(P), a(dS), a(lse), a(S), a(mass),
+                           a(dX), a(dP), a(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_forward_argument_errors_are_synchronous():
+    pr = _p()
+    assert _call_forward(pr, off=0) == sa.SA_ERR_NULL_ARG
+    assert _call_forward(pr, X=0) == sa.SA_ERR_NULL_ARG
+    assert _call_forward(pr, P=0) == sa.SA_ERR_NULL_ARG
+    assert _call_forward(pr, S=0) == sa.SA_ERR_NULL_ARG
+    assert _call_forward(pr, ws=0) == sa.SA_ERR_NULL_ARG
+    assert _call_forward(pr, ws_bytes=16) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+    assert _call_forward(_p(k=0)) == sa.SA_ERR_BAD_SHAPE
+    assert _call_forward(_p(dtype=5)) == sa.SA_ERR_BAD_DTYPE
+    lib = sa.load()
+    mis = lib.sa_forward(ctypes.byref(pr), ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8),
+                         ctypes.c_void_p(8192), ctypes.c_void_p(12288), None, None,
+                         ctypes.c_void_p(16384), ctypes.c_size_t(1 << 30), None)
+    assert mis == sa.SA_ERR_MISALIGNED
+    mis = lib.sa_forward(ctypes.byref(pr), ctypes.c_void_p(4096 + 4), ctypes.c_void_p(8192),
+                         ctypes.c_void_p(8192), ctypes.c_void_p(12288), None, None,
+                         ctypes.c_void_p(16384), ctypes.c_size_t(1 << 30), None)
+    assert mis == sa.SA_ERR_MISALIGNED
+
+
+def test_backward_argument_errors_are_synchronous():
+    pr = _p()
+    assert _call_backward(pr, dS=0) == sa.SA_ERR_NULL_ARG
+    assert _call_backward(pr, dX=0) == sa.SA_ERR_NULL_ARG
+    assert _call_backward(pr, dP=0) == sa.SA_ERR_NULL_ARG
+    assert _call_backward(pr, ws_bytes=16) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+    prm = _p(mass_norm=True)
+    assert _call_backward(prm) == sa.SA_ERR_NULL_ARG            # S and mass required
+    assert _call_backward(prm, S=2) == sa.SA_ERR_NULL_ARG
+    assert _call_backward(_p(d=40)) == sa.SA_ERR_BAD_SHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(sa, "_lib", None)
+    monkeypatch.setattr(sa, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        sa.load()
