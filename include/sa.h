@@ -151,6 +151,38 @@ sa_status sa_backward(const sa_problem* problem, const int64_t* offsets_dev,
                       float* dX, float* dP, void* ws, size_t ws_bytes,
                       void* stream);
 
+/*
+ * Per-kernel timing for benchmarks.  The pages report no measurement of
+ * their own; these variants exist so that a benchmark can time each kernel of
+ * one call on the stream it runs on.  They behave exactly like sa_forward /
+ * sa_backward and additionally record prof->events[2i] and
+ * prof->events[2i+1] on `stream` immediately before and after the i-th
+ * kernel they launch (at most SA_PROFILE_MAX_KERNELS kernels), set
+ * prof->names[i] to a static kernel name and prof->n_kernels to the number of
+ * kernels launched.  The caller creates all 2 * SA_PROFILE_MAX_KERNELS
+ * events (hipEvent_t handles, passed as void*) beforehand; any NULL handle
+ * gives SA_ERR_NULL_ARG and nothing is enqueued.  Recording events adds a
+ * little host overhead; use the plain entry points for end-to-end timing.
+ */
+#define SA_PROFILE_MAX_KERNELS 8
+
+typedef struct {
+  void* events[2 * SA_PROFILE_MAX_KERNELS]; /* in: hipEvent_t handles        */
+  int32_t n_kernels;                        /* out: kernels launched         */
+  const char* names[SA_PROFILE_MAX_KERNELS]; /* out: static kernel names     */
+} sa_profile;
+
+sa_status sa_forward_profiled(const sa_problem* problem, const int64_t* offsets_dev,
+                              const void* X, const void* P, float* S, float* lse,
+                              float* mass, void* ws, size_t ws_bytes, void* stream,
+                              sa_profile* prof);
+
+sa_status sa_backward_profiled(const sa_problem* problem, const int64_t* offsets_dev,
+                               const void* X, const void* P, const float* dS,
+                               const float* lse, const float* S, const float* mass,
+                               float* dX, float* dP, void* ws, size_t ws_bytes,
+                               void* stream, sa_profile* prof);
+
 /* Waits for `stream`, then reports whether a kernel of the last call that
  * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS) or not
  * (SA_OK).  SA_ERR_HIP if the wait or the read fails. */

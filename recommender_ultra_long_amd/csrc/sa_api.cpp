@@ -17,13 +17,21 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* 
   if (dtype != 0 && dtype != 1) return false;
   memset(p, 0, sizeof(*p));
   p->B = B; p->k = k; p->d = d; p->T = T; p->dtype = dtype; p->mass_norm = mass_norm;
+  // Segments: about one prototype-stationary workgroup per compute unit, and
+  // never more segments than tokens, so that every segment is non-empty.
+  auto segments = [T](int nchunks) {
+    int G = kTargetWorkgroups / nchunks;
+    if (G < 1) G = 1;
+    if ((int64_t)G > T) G = (int)(T > 0 ? T : 1);
+    return G;
+  };
   p->chunk = dtype == 1 ? kChunkBf16 : kChunkF32;
   p->nchunks = (k + p->chunk - 1) / p->chunk;
-  int G = kTargetWorkgroups / p->nchunks;
-  if (G < 1) G = 1;
-  if ((int64_t)G > T) G = (int)(T > 0 ? T : 1);   // every segment non-empty
-  p->G = G;
-  p->nslots = (int64_t)G + B - 1;
+  p->G = segments(p->nchunks);
+  p->nslots = (int64_t)p->G + B - 1;
+  p->bchunk = dtype == 1 ? kChunkBf16 : kChunkF32Bwd;
+  p->bnchunks = (k + p->bchunk - 1) / p->bchunk;
+  p->Gb = segments(p->bnchunks);
 
   const size_t Tn = (size_t)T;
   size_t off = 0;
@@ -34,14 +42,11 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* 
   p->fwd_bytes = off;
 
   const size_t esz = dtype == 1 ? 2 : 4;
-  off = 0;
-  p->off_status = 0; off += 256;
+  off = 256;   // status word shared with the forward layout
   p->off_G = off; off = align256(off + (size_t)B * k * d * esz);
   p->off_cv = off; off = align256(off + (size_t)B * k * 4);
-  p->off_g = off; off = align256(off + Tn * d * 4);
   p->off_delta = off; off = align256(off + Tn * 4);
-  p->off_dxp = off; off = align256(off + (size_t)p->nchunks * Tn * d * 4);
-  p->off_dpp = off; off = align256(off + (size_t)G * k * d * 4);
+  p->off_dpp = off; off = align256(off + (size_t)p->Gb * k * d * 4);
   p->off_blse = off; off = align256(off + Tn * 4);
   p->bwd_bytes = off;
   return true;
@@ -98,9 +103,9 @@ size_t sa_workspace_size(const sa_problem* pr, int op) {
   return 0;
 }
 
-sa_status sa_forward(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
-                     const void* P, float* S, float* lse, float* mass, void* ws,
-                     size_t ws_bytes, void* stream) {
+static sa_status forward_impl(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                              const void* P, float* S, float* lse, float* mass, void* ws,
+                              size_t ws_bytes, void* stream, Prof* prof) {
   sa_status v = sa_validate(pr, nullptr);
   if (v != SA_OK) return v;
   if (offsets_dev == nullptr || P == nullptr || S == nullptr || ws == nullptr) return SA_ERR_NULL_ARG;
@@ -128,14 +133,14 @@ sa_status sa_forward(const sa_problem* pr, const int64_t* offsets_dev, const voi
   a.G = p.G; a.nchunks = p.nchunks;
   a.mass_norm = mn ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = pr->dtype == SA_BF16 ? launch_fwd_bf16(a, st) : launch_fwd_f32(a, st);
+  hipError_t e = pr->dtype == SA_BF16 ? launch_fwd_bf16(a, st, prof) : launch_fwd_f32(a, st, prof);
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
-sa_status sa_backward(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
-                      const void* P, const float* dS, const float* lse, const float* S,
-                      const float* mass, float* dX, float* dP, void* ws, size_t ws_bytes,
-                      void* stream) {
+static sa_status backward_impl(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                               const void* P, const float* dS, const float* lse, const float* S,
+                               const float* mass, float* dX, float* dP, void* ws, size_t ws_bytes,
+                               void* stream, Prof* prof) {
   sa_status v = sa_validate(pr, nullptr);
   if (v != SA_OK) return v;
   const bool mn = (pr->flags & SA_FLAG_MASS_NORM) != 0u;
@@ -165,16 +170,62 @@ sa_status sa_backward(const sa_problem* pr, const int64_t* offsets_dev, const vo
   a.dX = dX; a.dP = dP;
   a.Gq = (void*)(w + p.off_G);
   a.cv = (float*)(w + p.off_cv);
-  a.g = (float*)(w + p.off_g);
   a.delta = (float*)(w + p.off_delta);
-  a.dxp = (float*)(w + p.off_dxp);
   a.dpp = (float*)(w + p.off_dpp);
   a.status = (uint32_t*)(w + p.off_status);
-  a.G = p.G; a.nchunks = p.nchunks;
+  a.Gb = p.Gb; a.bnchunks = p.bnchunks;
   a.mass_norm = mn ? 1 : 0;
-  hipError_t e = launch_bwd(a, (hipStream_t)stream);
-  if (e == hipErrorNotSupported) return SA_ERR_UNSUPPORTED;
+  hipError_t e = launch_bwd(a, (int)pr->dtype, (hipStream_t)stream, prof);
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+static sa_status profile_setup(sa_profile* prof, Prof* p) {
+  if (prof == nullptr) return SA_ERR_NULL_ARG;
+  for (int i = 0; i < 2 * SA_PROFILE_MAX_KERNELS; ++i)
+    if (prof->events[i] == nullptr) return SA_ERR_NULL_ARG;
+  p->ev = (hipEvent_t*)prof->events;
+  p->cap = SA_PROFILE_MAX_KERNELS;
+  p->n = 0;
+  p->names = prof->names;
+  prof->n_kernels = 0;
+  return SA_OK;
+}
+
+sa_status sa_forward(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                     const void* P, float* S, float* lse, float* mass, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return forward_impl(pr, offsets_dev, X, P, S, lse, mass, ws, ws_bytes, stream, nullptr);
+}
+
+sa_status sa_backward(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                      const void* P, const float* dS, const float* lse, const float* S,
+                      const float* mass, float* dX, float* dP, void* ws, size_t ws_bytes,
+                      void* stream) {
+  return backward_impl(pr, offsets_dev, X, P, dS, lse, S, mass, dX, dP, ws, ws_bytes, stream,
+                       nullptr);
+}
+
+sa_status sa_forward_profiled(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                              const void* P, float* S, float* lse, float* mass, void* ws,
+                              size_t ws_bytes, void* stream, sa_profile* prof) {
+  Prof p;
+  sa_status v = profile_setup(prof, &p);
+  if (v != SA_OK) return v;
+  v = forward_impl(pr, offsets_dev, X, P, S, lse, mass, ws, ws_bytes, stream, &p);
+  prof->n_kernels = p.n;
+  return v;
+}
+
+sa_status sa_backward_profiled(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                               const void* P, const float* dS, const float* lse, const float* S,
+                               const float* mass, float* dX, float* dP, void* ws,
+                               size_t ws_bytes, void* stream, sa_profile* prof) {
+  Prof p;
+  sa_status v = profile_setup(prof, &p);
+  if (v != SA_OK) return v;
+  v = backward_impl(pr, offsets_dev, X, P, dS, lse, S, mass, dX, dP, ws, ws_bytes, stream, &p);
+  prof->n_kernels = p.n;
+  return v;
 }
 
 sa_status sa_get_device_status(const void* ws, void* stream) {

@@ -1,7 +1,633 @@
-// sa_bwd.hip — Sketch Attention backward (placeholder until implemented).
+// sa_bwd.hip — Sketch Attention backward: dX and dP from dS.
+//
+// The pages state only that the sketch is fully differentiable (SequenceO1
+// reading notes, section 3.1, after Eq. (9)); the formulas are the chain rule
+// of Eq. (6)-(9) with the optional mass normalisation:
+//   G = dS, cv = 0                 (plain sum)
+//   G_j = dS_j / mu_j, cv_j = G_j . S_j          (mass norm, mu_j = 0 -> 0)
+//   dA'_ji = G_j . x_i,  w_ji = A_ji (dA'_ji - cv_j),  delta_i = sum_j w_ji
+//   dZ_ji = w_ji - A_ji delta_i
+//   dX_i = sum_j A_ji G_j + c sum_j dZ_ji p_j
+//        = g_i + c (b_i - delta_i a_i),  g = A^T G,  a = A^T P,  b = w^T P
+//   dP = c sum_u sum_i dZ_ji x_i
+// The softmax weights A are recomputed per tile from X, P and the forward's
+// per-token log-sum-exp; nothing of size k x n is stored.
+//
+// Kernels
+//  sa_bwd_prep:   G (input dtype) and cv per user and prototype.
+//  sa_bwdx_bf16:  token-stationary, one pass over all prototypes per token
+//                 tile: Z and dA' on the matrix cores (Z = P X^T orientation,
+//                 token per lane), then g^T, a^T, b^T += {G,P}^T {A,w} with
+//                 the A operands read transposed from LDS.  Writes dX and
+//                 delta.  10 k d MFMA flops per token.
+//  sa_bwdp_bf16:  prototype-stationary (256 prototypes per workgroup, like
+//                 the forward aggregation): Z^T, dA'^T, dZ, then
+//                 dP^T += X^T dZ^T.  One partial per token segment.  6 k d.
+//  sa_dp_reduce:  dP = c sum over segments in order (deterministic).
+// The fp32 variants do the same arithmetic on the vector ALU.
 #include "sa_device.h"
 #include "sa_kernels.h"
 
 namespace sa {
-hipError_t launch_bwd(const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+// ----------------------------------------------------------------------------
+// G and cv.  One group of D/4 threads per (user, prototype) row.
+template <typename OutT, int D>
+__global__ __launch_bounds__(256) void sa_bwd_prep(const float* __restrict__ dS,
+                                                   const float* __restrict__ S,
+                                                   const float* __restrict__ mass, int64_t rows,
+                                                   int mass_norm, OutT* __restrict__ Gq,
+                                                   float* __restrict__ cv) {
+  constexpr int TPR = D / 4;   // threads per row (8, 16 or 32)
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gt / TPR;
+  const int part = (int)(gt % TPR);
+  const bool live = row < rows;
+  const int64_t r = live ? row : 0;
+  f32x4 g = *(const f32x4*)(dS + r * D + 4 * part);
+  float c = 0.f;
+  if (mass_norm) {
+    const float mu = mass[r];
+    const float inv = mu > 0.f ? 1.0f / mu : 0.f;
+    g = mu > 0.f ? g * inv : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 s = *(const f32x4*)(S + r * D + 4 * part);
+    c = g[0] * s[0] + g[1] * s[1] + g[2] * s[2] + g[3] * s[3];
+  }
+#pragma unroll
+  for (int off = 1; off < TPR; off <<= 1) c += __shfl_xor(c, off, 64);
+  if (live) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Gq[r * D + 4 * part + e] = (OutT)g[e];
+    if (part == 0) cv[r] = mass_norm ? c : 0.f;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// bf16 dX pass.  grid = ceil(T / 128); block 256 = 4 waves x 32 tokens.
+// Tokens of the workgroup that belong to different users are handled one
+// user at a time (the others are masked), because G depends on the user.
+template <int D>
+__global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
+    const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
+    const bf16* __restrict__ P, const bf16* __restrict__ Gq, const float* __restrict__ cv, int k,
+    int64_t T, float alpha, float scale, const float* __restrict__ lse, float* __restrict__ dX,
+    float* __restrict__ delta_out) {
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int PCH = 64;                 // prototypes per LDS chunk
+  constexpr int ROW = D + 8;              // padded LDS row (elements)
+  constexpr int PIECES = PCH * D / 8;     // 16-byte pieces per matrix chunk
+  constexpr int PPT = PIECES / 256;       // per thread, per matrix
+  static_assert(PPT >= 1, "");
+  __shared__ __attribute__((aligned(16))) bf16 sP[2][PCH * ROW];
+  __shared__ __attribute__((aligned(16))) bf16 sG[2][PCH * ROW];
+  __shared__ __attribute__((aligned(16))) float sC[2][PCH];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int64_t r0 = (int64_t)blockIdx.x * kBwdxTokensBf16;
+  const int64_t r1 = r0 + kBwdxTokensBf16 < T ? r0 + kBwdxTokensBf16 : T;
+  const int64_t tok = r0 + wave * 32 + l32;
+
+  bf16x8 xb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    xb[ks] = tok < r1 ? *(const bf16x8*)(X + tok * D + 16 * ks + 8 * h) : bf16x8{};
+  const float l2 = tok < r1 ? lse[tok] * kLog2e : INFINITY;
+
+  const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
+  const int nch = (k + PCH - 1) / PCH;
+
+  int u = first_user_after(offsets, B, r0);
+  for (; u < B; ++u) {
+    const int64_t ulo = clamp64(offsets[u], r0, r1), uhi = clamp64(offsets[u + 1], ulo, r1);
+    if (ulo >= r1) break;
+    if (uhi <= ulo) continue;
+    const bool mine = tok >= ulo && tok < uhi;
+    const float lsh = mine ? l2 : INFINITY;
+    const bf16* Gu = Gq + (int64_t)u * k * D;
+    const float* cvu = cv + (int64_t)u * k;
+
+    bf16x8 rp[PPT], rg[PPT];
+    float rc = 0.f;
+    auto load_chunk = [&](int p0) {
+#pragma unroll
+      for (int e = 0; e < PPT; ++e) {
+        const int q = tid + 256 * e;
+        const int r = q / (D / 8), cp = q % (D / 8);
+        const int row = p0 + r;
+        rp[e] = row < k ? *(const bf16x8*)(P + (int64_t)row * D + 8 * cp) : bf16x8{};
+        rg[e] = row < k ? *(const bf16x8*)(Gu + (int64_t)row * D + 8 * cp) : bf16x8{};
+      }
+      if (tid < PCH) rc = p0 + tid < k ? cvu[p0 + tid] : 0.f;
+    };
+    auto store_chunk = [&](int buf) {
+#pragma unroll
+      for (int e = 0; e < PPT; ++e) {
+        const int q = tid + 256 * e;
+        const int r = q / (D / 8), cp = q % (D / 8);
+        *(bf16x8*)(&sP[buf][r * ROW + 8 * cp]) = rp[e];
+        *(bf16x8*)(&sG[buf][r * ROW + 8 * cp]) = rg[e];
+      }
+      if (tid < PCH) sC[buf][tid] = rc;
+    };
+
+    f32x16 ag[DB], aa[DB], ab[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { ag[db] = f32x16{}; aa[db] = f32x16{}; ab[db] = f32x16{}; }
+    float dsum = 0.f;
+
+    __syncthreads();   // previous user's last chunk fully consumed
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    for (int ci = 0; ci < nch; ++ci) {
+      const int p0 = ci * PCH;
+      const int buf = ci & 1;
+      if (ci + 1 < nch) load_chunk(p0 + PCH);
+      const SA_LDS bf16* ps = (const SA_LDS bf16*)&sP[buf][0];
+      const SA_LDS bf16* gs = (const SA_LDS bf16*)&sG[buf][0];
+      const SA_LDS float* cs = (const SA_LDS float*)&sC[buf][0];
+#pragma unroll
+      for (int pt = 0; pt < PCH / 32; ++pt) {
+        const int pbase = p0 + pt * 32;
+        if (pbase >= k) break;   // uniform
+        // Z and dA' tiles: rows = prototypes pbase + crow(i, h), column = token.
+        f32x16 z = {}, da = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 ap = *(const SA_LDS bf16x8*)(ps + (pt * 32 + l32) * ROW + 16 * ks + 8 * h);
+          const bf16x8 agr = *(const SA_LDS bf16x8*)(gs + (pt * 32 + l32) * ROW + 16 * ks + 8 * h);
+          z = mfma32(ap, xb[ks], z);
+          da = mfma32(agr, xb[ks], da);
+        }
+        f32x4 cq[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) cq[g4] = *(const SA_LDS f32x4*)(cs + pt * 32 + 8 * g4 + 4 * h);
+        const bool partial = pbase + 32 > k;
+        bf16x8 abf[2], wbf[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float a = exp2_fast(fmaf(z[i], alpha, -lsh));
+          if (partial && pbase + crow(i, h) >= k) a = 0.f;
+          const float w = a * (da[i] - cq[i >> 2][i & 3]);
+          dsum += w;
+          abf[i >> 3][i & 7] = (bf16)a;
+          wbf[i >> 3][i & 7] = (bf16)w;
+        }
+        // {g, a, b}^T (d x tokens) += {G, P, P}^T (d x prototypes) {A, A, w}.
+        // K slot j of half h in block kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int row0 = pt * 32 + 16 * kb + 4 * h + tr_r;
+            const int col = 32 * db + 16 * tr_half + 4 * tr_c;
+            const bf16x8 gT = concat4(lds_read_tr16(gs + row0 * ROW + col),
+                                      lds_read_tr16(gs + (row0 + 8) * ROW + col));
+            const bf16x8 pT = concat4(lds_read_tr16(ps + row0 * ROW + col),
+                                      lds_read_tr16(ps + (row0 + 8) * ROW + col));
+            ag[db] = mfma32(gT, abf[kb], ag[db]);
+            aa[db] = mfma32(pT, abf[kb], aa[db]);
+            ab[db] = mfma32(pT, wbf[kb], ab[db]);
+          }
+        }
+      }
+      if (ci + 1 < nch) store_chunk(buf ^ 1);
+      __syncthreads();
+    }
+
+    const float delta = dsum + shfl_xor32(dsum);
+    if (mine) {
+      // C layout: lane -> token, register i -> d = 32 db + crow(i, h).
+      float* dst = dX + tok * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g4 + r;
+            v[r] = ag[db][i] + scale * (ab[db][i] - delta * aa[db][i]);
+          }
+          *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * h) = v;
+        }
+      if (h == 0) delta_out[tok] = delta;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// bf16 dP pass.  grid = (Gb segments, nchunks); block 256 = 4 waves x 64
+// prototypes; the same tiling as the forward aggregation.
+template <int D>
+__global__ __launch_bounds__(256, 1) void sa_bwdp_bf16(
+    const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
+    const bf16* __restrict__ P, const bf16* __restrict__ Gq, const float* __restrict__ cv, int k,
+    int64_t T, int G, float alpha, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dpp) {
+  constexpr int KS = D / 16, DB = D / 32, PT = 2;
+  constexpr int KC = 4 * PT * 32;
+  constexpr int TILE = 32;
+  constexpr int ROW = D + 8;
+  constexpr int PIECES = TILE * D / 8;
+  constexpr int PPT = (PIECES + 255) / 256;
+
+  __shared__ __attribute__((aligned(16))) bf16 sX[2][TILE * ROW];
+  __shared__ __attribute__((aligned(16))) float sL[2][TILE];
+  __shared__ __attribute__((aligned(16))) float sD[2][TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int s = blockIdx.x, chunk = blockIdx.y;
+  const int pw0 = chunk * KC + wave * PT * 32;
+
+  bf16x8 pw[PT][KS], gw[PT][KS];
+  float cw[PT];
+#pragma unroll
+  for (int pt = 0; pt < PT; ++pt) {
+    const int row = pw0 + pt * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      pw[pt][ks] = row < k ? *(const bf16x8*)(P + (int64_t)row * D + 16 * ks + 8 * h) : bf16x8{};
+  }
+  auto load_user = [&](int u) {
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      const int row = pw0 + pt * 32 + l32;
+      const bf16* gr = Gq + ((int64_t)u * k + row) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        gw[pt][ks] = row < k ? *(const bf16x8*)(gr + 16 * ks + 8 * h) : bf16x8{};
+      cw[pt] = row < k ? cv[(int64_t)u * k + row] : 0.f;
+    }
+  };
+
+  f32x16 acc[PT][DB];
+#pragma unroll
+  for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[pt][db] = f32x16{};
+
+  const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
+  TileWalker<TILE> cur;
+  cur.start(offsets, B, lo, hi);
+  if (cur.valid) {
+    bf16x8 xr[PPT];
+    float lr = 0.f, dr = 0.f;
+    auto load_tile = [&](int64_t t0, int64_t t1) {
+#pragma unroll
+      for (int e = 0; e < PPT; ++e) {
+        const int q = tid + 256 * e;
+        const int r = q / (D / 8), cp = q % (D / 8);
+        xr[e] = (q < PIECES && t0 + r < t1) ? *(const bf16x8*)(X + (t0 + r) * D + 8 * cp) : bf16x8{};
+      }
+      if (tid < TILE) {
+        const bool in = t0 + tid < t1;
+        lr = in ? lse[t0 + tid] * kLog2e : INFINITY;
+        dr = in ? delta[t0 + tid] : 0.f;
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int e = 0; e < PPT; ++e) {
+        const int q = tid + 256 * e;
+        if (q < PIECES) {
+          const int r = q / (D / 8), cp = q % (D / 8);
+          *(bf16x8*)(&sX[buf][r * ROW + 8 * cp]) = xr[e];
+        }
+      }
+      if (tid < TILE) { sL[buf][tid] = lr; sD[buf][tid] = dr; }
+    };
+
+    const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
+    load_user(cur.user);
+    load_tile(cur.t0, cur.t1);
+    store_tile(0);
+    __syncthreads();
+    int buf = 0;
+    while (cur.valid) {
+      TileWalker<TILE> nxt = cur;
+      nxt.advance();
+      if (nxt.valid) load_tile(nxt.t0, nxt.t1);
+      const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
+      f32x16 z[PT], da[PT];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) { z[pt] = f32x16{}; da[pt] = f32x16{}; }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(const SA_LDS bf16x8*)(xs + l32 * ROW + 16 * ks + 8 * h);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          z[pt] = mfma32(a, pw[pt][ks], z[pt]);
+          da[pt] = mfma32(a, gw[pt][ks], da[pt]);
+        }
+      }
+      const SA_LDS float* ls = (const SA_LDS float*)&sL[buf][0];
+      const SA_LDS float* ds = (const SA_LDS float*)&sD[buf][0];
+      f32x4 lq[4], dq[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        lq[g4] = *(const SA_LDS f32x4*)(ls + 8 * g4 + 4 * h);
+        dq[g4] = *(const SA_LDS f32x4*)(ds + 8 * g4 + 4 * h);
+      }
+      bf16x8 zbf[PT][2];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = exp2_fast(fmaf(z[pt][i], alpha, -lq[i >> 2][i & 3]));
+          const float dz = a * (da[pt][i] - cw[pt] - dq[i >> 2][i & 3]);
+          zbf[pt][i >> 3][i & 7] = (bf16)dz;
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int row0 = 16 * kb + 4 * h + tr_r;
+          const int col = 32 * db + 16 * tr_half + 4 * tr_c;
+          const bf16x8 a = concat4(lds_read_tr16(xs + row0 * ROW + col),
+                                   lds_read_tr16(xs + (row0 + 8) * ROW + col));
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) acc[pt][db] = mfma32(a, zbf[pt][kb], acc[pt][db]);
+        }
+      }
+      if (nxt.valid && nxt.user != cur.user) load_user(nxt.user);
+      if (nxt.valid) store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+      cur = nxt;
+    }
+  }
+  // Flush this segment's partial: acc[pt][db] register i is
+  // dP[proto = pw0 + 32 pt + l32][d = 32 db + crow(i, h)] / c.
+#pragma unroll
+  for (int pt = 0; pt < PT; ++pt) {
+    const int proto = pw0 + pt * 32 + l32;
+    if (proto < k) {
+      float* dst = dpp + ((int64_t)s * k + proto) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 v = {acc[pt][db][4 * g4], acc[pt][db][4 * g4 + 1], acc[pt][db][4 * g4 + 2],
+                     acc[pt][db][4 * g4 + 3]};
+          *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * h) = v;
+        }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// fp32 dX pass.  grid = ceil(T / 32); block 256 = 32 tokens x 8 threads, each
+// thread owning D/8 columns.  Prototypes stream through LDS 32 at a time.
+template <int D>
+__global__ __launch_bounds__(256) void sa_bwdx_f32(
+    const int64_t* __restrict__ offsets, int B, const float* __restrict__ X,
+    const float* __restrict__ P, const float* __restrict__ Gq, const float* __restrict__ cv, int k,
+    int64_t T, float alpha, float scale, const float* __restrict__ lse, float* __restrict__ dX,
+    float* __restrict__ delta_out) {
+  constexpr int PC = 32, DS = D / 8;
+  __shared__ float sP[PC][D + 4];
+  __shared__ float sG[PC][D + 4];
+  __shared__ float sC[PC];
+  const int tid = threadIdx.x;
+  const int q = tid & 7;
+  const int64_t r0 = (int64_t)blockIdx.x * kBwdxTokensF32;
+  const int64_t r1 = r0 + kBwdxTokensF32 < T ? r0 + kBwdxTokensF32 : T;
+  const int64_t tok = r0 + (tid >> 3);
+  float x[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) x[e] = tok < r1 ? X[tok * D + q * DS + e] : 0.f;
+  const float l2 = tok < r1 ? lse[tok] * kLog2e : INFINITY;
+
+  int u = first_user_after(offsets, B, r0);
+  for (; u < B; ++u) {
+    const int64_t ulo = clamp64(offsets[u], r0, r1), uhi = clamp64(offsets[u + 1], ulo, r1);
+    if (ulo >= r1) break;
+    if (uhi <= ulo) continue;
+    const bool mine = tok >= ulo && tok < uhi;
+    const float lsh = mine ? l2 : INFINITY;
+    const float* Gu = Gq + (int64_t)u * k * D;
+    float g[DS], aa[DS], bb[DS];
+#pragma unroll
+    for (int e = 0; e < DS; ++e) { g[e] = 0.f; aa[e] = 0.f; bb[e] = 0.f; }
+    float dsum = 0.f;
+    for (int p0 = 0; p0 < k; p0 += PC) {
+      __syncthreads();
+      for (int i = tid; i < PC * D; i += 256) {
+        const int r = i / D, c = i % D;
+        const bool v = p0 + r < k;
+        sP[r][c] = v ? P[(int64_t)(p0 + r) * D + c] : 0.f;
+        sG[r][c] = v ? Gu[(int64_t)(p0 + r) * D + c] : 0.f;
+      }
+      if (tid < PC) sC[tid] = p0 + tid < k ? cv[(int64_t)u * k + p0 + tid] : 0.f;
+      __syncthreads();
+      const int np = k - p0 < PC ? k - p0 : PC;
+      for (int j = 0; j < np; ++j) {
+        float pz = 0.f, pg = 0.f;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) {
+          pz = fmaf(sP[j][q * DS + e], x[e], pz);
+          pg = fmaf(sG[j][q * DS + e], x[e], pg);
+        }
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+          pz += __shfl_xor(pz, off, 64);
+          pg += __shfl_xor(pg, off, 64);
+        }
+        const float a = exp2_fast(fmaf(pz, alpha, -lsh));
+        const float w = a * (pg - sC[j]);
+        dsum += w;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) {
+          g[e] = fmaf(a, sG[j][q * DS + e], g[e]);
+          aa[e] = fmaf(a, sP[j][q * DS + e], aa[e]);
+          bb[e] = fmaf(w, sP[j][q * DS + e], bb[e]);
+        }
+      }
+    }
+    if (mine) {
+#pragma unroll
+      for (int e = 0; e < DS; ++e) dX[tok * D + q * DS + e] = g[e] + scale * (bb[e] - dsum * aa[e]);
+      if (q == 0) delta_out[tok] = dsum;
+    }
+  }
+}
+
+// fp32 dP pass.  grid = (Gb, ceil(k / 32)); block 256: thread (j = t / 8,
+// q = t % 8) owns prototype j, columns q D/8 .. +D/8 of the partial, and
+// computes the weights of tokens 4q .. 4q+3 of each 32-token tile.
+template <int D>
+__global__ __launch_bounds__(256) void sa_bwdp_f32(
+    const int64_t* __restrict__ offsets, int B, const float* __restrict__ X,
+    const float* __restrict__ P, const float* __restrict__ Gq, const float* __restrict__ cv, int k,
+    int64_t T, int G, float alpha, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dpp) {
+  constexpr int PC = kChunkF32Bwd, TILE = 32, DS = D / 8;
+  __shared__ float sP[PC][D + 1];
+  __shared__ float sG[PC][D + 1];
+  __shared__ float sX[TILE][D + 1];
+  __shared__ float sZ[PC][TILE + 1];
+  __shared__ float sL[TILE], sDl[TILE], sC[PC];
+  const int tid = threadIdx.x;
+  const int j = tid >> 3, q = tid & 7;
+  const int s = blockIdx.x;
+  const int p0 = blockIdx.y * PC;
+  for (int i = tid; i < PC * D; i += 256) {
+    const int r = i / D, c = i % D;
+    sP[r][c] = (p0 + r < k) ? P[(int64_t)(p0 + r) * D + c] : 0.f;
+  }
+  float acc[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) acc[e] = 0.f;
+
+  const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
+  TileWalker<TILE> cur;
+  cur.start(offsets, B, lo, hi);
+  int loaded_user = -1;
+  while (cur.valid) {
+    __syncthreads();
+    if (cur.user != loaded_user) {
+      const float* Gu = Gq + (int64_t)cur.user * k * D;
+      for (int i = tid; i < PC * D; i += 256) {
+        const int r = i / D, c = i % D;
+        sG[r][c] = (p0 + r < k) ? Gu[(int64_t)(p0 + r) * D + c] : 0.f;
+      }
+      if (tid < PC) sC[tid] = p0 + tid < k ? cv[(int64_t)cur.user * k + p0 + tid] : 0.f;
+      loaded_user = cur.user;
+    }
+    for (int i = tid; i < TILE * D; i += 256) {
+      const int r = i / D, c = i % D;
+      sX[r][c] = (cur.t0 + r < cur.t1) ? X[(cur.t0 + r) * D + c] : 0.f;
+    }
+    if (tid < TILE) {
+      const bool in = cur.t0 + tid < cur.t1;
+      sL[tid] = in ? lse[cur.t0 + tid] * kLog2e : INFINITY;
+      sDl[tid] = in ? delta[cur.t0 + tid] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tt = 4 * q + t;
+      float z = 0.f, ga = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < D; ++e) {
+        z = fmaf(sP[j][e], sX[tt][e], z);
+        ga = fmaf(sG[j][e], sX[tt][e], ga);
+      }
+      const float a = exp2_fast(fmaf(z, alpha, -sL[tt]));
+      sZ[j][tt] = a * (ga - sC[j] - sDl[tt]);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int tt = 0; tt < TILE; ++tt) {
+      const float dz = sZ[j][tt];
+#pragma unroll
+      for (int e = 0; e < DS; ++e) acc[e] = fmaf(dz, sX[tt][q * DS + e], acc[e]);
+    }
+    cur.advance();
+  }
+  if (p0 + j < k) {
+    float* dst = dpp + ((int64_t)s * k + p0 + j) * D + q * DS;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) dst[e] = acc[e];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// dP = c * sum_s dpp[s] in segment order; block 0 also checks the offsets.
+__global__ __launch_bounds__(256) void sa_dp_reduce(const int64_t* __restrict__ offsets, int B,
+                                                    int64_t T, int k, int d, int G, float scale,
+                                                    const float* __restrict__ dpp,
+                                                    float* __restrict__ dP,
+                                                    uint32_t* __restrict__ status) {
+  if (blockIdx.x == 0) check_offsets_block(offsets, B, T, status, kStatusOk, kStatusBadOffsets);
+  const int64_t kd = (int64_t)k * d;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= kd) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (T > 0)
+    for (int s = 0; s < G; ++s) acc += *(const f32x4*)(dpp + (int64_t)s * kd + e);
+  *(f32x4*)(dP + e) = acc * scale;
+}
+
+// ----------------------------------------------------------------------------
+template <int D>
+static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof* prof) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const float alpha = scale * kLog2e;
+  hipError_t e;
+  if (a.recompute_lse && a.T > 0) {
+    FwdArgs f = {};
+    f.X = a.X; f.P = a.P; f.k = a.k; f.d = a.d; f.T = a.T; f.lse = a.lse_ws;
+    e = dtype == 1 ? launch_stats_bf16(f, st, prof) : launch_stats_f32(f, st, prof);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rows = (int64_t)a.B * a.k;
+  const unsigned nbp = (unsigned)((rows * (D / 4) + 255) / 256);
+  prof_begin(prof, "sa_bwd_prep", st);
+  if (dtype == 1)
+    hipLaunchKernelGGL((sa_bwd_prep<bf16, D>), dim3(nbp), dim3(256), 0, st, a.dS, a.S, a.mass, rows,
+                       a.mass_norm, (bf16*)a.Gq, a.cv);
+  else
+    hipLaunchKernelGGL((sa_bwd_prep<float, D>), dim3(nbp), dim3(256), 0, st, a.dS, a.S, a.mass,
+                       rows, a.mass_norm, (float*)a.Gq, a.cv);
+  e = hipGetLastError();
+  prof_end(prof, st);
+  if (e != hipSuccess) return e;
+  if (a.T > 0) {
+    if (dtype == 1) {
+      const unsigned nbx = (unsigned)((a.T + kBwdxTokensBf16 - 1) / kBwdxTokensBf16);
+      prof_begin(prof, "sa_bwdx_bf16", st);
+      hipLaunchKernelGGL(sa_bwdx_bf16<D>, dim3(nbx), dim3(256), 0, st, a.offsets, a.B,
+                         (const bf16*)a.X, (const bf16*)a.P, (const bf16*)a.Gq, a.cv, a.k, a.T,
+                         alpha, scale, a.lse, a.dX, a.delta);
+      e = hipGetLastError();
+      prof_end(prof, st);
+      if (e != hipSuccess) return e;
+      prof_begin(prof, "sa_bwdp_bf16", st);
+      hipLaunchKernelGGL(sa_bwdp_bf16<D>, dim3(a.Gb, a.bnchunks), dim3(256), 0, st, a.offsets, a.B,
+                         (const bf16*)a.X, (const bf16*)a.P, (const bf16*)a.Gq, a.cv, a.k, a.T,
+                         a.Gb, alpha, a.lse, a.delta, a.dpp);
+      e = hipGetLastError();
+      prof_end(prof, st);
+      if (e != hipSuccess) return e;
+    } else {
+      const unsigned nbx = (unsigned)((a.T + kBwdxTokensF32 - 1) / kBwdxTokensF32);
+      prof_begin(prof, "sa_bwdx_f32", st);
+      hipLaunchKernelGGL(sa_bwdx_f32<D>, dim3(nbx), dim3(256), 0, st, a.offsets, a.B,
+                         (const float*)a.X, (const float*)a.P, (const float*)a.Gq, a.cv, a.k, a.T,
+                         alpha, scale, a.lse, a.dX, a.delta);
+      e = hipGetLastError();
+      prof_end(prof, st);
+      if (e != hipSuccess) return e;
+      prof_begin(prof, "sa_bwdp_f32", st);
+      hipLaunchKernelGGL(sa_bwdp_f32<D>, dim3(a.Gb, a.bnchunks), dim3(256), 0, st, a.offsets, a.B,
+                         (const float*)a.X, (const float*)a.P, (const float*)a.Gq, a.cv, a.k, a.T,
+                         a.Gb, alpha, a.lse, a.delta, a.dpp);
+      e = hipGetLastError();
+      prof_end(prof, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  const int64_t kd = (int64_t)a.k * a.d;
+  prof_begin(prof, "sa_dp_reduce", st);
+  hipLaunchKernelGGL(sa_dp_reduce, dim3((unsigned)((kd / 4 + 255) / 256)), dim3(256), 0, st,
+                     a.offsets, a.B, a.T, a.k, a.d, a.Gb, scale, a.dpp, a.dP, a.status);
+  e = hipGetLastError();
+  prof_end(prof, st);
+  return e;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st, Prof* prof) {
+  switch (a.d) {
+    case 32: return launch_bwd_t<32>(a, dtype, st, prof);
+    case 64: return launch_bwd_t<64>(a, dtype, st, prof);
+    case 128: return launch_bwd_t<128>(a, dtype, st, prof);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace sa

@@ -133,29 +133,51 @@ __global__ __launch_bounds__(256) void sa_agg_f32(const int64_t* __restrict__ of
 }
 
 template <int D>
-static hipError_t launch_fwd_f32_t(const FwdArgs& a, hipStream_t st) {
+static hipError_t launch_stats_f32_t(const FwdArgs& a, hipStream_t st, Prof* prof) {
+  const float scale = 1.0f / sqrtf((float)D);
+  const float alpha = scale * kLog2e;
+  const unsigned nb = (unsigned)((a.T + 255) / 256);
+  prof_begin(prof, "sa_stats_f32", st);
+  hipLaunchKernelGGL(sa_stats_f32<D>, dim3(nb), dim3(256), 0, st, (const float*)a.X,
+                     (const float*)a.P, a.k, a.T, alpha, scale, a.lse);
+  const hipError_t e = hipGetLastError();
+  prof_end(prof, st);
+  return e;
+}
+
+template <int D>
+static hipError_t launch_fwd_f32_t(const FwdArgs& a, hipStream_t st, Prof* prof) {
   const float scale = 1.0f / sqrtf((float)D);
   const float alpha = scale * kLog2e;
   if (a.T > 0) {
-    const unsigned nb = (unsigned)((a.T + 255) / 256);
-    hipLaunchKernelGGL(sa_stats_f32<D>, dim3(nb), dim3(256), 0, st, (const float*)a.X,
-                       (const float*)a.P, a.k, a.T, alpha, scale, a.lse);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_stats_f32_t<D>(a, st, prof);
     if (e != hipSuccess) return e;
+    prof_begin(prof, "sa_agg_f32", st);
     hipLaunchKernelGGL(sa_agg_f32<D>, dim3(a.G, a.nchunks), dim3(256), 0, st, a.offsets, a.B,
                        (const float*)a.X, (const float*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part,
                        a.pmass);
     e = hipGetLastError();
+    prof_end(prof, st);
     if (e != hipSuccess) return e;
   }
-  return launch_reduce(a, st);
+  return launch_reduce(a, st, prof);
 }
 
-hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_stats_f32(const FwdArgs& a, hipStream_t st, Prof* prof) {
+  if (a.T == 0) return hipSuccess;
   switch (a.d) {
-    case 32: return launch_fwd_f32_t<32>(a, st);
-    case 64: return launch_fwd_f32_t<64>(a, st);
-    case 128: return launch_fwd_f32_t<128>(a, st);
+    case 32: return launch_stats_f32_t<32>(a, st, prof);
+    case 64: return launch_stats_f32_t<64>(a, st, prof);
+    case 128: return launch_stats_f32_t<128>(a, st, prof);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st, Prof* prof) {
+  switch (a.d) {
+    case 32: return launch_fwd_f32_t<32>(a, st, prof);
+    case 64: return launch_fwd_f32_t<64>(a, st, prof);
+    case 128: return launch_fwd_f32_t<128>(a, st, prof);
   }
   return hipErrorInvalidValue;
 }

@@ -11,8 +11,11 @@ namespace sa {
 // Work partition constants (MI355X: 256 compute units, one aggregation
 // workgroup per unit).
 constexpr int kTargetWorkgroups = 256;
-constexpr int kChunkBf16 = 256;   // prototypes per bf16 aggregation workgroup
-constexpr int kChunkF32 = 64;     // prototypes per fp32 aggregation workgroup
+constexpr int kChunkBf16 = 256;     // prototypes per bf16 prototype-stationary workgroup
+constexpr int kChunkF32 = 64;       // prototypes per fp32 forward aggregation workgroup
+constexpr int kChunkF32Bwd = 32;    // prototypes per fp32 backward dP workgroup
+constexpr int kBwdxTokensBf16 = 128;  // tokens per bf16 dX workgroup
+constexpr int kBwdxTokensF32 = 32;    // tokens per fp32 dX workgroup
 
 // Device status word values written into the first bytes of the workspace.
 constexpr uint32_t kStatusOk = 0u;
@@ -23,14 +26,15 @@ struct Plan {
   int64_t T;
   int dtype;            // 0 = fp32, 1 = bf16
   bool mass_norm;
-  int chunk;            // prototypes per aggregation workgroup
-  int nchunks;          // ceil(k / chunk)
-  int G;                // token segments
+  // forward
+  int chunk, nchunks, G;
   int64_t nslots;       // G + B - 1 partial slots
+  // backward (dP pass)
+  int bchunk, bnchunks, Gb;
   // forward workspace layout (byte offsets)
   size_t off_status, off_lse, off_part, off_pmass, fwd_bytes;
   // backward workspace layout (byte offsets)
-  size_t off_G, off_cv, off_g, off_delta, off_dxp, off_dpp, off_blse, bwd_bytes;
+  size_t off_G, off_cv, off_delta, off_dpp, off_blse, bwd_bytes;
 };
 
 // Fills the plan; returns false for an unsupported problem.
@@ -59,27 +63,51 @@ struct BwdArgs {
   const void* X;
   const void* P;
   const float* dS;     // [B, k, d]
-  const float* lse;    // [T]
-  float* lse_ws;       // [T] workspace for a recomputed lse
+  const float* lse;    // [T] (caller's, or lse_ws after recomputation)
+  float* lse_ws;       // [T]
   const float* S;      // [B, k, d] (mass norm only)
   const float* mass;   // [B, k]    (mass norm only)
   float* dX;           // [T, d]
   float* dP;           // [k, d]
-  void* Gq;            // [B, k, d] G in the input dtype
-  float* cv;           // [B, k]
-  float* g;            // [T, d]
+  void* Gq;            // [B, k, d] G = dS (or dS / mass) in the input dtype
+  float* cv;           // [B, k]    G[j] . S[j] (mass norm) or 0
   float* delta;        // [T]
-  float* dxp;          // [nchunks, T, d]
-  float* dpp;          // [G, k, d]
+  float* dpp;          // [Gb, k, d] dP partial per segment
   uint32_t* status;
-  int G, nchunks;
+  int Gb, bnchunks;
   int mass_norm;
   int recompute_lse;
 };
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
-hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
-hipError_t launch_reduce(const FwdArgs& a, hipStream_t st);
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+// Optional per-kernel timing: when ev is non-null, the launchers record
+// ev[2i] / ev[2i+1] on the launch stream right before / after the i-th kernel
+// and store a static name for it.
+struct Prof {
+  hipEvent_t* ev;
+  int cap;
+  int n;
+  const char** names;
+};
+
+inline void prof_begin(Prof* p, const char* name, hipStream_t st) {
+  if (p != nullptr && p->ev != nullptr && p->n < p->cap) {
+    p->names[p->n] = name;
+    (void)hipEventRecord(p->ev[2 * p->n], st);
+  }
+}
+
+inline void prof_end(Prof* p, hipStream_t st) {
+  if (p != nullptr && p->ev != nullptr && p->n < p->cap) {
+    (void)hipEventRecord(p->ev[2 * p->n + 1], st);
+    p->n++;
+  }
+}
+
+hipError_t launch_stats_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
+hipError_t launch_stats_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
+hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof);
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st, Prof* prof);
 
 }  // namespace sa

@@ -18,15 +18,7 @@ __global__ __launch_bounds__(256) void sa_reduce_kernel(
     float* __restrict__ mass, int mass_norm, uint32_t* __restrict__ status) {
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
-  if (blockIdx.y == 0 && u == 0) {
-    __shared__ int bad;
-    if (tid == 0) bad = (offsets[0] != 0 || offsets[B] != T) ? 1 : 0;
-    __syncthreads();
-    for (int i = tid; i < B; i += 256)
-      if (offsets[i + 1] < offsets[i]) bad = 1;
-    __syncthreads();
-    if (tid == 0) *status = bad ? kStatusBadOffsets : kStatusOk;
-  }
+  if (blockIdx.y == 0 && u == 0) check_offsets_block(offsets, B, T, status, kStatusOk, kStatusBadOffsets);
   const int64_t kd = (int64_t)k * d;
   const int64_t e = ((int64_t)blockIdx.y * 256 + tid) * 4;
   if (e >= kd) return;
@@ -51,12 +43,15 @@ __global__ __launch_bounds__(256) void sa_reduce_kernel(
   if (mass != nullptr && (e % d) == 0) mass[(int64_t)u * k + j] = mu;
 }
 
-hipError_t launch_reduce(const FwdArgs& a, hipStream_t st) {
+hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof) {
   const int64_t kd = (int64_t)a.k * a.d;
   const unsigned gy = (unsigned)((kd / 4 + 255) / 256);
+  prof_begin(prof, "sa_reduce", st);
   hipLaunchKernelGGL(sa_reduce_kernel, dim3(a.B, gy), dim3(256), 0, st, a.offsets, a.B, a.k, a.d,
                      a.T, a.G, a.part, a.pmass, a.S, a.mass, a.mass_norm, a.status);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  prof_end(prof, st);
+  return e;
 }
 
 }  // namespace sa

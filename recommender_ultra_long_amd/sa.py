@@ -35,14 +35,23 @@ SA_FLAG_MASS_NORM = 1
 SA_OP_FORWARD = 0
 SA_OP_BACKWARD = 1
 
+SA_PROFILE_MAX_KERNELS = 8
+
 EXPORTED = ("sa_version", "sa_status_string", "sa_validate", "sa_workspace_size",
-            "sa_forward", "sa_backward", "sa_get_device_status")
+            "sa_forward", "sa_backward", "sa_forward_profiled", "sa_backward_profiled",
+            "sa_get_device_status")
 
 
 class SaProblem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("k", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("total_tokens", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("flags", ctypes.c_uint32)]
+
+
+class SaProfile(ctypes.Structure):
+    _fields_ = [("events", ctypes.c_void_p * (2 * SA_PROFILE_MAX_KERNELS)),
+                ("n_kernels", ctypes.c_int32),
+                ("names", ctypes.c_char_p * SA_PROFILE_MAX_KERNELS)]
 
 
 class SAError(RuntimeError):
@@ -78,6 +87,12 @@ def load():
     lib.sa_forward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_backward.restype = i32
     lib.sa_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sa_forward_profiled.restype = i32
+    lib.sa_forward_profiled.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                        ctypes.POINTER(SaProfile)]
+    lib.sa_backward_profiled.restype = i32
+    lib.sa_backward_profiled.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                         ctypes.POINTER(SaProfile)]
     lib.sa_get_device_status.restype = i32
     lib.sa_get_device_status.argtypes = [vp, vp]
     _lib = lib
@@ -134,8 +149,30 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+class KernelTimer:
+    """Caller-owned events for the *_profiled entry points.  After a call and a
+    synchronisation, times() returns [(kernel name, milliseconds)]."""
+
+    def __init__(self):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * SA_PROFILE_MAX_KERNELS)]
+        st = torch.cuda.current_stream()
+        for e in self.events:          # torch creates the HIP event on first record
+            e.record(st)
+        torch.cuda.synchronize()
+        self.prof = SaProfile()
+        for i, e in enumerate(self.events):
+            self.prof.events[i] = ctypes.c_void_p(e.cuda_event)
+
+    def times(self):
+        out = []
+        for i in range(self.prof.n_kernels):
+            name = self.prof.names[i].decode()
+            out.append((name, self.events[2 * i].elapsed_time(self.events[2 * i + 1])))
+        return out
+
+
 def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, workspace=None,
-               stream=None, want_lse=True, want_mass=True):
+               stream=None, want_lse=True, want_mass=True, timer=None):
     """Calls sa_forward.  offsets: int64 [B+1] (device tensor, or host array
     copied to X's device); X [T, d] and P [k, d] float32 or bfloat16 on the
     GPU.  Returns (S [B, k, d] f32, lse [T] f32 or None, mass [B, k] f32 or
@@ -155,16 +192,19 @@ def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, work
         mass = torch.empty((B, k), dtype=torch.float32, device=dev)
     ws_bytes = workspace_size(pr, SA_OP_FORWARD)
     ws = _workspace(ws_bytes, dev, workspace)
-    st = lib.sa_forward(ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(S), _ptr(lse),
-                        _ptr(mass), _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
-                        _stream_handle(stream))
+    args = (ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(S), _ptr(lse), _ptr(mass),
+            _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    if timer is None:
+        st = lib.sa_forward(*args)
+    else:
+        st = lib.sa_forward_profiled(*args, ctypes.byref(timer.prof))
     if st != SA_OK:
         raise SAError(st, "sa_forward")
     return S, lse, mass
 
 
 def sa_backward(offsets, X, P, dS, lse=None, S=None, mass=None, mass_norm=False, dX=None,
-                dP=None, workspace=None, stream=None):
+                dP=None, workspace=None, stream=None, timer=None):
     """Calls sa_backward.  Returns (dX [T, d] f32, dP [k, d] f32)."""
     lib = load()
     dev = P.device
@@ -179,9 +219,13 @@ def sa_backward(offsets, X, P, dS, lse=None, S=None, mass=None, mass_norm=False,
         dP = torch.empty((k, d), dtype=torch.float32, device=dev)
     ws_bytes = workspace_size(pr, SA_OP_BACKWARD)
     ws = _workspace(ws_bytes, dev, workspace)
-    st = lib.sa_backward(ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(dS), _ptr(lse),
-                         _ptr(S), _ptr(mass), _ptr(dX), _ptr(dP), _ptr(ws),
-                         ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    args = (ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(dS), _ptr(lse), _ptr(S),
+            _ptr(mass), _ptr(dX), _ptr(dP), _ptr(ws),
+            ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    if timer is None:
+        st = lib.sa_backward(*args)
+    else:
+        st = lib.sa_backward_profiled(*args, ctypes.byref(timer.prof))
     if st != SA_OK:
         raise SAError(st, "sa_backward")
     return dX, dP
