@@ -1,0 +1,313 @@
+"""Benchmark of the Sketch Attention hot path on one MI355X.
+
+One step = sa_forward + sa_backward (every step of the path: ragged
+scheduling, affinities, per-token softmax statistics, aggregation, split-n
+reduction, and the backward with recomputed softmax weights) over the
+single-user workload n = 100,000 history tokens, k = 1024 prototypes,
+d = 128, bf16 inputs with fp32 accumulation, seeded synthetic data
+(X ~ N(0,1), P ~ N(0,1/d), dS ~ N(0,1)) already resident in GPU memory.
+
+Prints one JSON line: history tokens/s of the whole step, the roofline of
+the dominant kernel (per-kernel durations measured with HIP events recorded
+on the launch stream by the library's profiled entry points), the forward
+alone against the bf16 matrix-core peak, and the float64 CPU oracle timed on
+a bounded sample of the same input.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "history tokens/s sketched + % bf16 MFMA peak, SA fwd/bwd k=1024 d=128 n≤100K"
+WORKLOAD = "bf16_n100k_k1024_d128"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30          # calibration copy: reads and writes 1 GiB
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-reps", type=int, default=None,
+                    help="calls timed per kernel (default: --steps)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch one plain device copy of COPY_BYTES (for counter scaling)")
+    ap.add_argument("--parse-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-calibration run into profiles/traffic.json and exit")
+    return ap.parse_args()
+
+
+def _kernel_algorithmic(name, k, d, T):
+    """Algorithmic work credited to each kernel (flop, HBM bytes).
+
+    Forward: 4 k d flop per token, all of it done by the aggregation kernel
+    (both products); the statistics pass is recomputation and is not credited.
+    Backward: 10 k d per token = recomputed affinities (2) + dA (2) + g (2)
+    + the dZ P product (2), all in the dX kernel, + dZ X (2) in the dP kernel.
+    Bytes: each pass's compulsory traffic (X read, per-token statistics,
+    outputs)."""
+    bx = 2 * d           # bf16 X row
+    if name == "sa_agg_bf16":
+        return 4.0 * k * d * T, T * (bx + 4)
+    if name == "sa_stats_bf16":
+        return 0.0, T * (bx + 4)
+    if name == "sa_bwdx_bf16":
+        return 8.0 * k * d * T, T * (bx + 4 + 4 * d + 4)
+    if name == "sa_bwdp_bf16":
+        return 2.0 * k * d * T, T * (bx + 8)
+    return 0.0, 0.0
+
+
+def _traffic_for(kernel, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    if not ent or ent.get("source_sha256") != src_hash:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def _parse_traffic(fetch_csv, write_csv):
+    """Scale the per-dispatch FETCH_SIZE / WRITE_SIZE readings (KiB) of every
+    Sketch Attention kernel by the factor that maps the calibration copy's
+    readings onto its known byte counts, average per kernel, and store the
+    result with the hash of the kernel sources it was taken on."""
+    import csv
+    import statistics
+
+    def load(path, counter):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return per
+
+    fetch = load(fetch_csv, "FETCH_SIZE")
+    write = load(write_csv, "WRITE_SIZE")
+
+    def copy_reading(per):
+        # the calibration copy is the largest copy dispatch of the run
+        cands = [x for n, v in per.items() if "copybuffer" in n.lower() for x in v]
+        return max(cands)
+
+    f_scale = COPY_BYTES / copy_reading(fetch)
+    w_scale = COPY_BYTES / copy_reading(write)
+    out = {"source_sha256": _source_hash(), "copy_bytes": COPY_BYTES,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for name in fetch:
+        short = name.split("(")[0].replace("void ", "").split("::")[-1].split("<")[0]
+        if not short.startswith("sa_"):
+            continue
+        fb = statistics.median(fetch[name]) * f_scale
+        wb = statistics.median(write.get(name, [0.0])) * w_scale
+        ent = out["kernels"].setdefault(short, {"source_sha256": out["source_sha256"]})
+        ent["fetch_bytes_per_launch"] = fb
+        ent["write_bytes_per_launch"] = wb
+        ent["hbm_bytes_per_launch"] = fb + wb
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recommender_ultra_long_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()
+
+
+def _cpu_baseline(prob, budget_s=15.0):
+    """The float64 oracle, as it stands, on the first n_s tokens of the same
+    input: forward + backward, n_s sized for about budget_s seconds."""
+    import numpy as np
+    from oracle.sa_ref import sa_backward_ref, sa_forward_ref
+    from recommender_ultra_long_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    P64 = synth.to_f64(prob.P)
+    dS64 = synth.to_f64(prob.dS)
+
+    def run(n):
+        X64 = synth.to_f64(prob.X[:n])
+        off = np.array([0, n], dtype=np.int64)
+        t0 = time.perf_counter()
+        sa_forward_ref(off, X64, P64, prob.mass_norm)
+        sa_backward_ref(off, X64, P64, dS64[:1], prob.mass_norm)
+        return time.perf_counter() - t0
+
+    T = prob.total_tokens
+    n0 = min(T, 2048)
+    t0 = run(n0)
+    n = int(min(T, max(n0, n0 * budget_s / max(t0, 1e-6))))
+    t = run(n) if n != n0 else t0
+    return {"value": n / t, "unit": "history tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} tokens of the {T}-token user, sa_forward_ref + sa_backward_ref "
+                      f"(float64 numpy), {t:.1f} s on {os.cpu_count()} host CPUs",
+            "seconds": t, "tokens": n}
+
+
+def main():
+    args = _parse()
+    if args.parse_traffic:
+        _parse_traffic(*args.parse_traffic)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from recommender_ultra_long_amd import sa, synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    prob = synth.make_workload(args.workload, device=dev, with_dS=True)
+    w = prob.workload
+    T, k, d = prob.total_tokens, w.k, w.d
+    off = torch.as_tensor(prob.offsets, device=dev)
+    B = len(prob.offsets) - 1
+    S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((T,), dtype=torch.float32, device=dev)
+    mass = torch.empty((B, k), dtype=torch.float32, device=dev)
+    dX = torch.empty((T, d), dtype=torch.float32, device=dev)
+    dP = torch.empty((k, d), dtype=torch.float32, device=dev)
+    pr = sa.make_problem(B, k, d, T, prob.X.dtype, prob.mass_norm)
+    wsf = torch.empty(sa.workspace_size(pr, sa.SA_OP_FORWARD), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(sa.workspace_size(pr, sa.SA_OP_BACKWARD), dtype=torch.uint8, device=dev)
+
+    def fwd(timer=None):
+        sa.sa_forward(off, prob.X, prob.P, prob.mass_norm, S=S, lse=lse, mass=mass, workspace=wsf,
+                      timer=timer)
+
+    def bwd(timer=None):
+        sa.sa_backward(off, prob.X, prob.P, prob.dS, lse, S, mass, prob.mass_norm, dX=dX, dP=dP,
+                       workspace=wsb, timer=timer)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    def timed(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    reps = args.profile_reps or args.steps
+    ms_fwd = timed(fwd, reps)
+    ms_bwd = timed(bwd, reps)
+
+    # Per-kernel durations from events recorded around each kernel.
+    per_kernel = {}
+    for fn in (fwd, bwd):
+        for _ in range(reps):
+            tm = sa.KernelTimer()
+            fn(tm)
+            torch.cuda.synchronize()
+            for name, ms in tm.times():
+                per_kernel.setdefault(name, []).append(ms)
+    kern_ms = {n: sum(v) / len(v) for n, v in per_kernel.items()}
+
+    def roofline(name):
+        fl, by = _kernel_algorithmic(name, k, d, T)
+        ms = kern_ms[name]
+        ach = fl / (ms * 1e-3) / 1e12
+        return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": _traffic_for(name, _source_hash()),
+                "avg_launch_ms": round(ms, 5), "algorithmic_flop": fl,
+                "algorithmic_bytes": by,
+                "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1)}
+
+    dominant = max(kern_ms, key=kern_ms.get)
+    fwd_flop = 4.0 * k * d * T
+    bwd_flop = 10.0 * k * d * T
+    tokens_s = T / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "history tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "users": B, "tokens": T, "k": k, "d": d,
+                   "mass_norm": bool(prob.mass_norm),
+                   "step": "sa_forward + sa_backward", "inputs": "resident in HBM"},
+        "roofline": roofline(dominant),
+        "forward": {"ms": round(ms_fwd, 5), "tokens_per_s": round(T / (ms_fwd * 1e-3), 1),
+                    "tflops": round(fwd_flop / (ms_fwd * 1e-3) / 1e12, 2),
+                    "frac_bf16_peak": round(fwd_flop / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "roofline_aggregation_kernel": roofline("sa_agg_bf16")},
+        "backward": {"ms": round(ms_bwd, 5), "tokens_per_s": round(T / (ms_bwd * 1e-3), 1),
+                     "tflops": round(bwd_flop / (ms_bwd * 1e-3) / 1e12, 2),
+                     "frac_bf16_peak": round(bwd_flop / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "step_tflops": round((fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12, 2),
+        "kernel_avg_ms": {n: round(v, 5) for n, v in kern_ms.items()},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(prob)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,7 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/sa.h"
+#include "sa.h"
 #include "sa_kernels.h"
 
 namespace sa {

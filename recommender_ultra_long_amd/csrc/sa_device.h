@@ -81,6 +81,14 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// Load of a value that is the same for every lane, kept in scalar registers.
+__device__ __forceinline__ int64_t uload64(const int64_t* p) {
+  const uint64_t v = (uint64_t)*p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // First user whose row range ends after token t (offsets[u+1] > t).
 // Offsets are read as they are and every result is clamped, so corrupt
 // offsets cannot cause an out-of-range user index.
@@ -88,7 +96,7 @@ __device__ __forceinline__ int first_user_after(const int64_t* offsets, int B, i
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
-    if (offsets[mid + 1] <= t) lo = mid + 1; else hi = mid;
+    if (uload64(offsets + mid + 1) <= t) lo = mid + 1; else hi = mid;
   }
   return lo;
 }
@@ -126,7 +134,7 @@ struct TileWalker {
     if (!valid) return;
     user = first_user_after(off, nb, lo);
     t0 = lo;
-    piece_end = clamp64(off[user + 1], t0, hi);
+    piece_end = clamp64(uload64(off + user + 1), t0, hi);
     if (piece_end <= t0) piece_end = hi;   // only with corrupt offsets
     t1 = t0 + TILE < piece_end ? t0 + TILE : piece_end;
   }
@@ -139,10 +147,10 @@ struct TileWalker {
       t0 = piece_end;
       // next user with a non-empty range starting at t0
       int u = user + 1;
-      while (u < B - 1 && offsets[u + 1] <= t0) ++u;
+      while (u < B - 1 && uload64(offsets + u + 1) <= t0) ++u;
       if (u > B - 1) u = B - 1;
       user = u;
-      piece_end = clamp64(offsets[u + 1], t0, seg_end);
+      piece_end = clamp64(uload64(offsets + u + 1), t0, seg_end);
       if (piece_end <= t0) piece_end = seg_end;   // only with corrupt offsets
     }
     t1 = t0 + TILE < piece_end ? t0 + TILE : piece_end;

@@ -148,23 +148,35 @@ __global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
 
 // ----------------------------------------------------------------------------
 // Pass 2: partial sketches per (segment, user) piece for one 256-prototype
-// chunk.  grid = (G segments, nchunks); block = 256 threads (4 waves).
-template <int D>
-__global__ __launch_bounds__(256, 1) void sa_agg_bf16(
+// chunk.  grid = (G segments, nchunks); block = 256 threads (4 waves, one per
+// SIMD), each wave owning 64 prototypes: their rows as MFMA B operands in
+// VGPRs and their 64 x D fp32 partial sketch in AGPRs.
+//
+// The token stream of the segment is cut into 32-token tiles that never
+// straddle two users, staged in LDS (three buffers, two tiles ahead) and
+// software pipelined: while the vector ALU turns tile t's affinities into
+// softmax weights, the matrix cores already compute tile t+1's affinities.
+template <int D, bool MASS, int NW, int PT>
+__global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ P, int k, int64_t T, int G, float alpha,
     const float* __restrict__ lse, float* __restrict__ part, float* __restrict__ pmass) {
   constexpr int KS = D / 16;             // reduction steps of the affinity product
   constexpr int DB = D / 32;             // 32-row blocks of the transposed sketch
-  constexpr int PT = 2;                  // 32-prototype tiles per wave
-  constexpr int KC = 4 * PT * 32;        // prototypes per workgroup
+  constexpr int NT = NW * 64;            // threads per workgroup
+  constexpr int KC = NW * PT * 32;       // prototypes per workgroup
+  static_assert(KC == kChunkBf16, "one workgroup covers one prototype chunk");
   constexpr int TILE = 32;               // tokens per step
-  constexpr int ROW = D + 8;             // LDS row pitch in elements (16 B pad)
+  // LDS row pitch: D + 24 elements makes the pitch 12 words mod 64 banks, so
+  // both the 16-byte row reads (16 lanes, 16 rows) and the transpose reads
+  // (4 rows x 32 bytes per 16 lanes) hit distinct banks.
+  constexpr int ROW = D + 24;
   constexpr int PIECES = TILE * D / 8;   // 16-byte pieces per tile
-  constexpr int PPT = (PIECES + 255) / 256;
+  constexpr int PPT = (PIECES + NT - 1) / NT;
+  constexpr int NBUF = 3;
 
-  __shared__ __attribute__((aligned(16))) bf16 sX[2][TILE * ROW];
-  __shared__ __attribute__((aligned(16))) float sL[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sX[NBUF][TILE * ROW];
+  __shared__ __attribute__((aligned(16))) float sL[NBUF][TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -186,135 +198,165 @@ __global__ __launch_bounds__(256, 1) void sa_agg_bf16(
   TileWalker<TILE> cur;
   cur.start(offsets, B, lo, hi);
   if (!cur.valid) return;
+  TileWalker<TILE> n1 = cur;
+  n1.advance();
+  TileWalker<TILE> n2 = n1;
+  if (n2.valid) n2.advance();
 
   // Staging of one tile: rows [t0, t1) of X and lse * log2(e); rows past t1
   // are zero with lse = +inf, so they contribute exactly nothing.
   bf16x8 xr[PPT];
   float lr = 0.f;
-  auto load_tile = [&](int64_t t0, int64_t t1) {
+  // Branch-free: every lane loads an in-range row (clamped) and a select
+  // zeroes what lies outside [t0, t1), so the loop body stays one basic block.
+  auto load_tile = [&](bool valid, int64_t t0, int64_t t1) {
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
-      const int q = tid + 256 * e;
-      const int r = q / (D / 8), cp = q % (D / 8);
-      xr[e] = (q < PIECES && t0 + r < t1) ? *(const bf16x8*)(X + (t0 + r) * D + 8 * cp) : bf16x8{};
+      const int q = tid + NT * e;
+      const int qc = q < PIECES ? q : PIECES - 1;
+      const int r = qc / (D / 8), cp = qc % (D / 8);
+      const bool in = valid && q < PIECES && t0 + r < t1;
+      const int64_t row = in ? t0 + r : 0;
+      const bf16x8 v = *(const bf16x8*)(X + row * D + 8 * cp);
+      xr[e] = in ? v : bf16x8{};
     }
-    if (tid < TILE) lr = (t0 + tid < t1) ? lse[t0 + tid] * kLog2e : INFINITY;
+    // raw value; the scaling happens at the LDS store, after the load landed
+    const bool lin = valid && t0 + (tid & (TILE - 1)) < t1;
+    const float lv = lse[lin ? t0 + (tid & (TILE - 1)) : 0];
+    lr = lin ? lv : INFINITY;
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
-      const int q = tid + 256 * e;
+      const int q = tid + NT * e;
       if (q < PIECES) {
         const int r = q / (D / 8), cp = q % (D / 8);
         *(bf16x8*)(&sX[buf][r * ROW + 8 * cp]) = xr[e];
       }
     }
-    if (tid < TILE) sL[buf][tid] = lr;
+    if (tid < TILE) sL[buf][tid] = lr * kLog2e;
+  };
+  // Z^T tile (32 tokens x 32 prototypes per pt) of the tile in buffer buf.
+  auto affinities = [&](int buf, f32x16 (&z)[PT]) {
+    const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
+    bf16x8 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = *(const SA_LDS bf16x8*)(xs + l32 * ROW + 16 * ks + 8 * h);
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) z[pt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) z[pt] = mfma32(a[ks], pw[pt][ks], z[pt]);
   };
 
-  f32x16 acc[PT][DB];
-#pragma unroll
-  for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[pt][db] = f32x16{};
-  float mass[PT] = {0.f, 0.f};
-
-  load_tile(cur.t0, cur.t1);
+  load_tile(true, cur.t0, cur.t1);
   store_tile(0);
+  load_tile(n1.valid, n1.t0, n1.t1);
+  store_tile(1);
   __syncthreads();
 
   // transpose-read geometry (see lds_read_tr16): 16-lane group g = lane / 16
   const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
 
+  f32x16 znext[PT];
+  affinities(0, znext);
   int buf = 0;
+  // Outer loop: one (segment, user) piece per iteration; inner loop: its
+  // tiles.  The accumulators are only touched by the matrix cores inside the
+  // inner loop, and flushed once per piece.
   while (cur.valid) {
-    TileWalker<TILE> nxt = cur;
-    nxt.advance();
-    if (nxt.valid) load_tile(nxt.t0, nxt.t1);
+    const int64_t slot = (int64_t)s + cur.user;
+    f32x16 acc[PT][DB];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[pt][db] = f32x16{};
+    float mass[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) mass[pt] = 0.f;
+    bool last;
+    do {
+      load_tile(n2.valid, n2.t0, n2.t1);
+      f32x16 z[PT];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) z[pt] = znext[pt];
+      const int b1 = buf == NBUF - 1 ? 0 : buf + 1;
+      affinities(b1, znext);   // unused after the last tile
 
-    const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
+      // Softmax weights of tile `buf`.  Register i of a lane is token
+      // crow(i, h) of the tile; the lane's prototype is pw0 + 32 pt + l32.
+      const SA_LDS float* ls = (const SA_LDS float*)&sL[buf][0];
+      bf16x8 abf[PT][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lq = *(const SA_LDS f32x4*)(ls + 8 * g + 4 * h);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            const float a = exp2_fast(fmaf(z[pt][i], alpha, -lq[r]));
+            if (MASS) mass[pt] += a;
+            abf[pt][i >> 3][i & 7] = (bf16)a;
+          }
+        }
+      }
 
-    // Z^T tile (32 tokens x 32 prototypes per pt): A = X rows, B = P rows.
-    f32x16 z[PT];
+      // U^T (d x prototypes) += X^T (d x tokens) A^T (tokens x prototypes).
+      // K slot j of half h in block kb is token 16 kb + 8 (j / 4) + 4h + (j % 4),
+      // matching the C fragment rows above.
+      const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) z[pt] = f32x16{};
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *(const SA_LDS bf16x8*)(xs + l32 * ROW + 16 * ks + 8 * h);
+        for (int db = 0; db < DB; ++db) {
+          const int row0 = 16 * kb + 4 * h + tr_r;
+          const int col = 32 * db + 16 * tr_half + 4 * tr_c;
+          const bf16x8 a = concat4(lds_read_tr16(xs + row0 * ROW + col),
+                                   lds_read_tr16(xs + (row0 + 8) * ROW + col));
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) z[pt] = mfma32(a, pw[pt][ks], z[pt]);
-    }
+          for (int pt = 0; pt < PT; ++pt) acc[pt][db] = mfma32(a, abf[pt][kb], acc[pt][db]);
+        }
+      }
 
-    // Softmax weights.  Register i of a lane is token crow(i, h) of the tile.
-    const SA_LDS float* ls = (const SA_LDS float*)&sL[buf][0];
-    f32x4 lq[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) lq[g] = *(const SA_LDS f32x4*)(ls + 8 * g + 4 * h);
-    bf16x8 abf[PT][2];
+      store_tile(buf == 0 ? NBUF - 1 : buf - 1);   // zeros when there is no such tile
+      __syncthreads();
+      last = cur.last_in_piece();
+      buf = b1;
+      cur = n1;
+      n1 = n2;
+      if (n2.valid) n2.advance();
+    } while (!last);
+
+    // Flush the piece.  acc[pt][db] register i holds
+    // U[proto = pw0 + 32 pt + l32][d = 32 db + crow(i, h)].
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
-      float ms = 0.f;
+      const int proto = pw0 + pt * 32 + l32;
+      const float mo = MASS ? shfl_xor32(mass[pt]) : 0.f;
+      if (proto < k) {
+        float* dst = part + (slot * k + proto) * D;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float a = exp2_fast(fmaf(z[pt][i], alpha, -lq[i >> 2][i & 3]));
-        ms += a;
-        abf[pt][i >> 3][i & 7] = (bf16)a;
-      }
-      mass[pt] += ms;
-    }
-
-    // U^T (d x prototypes) += X^T (d x tokens) A^T (tokens x prototypes).
-    // K slot j of half h in block kb is token 16 kb + 8 (j / 4) + 4h + (j % 4),
-    // matching the C fragment rows above.
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int row0 = 16 * kb + 4 * h + tr_r;
-        const int col = 32 * db + 16 * tr_half + 4 * tr_c;
-        const bf16x4 v0 = lds_read_tr16(xs + row0 * ROW + col);
-        const bf16x4 v1 = lds_read_tr16(xs + (row0 + 8) * ROW + col);
-        const bf16x8 a = concat4(v0, v1);
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[pt][db] = mfma32(a, abf[pt][kb], acc[pt][db]);
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v = {acc[pt][db][4 * g], acc[pt][db][4 * g + 1], acc[pt][db][4 * g + 2],
+                       acc[pt][db][4 * g + 3]};
+            *(f32x4*)(dst + 32 * db + 8 * g + 4 * h) = v;
+          }
+        if (MASS && h == 0) pmass[slot * k + proto] = mass[pt] + mo;
       }
     }
-
-    if (cur.last_in_piece()) {
-      // Flush the piece to slot s + user.  acc[pt][db] register i holds
-      // U[proto = pw0 + 32 pt + l32][d = 32 db + crow(i, h)].
-      const int64_t slot = (int64_t)s + cur.user;
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        const int proto = pw0 + pt * 32 + l32;
-        const float mo = shfl_xor32(mass[pt]);
-        if (proto < k) {
-          float* dst = part + (slot * k + proto) * D;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              f32x4 v = {acc[pt][db][4 * g], acc[pt][db][4 * g + 1], acc[pt][db][4 * g + 2],
-                         acc[pt][db][4 * g + 3]};
-              *(f32x4*)(dst + 32 * db + 8 * g + 4 * h) = v;
-            }
-          if (h == 0) pmass[slot * k + proto] = mass[pt] + mo;
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[pt][db] = f32x16{};
-        mass[pt] = 0.f;
-      }
-    }
-
-    if (nxt.valid) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    cur = nxt;
   }
 }
 
 // ----------------------------------------------------------------------------
 // Host-side launchers.
+#ifndef SA_AGG_WAVES
+#define SA_AGG_WAVES 8
+#endif
+constexpr int kAggWaves = SA_AGG_WAVES;   // waves per aggregation workgroup
 template <int D>
 static hipError_t launch_stats_bf16_t(const FwdArgs& a, hipStream_t st, Prof* prof) {
   const float scale = 1.0f / sqrtf((float)D);
@@ -336,9 +378,16 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t st, Prof* prof
     hipError_t e = launch_stats_bf16_t<D>(a, st, prof);
     if (e != hipSuccess) return e;
     prof_begin(prof, "sa_agg_bf16", st);
-    hipLaunchKernelGGL(sa_agg_bf16<D>, dim3(a.G, a.nchunks), dim3(256), 0, st, a.offsets, a.B,
-                       (const bf16*)a.X, (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part,
-                       a.pmass);
+    if (a.mass_norm || a.mass != nullptr)
+      hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, kChunkBf16 / (32 * kAggWaves)>),
+                         dim3(a.G, a.nchunks), dim3(64 * kAggWaves), 0, st, a.offsets,
+                         a.B, (const bf16*)a.X, (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse,
+                         a.part, a.pmass);
+    else
+      hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, kChunkBf16 / (32 * kAggWaves)>),
+                         dim3(a.G, a.nchunks), dim3(64 * kAggWaves), 0, st,
+                         a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.P, a.k, a.T, a.G, alpha,
+                         a.lse, a.part, a.pmass);
     e = hipGetLastError();
     prof_end(prof, st);
     if (e != hipSuccess) return e;
