@@ -52,6 +52,39 @@ __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Direct global -> LDS copies (global_load_lds_dword{,x4}).  Lane i's 4 or 16
+// bytes land at lds_base + 4 i or 16 i; lds_base must be the same for every
+// lane of the wave.  Written as assembly so that the compiler does not turn
+// every later LDS read into a wait for all copies in flight: the caller orders
+// them with explicit s_waitcnt vmcnt counts.  The instructions write no
+// register, and a copy the compiler does not count can only make the
+// compiler's own vmcnt waits stricter, never looser.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const SA_LDS void*)p;   // generic -> LDS offset
+}
+__device__ __forceinline__ void lds_copy16(const void* gptr, const void* lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* gptr, const void* lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+// Also a compiler memory barrier, so no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier after this wave's LDS reads and writes have completed.
+// Unlike __syncthreads() it does not wait for global loads (or the direct
+// global -> LDS copies) still in flight.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
 // ---------------------------------------------------------------------------

@@ -15,24 +15,42 @@
 //     (orientation Z = P X^T puts a token in each lane and prototypes in the
 //     registers).  Writes lse (natural log) per token.
 //  2. sa_agg_bf16: prototype-stationary.  A workgroup owns 256 prototypes
-//     (4 waves x 64, B operands in registers, fp32 accumulators in AGPRs) and a
-//     contiguous segment of tokens.  Per 32-token tile: Z^T = X P_w^T on the
-//     matrix cores, A = exp2(Z alpha - lse2) in registers, then
-//     U^T += X^T A^T, whose B operand is the first product's C fragment as is
-//     (prototype per lane, tokens per register) and whose A operand (X^T) is
-//     read from the LDS tile with the gfx950 transpose read.  Partial sketches
-//     go to a workspace slot per (segment, user) piece; sa_reduce sums them
-//     in segment order.
+//     (waves x prototype tiles, B operands in registers, fp32 accumulators in
+//     AGPRs) and a contiguous segment of tokens.  Per 32-token tile:
+//     Z^T = X P_w^T on the matrix cores, A = exp2(Z alpha - lse2) in
+//     registers, then U^T += X^T A^T, whose B operand is the first product's C
+//     fragment as is (prototype per lane, tokens per register) and whose A
+//     operand (X^T) is read from the LDS tile with the gfx950 transpose read.
+//     Partial sketches go to a workspace slot per (segment, user) piece;
+//     sa_reduce sums them in segment order.
 #include "sa_device.h"
 #include "sa_kernels.h"
 
 namespace sa {
 
 // ----------------------------------------------------------------------------
+// LDS layout of a 32-token x D tile without padding: row r holds D/8 units of
+// 16 bytes, unit u stored at position u ^ xswz(r).  The swizzle makes both
+// access patterns bank-conflict free:
+//  - 16 lanes reading one unit of 16 consecutive rows (the affinity product's
+//    A operand), and
+//  - 32 lanes transpose-reading 4 consecutive rows x one 32-column block (the
+//    aggregation product's A operand).
+template <int D>
+__device__ __forceinline__ int xswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return (r >> 2) & 3;
+}
+
+template <int D>
+__device__ __forceinline__ int xoff(int r, int u) { return r * D + ((u ^ xswz<D>(r)) << 3); }
+
+// ----------------------------------------------------------------------------
 // Pass 1: per-token log-sum-exp over all k prototypes.
 // Block: 256 threads = 4 waves; wave w handles tokens blk*256 + 64w .. +63 as
 // two 32-token MFMA tiles.  Prototypes are streamed in chunks of 64 rows
-// through LDS in fragment order, double buffered via registers.
+// through LDS in MFMA fragment order, double buffered via registers.
 template <int D>
 __global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
                                                      const bf16* __restrict__ P, int k,
@@ -61,27 +79,25 @@ __global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
     }
   }
 
-  // Piece q of a chunk: prototype row r = q / (D/8), 16-byte column piece
-  // cp = q % (D/8).  Fragment-order slot: tile r/32, step cp/2,
-  // lane (r % 32) + 32 (cp % 2).
+  // Thread t fills fragment-order slots t, t + 256, ...: slot
+  // ((pt KS + ks) 64 + L) is lane L's A operand for prototype tile pt and
+  // step ks, i.e. P[p0 + 32 pt + L % 32][16 ks + 8 (L / 32) .. +7].  Consecutive
+  // lanes write consecutive 16-byte slots (no LDS bank conflicts).
   auto load_chunk = [&](int p0, bf16x8 (&reg)[PPT]) {
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
-      const int q = tid + 256 * e;
-      const int r = q / (D / 8), cp = q % (D / 8);
-      const int row = p0 + r;
+      const int slot = tid + 256 * e;
+      const int pt = slot / (KS * 64), rem = slot % (KS * 64);
+      const int ks = rem / 64, L = rem % 64;
+      const int row = p0 + pt * 32 + (L & 31);
+      const int cp = 2 * ks + (L >> 5);
       if (row < k) reg[e] = *(const bf16x8*)(P + (int64_t)row * D + 8 * cp);
       else reg[e] = bf16x8{};
     }
   };
   auto store_chunk = [&](int buf, const bf16x8 (&reg)[PPT]) {
 #pragma unroll
-    for (int e = 0; e < PPT; ++e) {
-      const int q = tid + 256 * e;
-      const int r = q / (D / 8), cp = q % (D / 8);
-      const int slot = ((r >> 5) * KS + (cp >> 1)) * 64 + (r & 31) + 32 * (cp & 1);
-      sP[buf][slot] = reg[e];
-    }
+    for (int e = 0; e < PPT; ++e) sP[buf][tid + 256 * e] = reg[e];
   };
 
   float m[2] = {-INFINITY, -INFINITY};   // running max of raw dot products
@@ -148,14 +164,17 @@ __global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
 
 // ----------------------------------------------------------------------------
 // Pass 2: partial sketches per (segment, user) piece for one 256-prototype
-// chunk.  grid = (G segments, nchunks); block = 256 threads (4 waves, one per
-// SIMD), each wave owning 64 prototypes: their rows as MFMA B operands in
-// VGPRs and their 64 x D fp32 partial sketch in AGPRs.
+// chunk.  grid = (G segments, nchunks); block = NW waves, each owning PT x 32
+// prototypes: their rows as MFMA B operands in registers and their PT x 32 x D
+// fp32 partial sketch as MFMA accumulators.
 //
 // The token stream of the segment is cut into 32-token tiles that never
-// straddle two users, staged in LDS (three buffers, two tiles ahead) and
-// software pipelined: while the vector ALU turns tile t's affinities into
-// softmax weights, the matrix cores already compute tile t+1's affinities.
+// straddle two users.  Tiles are copied global -> LDS by the direct-to-LDS
+// loads (global_load_lds_dwordx4), four tiles ahead, into five LDS buffers, so
+// the memory latency of a tile has three iterations to resolve; waits are
+// explicit vmcnt counts and the barrier carries no fence.  Within an
+// iteration the matrix cores compute tile t+1's affinities while the vector
+// ALU turns tile t's affinities into softmax weights.
 template <int D, bool MASS, int NW, int PT>
 __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
@@ -163,19 +182,20 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     const float* __restrict__ lse, float* __restrict__ part, float* __restrict__ pmass) {
   constexpr int KS = D / 16;             // reduction steps of the affinity product
   constexpr int DB = D / 32;             // 32-row blocks of the transposed sketch
-  constexpr int NT = NW * 64;            // threads per workgroup
+  constexpr int U = D / 8;               // 16-byte units per token row
   constexpr int KC = NW * PT * 32;       // prototypes per workgroup
   static_assert(KC == kChunkBf16, "one workgroup covers one prototype chunk");
   constexpr int TILE = 32;               // tokens per step
-  // LDS row pitch: D + 24 elements makes the pitch 12 words mod 64 banks, so
-  // both the 16-byte row reads (16 lanes, 16 rows) and the transpose reads
-  // (4 rows x 32 bytes per 16 lanes) hit distinct banks.
-  constexpr int ROW = D + 24;
-  constexpr int PIECES = TILE * D / 8;   // 16-byte pieces per tile
-  constexpr int PPT = (PIECES + NT - 1) / NT;
-  constexpr int NBUF = 3;
+  constexpr int UNITS = TILE * U;        // 16-byte units per tile
+  constexpr int UPW = UNITS / NW;        // units copied by each wave
+  static_assert(UNITS % NW == 0 && (UPW <= 64 || UPW % 64 == 0), "");
+  constexpr int XI = (UPW + 63) / 64;    // copy instructions per wave per tile
+  constexpr int LPW = TILE / NW;         // lse entries copied by each wave
+  constexpr int NBUF = 5;                // tiles t .. t+4
+  constexpr int L = XI + 1;              // loads per wave per tile
+  constexpr int WAIT2 = 2 * L;           // leaves the loads of two tiles in flight
 
-  __shared__ __attribute__((aligned(16))) bf16 sX[NBUF][TILE * ROW];
+  __shared__ __attribute__((aligned(16))) bf16 sX[NBUF][TILE * D];
   __shared__ __attribute__((aligned(16))) float sL[NBUF][TILE];
 
   const int tid = threadIdx.x;
@@ -200,67 +220,67 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
   if (!cur.valid) return;
   TileWalker<TILE> n1 = cur;
   n1.advance();
-  TileWalker<TILE> n2 = n1;
+  TileWalker<TILE> n2 = n1, n3, n4;
   if (n2.valid) n2.advance();
+  n3 = n2;
+  if (n3.valid) n3.advance();
+  n4 = n3;
+  if (n4.valid) n4.advance();
 
-  // Staging of one tile: rows [t0, t1) of X and lse * log2(e); rows past t1
-  // are zero with lse = +inf, so they contribute exactly nothing.
-  bf16x8 xr[PPT];
-  float lr = 0.f;
-  // Branch-free: every lane loads an in-range row (clamped) and a select
-  // zeroes what lies outside [t0, t1), so the loop body stays one basic block.
-  auto load_tile = [&](bool valid, int64_t t0, int64_t t1) {
+  // Copy tile (t0, t1) into buffer b.  Every wave issues exactly L loads per
+  // tile, also for tiles past the end of the stream (then from row 0 into a
+  // buffer nobody reads), so that vmcnt counts are the same every iteration.
+  // Rows past t1 copy row t0; their weights are zeroed through lse = +inf.
+  auto copy_tile = [&](bool valid, int64_t t0, int64_t t1, int b) {
 #pragma unroll
-    for (int e = 0; e < PPT; ++e) {
-      const int q = tid + NT * e;
-      const int qc = q < PIECES ? q : PIECES - 1;
-      const int r = qc / (D / 8), cp = qc % (D / 8);
-      const bool in = valid && q < PIECES && t0 + r < t1;
-      const int64_t row = in ? t0 + r : 0;
-      const bf16x8 v = *(const bf16x8*)(X + row * D + 8 * cp);
-      xr[e] = in ? v : bf16x8{};
+    for (int j = 0; j < XI; ++j) {
+      const int v0 = wave * UPW + j * 64;          // first unit of this instruction
+      const int v = v0 + lane;
+      const int r = v / U, pu = v % U;
+      const int cp = pu ^ xswz<D>(r);
+      const int64_t row = (valid && t0 + r < t1) ? t0 + r : (valid ? t0 : 0);
+      if (UPW >= 64 || lane < UPW) lds_copy16(X + row * D + 8 * cp, &sX[b][v0 * 8]);
     }
-    // raw value; the scaling happens at the LDS store, after the load landed
-    const bool lin = valid && t0 + (tid & (TILE - 1)) < t1;
-    const float lv = lse[lin ? t0 + (tid & (TILE - 1)) : 0];
-    lr = lin ? lv : INFINITY;
+    const int lr = wave * LPW + lane;
+    const int64_t lrow = (valid && t0 + lr < t1) ? t0 + lr : (valid ? t0 : 0);
+    if (lane < LPW) lds_copy4(lse + lrow, &sL[b][wave * LPW]);
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < PPT; ++e) {
-      const int q = tid + NT * e;
-      if (q < PIECES) {
-        const int r = q / (D / 8), cp = q % (D / 8);
-        *(bf16x8*)(&sX[buf][r * ROW + 8 * cp]) = xr[e];
-      }
+  // After this wave's copy of (t0, t1) has landed: lse rows past t1 -> +inf
+  // (zero weight), the others scaled by log2(e).
+  auto finish_lse = [&](bool valid, int64_t t0, int64_t t1, int b) {
+    if (lane < LPW) {
+      const int r = wave * LPW + lane;
+      const float v = sL[b][r];
+      sL[b][r] = (valid && t0 + r < t1) ? v * kLog2e : INFINITY;
     }
-    if (tid < TILE) sL[buf][tid] = lr * kLog2e;
-  };
-  // Z^T tile (32 tokens x 32 prototypes per pt) of the tile in buffer buf.
-  auto affinities = [&](int buf, f32x16 (&z)[PT]) {
-    const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
-    bf16x8 a[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = *(const SA_LDS bf16x8*)(xs + l32 * ROW + 16 * ks + 8 * h);
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) z[pt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) z[pt] = mfma32(a[ks], pw[pt][ks], z[pt]);
   };
 
-  load_tile(true, cur.t0, cur.t1);
-  store_tile(0);
-  load_tile(n1.valid, n1.t0, n1.t1);
-  store_tile(1);
+  copy_tile(true, cur.t0, cur.t1, 0);
+  copy_tile(n1.valid, n1.t0, n1.t1, 1);
+  copy_tile(n2.valid, n2.t0, n2.t1, 2);
+  copy_tile(n3.valid, n3.t0, n3.t1, 3);
+  wait_vmcnt<WAIT2>();                           // tiles 0 and 1 landed
+  finish_lse(true, cur.t0, cur.t1, 0);
+  finish_lse(n1.valid, n1.t0, n1.t1, 1);
   __syncthreads();
 
   // transpose-read geometry (see lds_read_tr16): 16-lane group g = lane / 16
   const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
 
+  // Affinities of the first tile.
   f32x16 znext[PT];
-  affinities(0, znext);
+  {
+    const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[0][0];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) znext[pt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *(const SA_LDS bf16x8*)(xs + xoff<D>(l32, 2 * ks + h));
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) znext[pt] = mfma32(a, pw[pt][ks], znext[pt]);
+    }
+  }
+
   int buf = 0;
   // Outer loop: one (segment, user) piece per iteration; inner loop: its
   // tiles.  The accumulators are only touched by the matrix cores inside the
@@ -277,56 +297,78 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     for (int pt = 0; pt < PT; ++pt) mass[pt] = 0.f;
     bool last;
     do {
-      load_tile(n2.valid, n2.t0, n2.t1);
+      const int b1 = buf + 1 >= NBUF ? buf + 1 - NBUF : buf + 1;
+      const int b2 = buf + 2 >= NBUF ? buf + 2 - NBUF : buf + 2;
+      const int b4 = buf + 4 >= NBUF ? buf + 4 - NBUF : buf + 4;
+      copy_tile(n4.valid, n4.t0, n4.t1, b4);
+
+      const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
+      const SA_LDS bf16* xs1 = (const SA_LDS bf16*)&sX[b1][0];
+      const SA_LDS float* ls = (const SA_LDS float*)&sL[buf][0];
+
+      // LDS reads: the next tile's affinity operands and this tile's lse.
+      bf16x8 an[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) an[ks] = *(const SA_LDS bf16x8*)(xs1 + xoff<D>(l32, 2 * ks + h));
+      f32x4 lq[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) lq[g] = *(const SA_LDS f32x4*)(ls + 8 * g + 4 * h);
+
       f32x16 z[PT];
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) z[pt] = znext[pt];
-      const int b1 = buf == NBUF - 1 ? 0 : buf + 1;
-      affinities(b1, znext);   // unused after the last tile
+      for (int pt = 0; pt < PT; ++pt) {
+        z[pt] = znext[pt];
+        znext[pt] = f32x16{};
+      }
+      // Affinities of tile t+1 (unused after the last tile).
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) znext[pt] = mfma32(an[ks], pw[pt][ks], znext[pt]);
 
-      // Softmax weights of tile `buf`.  Register i of a lane is token
-      // crow(i, h) of the tile; the lane's prototype is pw0 + 32 pt + l32.
-      const SA_LDS float* ls = (const SA_LDS float*)&sL[buf][0];
+      // Softmax weights of tile t.  Register i of a lane is token crow(i, h)
+      // of the tile; the lane's prototype is pw0 + 32 pt + l32.
       bf16x8 abf[PT][2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lq = *(const SA_LDS f32x4*)(ls + 8 * g + 4 * h);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
+        for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * g + r;
-            const float a = exp2_fast(fmaf(z[pt][i], alpha, -lq[r]));
+          for (int j = 0; j < 8; ++j) {
+            const int i = 8 * kb + j;
+            const float a = exp2_fast(fmaf(z[pt][i], alpha, -lq[i >> 2][i & 3]));
             if (MASS) mass[pt] += a;
-            abf[pt][i >> 3][i & 7] = (bf16)a;
+            abf[pt][kb][j] = (bf16)a;
           }
-        }
-      }
 
       // U^T (d x prototypes) += X^T (d x tokens) A^T (tokens x prototypes).
       // K slot j of half h in block kb is token 16 kb + 8 (j / 4) + 4h + (j % 4),
       // matching the C fragment rows above.
-      const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int row0 = 16 * kb + 4 * h + tr_r;
-          const int col = 32 * db + 16 * tr_half + 4 * tr_c;
-          const bf16x8 a = concat4(lds_read_tr16(xs + row0 * ROW + col),
-                                   lds_read_tr16(xs + (row0 + 8) * ROW + col));
+          const int unit = 4 * db + 2 * tr_half + (tr_c >> 1);
+          const int sub = (tr_c & 1) * 4;
+          const bf16x8 xt = concat4(lds_read_tr16(xs + xoff<D>(row0, unit) + sub),
+                                    lds_read_tr16(xs + xoff<D>(row0 + 8, unit) + sub));
 #pragma unroll
-          for (int pt = 0; pt < PT; ++pt) acc[pt][db] = mfma32(a, abf[pt][kb], acc[pt][db]);
+          for (int pt = 0; pt < PT; ++pt) acc[pt][db] = mfma32(xt, abf[pt][kb], acc[pt][db]);
         }
-      }
 
-      store_tile(buf == 0 ? NBUF - 1 : buf - 1);   // zeros when there is no such tile
-      __syncthreads();
+      // Tile t+2 must be complete before the barrier: its loads were issued
+      // two iterations ago, those of t+3 and t+4 may still be in flight.
+      wait_vmcnt<WAIT2>();
+      finish_lse(n2.valid, n2.t0, n2.t1, b2);
+      barrier_lds();
       last = cur.last_in_piece();
       buf = b1;
       cur = n1;
       n1 = n2;
-      if (n2.valid) n2.advance();
+      n2 = n3;
+      n3 = n4;
+      if (n4.valid) n4.advance();
     } while (!last);
 
     // Flush the piece.  acc[pt][db] register i holds
@@ -349,14 +391,16 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
       }
     }
   }
+  wait_vmcnt<0>();   // no copy left in flight at exit
 }
 
 // ----------------------------------------------------------------------------
 // Host-side launchers.
 #ifndef SA_AGG_WAVES
-#define SA_AGG_WAVES 8
+#define SA_AGG_WAVES 4
 #endif
 constexpr int kAggWaves = SA_AGG_WAVES;   // waves per aggregation workgroup
+
 template <int D>
 static hipError_t launch_stats_bf16_t(const FwdArgs& a, hipStream_t st, Prof* prof) {
   const float scale = 1.0f / sqrtf((float)D);
@@ -374,20 +418,19 @@ template <int D>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t st, Prof* prof) {
   const float scale = 1.0f / sqrtf((float)D);
   const float alpha = scale * kLog2e;
+  constexpr int PT = kChunkBf16 / (32 * kAggWaves);
   if (a.T > 0) {
     hipError_t e = launch_stats_bf16_t<D>(a, st, prof);
     if (e != hipSuccess) return e;
     prof_begin(prof, "sa_agg_bf16", st);
     if (a.mass_norm || a.mass != nullptr)
-      hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, kChunkBf16 / (32 * kAggWaves)>),
-                         dim3(a.G, a.nchunks), dim3(64 * kAggWaves), 0, st, a.offsets,
-                         a.B, (const bf16*)a.X, (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse,
-                         a.part, a.pmass);
+      hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, PT>), dim3(a.G, a.nchunks),
+                         dim3(64 * kAggWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
+                         (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part, a.pmass);
     else
-      hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, kChunkBf16 / (32 * kAggWaves)>),
-                         dim3(a.G, a.nchunks), dim3(64 * kAggWaves), 0, st,
-                         a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.P, a.k, a.T, a.G, alpha,
-                         a.lse, a.part, a.pmass);
+      hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, PT>), dim3(a.G, a.nchunks),
+                         dim3(64 * kAggWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
+                         (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part, a.pmass);
     e = hipGetLastError();
     prof_end(prof, st);
     if (e != hipSuccess) return e;
