@@ -37,6 +37,7 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* 
   size_t off = 0;
   p->off_status = off; off += 256;
   p->off_lse = off; off = align256(off + Tn * 4);
+  p->off_lse2 = off; off = align256(off + (Tn + 1) * 4);
   p->off_part = off; off = align256(off + (size_t)p->nslots * k * d * 4);
   p->off_pmass = off; off = align256(off + (size_t)p->nslots * k * 4);
   p->fwd_bytes = off;
@@ -126,6 +127,7 @@ static sa_status forward_impl(const sa_problem* pr, const int64_t* offsets_dev, 
   a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
   a.X = X; a.P = P;
   a.lse = lse ? lse : (float*)(w + p.off_lse);
+  a.lse2 = (float*)(w + p.off_lse2);
   a.S = S; a.mass = mass;
   a.part = (float*)(w + p.off_part);
   a.pmass = (float*)(w + p.off_pmass);

@@ -52,23 +52,27 @@ __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Direct global -> LDS copies (global_load_lds_dword{,x4}).  Lane i's 4 or 16
-// bytes land at lds_base + 4 i or 16 i; lds_base must be the same for every
-// lane of the wave.  Written as assembly so that the compiler does not turn
-// every later LDS read into a wait for all copies in flight: the caller orders
-// them with explicit s_waitcnt vmcnt counts.  The instructions write no
-// register, and a copy the compiler does not count can only make the
-// compiler's own vmcnt waits stricter, never looser.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const SA_LDS void*)p;   // generic -> LDS offset
+// Direct global -> LDS copies (global_load_lds_dword{,x4}).  lds_copy16:
+// lane i copies the 16 bytes at sbase + voff_i to LDS byte address
+// lds + 16 i; sbase and lds must be the same for every lane of the wave.
+// Written as assembly so that the compiler does not turn every later LDS read
+// into a wait for all copies in flight: the caller orders them with explicit
+// vmcnt waits.  The instructions write no register.  Every call sets M0, and
+// no compiler-generated code in these kernels keeps a value in M0.
+__device__ __forceinline__ uint32_t lds_addr(const SA_LDS void* p) {
+  return (uint32_t)(uintptr_t)p;
 }
-__device__ __forceinline__ void lds_copy16(const void* gptr, const void* lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
+__device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
 }
-__device__ __forceinline__ void lds_copy4(const void* gptr, const void* lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr), "s"(base) : "memory", "m0");
+// Lane i copies the 4 bytes at its own address src_i to LDS byte address
+// lds + 4 i.
+__device__ __forceinline__ void lds_copy4v(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -78,6 +82,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Wait for all vector-memory operations of this wave, written so that the
+// compiler sees the wait (s_waitcnt vmcnt(0), expcnt and lgkmcnt untouched).
+// Its own earlier loads and stores then count as complete, and it adds no wait
+// for them inside a following loop, where such a wait would also hold up every
+// copy in flight on every trip.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0xF70); }
 // Workgroup barrier after this wave's LDS reads and writes have completed.
 // Unlike __syncthreads() it does not wait for global loads (or the direct
 // global -> LDS copies) still in flight.

@@ -55,7 +55,8 @@ template <int D>
 __global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
                                                      const bf16* __restrict__ P, int k,
                                                      int64_t T, float alpha, float scale,
-                                                     float* __restrict__ lse_out) {
+                                                     float* __restrict__ lse_out,
+                                                     float* __restrict__ lse2_out) {
   constexpr int KS = D / 16;            // 16-wide reduction steps over d
   constexpr int PCH = 64;               // prototypes per LDS chunk
   constexpr int NPIECE = PCH * D / 8;   // 16-byte pieces per chunk
@@ -158,28 +159,36 @@ __global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
     const float Ma = M * alpha;
     const float L = l[tt] * exp2_fast(fmaf(m[tt], alpha, -Ma)) + lo * exp2_fast(fmaf(mo, alpha, -Ma));
     const int64_t tok = tok0 + tt * 32 + l32;
-    if (h == 0 && tok < T) lse_out[tok] = M * scale + __logf(L);
+    if (h == 0 && tok < T) {
+      lse_out[tok] = M * scale + __logf(L);
+      if (lse2_out != nullptr) lse2_out[tok] = Ma + __log2f(L);
+    }
   }
+  // Sentinel read by the aggregation pass for rows past the end of a tile.
+  if (lse2_out != nullptr && blockIdx.x == 0 && tid == 0) lse2_out[T] = INFINITY;
 }
 
 // ----------------------------------------------------------------------------
 // Pass 2: partial sketches per (segment, user) piece for one 256-prototype
 // chunk.  grid = (G segments, nchunks); block = NW waves, each owning PT x 32
 // prototypes: their rows as MFMA B operands in registers and their PT x 32 x D
-// fp32 partial sketch as MFMA accumulators.
+// fp32 partial sketch as MFMA accumulators (AGPRs).
 //
 // The token stream of the segment is cut into 32-token tiles that never
-// straddle two users.  Tiles are copied global -> LDS by the direct-to-LDS
-// loads (global_load_lds_dwordx4), four tiles ahead, into five LDS buffers, so
-// the memory latency of a tile has three iterations to resolve; waits are
-// explicit vmcnt counts and the barrier carries no fence.  Within an
-// iteration the matrix cores compute tile t+1's affinities while the vector
-// ALU turns tile t's affinities into softmax weights.
+// straddle two users.  Tile t + 6 is copied global -> LDS by the
+// direct-to-LDS loads while tile t is computed, into eight rotating buffers;
+// a barrier after every second tile publishes the copies (waits are explicit
+// vmcnt counts and the barrier carries no fence).  Step t computes the
+// affinities of tile t+1 on the matrix cores while the vector ALU turns those
+// of tile t into softmax weights, then the sketch update of tile t.
+//
+// lse2 holds the per-token log-sum-exp in log2 units, with lse2[T] = +inf:
+// rows of a tile past its end read that entry and get weight 0.
 template <int D, bool MASS, int NW, int PT>
 __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ P, int k, int64_t T, int G, float alpha,
-    const float* __restrict__ lse, float* __restrict__ part, float* __restrict__ pmass) {
+    const float* __restrict__ lse2, float* __restrict__ part, float* __restrict__ pmass) {
   constexpr int KS = D / 16;             // reduction steps of the affinity product
   constexpr int DB = D / 32;             // 32-row blocks of the transposed sketch
   constexpr int U = D / 8;               // 16-byte units per token row
@@ -191,9 +200,10 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
   static_assert(UNITS % NW == 0 && (UPW <= 64 || UPW % 64 == 0), "");
   constexpr int XI = (UPW + 63) / 64;    // copy instructions per wave per tile
   constexpr int LPW = TILE / NW;         // lse entries copied by each wave
-  constexpr int NBUF = 5;                // tiles t .. t+4
+  constexpr int NBUF = 8;                // tiles t-1 .. t+6
+  constexpr int AHEAD = 6;               // copy distance in tiles
   constexpr int L = XI + 1;              // loads per wave per tile
-  constexpr int WAIT2 = 2 * L;           // leaves the loads of two tiles in flight
+  constexpr uint32_t XBYTES = TILE * D * 2;
 
   __shared__ __attribute__((aligned(16))) bf16 sX[NBUF][TILE * D];
   __shared__ __attribute__((aligned(16))) float sL[NBUF][TILE];
@@ -202,6 +212,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int s = blockIdx.x, chunk = blockIdx.y;
   const int pw0 = chunk * KC + wave * PT * 32;   // first prototype of this wave
+  const uint32_t sx0 = lds_addr((const SA_LDS void*)&sX[0][0]);
+  const uint32_t sl0 = lds_addr((const SA_LDS void*)&sL[0][0]);
+  const SA_LDS char* lds = (const SA_LDS char*)0;
 
   // Prototype rows as B operands of Z^T = X P^T: pw[pt][ks] holds
   // P[pw0 + 32 pt + l32][16 ks + 8h .. +7].
@@ -215,78 +228,94 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
   }
 
   const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
-  TileWalker<TILE> cur;
-  cur.start(offsets, B, lo, hi);
-  if (!cur.valid) return;
-  TileWalker<TILE> n1 = cur;
-  n1.advance();
-  TileWalker<TILE> n2 = n1, n3, n4;
-  if (n2.valid) n2.advance();
-  n3 = n2;
-  if (n3.valid) n3.advance();
-  n4 = n3;
-  if (n4.valid) n4.advance();
+  TileWalker<TILE> cw;                 // tile being computed
+  cw.start(offsets, B, lo, hi);
+  if (!cw.valid) return;
+  TileWalker<TILE> qw = cw;            // next tile to copy
 
-  // Copy tile (t0, t1) into buffer b.  Every wave issues exactly L loads per
-  // tile, also for tiles past the end of the stream (then from row 0 into a
-  // buffer nobody reads), so that vmcnt counts are the same every iteration.
-  // Rows past t1 copy row t0; their weights are zeroed through lse = +inf.
-  auto copy_tile = [&](bool valid, int64_t t0, int64_t t1, int b) {
+  // Copy geometry.  Copy instruction j of this wave moves units
+  // v0 .. v0 + 63 of the tile, v0 = wave UPW + 64 j; the lane's unit v sits in
+  // row v / U at stored position v % U and holds global unit (v % U) ^ g(row).
+  int crow_[XI];
+  uint32_t ccol[XI];
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int v = wave * UPW + j * 64 + lane;
+    crow_[j] = v / U;
+    ccol[j] = (uint32_t)(((v % U) ^ xswz<D>(v / U)) * 16);
+  }
+  const int lrow = wave * LPW + lane;            // lse row copied (lane < LPW)
+
+  // Copy the tile of qw into buffer b and advance qw.  Every wave issues
+  // exactly L loads per tile, also past the end of the stream (then row 0 of
+  // X and lse2[T]), so that vmcnt counts are the same every time.  Rows past
+  // the tile's end copy its first row of X and lse2[T] = +inf.
+  auto copy_next = [&](uint32_t b) {
+    const bool valid = qw.valid;
+    const int64_t base = valid ? qw.t0 : 0;
+    const int nr = valid ? (int)(qw.t1 - qw.t0) : 0;
+    const bf16* xb = X + base * D;
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
-      const int v0 = wave * UPW + j * 64;          // first unit of this instruction
-      const int v = v0 + lane;
-      const int r = v / U, pu = v % U;
-      const int cp = pu ^ xswz<D>(r);
-      const int64_t row = (valid && t0 + r < t1) ? t0 + r : (valid ? t0 : 0);
-      if (UPW >= 64 || lane < UPW) lds_copy16(X + row * D + 8 * cp, &sX[b][v0 * 8]);
+      const int r = crow_[j] < nr ? crow_[j] : 0;
+      if (UPW >= 64 || lane < UPW)
+        lds_copy16(xb, (uint32_t)(r * D * 2) + ccol[j],
+                   sx0 + b * XBYTES + (uint32_t)(wave * UPW + j * 64) * 16);
     }
-    const int lr = wave * LPW + lane;
-    const int64_t lrow = (valid && t0 + lr < t1) ? t0 + lr : (valid ? t0 : 0);
-    if (lane < LPW) lds_copy4(lse + lrow, &sL[b][wave * LPW]);
-  };
-  // After this wave's copy of (t0, t1) has landed: lse rows past t1 -> +inf
-  // (zero weight), the others scaled by log2(e).
-  auto finish_lse = [&](bool valid, int64_t t0, int64_t t1, int b) {
-    if (lane < LPW) {
-      const int r = wave * LPW + lane;
-      const float v = sL[b][r];
-      sL[b][r] = (valid && t0 + r < t1) ? v * kLog2e : INFINITY;
-    }
+    if (lane < LPW)
+      lds_copy4v(lrow < nr ? lse2 + base + lrow : lse2 + T, sl0 + (b * TILE + wave * LPW) * 4);
+    if (valid) qw.advance();
   };
 
-  copy_tile(true, cur.t0, cur.t1, 0);
-  copy_tile(n1.valid, n1.t0, n1.t1, 1);
-  copy_tile(n2.valid, n2.t0, n2.t1, 2);
-  copy_tile(n3.valid, n3.t0, n3.t1, 3);
-  wait_vmcnt<WAIT2>();                           // tiles 0 and 1 landed
-  finish_lse(true, cur.t0, cur.t1, 0);
-  finish_lse(n1.valid, n1.t0, n1.t1, 1);
+#pragma unroll
+  for (int b = 0; b < AHEAD; ++b) copy_next(b);
+  // The prototype rows must have arrived before the loop, and the compiler
+  // must see the wait for them here: otherwise it places one inside the loop,
+  // where it would also wait for every copy in flight.  The copies above are
+  // waited for as well, which the first tiles need anyway.
+#pragma unroll
+  for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(pw[pt][ks]));
+  wait_vmcnt<0>();
   __syncthreads();
 
-  // transpose-read geometry (see lds_read_tr16): 16-lane group g = lane / 16
+  // LDS byte offsets within a tile buffer (loop invariant).
+  //  aoff[ks]: affinity A operand, token row l32, unit 2 ks + h.
+  //  toff[db][e]: transpose read for token rows 4h + tr_r + 8e (+ 16 kb, which
+  //  the swizzle leaves additive) and the lane's 4-column piece of d block db.
   const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
+  uint32_t aoff[KS], toff[DB][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aoff[ks] = (uint32_t)xoff<D>(l32, 2 * ks + h) * 2;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      toff[db][e] = (uint32_t)(xoff<D>(4 * h + tr_r + 8 * e, 4 * db + 2 * tr_half + (tr_c >> 1)) +
+                               (tr_c & 1) * 4) * 2;
+  const uint32_t lqoff = (uint32_t)(4 * h) * 4;
 
   // Affinities of the first tile.
   f32x16 znext[PT];
   {
-    const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[0][0];
+    bf16x8 a0[KS];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) znext[pt] = f32x16{};
+    for (int ks = 0; ks < KS; ++ks) a0[ks] = *(const SA_LDS bf16x8*)(lds + sx0 + aoff[ks]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *(const SA_LDS bf16x8*)(xs + xoff<D>(l32, 2 * ks + h));
+    for (int pt = 0; pt < PT; ++pt) {
+      znext[pt] = mfma32(a0[0], pw[pt][0], f32x16{});
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) znext[pt] = mfma32(a, pw[pt][ks], znext[pt]);
+      for (int ks = 1; ks < KS; ++ks) znext[pt] = mfma32(a0[ks], pw[pt][ks], znext[pt]);
     }
   }
 
-  int buf = 0;
+  uint32_t t = 0;                                 // tile counter of the segment
   // Outer loop: one (segment, user) piece per iteration; inner loop: its
   // tiles.  The accumulators are only touched by the matrix cores inside the
   // inner loop, and flushed once per piece.
-  while (cur.valid) {
-    const int64_t slot = (int64_t)s + cur.user;
+  while (cw.valid) {
+    const int64_t slot = (int64_t)s + cw.user;
     f32x16 acc[PT][DB];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
@@ -297,42 +326,48 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     for (int pt = 0; pt < PT; ++pt) mass[pt] = 0.f;
     bool last;
     do {
-      const int b1 = buf + 1 >= NBUF ? buf + 1 - NBUF : buf + 1;
-      const int b2 = buf + 2 >= NBUF ? buf + 2 - NBUF : buf + 2;
-      const int b4 = buf + 4 >= NBUF ? buf + 4 - NBUF : buf + 4;
-      copy_tile(n4.valid, n4.t0, n4.t1, b4);
+      const uint32_t buf = t & (NBUF - 1), b1 = (t + 1) & (NBUF - 1);
+      copy_next((t + AHEAD) & (NBUF - 1));        // into the buffer of tile t-2
 
-      const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
-      const SA_LDS bf16* xs1 = (const SA_LDS bf16*)&sX[b1][0];
-      const SA_LDS float* ls = (const SA_LDS float*)&sL[buf][0];
+      const SA_LDS char* xs = lds + sx0 + buf * XBYTES;
+      const SA_LDS char* xs1 = lds + sx0 + b1 * XBYTES;
+      const SA_LDS char* ls = lds + sl0 + buf * (TILE * 4) + lqoff;
 
-      // LDS reads: the next tile's affinity operands and this tile's lse.
+      // Affinities of tile t+1 (unused after the last tile of the stream).
       bf16x8 an[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) an[ks] = *(const SA_LDS bf16x8*)(xs1 + xoff<D>(l32, 2 * ks + h));
-      f32x4 lq[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) lq[g] = *(const SA_LDS f32x4*)(ls + 8 * g + 4 * h);
-
+      for (int ks = 0; ks < KS; ++ks) an[ks] = *(const SA_LDS bf16x8*)(xs1 + aoff[ks]);
       f32x16 z[PT];
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        z[pt] = znext[pt];
-        znext[pt] = f32x16{};
-      }
-      // Affinities of tile t+1 (unused after the last tile).
+      for (int pt = 0; pt < PT; ++pt) z[pt] = znext[pt];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) znext[pt] = mfma32(an[ks], pw[pt][ks], znext[pt]);
+        for (int pt = 0; pt < PT; ++pt)
+          znext[pt] = mfma32(an[ks], pw[pt][ks], ks == 0 ? f32x16{} : znext[pt]);
+
+      // This tile's lse and transposed token block (sketch-update operands).
+      f32x4 lq[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) lq[g] = *(const SA_LDS f32x4*)(ls + 32 * g);
+      bf16x8 xt[2][DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const SA_LDS char* p0 = xs + toff[db][0];
+        const SA_LDS char* p1 = xs + toff[db][1];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          xt[kb][db] = concat4(lds_read_tr16((const SA_LDS bf16*)(p0 + kb * 32 * D)),
+                               lds_read_tr16((const SA_LDS bf16*)(p1 + kb * 32 * D)));
+      }
 
       // Softmax weights of tile t.  Register i of a lane is token crow(i, h)
       // of the tile; the lane's prototype is pw0 + 32 pt + l32.
       bf16x8 abf[PT][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int i = 8 * kb + j;
@@ -345,30 +380,21 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
       // K slot j of half h in block kb is token 16 kb + 8 (j / 4) + 4h + (j % 4),
       // matching the C fragment rows above.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int row0 = 16 * kb + 4 * h + tr_r;
-          const int unit = 4 * db + 2 * tr_half + (tr_c >> 1);
-          const int sub = (tr_c & 1) * 4;
-          const bf16x8 xt = concat4(lds_read_tr16(xs + xoff<D>(row0, unit) + sub),
-                                    lds_read_tr16(xs + xoff<D>(row0 + 8, unit) + sub));
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int pt = 0; pt < PT; ++pt) acc[pt][db] = mfma32(xt, abf[pt][kb], acc[pt][db]);
-        }
+          for (int db = 0; db < DB; ++db) acc[pt][db] = mfma32(xt[kb][db], abf[pt][kb], acc[pt][db]);
 
-      // Tile t+2 must be complete before the barrier: its loads were issued
-      // two iterations ago, those of t+3 and t+4 may still be in flight.
-      wait_vmcnt<WAIT2>();
-      finish_lse(n2.valid, n2.t0, n2.t1, b2);
-      barrier_lds();
-      last = cur.last_in_piece();
-      buf = b1;
-      cur = n1;
-      n1 = n2;
-      n2 = n3;
-      n3 = n4;
-      if (n4.valid) n4.advance();
+      if (t & 1) {
+        // Tiles up to t+3 must be complete before the barrier (the next two
+        // steps read up to tile t+3); those of t+4 .. t+6 may be in flight.
+        wait_vmcnt<3 * L>();
+        barrier_lds();
+      }
+      last = cw.last_in_piece();
+      cw.advance();
+      ++t;
     } while (!last);
 
     // Flush the piece.  acc[pt][db] register i holds
@@ -390,6 +416,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
         if (MASS && h == 0) pmass[slot * k + proto] = mass[pt] + mo;
       }
     }
+    wait_vmem_all();   // once per piece: the stores above are complete
   }
   wait_vmcnt<0>();   // no copy left in flight at exit
 }
@@ -397,7 +424,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
 // ----------------------------------------------------------------------------
 // Host-side launchers.
 #ifndef SA_AGG_WAVES
-#define SA_AGG_WAVES 4
+#define SA_AGG_WAVES 8
 #endif
 constexpr int kAggWaves = SA_AGG_WAVES;   // waves per aggregation workgroup
 
@@ -408,7 +435,7 @@ static hipError_t launch_stats_bf16_t(const FwdArgs& a, hipStream_t st, Prof* pr
   const unsigned nb = (unsigned)((a.T + 255) / 256);
   prof_begin(prof, "sa_stats_bf16", st);
   hipLaunchKernelGGL(sa_stats_bf16<D>, dim3(nb), dim3(256), 0, st, (const bf16*)a.X,
-                     (const bf16*)a.P, a.k, a.T, alpha, scale, a.lse);
+                     (const bf16*)a.P, a.k, a.T, alpha, scale, a.lse, a.lse2);
   const hipError_t e = hipGetLastError();
   prof_end(prof, st);
   return e;
@@ -426,11 +453,11 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t st, Prof* prof
     if (a.mass_norm || a.mass != nullptr)
       hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, PT>), dim3(a.G, a.nchunks),
                          dim3(64 * kAggWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
-                         (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part, a.pmass);
+                         (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse2, a.part, a.pmass);
     else
       hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, PT>), dim3(a.G, a.nchunks),
                          dim3(64 * kAggWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
-                         (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part, a.pmass);
+                         (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse2, a.part, a.pmass);
     e = hipGetLastError();
     prof_end(prof, st);
     if (e != hipSuccess) return e;

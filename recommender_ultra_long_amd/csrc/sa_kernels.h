@@ -32,7 +32,7 @@ struct Plan {
   // backward (dP pass)
   int bchunk, bnchunks, Gb;
   // forward workspace layout (byte offsets)
-  size_t off_status, off_lse, off_part, off_pmass, fwd_bytes;
+  size_t off_status, off_lse, off_lse2, off_part, off_pmass, fwd_bytes;
   // backward workspace layout (byte offsets)
   size_t off_G, off_cv, off_delta, off_dpp, off_blse, bwd_bytes;
 };
@@ -47,6 +47,7 @@ struct FwdArgs {
   const void* X;
   const void* P;
   float* lse;          // [T] (caller's buffer or workspace)
+  float* lse2;         // [T + 1] log2-unit lse and +inf sentinel, or nullptr (bf16 stats only)
   float* S;            // [B, k, d]
   float* mass;         // [B, k] or nullptr
   float* part;         // [nslots, k, d]
