@@ -52,7 +52,7 @@ __device__ __forceinline__ int xoff(int r, int u) { return r * D + ((u ^ xswz<D>
 // two 32-token MFMA tiles.  Prototypes are streamed in chunks of 64 rows
 // through LDS in MFMA fragment order, double buffered via registers.
 template <int D>
-__global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
+__global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__ X,
                                                      const bf16* __restrict__ P, int k,
                                                      int64_t T, float alpha, float scale,
                                                      float* __restrict__ lse_out,
@@ -104,51 +104,94 @@ __global__ __launch_bounds__(256) void sa_stats_bf16(const bf16* __restrict__ X,
   float m[2] = {-INFINITY, -INFINITY};   // running max of raw dot products
   float l[2] = {0.f, 0.f};               // running sum of exp2((z - m) alpha)
 
+  // Folds one 32-prototype x 32-token product tile (register i of a lane is
+  // prototype crow(i, h) of the tile, the lane's token is tt 32 + l32) into
+  // the running max and sum of token tile tt.
+  auto fold = [&](const f32x16& v, int tt) {
+    float t0 = fmaxf(fmaxf(v[0], v[1]), v[2]), t1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+    float t2 = fmaxf(fmaxf(v[6], v[7]), v[8]), t3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+    float t4 = fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15]));
+    const float tmax = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(t3, t4));
+    const float mnew = fmaxf(m[tt], tmax);
+    // A lane whose prototypes are all padding so far keeps m = -inf; a zero
+    // shift then keeps every term at exp2(-inf) = 0 instead of NaN.
+    const float ma = mnew == -INFINITY ? 0.f : mnew * alpha;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      s0 += exp2_fast(fmaf(v[i], alpha, -ma));
+      s1 += exp2_fast(fmaf(v[i + 1], alpha, -ma));
+      s2 += exp2_fast(fmaf(v[i + 2], alpha, -ma));
+      s3 += exp2_fast(fmaf(v[i + 3], alpha, -ma));
+    }
+    l[tt] = fmaf(l[tt], exp2_fast(fmaf(m[tt], alpha, -ma)), (s0 + s1) + (s2 + s3));
+    m[tt] = mnew;
+  };
+
+  // Products of prototype tile pt of the chunk in LDS buffer buf.
+  auto products = [&](int buf, int pt, f32x16& c0, f32x16& c1) {
+    {
+      const bf16x8 a = sP[buf][(pt * KS) * 64 + lane];
+      c0 = mfma32(a, xb[0][0], f32x16{});
+      c1 = mfma32(a, xb[1][0], f32x16{});
+    }
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      const bf16x8 a = sP[buf][(pt * KS + ks) * 64 + lane];
+      c0 = mfma32(a, xb[0][ks], c0);
+      c1 = mfma32(a, xb[1][ks], c1);
+    }
+  };
+
+  // Software pipeline over prototype tiles: the products of tile p are
+  // issued in the same straight-line block as the vector work on tile p - 1,
+  // so the matrix cores and the vector ALU overlap.  All chunks but the last
+  // are full; q starts as an all -inf tile, whose fold changes nothing.
   bf16x8 pre[PPT];
   load_chunk(0, pre);
   store_chunk(0, pre);
   __syncthreads();
   const int nch = (k + PCH - 1) / PCH;
-  for (int ci = 0; ci < nch; ++ci) {
-    const int p0 = ci * PCH;
-    if (ci + 1 < nch) load_chunk(p0 + PCH, pre);
+  f32x16 q0, q1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
+  static_assert(PCH == 64, "two prototype tiles per chunk");
+  for (int ci = 0; ci + 1 < nch; ++ci) {
+    load_chunk((ci + 1) * PCH, pre);
     const int buf = ci & 1;
+    // The two tiles of the chunk swap roles with q, so nothing is copied.
+    f32x16 c0, c1;
+    products(buf, 0, c0, c1);
+    fold(q0, 0);
+    fold(q1, 1);
+    products(buf, 1, q0, q1);
+    fold(c0, 0);
+    fold(c1, 1);
+    store_chunk(buf ^ 1, pre);
+    __syncthreads();
+  }
+  {
+    // Last chunk: tiles may be partial or past k; padding rows drop out as
+    // -inf.
+    const int ci = nch - 1, buf = ci & 1;
 #pragma unroll
     for (int pt = 0; pt < PCH / 32; ++pt) {
-      const int pbase = p0 + pt * 32;
+      const int pbase = ci * PCH + pt * 32;
       if (pbase >= k) break;             // uniform across the block
-      f32x16 c0 = {}, c1 = {};
+      f32x16 c0, c1;
+      products(buf, pt, c0, c1);
+      fold(q0, 0);
+      fold(q1, 1);
+      q0 = c0;
+      q1 = c1;
+      if (pbase + 32 > k) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = sP[buf][(pt * KS + ks) * 64 + lane];
-        c0 = mfma32(a, xb[0][ks], c0);
-        c1 = mfma32(a, xb[1][ks], c1);
-      }
-      const bool partial = pbase + 32 > k;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        f32x16 v = tt == 0 ? c0 : c1;
-        if (partial) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (pbase + crow(i, h) >= k) v[i] = -INFINITY;
-        }
-        float tmax = v[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, v[i]);
-        const float mnew = fmaxf(m[tt], tmax);
-        // A lane whose prototypes are all padding so far keeps m = -inf; a
-        // zero shift then keeps every term at exp2(-inf) = 0 instead of NaN.
-        const float ma = mnew == -INFINITY ? 0.f : mnew * alpha;
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += exp2_fast(fmaf(v[i], alpha, -ma));
-        l[tt] = fmaf(l[tt], exp2_fast(fmaf(m[tt], alpha, -ma)), s);
-        m[tt] = mnew;
+        for (int i = 0; i < 16; ++i)
+          if (pbase + crow(i, h) >= k) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
       }
     }
-    if (ci + 1 < nch) store_chunk(buf ^ 1, pre);
-    __syncthreads();
+    fold(q0, 0);
+    fold(q1, 1);
   }
 
   // Lanes l and l ^ 32 saw disjoint halves of the prototypes of one token.

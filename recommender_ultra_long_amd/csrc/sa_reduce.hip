@@ -34,11 +34,22 @@ __global__ __launch_bounds__(256) void sa_reduce_kernel(
   float mu = 0.f;
   if (hi > lo && live) {
     const int s0 = seg_of(T, G, lo), s1 = seg_of(T, G, hi - 1);
-#pragma unroll 4
-    for (int s = s0 + wave; s <= s1; s += 4) {
-      const int64_t slot = (int64_t)s + u;
-      acc += *(const f32x4*)(part + slot * kd + e);
-      if (use_mass) mu += pmass[slot * k + j];
+    const int n = s1 - s0 + 1;                       // pieces of user u
+    const float* pp = part + ((int64_t)s0 + u) * kd + e;
+    // Wave w adds pieces w, w + 4, ... in increasing order; eight loads are
+    // in flight at a time.
+    int q = wave;
+    for (; q + 28 < n; q += 32) {
+      f32x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = *(const f32x4*)(pp + (int64_t)(q + 4 * r) * kd);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc += v[r];
+    }
+    for (; q < n; q += 4) acc += *(const f32x4*)(pp + (int64_t)q * kd);
+    if (use_mass) {
+      const float* pm = pmass + ((int64_t)s0 + u) * k + j;
+      for (int r = wave; r < n; r += 4) mu += pm[(int64_t)r * k];
     }
   }
   red[wave][lane] = acc;
