@@ -49,6 +49,7 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* 
   p->off_delta = off; off = align256(off + Tn * 4);
   p->off_dpp = off; off = align256(off + (size_t)p->Gb * k * d * 4);
   p->off_blse = off; off = align256(off + Tn * 4);
+  p->off_blse2 = off; off = align256(off + (Tn + 1) * 4);
   p->bwd_bytes = off;
   return true;
 }
@@ -166,6 +167,7 @@ static sa_status backward_impl(const sa_problem* pr, const int64_t* offsets_dev,
   a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
   a.X = X; a.P = P; a.dS = dS;
   a.lse_ws = (float*)(w + p.off_blse);
+  a.lse2 = (float*)(w + p.off_blse2);
   a.recompute_lse = lse == nullptr ? 1 : 0;
   a.lse = lse ? lse : a.lse_ws;
   a.S = S; a.mass = mass;

@@ -218,165 +218,211 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
 }
 
 // ----------------------------------------------------------------------------
-// bf16 dP pass.  grid = (Gb segments, nchunks); block 256 = 4 waves x 64
-// prototypes; the same tiling as the forward aggregation.
-template <int D>
-__global__ __launch_bounds__(256, 1) void sa_bwdp_bf16(
+// bf16 dP pass.  grid = (Gb segments, nchunks); block = NW waves x 32
+// prototypes, the tiling and copy pipeline of the forward aggregation:
+// 32-token tiles copied global -> LDS (X, lse2, delta) six tiles ahead into
+// eight buffers, a barrier after every second tile.  Per tile: Z^T and dA'^T
+// (matrix cores), dZ (vector ALU), dP^T += X^T dZ^T (matrix cores).  The
+// partial spans the whole segment, across users (P is shared).
+//
+// lse2 holds the log-sum-exp in log2 units with lse2[T] = +inf, which rows
+// past the end of a tile read (weight 0, so dZ = 0).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ P, const bf16* __restrict__ Gq, const float* __restrict__ cv, int k,
-    int64_t T, int G, float alpha, const float* __restrict__ lse, const float* __restrict__ delta,
+    int64_t T, int G, float alpha, const float* __restrict__ lse2, const float* __restrict__ delta,
     float* __restrict__ dpp) {
-  constexpr int KS = D / 16, DB = D / 32, PT = 2;
-  constexpr int KC = 4 * PT * 32;
+  constexpr int KS = D / 16;             // reduction steps over d
+  constexpr int DB = D / 32;             // 32-row blocks of the transposed partial
+  constexpr int U = D / 8;               // 16-byte units per token row
+  constexpr int KC = NW * 32;            // prototypes per workgroup
+  static_assert(KC == kChunkBf16, "one workgroup covers one prototype chunk");
   constexpr int TILE = 32;
-  constexpr int ROW = D + 8;
-  constexpr int PIECES = TILE * D / 8;
-  constexpr int PPT = (PIECES + 255) / 256;
+  constexpr int UNITS = TILE * U;
+  constexpr int UPW = UNITS / NW;        // units copied by each wave
+  static_assert(UNITS % NW == 0 && (UPW <= 64 || UPW % 64 == 0), "");
+  constexpr int XI = (UPW + 63) / 64;    // X copy instructions per wave per tile
+  constexpr int LPW = TILE / NW;         // lse and delta entries copied by each wave
+  constexpr int NBUF = 8, AHEAD = 6;
+  constexpr int L = XI + 2;              // loads per wave per tile
+  constexpr uint32_t XBYTES = TILE * D * 2;
 
-  __shared__ __attribute__((aligned(16))) bf16 sX[2][TILE * ROW];
-  __shared__ __attribute__((aligned(16))) float sL[2][TILE];
-  __shared__ __attribute__((aligned(16))) float sD[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sX[NBUF][TILE * D];
+  __shared__ __attribute__((aligned(16))) float sL[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) float sD[NBUF][TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int s = blockIdx.x, chunk = blockIdx.y;
-  const int pw0 = chunk * KC + wave * PT * 32;
+  const int proto = chunk * KC + wave * 32 + l32;   // this lane's prototype
+  const int prow = proto < k ? proto : k - 1;       // rows past k: results unused
+  const uint32_t sx0 = lds_addr((const SA_LDS void*)&sX[0][0]);
+  const uint32_t sl0 = lds_addr((const SA_LDS void*)&sL[0][0]);
+  const uint32_t sd0 = lds_addr((const SA_LDS void*)&sD[0][0]);
+  const SA_LDS char* lds = (const SA_LDS char*)0;
 
-  bf16x8 pw[PT][KS], gw[PT][KS];
-  float cw[PT];
+  // B operands: pw[ks] = P[proto][16 ks + 8h .. +7], gw likewise for the
+  // current user's G; cw = cv[user][proto].
+  bf16x8 pw[KS], gw[KS];
+  float cw;
 #pragma unroll
-  for (int pt = 0; pt < PT; ++pt) {
-    const int row = pw0 + pt * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      pw[pt][ks] = row < k ? *(const bf16x8*)(P + (int64_t)row * D + 16 * ks + 8 * h) : bf16x8{};
-  }
-  auto load_user = [&](int u) {
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-      const int row = pw0 + pt * 32 + l32;
-      const bf16* gr = Gq + ((int64_t)u * k + row) * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        gw[pt][ks] = row < k ? *(const bf16x8*)(gr + 16 * ks + 8 * h) : bf16x8{};
-      cw[pt] = row < k ? cv[(int64_t)u * k + row] : 0.f;
-    }
-  };
+  for (int ks = 0; ks < KS; ++ks) pw[ks] = *(const bf16x8*)(P + (int64_t)prow * D + 16 * ks + 8 * h);
 
-  f32x16 acc[PT][DB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[pt][db] = f32x16{};
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
   const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
-  TileWalker<TILE> cur;
-  cur.start(offsets, B, lo, hi);
-  if (cur.valid) {
-    bf16x8 xr[PPT];
-    float lr = 0.f, dr = 0.f;
-    auto load_tile = [&](int64_t t0, int64_t t1) {
+  TileWalker<TILE> cw_;                // tile being computed
+  cw_.start(offsets, B, lo, hi);
+  if (cw_.valid) {
+    TileWalker<TILE> qw = cw_;         // next tile to copy
+
+    int crow_[XI];
+    uint32_t ccol[XI];
 #pragma unroll
-      for (int e = 0; e < PPT; ++e) {
-        const int q = tid + 256 * e;
-        const int r = q / (D / 8), cp = q % (D / 8);
-        xr[e] = (q < PIECES && t0 + r < t1) ? *(const bf16x8*)(X + (t0 + r) * D + 8 * cp) : bf16x8{};
-      }
-      if (tid < TILE) {
-        const bool in = t0 + tid < t1;
-        lr = in ? lse[t0 + tid] * kLog2e : INFINITY;
-        dr = in ? delta[t0 + tid] : 0.f;
-      }
-    };
-    auto store_tile = [&](int buf) {
+    for (int j = 0; j < XI; ++j) {
+      const int v = wave * UPW + j * 64 + lane;
+      crow_[j] = v / U;
+      ccol[j] = (uint32_t)(((v % U) ^ xswz<D>(v / U)) * 16);
+    }
+    const int lrow = wave * LPW + lane;
+
+    // Every wave issues exactly L loads per tile (also past the end of the
+    // stream), so that vmcnt counts are the same every time.
+    auto copy_next = [&](uint32_t b) {
+      const bool valid = qw.valid;
+      const int64_t base = valid ? qw.t0 : 0;
+      const int nr = valid ? (int)(qw.t1 - qw.t0) : 0;
+      const bf16* xb = X + base * D;
 #pragma unroll
-      for (int e = 0; e < PPT; ++e) {
-        const int q = tid + 256 * e;
-        if (q < PIECES) {
-          const int r = q / (D / 8), cp = q % (D / 8);
-          *(bf16x8*)(&sX[buf][r * ROW + 8 * cp]) = xr[e];
-        }
+      for (int j = 0; j < XI; ++j) {
+        const int r = crow_[j] < nr ? crow_[j] : 0;
+        if (UPW >= 64 || lane < UPW)
+          lds_copy16(xb, (uint32_t)(r * D * 2) + ccol[j],
+                     sx0 + b * XBYTES + (uint32_t)(wave * UPW + j * 64) * 16);
       }
-      if (tid < TILE) { sL[buf][tid] = lr; sD[buf][tid] = dr; }
+      if (lane < LPW) {
+        const bool in = lrow < nr;
+        lds_copy4v(in ? lse2 + base + lrow : lse2 + T, sl0 + (b * TILE + wave * LPW) * 4);
+        lds_copy4v(delta + base + (in ? lrow : 0), sd0 + (b * TILE + wave * LPW) * 4);
+      }
+      if (valid) qw.advance();
     };
 
-    const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
-    load_user(cur.user);
-    load_tile(cur.t0, cur.t1);
-    store_tile(0);
-    __syncthreads();
-    int buf = 0;
-    while (cur.valid) {
-      TileWalker<TILE> nxt = cur;
-      nxt.advance();
-      if (nxt.valid) load_tile(nxt.t0, nxt.t1);
-      const SA_LDS bf16* xs = (const SA_LDS bf16*)&sX[buf][0];
-      f32x16 z[PT], da[PT];
+    int guser = cw_.user;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) { z[pt] = f32x16{}; da[pt] = f32x16{}; }
+    for (int ks = 0; ks < KS; ++ks)
+      gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * k + prow) * D + 16 * ks + 8 * h);
+    cw = cv[(int64_t)guser * k + prow];
+#pragma unroll
+    for (int b = 0; b < AHEAD; ++b) copy_next(b);
+    // The compiler must see the waits for the operand loads above here, not
+    // inside the loop (where they would also wait for every copy in flight).
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(pw[ks]), "v"(gw[ks]));
+    asm volatile("" ::"v"(cw));
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
+    uint32_t aoff[KS], toff[DB][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aoff[ks] = (uint32_t)xoff<D>(l32, 2 * ks + h) * 2;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        toff[db][e] = (uint32_t)(xoff<D>(4 * h + tr_r + 8 * e, 4 * db + 2 * tr_half + (tr_c >> 1)) +
+                                 (tr_c & 1) * 4) * 2;
+    const uint32_t lqoff = (uint32_t)(4 * h) * 4;
+
+    uint32_t t = 0;
+    while (true) {
+      const uint32_t buf = t & (NBUF - 1);
+      copy_next((t + AHEAD) & (NBUF - 1));
+      if (cw_.user != guser) {
+        // A new user: its G rows and cv (rare; waits for the loads here).
+        guser = cw_.user;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * k + prow) * D + 16 * ks + 8 * h);
+        cw = cv[(int64_t)guser * k + prow];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(gw[ks]));
+        asm volatile("" ::"v"(cw));
+      }
+
+      const SA_LDS char* xs = lds + sx0 + buf * XBYTES;
+      // Z^T and dA'^T (tokens x prototypes) of this tile.
+      f32x16 z = f32x16{}, da = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const SA_LDS bf16x8*)(xs + l32 * ROW + 16 * ks + 8 * h);
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          z[pt] = mfma32(a, pw[pt][ks], z[pt]);
-          da[pt] = mfma32(a, gw[pt][ks], da[pt]);
-        }
+        const bf16x8 a = *(const SA_LDS bf16x8*)(xs + aoff[ks]);
+        z = mfma32(a, pw[ks], z);
+        da = mfma32(a, gw[ks], da);
       }
-      const SA_LDS float* ls = (const SA_LDS float*)&sL[buf][0];
-      const SA_LDS float* ds = (const SA_LDS float*)&sD[buf][0];
+      // dZ = A (dA' - cv - delta); register i of a lane is token crow(i, h).
+      const SA_LDS char* ls = lds + sl0 + buf * (TILE * 4) + lqoff;
+      const SA_LDS char* ds = lds + sd0 + buf * (TILE * 4) + lqoff;
       f32x4 lq[4], dq[4];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        lq[g4] = *(const SA_LDS f32x4*)(ls + 8 * g4 + 4 * h);
-        dq[g4] = *(const SA_LDS f32x4*)(ds + 8 * g4 + 4 * h);
+      for (int g = 0; g < 4; ++g) {
+        lq[g] = *(const SA_LDS f32x4*)(ls + 32 * g);
+        dq[g] = *(const SA_LDS f32x4*)(ds + 32 * g);
       }
-      bf16x8 zbf[PT][2];
+      bf16x8 zbf[2];
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
+      for (int i = 0; i < 16; ++i) {
+        const float a = exp2_fast(fmaf(z[i], alpha, -lq[i >> 2][i & 3]));
+        zbf[i >> 3][i & 7] = (bf16)(a * (da[i] - cw - dq[i >> 2][i & 3]));
+      }
+      // dP^T (d x prototypes) += X^T (d x tokens) dZ^T (tokens x prototypes).
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float a = exp2_fast(fmaf(z[pt][i], alpha, -lq[i >> 2][i & 3]));
-          const float dz = a * (da[pt][i] - cw[pt] - dq[i >> 2][i & 3]);
-          zbf[pt][i >> 3][i & 7] = (bf16)dz;
+      for (int db = 0; db < DB; ++db) {
+        const SA_LDS char* p0 = xs + toff[db][0];
+        const SA_LDS char* p1 = xs + toff[db][1];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 xt = concat4(lds_read_tr16((const SA_LDS bf16*)(p0 + kb * 32 * D)),
+                                    lds_read_tr16((const SA_LDS bf16*)(p1 + kb * 32 * D)));
+          acc[db] = mfma32(xt, zbf[kb], acc[db]);
         }
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int row0 = 16 * kb + 4 * h + tr_r;
-          const int col = 32 * db + 16 * tr_half + 4 * tr_c;
-          const bf16x8 a = concat4(lds_read_tr16(xs + row0 * ROW + col),
-                                   lds_read_tr16(xs + (row0 + 8) * ROW + col));
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt) acc[pt][db] = mfma32(a, zbf[pt][kb], acc[pt][db]);
-        }
+
+      cw_.advance();
+      if (!cw_.valid) break;
+      if (t & 1) {
+        // The next two steps read tiles up to t+2; t+3 .. t+6 may be in flight.
+        wait_vmcnt<4 * L>();
+        barrier_lds();
       }
-      if (nxt.valid && nxt.user != cur.user) load_user(nxt.user);
-      if (nxt.valid) store_tile(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-      cur = nxt;
+      ++t;
     }
+    wait_vmcnt<0>();   // no copy left in flight
   }
-  // Flush this segment's partial: acc[pt][db] register i is
-  // dP[proto = pw0 + 32 pt + l32][d = 32 db + crow(i, h)] / c.
+  // Flush this segment's partial: acc[db] register i is
+  // dP[proto][d = 32 db + crow(i, h)] / c.
+  if (proto < k) {
+    float* dst = dpp + ((int64_t)s * k + proto) * D;
 #pragma unroll
-  for (int pt = 0; pt < PT; ++pt) {
-    const int proto = pw0 + pt * 32 + l32;
-    if (proto < k) {
-      float* dst = dpp + ((int64_t)s * k + proto) * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 v = {acc[pt][db][4 * g4], acc[pt][db][4 * g4 + 1], acc[pt][db][4 * g4 + 2],
-                     acc[pt][db][4 * g4 + 3]};
-          *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * h) = v;
-        }
-    }
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+        *(f32x4*)(dst + 32 * db + 8 * g + 4 * h) = v;
+      }
   }
+}
+
+// lse in log2 units with the +inf sentinel at index T (for the dP pass when
+// the caller supplies the forward's lse).
+__global__ __launch_bounds__(256) void sa_lse2_kernel(const float* __restrict__ lse, int64_t T,
+                                                      float* __restrict__ lse2) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < T) lse2[i] = lse[i] * kLog2e;
+  else if (i == T) lse2[i] = INFINITY;
 }
 
 // ----------------------------------------------------------------------------
@@ -562,7 +608,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
   if (a.recompute_lse && a.T > 0) {
     FwdArgs f = {};
     f.X = a.X; f.P = a.P; f.k = a.k; f.d = a.d; f.T = a.T; f.lse = a.lse_ws;
+    f.lse2 = dtype == 1 ? a.lse2 : nullptr;
     e = dtype == 1 ? launch_stats_bf16(f, st, prof) : launch_stats_f32(f, st, prof);
+    if (e != hipSuccess) return e;
+  } else if (dtype == 1 && a.T > 0) {
+    prof_begin(prof, "sa_lse2", st);
+    hipLaunchKernelGGL(sa_lse2_kernel, dim3((unsigned)((a.T + 1 + 255) / 256)), dim3(256), 0, st,
+                       a.lse, a.T, a.lse2);
+    e = hipGetLastError();
+    prof_end(prof, st);
     if (e != hipSuccess) return e;
   }
   const int64_t rows = (int64_t)a.B * a.k;
@@ -588,9 +642,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
       prof_end(prof, st);
       if (e != hipSuccess) return e;
       prof_begin(prof, "sa_bwdp_bf16", st);
-      hipLaunchKernelGGL(sa_bwdp_bf16<D>, dim3(a.Gb, a.bnchunks), dim3(256), 0, st, a.offsets, a.B,
-                         (const bf16*)a.X, (const bf16*)a.P, (const bf16*)a.Gq, a.cv, a.k, a.T,
-                         a.Gb, alpha, a.lse, a.delta, a.dpp);
+      hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves>), dim3(a.Gb, a.bnchunks), dim3(64 * kBwdpWaves),
+                         0, st, a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.P,
+                         (const bf16*)a.Gq, a.cv, a.k, a.T, a.Gb, alpha, a.lse2, a.delta, a.dpp);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;

@@ -158,6 +158,23 @@ __device__ __forceinline__ void check_offsets_block(const int64_t* offsets, int 
   if (threadIdx.x == 0) *status = bad ? bad_code : ok;
 }
 
+// LDS layout of a 32-token x D tile without padding: row r holds D/8 units of
+// 16 bytes, unit u stored at position u ^ xswz(r).  The swizzle makes both
+// access patterns bank-conflict free:
+//  - 16 lanes reading one unit of 16 consecutive rows (the affinity product's
+//    A operand), and
+//  - 32 lanes transpose-reading 4 consecutive rows x one 32-column block (the
+//    aggregation product's A operand).
+template <int D>
+__device__ __forceinline__ int xswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return (r >> 2) & 3;
+}
+
+template <int D>
+__device__ __forceinline__ int xoff(int r, int u) { return r * D + ((u ^ xswz<D>(r)) << 3); }
+
 // Walks the pieces of one segment in token order, in tiles of TILE tokens.
 // A tile never straddles two users.
 template <int TILE>

@@ -29,24 +29,6 @@
 namespace sa {
 
 // ----------------------------------------------------------------------------
-// LDS layout of a 32-token x D tile without padding: row r holds D/8 units of
-// 16 bytes, unit u stored at position u ^ xswz(r).  The swizzle makes both
-// access patterns bank-conflict free:
-//  - 16 lanes reading one unit of 16 consecutive rows (the affinity product's
-//    A operand), and
-//  - 32 lanes transpose-reading 4 consecutive rows x one 32-column block (the
-//    aggregation product's A operand).
-template <int D>
-__device__ __forceinline__ int xswz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  else return (r >> 2) & 3;
-}
-
-template <int D>
-__device__ __forceinline__ int xoff(int r, int u) { return r * D + ((u ^ xswz<D>(r)) << 3); }
-
-// ----------------------------------------------------------------------------
 // Pass 1: per-token log-sum-exp over all k prototypes.
 // Block: 256 threads = 4 waves; wave w handles tokens blk*256 + 64w .. +63 as
 // two 32-token MFMA tiles.  Prototypes are streamed in chunks of 64 rows

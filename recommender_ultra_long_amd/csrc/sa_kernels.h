@@ -16,6 +16,7 @@ constexpr int kChunkF32 = 64;       // prototypes per fp32 forward aggregation w
 constexpr int kChunkF32Bwd = 32;    // prototypes per fp32 backward dP workgroup
 constexpr int kBwdxTokensBf16 = 128;  // tokens per bf16 dX workgroup
 constexpr int kBwdxTokensF32 = 32;    // tokens per fp32 dX workgroup
+constexpr int kBwdpWaves = 8;         // waves of a bf16 dP workgroup (32 prototypes each)
 
 // Device status word values written into the first bytes of the workspace.
 constexpr uint32_t kStatusOk = 0u;
@@ -34,7 +35,7 @@ struct Plan {
   // forward workspace layout (byte offsets)
   size_t off_status, off_lse, off_lse2, off_part, off_pmass, fwd_bytes;
   // backward workspace layout (byte offsets)
-  size_t off_G, off_cv, off_delta, off_dpp, off_blse, bwd_bytes;
+  size_t off_G, off_cv, off_delta, off_dpp, off_blse, off_blse2, bwd_bytes;
 };
 
 // Fills the plan; returns false for an unsupported problem.
@@ -66,6 +67,7 @@ struct BwdArgs {
   const float* dS;     // [B, k, d]
   const float* lse;    // [T] (caller's, or lse_ws after recomputation)
   float* lse_ws;       // [T]
+  float* lse2;         // [T + 1] log2-unit lse with +inf sentinel (bf16 dP pass)
   const float* S;      // [B, k, d] (mass norm only)
   const float* mass;   // [B, k]    (mass norm only)
   float* dX;           // [T, d]
