@@ -131,9 +131,11 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
       if (tid < PCH) sC[buf][tid] = rc;
     };
 
-    f32x16 ag[DB], aa[DB], ab[DB];
+    // acc1 = g + c b = sum_j (A_ji G_j + c w_ji p_j) (one accumulator for
+    // both products), acc2 = a = sum_j A_ji p_j.
+    f32x16 acc1[DB], acc2[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { ag[db] = f32x16{}; aa[db] = f32x16{}; ab[db] = f32x16{}; }
+    for (int db = 0; db < DB; ++db) { acc1[db] = f32x16{}; acc2[db] = f32x16{}; }
     float dsum = 0.f;
 
     __syncthreads();   // previous user's last chunk fully consumed
@@ -172,9 +174,9 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
           const float w = a * (da[i] - cq[i >> 2][i & 3]);
           dsum += w;
           abf[i >> 3][i & 7] = (bf16)a;
-          wbf[i >> 3][i & 7] = (bf16)w;
+          wbf[i >> 3][i & 7] = (bf16)(scale * w);
         }
-        // {g, a, b}^T (d x tokens) += {G, P, P}^T (d x prototypes) {A, A, w}.
+        // {acc1, acc2}^T (d x tokens) += {G, P, P}^T (d x prototypes) {A, c w, A}.
         // K slot j of half h in block kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -186,9 +188,9 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
                                       lds_read_tr16(gs + (row0 + 8) * ROW + col));
             const bf16x8 pT = concat4(lds_read_tr16(ps + row0 * ROW + col),
                                       lds_read_tr16(ps + (row0 + 8) * ROW + col));
-            ag[db] = mfma32(gT, abf[kb], ag[db]);
-            aa[db] = mfma32(pT, abf[kb], aa[db]);
-            ab[db] = mfma32(pT, wbf[kb], ab[db]);
+            acc1[db] = mfma32(gT, abf[kb], acc1[db]);
+            acc1[db] = mfma32(pT, wbf[kb], acc1[db]);
+            acc2[db] = mfma32(pT, abf[kb], acc2[db]);
           }
         }
       }
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * g4 + r;
-            v[r] = ag[db][i] + scale * (ab[db][i] - delta * aa[db][i]);
+            v[r] = acc1[db][i] - scale * delta * acc2[db][i];
           }
           *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * h) = v;
         }
