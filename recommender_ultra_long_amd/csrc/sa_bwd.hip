@@ -31,13 +31,23 @@
 namespace sa {
 
 // ----------------------------------------------------------------------------
-// G and cv.  One group of D/4 threads per (user, prototype) row.
+// G and cv.  One group of D/4 threads per (user, prototype) row.  Blocks from
+// nbrows on instead write lse2 = lse log2(e) for the dP pass, with the +inf
+// sentinel at index T (when lse2 is not null).
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void sa_bwd_prep(const float* __restrict__ dS,
                                                    const float* __restrict__ S,
                                                    const float* __restrict__ mass, int64_t rows,
                                                    int mass_norm, OutT* __restrict__ Gq,
-                                                   float* __restrict__ cv) {
+                                                   float* __restrict__ cv, unsigned nbrows,
+                                                   const float* __restrict__ lse, int64_t T,
+                                                   float* __restrict__ lse2) {
+  if (blockIdx.x >= nbrows) {
+    const int64_t i = (int64_t)(blockIdx.x - nbrows) * 256 + threadIdx.x;
+    if (i < T) lse2[i] = lse[i] * kLog2e;
+    else if (i == T) lse2[i] = INFINITY;
+    return;
+  }
   constexpr int TPR = D / 4;   // threads per row (8, 16 or 32)
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gt / TPR;
@@ -418,14 +428,6 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
   }
 }
 
-// lse in log2 units with the +inf sentinel at index T (for the dP pass when
-// the caller supplies the forward's lse).
-__global__ __launch_bounds__(256) void sa_lse2_kernel(const float* __restrict__ lse, int64_t T,
-                                                      float* __restrict__ lse2) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < T) lse2[i] = lse[i] * kLog2e;
-  else if (i == T) lse2[i] = INFINITY;
-}
 
 // ----------------------------------------------------------------------------
 // fp32 dX pass.  grid = ceil(T / 32); block 256 = 32 tokens x 8 threads, each
@@ -585,20 +587,37 @@ __global__ __launch_bounds__(256) void sa_bwdp_f32(
 }
 
 // ----------------------------------------------------------------------------
-// dP = c * sum_s dpp[s] in segment order; block 0 also checks the offsets.
+// dP = c * sum_s dpp[s]; block 0 also checks the offsets.  Block = 4 waves
+// over 256 consecutive elements: wave w adds segments w, w + 4, ... (eight
+// loads in flight), and the four wave sums are added in wave order, so the
+// result does not depend on scheduling.
 __global__ __launch_bounds__(256) void sa_dp_reduce(const int64_t* __restrict__ offsets, int B,
                                                     int64_t T, int k, int d, int G, float scale,
                                                     const float* __restrict__ dpp,
                                                     float* __restrict__ dP,
                                                     uint32_t* __restrict__ status) {
+  __shared__ f32x4 red[4][64];
   if (blockIdx.x == 0) check_offsets_block(offsets, B, T, status, kStatusOk, kStatusBadOffsets);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t kd = (int64_t)k * d;
-  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= kd) return;
+  const int64_t e = ((int64_t)blockIdx.x * 64 + lane) * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (T > 0)
-    for (int s = 0; s < G; ++s) acc += *(const f32x4*)(dpp + (int64_t)s * kd + e);
-  *(f32x4*)(dP + e) = acc * scale;
+  if (T > 0 && e < kd) {
+    const float* pp = dpp + e;
+    int q = wave;
+    for (; q + 28 < G; q += 32) {
+      f32x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = *(const f32x4*)(pp + (int64_t)(q + 4 * r) * kd);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc += v[r];
+    }
+    for (; q < G; q += 4) acc += *(const f32x4*)(pp + (int64_t)q * kd);
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && e < kd)
+    *(f32x4*)(dP + e) = (red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane]) * scale;
 }
 
 // ----------------------------------------------------------------------------
@@ -613,23 +632,20 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
     f.lse2 = dtype == 1 ? a.lse2 : nullptr;
     e = dtype == 1 ? launch_stats_bf16(f, st, prof) : launch_stats_f32(f, st, prof);
     if (e != hipSuccess) return e;
-  } else if (dtype == 1 && a.T > 0) {
-    prof_begin(prof, "sa_lse2", st);
-    hipLaunchKernelGGL(sa_lse2_kernel, dim3((unsigned)((a.T + 1 + 255) / 256)), dim3(256), 0, st,
-                       a.lse, a.T, a.lse2);
-    e = hipGetLastError();
-    prof_end(prof, st);
-    if (e != hipSuccess) return e;
   }
   const int64_t rows = (int64_t)a.B * a.k;
   const unsigned nbp = (unsigned)((rows * (D / 4) + 255) / 256);
+  // The bf16 dP pass reads lse in log2 units; when the caller supplied lse
+  // (not recomputed above), the prep kernel's extra blocks convert it.
+  const bool lse2 = dtype == 1 && a.T > 0 && !a.recompute_lse;
+  const unsigned nbl = lse2 ? (unsigned)((a.T + 1 + 255) / 256) : 0u;
   prof_begin(prof, "sa_bwd_prep", st);
   if (dtype == 1)
-    hipLaunchKernelGGL((sa_bwd_prep<bf16, D>), dim3(nbp), dim3(256), 0, st, a.dS, a.S, a.mass, rows,
-                       a.mass_norm, (bf16*)a.Gq, a.cv);
+    hipLaunchKernelGGL((sa_bwd_prep<bf16, D>), dim3(nbp + nbl), dim3(256), 0, st, a.dS, a.S, a.mass,
+                       rows, a.mass_norm, (bf16*)a.Gq, a.cv, nbp, a.lse, a.T, a.lse2);
   else
     hipLaunchKernelGGL((sa_bwd_prep<float, D>), dim3(nbp), dim3(256), 0, st, a.dS, a.S, a.mass,
-                       rows, a.mass_norm, (float*)a.Gq, a.cv);
+                       rows, a.mass_norm, (float*)a.Gq, a.cv, nbp, a.lse, a.T, a.lse2);
   e = hipGetLastError();
   prof_end(prof, st);
   if (e != hipSuccess) return e;
@@ -670,7 +686,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
   }
   const int64_t kd = (int64_t)a.k * a.d;
   prof_begin(prof, "sa_dp_reduce", st);
-  hipLaunchKernelGGL(sa_dp_reduce, dim3((unsigned)((kd / 4 + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(sa_dp_reduce, dim3((unsigned)((kd + 255) / 256)), dim3(256), 0, st,
                      a.offsets, a.B, a.T, a.k, a.d, a.Gb, scale, a.dpp, a.dP, a.status);
   e = hipGetLastError();
   prof_end(prof, st);
