@@ -107,12 +107,18 @@ __device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 
 // appear in increasing (s, u) order and consecutive pieces raise s + u by at
 // least one.  The slot count is therefore G + B - 1.
 __device__ __forceinline__ int64_t seg_lo(int64_t T, int G, int s) {
-  return (T * (int64_t)s) / G;   // T < 2^36 and s < 2^16: no overflow
+  // floor(T s / G) without a 64-bit integer division: T s < 2^44 is exact in
+  // double, and the integer check makes the rounded quotient exact.
+  const int64_t x = T * (int64_t)s;
+  int64_t q = (int64_t)((double)x / (double)G);
+  if (q * G > x) --q;
+  else if ((q + 1) * G <= x) ++q;
+  return q;
 }
 
 // Largest s with seg_lo(s) <= t (the segment holding token t).
 __device__ __forceinline__ int seg_of(int64_t T, int G, int64_t t) {
-  int s = (int)((t * (int64_t)G) / T);
+  int s = (int)((double)t * (double)G / (double)T);
   if (s > G - 1) s = G - 1;
   if (s < 0) s = 0;
   while (s + 1 < G && seg_lo(T, G, s + 1) <= t) ++s;

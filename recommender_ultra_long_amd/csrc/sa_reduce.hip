@@ -49,7 +49,15 @@ __global__ __launch_bounds__(256) void sa_reduce_kernel(
     for (; q < n; q += 4) acc += *(const f32x4*)(pp + (int64_t)q * kd);
     if (use_mass) {
       const float* pm = pmass + ((int64_t)s0 + u) * k + j;
-      for (int r = wave; r < n; r += 4) mu += pm[(int64_t)r * k];
+      int r = wave;
+      for (; r + 28 < n; r += 32) {
+        float m8[8];
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) m8[q8] = pm[(int64_t)(r + 4 * q8) * k];
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) mu += m8[q8];
+      }
+      for (; r < n; r += 4) mu += pm[(int64_t)r * k];
     }
   }
   red[wave][lane] = acc;
