@@ -76,27 +76,42 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(const float* __restrict__ dS,
 // bf16 dX pass.  grid = ceil(T / 128); block 256 = 4 waves x 32 tokens.
 // Tokens of the workgroup that belong to different users are handled one
 // user at a time (the others are masked), because G depends on the user.
+// For each user, 64-prototype chunks of P and G (and cv) are copied
+// global -> LDS by the direct-to-LDS loads three chunks ahead into four
+// buffers (rows stored with the tile swizzle of sa_device.h), one barrier per
+// chunk.  Per 32-prototype tile: Z and dA' on the matrix cores (Z = P X^T
+// orientation, a token per lane, X rows resident as B operands), the weights
+// A and w on the vector ALU, then
+//   acc1^T += G^T A + P^T (c w),  acc2^T += P^T A
+// with the A operands transpose-read from LDS; dX = acc1 - c delta acc2.
 template <int D>
 __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ P, const bf16* __restrict__ Gq, const float* __restrict__ cv, int k,
     int64_t T, float alpha, float scale, const float* __restrict__ lse, float* __restrict__ dX,
     float* __restrict__ delta_out) {
-  constexpr int KS = D / 16, DB = D / 32;
-  constexpr int PCH = 64;                 // prototypes per LDS chunk
-  constexpr int ROW = D + 8;              // padded LDS row (elements)
-  constexpr int PIECES = PCH * D / 8;     // 16-byte pieces per matrix chunk
-  constexpr int PPT = PIECES / 256;       // per thread, per matrix
-  static_assert(PPT >= 1, "");
-  __shared__ __attribute__((aligned(16))) bf16 sP[2][PCH * ROW];
-  __shared__ __attribute__((aligned(16))) bf16 sG[2][PCH * ROW];
-  __shared__ __attribute__((aligned(16))) float sC[2][PCH];
+  constexpr int KS = D / 16, DB = D / 32, U = D / 8;
+  constexpr int PCH = 64;                 // prototypes per chunk
+  constexpr int NB = 4, AHEAD = 3;        // chunk buffers, copy distance
+  constexpr int CU = PCH * U;             // 16-byte units per matrix chunk
+  constexpr int UPW = CU / 4;             // units per wave per matrix
+  static_assert(UPW % 64 == 0, "");
+  constexpr int XI = UPW / 64;            // copy instructions per wave per matrix
+  constexpr int L = 2 * XI + 1;           // loads per wave per chunk
+  constexpr uint32_t CBYTES = PCH * D * 2;
+  __shared__ __attribute__((aligned(16))) bf16 sP[NB][PCH * D];
+  __shared__ __attribute__((aligned(16))) bf16 sG[NB][PCH * D];
+  __shared__ __attribute__((aligned(16))) float sC[NB][PCH];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int64_t r0 = (int64_t)blockIdx.x * kBwdxTokensBf16;
   const int64_t r1 = r0 + kBwdxTokensBf16 < T ? r0 + kBwdxTokensBf16 : T;
   const int64_t tok = r0 + wave * 32 + l32;
+  const uint32_t sp0 = lds_addr((const SA_LDS void*)&sP[0][0]);
+  const uint32_t sg0 = lds_addr((const SA_LDS void*)&sG[0][0]);
+  const uint32_t sc0 = lds_addr((const SA_LDS void*)&sC[0][0]);
+  const SA_LDS char* lds = (const SA_LDS char*)0;
 
   bf16x8 xb[KS];
 #pragma unroll
@@ -104,12 +119,35 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
     xb[ks] = tok < r1 ? *(const bf16x8*)(X + tok * D + 16 * ks + 8 * h) : bf16x8{};
   const float l2 = tok < r1 ? lse[tok] * kLog2e : INFINITY;
 
+  // Copy geometry (per matrix): instruction j of this wave moves units
+  // v0 .. v0 + 63, v0 = wave UPW + 64 j; unit v is row v / U at stored
+  // position v % U, holding global unit (v % U) ^ g(row).
+  int crow_[XI];
+  uint32_t ccol[XI];
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int v = wave * UPW + j * 64 + lane;
+    crow_[j] = v / U;
+    ccol[j] = (uint32_t)(((v % U) ^ xswz<D>(v / U)) * 16);
+  }
+  // LDS byte offsets within a chunk buffer (prototype rows).
   const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
+  uint32_t aoff[KS], toff[DB][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) aoff[ks] = (uint32_t)xoff<D>(l32, 2 * ks + h) * 2;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      toff[db][e] = (uint32_t)(xoff<D>(4 * h + tr_r + 8 * e, 4 * db + 2 * tr_half + (tr_c >> 1)) +
+                               (tr_c & 1) * 4) * 2;
+  const uint32_t cqoff = (uint32_t)(4 * h) * 4;
   const int nch = (k + PCH - 1) / PCH;
 
   int u = first_user_after(offsets, B, r0);
   for (; u < B; ++u) {
-    const int64_t ulo = clamp64(offsets[u], r0, r1), uhi = clamp64(offsets[u + 1], ulo, r1);
+    const int64_t ulo = clamp64(uload64(offsets + u), r0, r1);
+    const int64_t uhi = clamp64(uload64(offsets + u + 1), ulo, r1);
     if (ulo >= r1) break;
     if (uhi <= ulo) continue;
     const bool mine = tok >= ulo && tok < uhi;
@@ -117,28 +155,21 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
     const bf16* Gu = Gq + (int64_t)u * k * D;
     const float* cvu = cv + (int64_t)u * k;
 
-    bf16x8 rp[PPT], rg[PPT];
-    float rc = 0.f;
-    auto load_chunk = [&](int p0) {
+    // Copy chunk c (rows past k repeat row k - 1, and cv past k reads
+    // cv[k - 1]; their weights are zeroed below) into buffer b.  Every wave
+    // issues exactly L loads per chunk, also for chunks past the end.
+    auto copy_chunk = [&](int c, uint32_t b) {
+      const int p0 = c < nch ? c * PCH : 0;
 #pragma unroll
-      for (int e = 0; e < PPT; ++e) {
-        const int q = tid + 256 * e;
-        const int r = q / (D / 8), cp = q % (D / 8);
-        const int row = p0 + r;
-        rp[e] = row < k ? *(const bf16x8*)(P + (int64_t)row * D + 8 * cp) : bf16x8{};
-        rg[e] = row < k ? *(const bf16x8*)(Gu + (int64_t)row * D + 8 * cp) : bf16x8{};
+      for (int j = 0; j < XI; ++j) {
+        const int row = min(p0 + crow_[j], k - 1);
+        const uint32_t dst = b * CBYTES + (uint32_t)(wave * UPW + j * 64) * 16;
+        lds_copy16(P, (uint32_t)row * (D * 2) + ccol[j], sp0 + dst);
+        lds_copy16(Gu, (uint32_t)row * (D * 2) + ccol[j], sg0 + dst);
       }
-      if (tid < PCH) rc = p0 + tid < k ? cvu[p0 + tid] : 0.f;
-    };
-    auto store_chunk = [&](int buf) {
-#pragma unroll
-      for (int e = 0; e < PPT; ++e) {
-        const int q = tid + 256 * e;
-        const int r = q / (D / 8), cp = q % (D / 8);
-        *(bf16x8*)(&sP[buf][r * ROW + 8 * cp]) = rp[e];
-        *(bf16x8*)(&sG[buf][r * ROW + 8 * cp]) = rg[e];
-      }
-      if (tid < PCH) sC[buf][tid] = rc;
+      if (lane < PCH / 4)
+        lds_copy4v(cvu + min(p0 + wave * (PCH / 4) + lane, k - 1),
+                   sc0 + (b * PCH + wave * (PCH / 4)) * 4);
     };
 
     // acc1 = g + c b = sum_j (A_ji G_j + c w_ji p_j) (one accumulator for
@@ -148,33 +179,34 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
     for (int db = 0; db < DB; ++db) { acc1[db] = f32x16{}; acc2[db] = f32x16{}; }
     float dsum = 0.f;
 
-    __syncthreads();   // previous user's last chunk fully consumed
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
+    barrier_lds();   // the previous user's chunks are fully consumed
+#pragma unroll
+    for (int c = 0; c < AHEAD; ++c) copy_chunk(c, c);
+    wait_vmcnt<0>();
+    barrier_lds();
     for (int ci = 0; ci < nch; ++ci) {
-      const int p0 = ci * PCH;
-      const int buf = ci & 1;
-      if (ci + 1 < nch) load_chunk(p0 + PCH);
-      const SA_LDS bf16* ps = (const SA_LDS bf16*)&sP[buf][0];
-      const SA_LDS bf16* gs = (const SA_LDS bf16*)&sG[buf][0];
-      const SA_LDS float* cs = (const SA_LDS float*)&sC[buf][0];
+      const uint32_t buf = ci & (NB - 1);
+      copy_chunk(ci + AHEAD, (ci + AHEAD) & (NB - 1));   // into the buffer of chunk ci - 1
+      const SA_LDS char* ps = lds + sp0 + buf * CBYTES;
+      const SA_LDS char* gs = lds + sg0 + buf * CBYTES;
+      const SA_LDS char* cs = lds + sc0 + buf * (PCH * 4) + cqoff;
 #pragma unroll
       for (int pt = 0; pt < PCH / 32; ++pt) {
-        const int pbase = p0 + pt * 32;
+        const int pbase = ci * PCH + pt * 32;
         if (pbase >= k) break;   // uniform
+        const uint32_t rb = (uint32_t)(pt * 32 * D * 2);   // byte offset of the tile's rows
         // Z and dA' tiles: rows = prototypes pbase + crow(i, h), column = token.
-        f32x16 z = {}, da = {};
+        f32x16 z = f32x16{}, da = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ap = *(const SA_LDS bf16x8*)(ps + (pt * 32 + l32) * ROW + 16 * ks + 8 * h);
-          const bf16x8 agr = *(const SA_LDS bf16x8*)(gs + (pt * 32 + l32) * ROW + 16 * ks + 8 * h);
+          const bf16x8 ap = *(const SA_LDS bf16x8*)(ps + rb + aoff[ks]);
+          const bf16x8 agr = *(const SA_LDS bf16x8*)(gs + rb + aoff[ks]);
           z = mfma32(ap, xb[ks], z);
           da = mfma32(agr, xb[ks], da);
         }
         f32x4 cq[4];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) cq[g4] = *(const SA_LDS f32x4*)(cs + pt * 32 + 8 * g4 + 4 * h);
+        for (int g4 = 0; g4 < 4; ++g4) cq[g4] = *(const SA_LDS f32x4*)(cs + pt * 128 + 32 * g4);
         const bool partial = pbase + 32 > k;
         bf16x8 abf[2], wbf[2];
 #pragma unroll
@@ -189,24 +221,27 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
         // {acc1, acc2}^T (d x tokens) += {G, P, P}^T (d x prototypes) {A, c w, A}.
         // K slot j of half h in block kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int db = 0; db < DB; ++db) {
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int row0 = pt * 32 + 16 * kb + 4 * h + tr_r;
-            const int col = 32 * db + 16 * tr_half + 4 * tr_c;
-            const bf16x8 gT = concat4(lds_read_tr16(gs + row0 * ROW + col),
-                                      lds_read_tr16(gs + (row0 + 8) * ROW + col));
-            const bf16x8 pT = concat4(lds_read_tr16(ps + row0 * ROW + col),
-                                      lds_read_tr16(ps + (row0 + 8) * ROW + col));
+          for (int kb = 0; kb < 2; ++kb) {
+            const uint32_t o0 = rb + (uint32_t)(kb * 16 * D * 2) + toff[db][0];
+            const uint32_t o1 = rb + (uint32_t)(kb * 16 * D * 2) + toff[db][1];
+            const bf16x8 gT = concat4(lds_read_tr16((const SA_LDS bf16*)(gs + o0)),
+                                      lds_read_tr16((const SA_LDS bf16*)(gs + o1)));
+            const bf16x8 pT = concat4(lds_read_tr16((const SA_LDS bf16*)(ps + o0)),
+                                      lds_read_tr16((const SA_LDS bf16*)(ps + o1)));
             acc1[db] = mfma32(gT, abf[kb], acc1[db]);
             acc1[db] = mfma32(pT, wbf[kb], acc1[db]);
             acc2[db] = mfma32(pT, abf[kb], acc2[db]);
           }
         }
       }
-      if (ci + 1 < nch) store_chunk(buf ^ 1);
-      __syncthreads();
+      // Chunk ci + 1 must be complete before the barrier; chunks ci + 2 and
+      // ci + 3 may still be in flight.
+      wait_vmcnt<2 * L>();
+      barrier_lds();
     }
+    wait_vmcnt<0>();
 
     const float delta = dsum + shfl_xor32(dsum);
     if (mine) {
