@@ -44,8 +44,12 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* 
 
   const size_t esz = dtype == 1 ? 2 : 4;
   off = 256;   // status word shared with the forward layout
-  p->off_G = off; off = align256(off + (size_t)B * k * d * esz);
-  p->off_cv = off; off = align256(off + (size_t)B * k * 4);
+  p->kp = dtype == 1 ? (k + kBwdxChunkBf16 - 1) / kBwdxChunkBf16 * kBwdxChunkBf16 : k;
+  const size_t kp = (size_t)p->kp;
+  p->off_G = off; off = align256(off + (size_t)B * kp * d * esz);
+  p->off_cv = off; off = align256(off + (size_t)B * kp * 4);
+  p->off_cvs = off; off = align256(off + (size_t)B * kp * 4);
+  p->off_Pq = off; off = align256(off + kp * d * 2);
   p->off_delta = off; off = align256(off + Tn * 4);
   p->off_dpp = off; off = align256(off + (size_t)p->Gb * k * d * 4);
   p->off_blse = off; off = align256(off + Tn * 4);
@@ -174,6 +178,9 @@ static sa_status backward_impl(const sa_problem* pr, const int64_t* offsets_dev,
   a.dX = dX; a.dP = dP;
   a.Gq = (void*)(w + p.off_G);
   a.cv = (float*)(w + p.off_cv);
+  a.cvs = (float*)(w + p.off_cvs);
+  a.Pq = (void*)(w + p.off_Pq);
+  a.kp = p.kp;
   a.delta = (float*)(w + p.off_delta);
   a.dpp = (float*)(w + p.off_dpp);
   a.status = (uint32_t*)(w + p.off_status);

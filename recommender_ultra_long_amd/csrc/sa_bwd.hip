@@ -31,76 +31,122 @@
 namespace sa {
 
 // ----------------------------------------------------------------------------
-// G and cv.  One group of D/4 threads per (user, prototype) row.  Blocks from
-// nbrows on instead write lse2 = lse log2(e) for the dP pass, with the +inf
-// sentinel at index T (when lse2 is not null).
+// G, cv and the padded copies.  Rows of G and cv have stride kp >= k; rows
+// from k on are zero.  Block ranges:
+//   [0, nbg)          one group of D/4 threads per (user, prototype) row: G in
+//                     the input dtype, cv, and -cv (when cvs is not null);
+//   [nbg, nbg + nbq)  Pq = P with zero rows k .. kp - 1, 16 bytes per thread
+//                     (bf16 only);
+//   from nbg + nbq    lse2 = lse log2(e), with the +inf sentinel at index T.
 template <typename OutT, int D>
-__global__ __launch_bounds__(256) void sa_bwd_prep(const float* __restrict__ dS,
-                                                   const float* __restrict__ S,
-                                                   const float* __restrict__ mass, int64_t rows,
-                                                   int mass_norm, OutT* __restrict__ Gq,
-                                                   float* __restrict__ cv, unsigned nbrows,
-                                                   const float* __restrict__ lse, int64_t T,
-                                                   float* __restrict__ lse2) {
-  if (blockIdx.x >= nbrows) {
-    const int64_t i = (int64_t)(blockIdx.x - nbrows) * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void sa_bwd_prep(
+    const float* __restrict__ dS, const float* __restrict__ S, const float* __restrict__ mass,
+    int B, int k, int kp, int mass_norm, float scale, OutT* __restrict__ Gq,
+    float* __restrict__ cv, float* __restrict__ cvs, unsigned nbg, const bf16* __restrict__ P,
+    bf16* __restrict__ Pq, unsigned nbq, const float* __restrict__ lse, int64_t T,
+    float* __restrict__ lse2) {
+  if (blockIdx.x >= nbg + nbq) {
+    const int64_t i = (int64_t)(blockIdx.x - nbg - nbq) * 256 + threadIdx.x;
     if (i < T) lse2[i] = lse[i] * kLog2e;
     else if (i == T) lse2[i] = INFINITY;
+    return;
+  }
+  if (blockIdx.x >= nbg) {
+    constexpr int UPR = D / 8;   // 16-byte units per row
+    const int64_t unit = (int64_t)(blockIdx.x - nbg) * 256 + threadIdx.x;
+    const int row = (int)(unit / UPR), part = (int)(unit % UPR);
+    if (row < kp) {
+      bf16x8 v = {};
+      if (row < k) v = *(const bf16x8*)(P + (int64_t)row * D + 8 * part);
+      *(bf16x8*)(Pq + (int64_t)row * D + 8 * part) = v;
+    }
     return;
   }
   constexpr int TPR = D / 4;   // threads per row (8, 16 or 32)
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gt / TPR;
   const int part = (int)(gt % TPR);
-  const bool live = row < rows;
-  const int64_t r = live ? row : 0;
-  f32x4 g = *(const f32x4*)(dS + r * D + 4 * part);
+  const int64_t rows = (int64_t)B * kp;
+  const int u = (int)(row / kp), j = (int)(row % kp);
+  const bool inrange = row < rows;
+  const bool live = inrange && j < k;
+  const int64_t r = live ? (int64_t)u * k + j : 0;   // source row of dS, S, mass
+  f32x4 g = {0.f, 0.f, 0.f, 0.f};
   float c = 0.f;
-  if (mass_norm) {
-    const float mu = mass[r];
-    const float inv = mu > 0.f ? 1.0f / mu : 0.f;
-    g = mu > 0.f ? g * inv : f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 s = *(const f32x4*)(S + r * D + 4 * part);
-    c = g[0] * s[0] + g[1] * s[1] + g[2] * s[2] + g[3] * s[3];
+  if (live) {
+    g = *(const f32x4*)(dS + r * D + 4 * part);
+    if (mass_norm) {
+      const float mu = mass[r];
+      const float inv = mu > 0.f ? 1.0f / mu : 0.f;
+      g = mu > 0.f ? g * inv : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 sv = *(const f32x4*)(S + r * D + 4 * part);
+      c = g[0] * sv[0] + g[1] * sv[1] + g[2] * sv[2] + g[3] * sv[3];
+    }
   }
 #pragma unroll
   for (int off = 1; off < TPR; off <<= 1) c += __shfl_xor(c, off, 64);
-  if (live) {
+  if (inrange) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Gq[r * D + 4 * part + e] = (OutT)g[e];
-    if (part == 0) cv[r] = mass_norm ? c : 0.f;
+    for (int e = 0; e < 4; ++e) Gq[row * D + 4 * part + e] = (OutT)g[e];
+    if (part == 0) {
+      cv[row] = c;
+      if (cvs != nullptr) cvs[row] = -c;
+    }
   }
 }
 
 // ----------------------------------------------------------------------------
-// bf16 dX pass.  grid = ceil(T / 128); block 256 = 4 waves x 32 tokens.
-// Tokens of the workgroup that belong to different users are handled one
-// user at a time (the others are masked), because G depends on the user.
-// For each user, 64-prototype chunks of P and G (and cv) are copied
-// global -> LDS by the direct-to-LDS loads three chunks ahead into four
-// buffers (rows stored with the tile swizzle of sa_device.h), one barrier per
-// chunk.  Per 32-prototype tile: Z and dA' on the matrix cores (Z = P X^T
-// orientation, a token per lane, X rows resident as B operands), the weights
-// A and w on the vector ALU, then
-//   acc1^T += G^T A + P^T (c w),  acc2^T += P^T A
-// with the A operands transpose-read from LDS; dX = acc1 - c delta acc2.
+// bf16 dX pass.  grid = ceil(T / 256); block 512 = 8 waves x 32 tokens, two
+// waves per SIMD so that one wave's vector work overlaps the other's matrix
+// products.  Tokens of the workgroup that belong to different users are
+// handled one user at a time (the others get weight 0), because G depends on
+// the user.
+//
+// With w'_ji = c A_ji (dA'_ji - cv_j) and s_i = sum_j w'_ji (= c delta_i),
+//   dX_i = sum_j (A_ji G_j + w'_ji p_j) - s_i sum_j A_ji p_j.
+// Holding both sums would need two 32 x d fp32 accumulators per wave, which
+// does not fit two waves per SIMD, so the pass runs over the prototypes twice:
+//   stage 1: Z, dA' - cv (the product starts from -cv), A, w';
+//            acc^T += G^T A + P^T w', s += w';
+//   stage 2: Z, A;  acc^T += P^T (-s A).
+// Stage 2 recomputes Z (and adds P^T A) for 16 of the 48 matrix products
+// per tile.
+//
+// Prototypes stream through LDS in chunks of 64 rows: P, G and -cv in stage 1,
+// P alone in stage 2, copied global -> LDS by the direct-to-LDS loads three
+// chunks ahead into four buffers (rows stored with the tile swizzle of
+// sa_device.h), one barrier per chunk.  P, G and cv are padded with zero rows
+// to a whole number of chunks: a padded prototype's weight is at most 1 and
+// multiplies zero rows.  The token is the lane (Z = P X^T orientation, X rows
+// resident as B operands); the A operands of the accumulation are
+// transpose-read from LDS.  dX goes out through LDS so that every store
+// covers whole token rows.
 template <int D>
-__global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
+__global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
-    const bf16* __restrict__ P, const bf16* __restrict__ Gq, const float* __restrict__ cv, int k,
-    int64_t T, float alpha, float scale, const float* __restrict__ lse, float* __restrict__ dX,
-    float* __restrict__ delta_out) {
+    const bf16* __restrict__ Pq, const bf16* __restrict__ Gq, const float* __restrict__ cvn,
+    int kp, int64_t T, float alpha, float scale, const float* __restrict__ lse,
+    float* __restrict__ dX, float* __restrict__ delta_out) {
+  constexpr int NW = 8;                   // waves
+  static_assert(NW * 32 == kBwdxTokensBf16, "");
   constexpr int KS = D / 16, DB = D / 32, U = D / 8;
-  constexpr int PCH = 64;                 // prototypes per chunk
-  constexpr int NB = 4, AHEAD = 3;        // chunk buffers, copy distance
+  constexpr int PCH = kBwdxChunkBf16;     // prototypes per chunk
+  static_assert(PCH == 64, "two 32-prototype tiles per chunk");
+  constexpr int NB = 4;                   // chunk buffers
   constexpr int CU = PCH * U;             // 16-byte units per matrix chunk
-  constexpr int UPW = CU / 4;             // units per wave per matrix
-  static_assert(UPW % 64 == 0, "");
-  constexpr int XI = UPW / 64;            // copy instructions per wave per matrix
-  constexpr int L = 2 * XI + 1;           // loads per wave per chunk
-  constexpr uint32_t CBYTES = PCH * D * 2;
-  __shared__ __attribute__((aligned(16))) bf16 sP[NB][PCH * D];
-  __shared__ __attribute__((aligned(16))) bf16 sG[NB][PCH * D];
+  constexpr int UPW = CU / NW;            // units per wave per matrix
+  static_assert(UPW < 64 || UPW % 64 == 0, "");
+  constexpr int XI = (UPW + 63) / 64;     // copy instructions per wave per matrix
+  constexpr int L1 = 2 * XI + 1;          // loads per wave per stage-1 chunk
+  constexpr int L2 = XI;                  // loads per wave per stage-2 chunk
+  constexpr int CW = PCH / NW;            // cv entries copied per wave
+  constexpr uint32_t MB = PCH * D * 2;    // bytes of one matrix chunk
+  constexpr uint32_t GOFF = MB;           // G follows P in a buffer
+  constexpr uint32_t CB = 2 * MB;         // bytes of one chunk buffer
+  constexpr uint32_t TB = 32 * D * 2;     // bytes of a 32-row tile
+  constexpr uint32_t KB = 16 * D * 2;     // bytes of 16 rows
+  static_assert(NW * 32 * D * 4 <= NB * CB, "dX staging fits in the chunk buffers");
+  __shared__ __attribute__((aligned(16))) bf16 sbuf[NB * 2 * PCH * D];
   __shared__ __attribute__((aligned(16))) float sC[NB][PCH];
 
   const int tid = threadIdx.x;
@@ -108,8 +154,7 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
   const int64_t r0 = (int64_t)blockIdx.x * kBwdxTokensBf16;
   const int64_t r1 = r0 + kBwdxTokensBf16 < T ? r0 + kBwdxTokensBf16 : T;
   const int64_t tok = r0 + wave * 32 + l32;
-  const uint32_t sp0 = lds_addr((const SA_LDS void*)&sP[0][0]);
-  const uint32_t sg0 = lds_addr((const SA_LDS void*)&sG[0][0]);
+  const uint32_t sb0 = lds_addr((const SA_LDS void*)&sbuf[0]);
   const uint32_t sc0 = lds_addr((const SA_LDS void*)&sC[0][0]);
   const SA_LDS char* lds = (const SA_LDS char*)0;
 
@@ -122,15 +167,14 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
   // Copy geometry (per matrix): instruction j of this wave moves units
   // v0 .. v0 + 63, v0 = wave UPW + 64 j; unit v is row v / U at stored
   // position v % U, holding global unit (v % U) ^ g(row).
-  int crow_[XI];
-  uint32_t ccol[XI];
+  uint32_t cgo[XI];   // global byte offset within a chunk
 #pragma unroll
   for (int j = 0; j < XI; ++j) {
     const int v = wave * UPW + j * 64 + lane;
-    crow_[j] = v / U;
-    ccol[j] = (uint32_t)(((v % U) ^ xswz<D>(v / U)) * 16);
+    cgo[j] = (uint32_t)((v / U) * D * 2 + ((v % U) ^ xswz<D>(v / U)) * 16);
   }
-  // LDS byte offsets within a chunk buffer (prototype rows).
+  // Per-lane LDS byte offsets within a chunk buffer: aoff for the A operand
+  // of Z and dA' (row l32, unit 2 ks + h), toff for the transpose reads.
   const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
   uint32_t aoff[KS], toff[DB][2];
 #pragma unroll
@@ -141,8 +185,7 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
     for (int e = 0; e < 2; ++e)
       toff[db][e] = (uint32_t)(xoff<D>(4 * h + tr_r + 8 * e, 4 * db + 2 * tr_half + (tr_c >> 1)) +
                                (tr_c & 1) * 4) * 2;
-  const uint32_t cqoff = (uint32_t)(4 * h) * 4;
-  const int nch = (k + PCH - 1) / PCH;
+  const int nch = kp / PCH;
 
   int u = first_user_after(offsets, B, r0);
   for (; u < B; ++u) {
@@ -152,114 +195,210 @@ __global__ __launch_bounds__(256, 1) void sa_bwdx_bf16(
     if (uhi <= ulo) continue;
     const bool mine = tok >= ulo && tok < uhi;
     const float lsh = mine ? l2 : INFINITY;
-    const bf16* Gu = Gq + (int64_t)u * k * D;
-    const float* cvu = cv + (int64_t)u * k;
+    const bf16* Gu = Gq + (int64_t)u * kp * D;
+    const float* cvu = cvn + (int64_t)u * kp;
 
-    // Copy chunk c (rows past k repeat row k - 1, and cv past k reads
-    // cv[k - 1]; their weights are zeroed below) into buffer b.  Every wave
-    // issues exactly L loads per chunk, also for chunks past the end.
-    auto copy_chunk = [&](int c, uint32_t b) {
-      const int p0 = c < nch ? c * PCH : 0;
+    // Chunk q of the stream: q < nch is stage-1 chunk q (P, G, -cv), then
+    // stage-2 chunk q - nch (P), then copies of chunk 0 that are never read.
+    // Into buffer q % NB.
+    auto copy_chunk = [&](int q) {
+      const uint32_t dst = sb0 + (uint32_t)(q & (NB - 1)) * CB + (uint32_t)(wave * UPW) * 16;
+      if (q < nch) {
+        const uint32_t goff = (uint32_t)q * MB;
 #pragma unroll
-      for (int j = 0; j < XI; ++j) {
-        const int row = min(p0 + crow_[j], k - 1);
-        const uint32_t dst = b * CBYTES + (uint32_t)(wave * UPW + j * 64) * 16;
-        lds_copy16(P, (uint32_t)row * (D * 2) + ccol[j], sp0 + dst);
-        lds_copy16(Gu, (uint32_t)row * (D * 2) + ccol[j], sg0 + dst);
+        for (int j = 0; j < XI; ++j) {
+          if (UPW >= 64 || lane < UPW) {
+            lds_copy16(Pq, goff + cgo[j], dst + j * 1024);
+            lds_copy16(Gu, goff + cgo[j], dst + GOFF + j * 1024);
+          }
+        }
+        if (lane < CW)
+          lds_copy4v(cvu + q * PCH + wave * CW + lane, sc0 + ((q & (NB - 1)) * PCH + wave * CW) * 4);
+      } else {
+        const uint32_t goff = (uint32_t)(q < 2 * nch ? q - nch : 0) * MB;
+#pragma unroll
+        for (int j = 0; j < XI; ++j)
+          if (UPW >= 64 || lane < UPW) lds_copy16(Pq, goff + cgo[j], dst + j * 1024);
       }
-      if (lane < PCH / 4)
-        lds_copy4v(cvu + min(p0 + wave * (PCH / 4) + lane, k - 1),
-                   sc0 + (b * PCH + wave * (PCH / 4)) * 4);
+    };
+    // After chunk q: wait until chunk q + 1 has landed (q + 2 may still be in
+    // flight); after the barrier no wave reads chunk q - 1 any more, and its
+    // buffer takes chunk q + 3.
+    auto advance = [&](int q) {
+      if (q + 2 < nch) wait_vmcnt<L1>(); else wait_vmcnt<L2>();
+      barrier_lds();
+      copy_chunk(q + 3);
     };
 
-    // acc1 = g + c b = sum_j (A_ji G_j + c w_ji p_j) (one accumulator for
-    // both products), acc2 = a = sum_j A_ji p_j.
-    f32x16 acc1[DB], acc2[DB];
+    f32x16 acc[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { acc1[db] = f32x16{}; acc2[db] = f32x16{}; }
-    float dsum = 0.f;
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    float ssum = 0.f;
 
-    barrier_lds();   // the previous user's chunks are fully consumed
+    __syncthreads();   // the previous user's buffers are no longer read
 #pragma unroll
-    for (int c = 0; c < AHEAD; ++c) copy_chunk(c, c);
-    wait_vmcnt<0>();
-    barrier_lds();
-    for (int ci = 0; ci < nch; ++ci) {
-      const uint32_t buf = ci & (NB - 1);
-      copy_chunk(ci + AHEAD, (ci + AHEAD) & (NB - 1));   // into the buffer of chunk ci - 1
-      const SA_LDS char* ps = lds + sp0 + buf * CBYTES;
-      const SA_LDS char* gs = lds + sg0 + buf * CBYTES;
-      const SA_LDS char* cs = lds + sc0 + buf * (PCH * 4) + cqoff;
+    for (int q = 0; q < 3; ++q) copy_chunk(q);
+    if (nch > 2) wait_vmcnt<2 * L1>();
+    else if (nch == 2) wait_vmcnt<L1 + L2>();
+    else wait_vmcnt<2 * L2>();
+    __syncthreads();   // chunk 0 has landed
+
+    // The loops below are written in the order the instructions should
+    // issue: LDS operands are read a few products ahead of their use, and
+    // scheduling fences keep the compiler from moving the reads back next to
+    // the products (where each product would wait for its read).
+    constexpr int NS = 2 * DB;               // accumulation steps (db, kb) per tile
+    constexpr int ZA = KS < 3 ? KS : 3;      // stage-1 Z / dA' operand look-ahead (products)
+    constexpr int ZB = KS < 4 ? KS : 4;      // stage-2 Z operand look-ahead
+    constexpr int TA = NS < 2 ? NS : 2;      // stage-1 accumulation operand look-ahead (steps)
+    constexpr int TB2 = NS < 3 ? NS : 3;     // stage-2 accumulation operand look-ahead
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    auto rd16 = [&](uint32_t a) { return *(const SA_LDS bf16x8*)(lds + a); };
+    auto rdtr = [&](uint32_t a0, uint32_t a1) {
+      return concat4(lds_read_tr16((const SA_LDS bf16*)(lds + a0)),
+                     lds_read_tr16((const SA_LDS bf16*)(lds + a1)));
+    };
+    // Transpose-read addresses of accumulation step st = 2 db + kb.
+    auto tra = [&](uint32_t base, int st, int e) {
+      return base + toff[st >> 1][e] + (uint32_t)((st & 1) * KB);
+    };
+
+    // Stage 1.
+    for (int q = 0; q < nch; ++q) {
+      const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
+      const uint32_t cb = sc0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
 #pragma unroll
-      for (int pt = 0; pt < PCH / 32; ++pt) {
-        const int pbase = ci * PCH + pt * 32;
-        if (pbase >= k) break;   // uniform
-        const uint32_t rb = (uint32_t)(pt * 32 * D * 2);   // byte offset of the tile's rows
-        // Z and dA' tiles: rows = prototypes pbase + crow(i, h), column = token.
-        f32x16 z = f32x16{}, da = f32x16{};
+      for (int pt = 0; pt < 2; ++pt) {
+        const uint32_t tbuf = buf + pt * TB;
+        // Z and dA' - cv: rows = prototypes crow(i, h), column = this token.
+        f32x16 z = f32x16{}, da;
+        bf16x8 pa[KS], ga[KS];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 c4 = *(const SA_LDS f32x4*)(lds + cb + pt * 128 + 32 * g4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) da[4 * g4 + r] = c4[r];
+        }
+#pragma unroll
+        for (int ks = 0; ks < ZA; ++ks) {
+          pa[ks] = rd16(tbuf + aoff[ks]);
+          ga[ks] = rd16(tbuf + aoff[ks] + GOFF);
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 ap = *(const SA_LDS bf16x8*)(ps + rb + aoff[ks]);
-          const bf16x8 agr = *(const SA_LDS bf16x8*)(gs + rb + aoff[ks]);
-          z = mfma32(ap, xb[ks], z);
-          da = mfma32(agr, xb[ks], da);
+          fence();
+          if (ks + ZA < KS) {
+            pa[ks + ZA] = rd16(tbuf + aoff[ks + ZA]);
+            ga[ks + ZA] = rd16(tbuf + aoff[ks + ZA] + GOFF);
+          }
+          z = mfma32(pa[ks], xb[ks], z);
+          da = mfma32(ga[ks], xb[ks], da);
         }
-        f32x4 cq[4];
+        fence();
+        // The first accumulation operands, read while the weights are formed.
+        bf16x8 gt[NS], ptr[NS];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) cq[g4] = *(const SA_LDS f32x4*)(cs + pt * 128 + 32 * g4);
-        const bool partial = pbase + 32 > k;
+        for (int st = 0; st < TA; ++st) {
+          gt[st] = rdtr(tra(tbuf, st, 0) + GOFF, tra(tbuf, st, 1) + GOFF);
+          ptr[st] = rdtr(tra(tbuf, st, 0), tra(tbuf, st, 1));
+        }
+        fence();
         bf16x8 abf[2], wbf[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float a = exp2_fast(fmaf(z[i], alpha, -lsh));
-          if (partial && pbase + crow(i, h) >= k) a = 0.f;
-          const float w = a * (da[i] - cq[i >> 2][i & 3]);
-          dsum += w;
+          // A <= 1 for real prototypes; the clamp keeps padded ones finite.
+          const float a = __builtin_amdgcn_fmed3f(exp2_fast(fmaf(z[i], alpha, -lsh)), 0.f, 1.f);
+          const float w = a * (da[i] * scale);
+          ssum += w;
           abf[i >> 3][i & 7] = (bf16)a;
-          wbf[i >> 3][i & 7] = (bf16)(scale * w);
+          wbf[i >> 3][i & 7] = (bf16)w;
         }
-        // {acc1, acc2}^T (d x tokens) += {G, P, P}^T (d x prototypes) {A, c w, A}.
-        // K slot j of half h in block kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
+        // acc^T (d x tokens) += G^T A + P^T w'.  K slot j of half h in block
+        // kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const uint32_t o0 = rb + (uint32_t)(kb * 16 * D * 2) + toff[db][0];
-            const uint32_t o1 = rb + (uint32_t)(kb * 16 * D * 2) + toff[db][1];
-            const bf16x8 gT = concat4(lds_read_tr16((const SA_LDS bf16*)(gs + o0)),
-                                      lds_read_tr16((const SA_LDS bf16*)(gs + o1)));
-            const bf16x8 pT = concat4(lds_read_tr16((const SA_LDS bf16*)(ps + o0)),
-                                      lds_read_tr16((const SA_LDS bf16*)(ps + o1)));
-            acc1[db] = mfma32(gT, abf[kb], acc1[db]);
-            acc1[db] = mfma32(pT, wbf[kb], acc1[db]);
-            acc2[db] = mfma32(pT, abf[kb], acc2[db]);
+        for (int st = 0; st < NS; ++st) {
+          fence();
+          if (st + TA < NS) {
+            gt[st + TA] = rdtr(tra(tbuf, st + TA, 0) + GOFF, tra(tbuf, st + TA, 1) + GOFF);
+            ptr[st + TA] = rdtr(tra(tbuf, st + TA, 0), tra(tbuf, st + TA, 1));
           }
+          acc[st >> 1] = mfma32(gt[st], abf[st & 1], acc[st >> 1]);
+          acc[st >> 1] = mfma32(ptr[st], wbf[st & 1], acc[st >> 1]);
         }
+        fence();
       }
-      // Chunk ci + 1 must be complete before the barrier; chunks ci + 2 and
-      // ci + 3 may still be in flight.
-      wait_vmcnt<2 * L>();
-      barrier_lds();
+      advance(q);
+    }
+
+    // Stage 2: acc^T += P^T (-s A).
+    const float s = ssum + shfl_xor32(ssum);   // c delta of this lane's token
+    for (int q = nch; q < 2 * nch; ++q) {
+      const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const uint32_t tbuf = buf + pt * TB;
+        f32x16 z = f32x16{};
+        bf16x8 pa[KS];
+#pragma unroll
+        for (int ks = 0; ks < ZB; ++ks) pa[ks] = rd16(tbuf + aoff[ks]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          fence();
+          if (ks + ZB < KS) pa[ks + ZB] = rd16(tbuf + aoff[ks + ZB]);
+          z = mfma32(pa[ks], xb[ks], z);
+        }
+        fence();
+        bf16x8 ptr[NS];
+#pragma unroll
+        for (int st = 0; st < TB2; ++st) ptr[st] = rdtr(tra(tbuf, st, 0), tra(tbuf, st, 1));
+        fence();
+        bf16x8 bbf[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = __builtin_amdgcn_fmed3f(exp2_fast(fmaf(z[i], alpha, -lsh)), 0.f, 1.f);
+          bbf[i >> 3][i & 7] = (bf16)(-s * a);
+        }
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          fence();
+          if (st + TB2 < NS) ptr[st + TB2] = rdtr(tra(tbuf, st + TB2, 0), tra(tbuf, st + TB2, 1));
+          acc[st >> 1] = mfma32(ptr[st], bbf[st & 1], acc[st >> 1]);
+        }
+        fence();
+      }
+      advance(q);
     }
     wait_vmcnt<0>();
+    __syncthreads();   // every wave's copies have landed and every read is done
 
-    const float delta = dsum + shfl_xor32(dsum);
-    if (mine) {
-      // C layout: lane -> token, register i -> d = 32 db + crow(i, h).
-      float* dst = dX + tok * D;
+    // dX rows through LDS.  Register i of accumulator block db is column
+    // 32 db + crow(i, h) of this lane's token.  16-byte unit q of staging
+    // row r sits at unit q ^ f(r), which keeps the 16-lane groups of both the
+    // writes and the reads on distinct banks.
+    auto sw = [](int r) { return D >= 64 ? (r & 15) : ((r >> 1) & 7); };
+    SA_LDS f32x4* st = (SA_LDS f32x4*)(lds + sb0) + wave * 32 * (D / 4);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 v;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v = {acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2],
+                         acc[db][4 * g4 + 3]};
+        st[l32 * (D / 4) + ((8 * db + 2 * g4 + h) ^ sw(l32))] = v;
+      }
+    if (mine && h == 0) delta_out[tok] = s / scale;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+    // Each store instruction writes 64 x 16 bytes = 256 / D whole rows.
+    constexpr int RPI = 256 / D;
+    int rr = lane / (D / 4), cc = lane % (D / 4);
+    // Opaque here, so that the row addresses below are not computed once
+    // before the user loop and kept (spilled) across it.
+    asm volatile("" : "+v"(rr), "+v"(cc));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * g4 + r;
-            v[r] = acc1[db][i] - scale * delta * acc2[db][i];
-          }
-          *(f32x4*)(dst + 32 * db + 8 * g4 + 4 * h) = v;
-        }
-      if (h == 0) delta_out[tok] = delta;
+    for (int q = 0; q < 32 / RPI; ++q) {
+      const int row = q * RPI + rr;
+      const int64_t t = r0 + wave * 32 + row;
+      const f32x4 v = st[row * (D / 4) + (cc ^ sw(row))];
+      if (t >= ulo && t < uhi) *(f32x4*)(dX + t * D + 4 * cc) = v;
     }
   }
 }
@@ -278,8 +417,8 @@ template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ P, const bf16* __restrict__ Gq, const float* __restrict__ cv, int k,
-    int64_t T, int G, float alpha, const float* __restrict__ lse2, const float* __restrict__ delta,
-    float* __restrict__ dpp) {
+    int kp, int64_t T, int G, float alpha, const float* __restrict__ lse2,
+    const float* __restrict__ delta, float* __restrict__ dpp) {
   constexpr int KS = D / 16;             // reduction steps over d
   constexpr int DB = D / 32;             // 32-row blocks of the transposed partial
   constexpr int U = D / 8;               // 16-byte units per token row
@@ -310,7 +449,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
   const SA_LDS char* lds = (const SA_LDS char*)0;
 
   // B operands: pw[ks] = P[proto][16 ks + 8h .. +7], gw likewise for the
-  // current user's G; cw = cv[user][proto].
+  // current user's G (row stride kp); cw = cv[user][proto].
   bf16x8 pw[KS], gw[KS];
   float cw;
 #pragma unroll
@@ -361,8 +500,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
     int guser = cw_.user;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * k + prow) * D + 16 * ks + 8 * h);
-    cw = cv[(int64_t)guser * k + prow];
+      gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * kp + prow) * D + 16 * ks + 8 * h);
+    cw = cv[(int64_t)guser * kp + prow];
 #pragma unroll
     for (int b = 0; b < AHEAD; ++b) copy_next(b);
     // The compiler must see the waits for the operand loads above here, not
@@ -394,8 +533,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
         guser = cw_.user;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * k + prow) * D + 16 * ks + 8 * h);
-        cw = cv[(int64_t)guser * k + prow];
+          gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * kp + prow) * D + 16 * ks + 8 * h);
+        cw = cv[(int64_t)guser * kp + prow];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(gw[ks]));
         asm volatile("" ::"v"(cw));
@@ -668,28 +807,33 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
     e = dtype == 1 ? launch_stats_bf16(f, st, prof) : launch_stats_f32(f, st, prof);
     if (e != hipSuccess) return e;
   }
-  const int64_t rows = (int64_t)a.B * a.k;
-  const unsigned nbp = (unsigned)((rows * (D / 4) + 255) / 256);
-  // The bf16 dP pass reads lse in log2 units; when the caller supplied lse
-  // (not recomputed above), the prep kernel's extra blocks convert it.
-  const bool lse2 = dtype == 1 && a.T > 0 && !a.recompute_lse;
+  // G and cv rows (padded to kp per user), the zero-padded copy of P (bf16),
+  // and, when the caller supplied lse (not recomputed above), lse2 for the
+  // bf16 dP pass.
+  const int64_t rows = (int64_t)a.B * a.kp;
+  const unsigned nbg = (unsigned)((rows * (D / 4) + 255) / 256);
+  const bool bf = dtype == 1;
+  const unsigned nbq = bf ? (unsigned)(((int64_t)a.kp * (D / 8) + 255) / 256) : 0u;
+  const bool lse2 = bf && a.T > 0 && !a.recompute_lse;
   const unsigned nbl = lse2 ? (unsigned)((a.T + 1 + 255) / 256) : 0u;
   prof_begin(prof, "sa_bwd_prep", st);
-  if (dtype == 1)
-    hipLaunchKernelGGL((sa_bwd_prep<bf16, D>), dim3(nbp + nbl), dim3(256), 0, st, a.dS, a.S, a.mass,
-                       rows, a.mass_norm, (bf16*)a.Gq, a.cv, nbp, a.lse, a.T, a.lse2);
+  if (bf)
+    hipLaunchKernelGGL((sa_bwd_prep<bf16, D>), dim3(nbg + nbq + nbl), dim3(256), 0, st, a.dS, a.S,
+                       a.mass, a.B, a.k, a.kp, a.mass_norm, scale, (bf16*)a.Gq, a.cv, a.cvs, nbg,
+                       (const bf16*)a.P, (bf16*)a.Pq, nbq, a.lse, a.T, a.lse2);
   else
-    hipLaunchKernelGGL((sa_bwd_prep<float, D>), dim3(nbp), dim3(256), 0, st, a.dS, a.S, a.mass,
-                       rows, a.mass_norm, (float*)a.Gq, a.cv, nbp, a.lse, a.T, a.lse2);
+    hipLaunchKernelGGL((sa_bwd_prep<float, D>), dim3(nbg), dim3(256), 0, st, a.dS, a.S, a.mass,
+                       a.B, a.k, a.kp, a.mass_norm, scale, (float*)a.Gq, a.cv, (float*)nullptr,
+                       nbg, (const bf16*)nullptr, (bf16*)nullptr, 0u, a.lse, a.T, a.lse2);
   e = hipGetLastError();
   prof_end(prof, st);
   if (e != hipSuccess) return e;
   if (a.T > 0) {
-    if (dtype == 1) {
+    if (bf) {
       const unsigned nbx = (unsigned)((a.T + kBwdxTokensBf16 - 1) / kBwdxTokensBf16);
       prof_begin(prof, "sa_bwdx_bf16", st);
-      hipLaunchKernelGGL(sa_bwdx_bf16<D>, dim3(nbx), dim3(256), 0, st, a.offsets, a.B,
-                         (const bf16*)a.X, (const bf16*)a.P, (const bf16*)a.Gq, a.cv, a.k, a.T,
+      hipLaunchKernelGGL(sa_bwdx_bf16<D>, dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st, a.offsets,
+                         a.B, (const bf16*)a.X, (const bf16*)a.Pq, (const bf16*)a.Gq, a.cvs, a.kp, a.T,
                          alpha, scale, a.lse, a.dX, a.delta);
       e = hipGetLastError();
       prof_end(prof, st);
@@ -697,7 +841,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
       prof_begin(prof, "sa_bwdp_bf16", st);
       hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves>), dim3(a.Gb, a.bnchunks), dim3(64 * kBwdpWaves),
                          0, st, a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.P,
-                         (const bf16*)a.Gq, a.cv, a.k, a.T, a.Gb, alpha, a.lse2, a.delta, a.dpp);
+                         (const bf16*)a.Gq, a.cv, a.k, a.kp, a.T, a.Gb, alpha, a.lse2, a.delta,
+                         a.dpp);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;

@@ -14,7 +14,8 @@ constexpr int kTargetWorkgroups = 256;
 constexpr int kChunkBf16 = 256;     // prototypes per bf16 prototype-stationary workgroup
 constexpr int kChunkF32 = 64;       // prototypes per fp32 forward aggregation workgroup
 constexpr int kChunkF32Bwd = 32;    // prototypes per fp32 backward dP workgroup
-constexpr int kBwdxTokensBf16 = 128;  // tokens per bf16 dX workgroup
+constexpr int kBwdxTokensBf16 = 256;  // tokens per bf16 dX workgroup (8 waves x 32)
+constexpr int kBwdxChunkBf16 = 64;    // prototypes per chunk of the bf16 dX pass (and row padding)
 constexpr int kBwdxTokensF32 = 32;    // tokens per fp32 dX workgroup
 constexpr int kBwdpWaves = 8;         // waves of a bf16 dP workgroup (32 prototypes each)
 
@@ -32,10 +33,11 @@ struct Plan {
   int64_t nslots;       // G + B - 1 partial slots
   // backward (dP pass)
   int bchunk, bnchunks, Gb;
+  int kp;               // row stride of G and cv: k rounded up to the dX chunk (bf16), else k
   // forward workspace layout (byte offsets)
   size_t off_status, off_lse, off_lse2, off_part, off_pmass, fwd_bytes;
   // backward workspace layout (byte offsets)
-  size_t off_G, off_cv, off_delta, off_dpp, off_blse, off_blse2, bwd_bytes;
+  size_t off_G, off_cv, off_cvs, off_Pq, off_delta, off_dpp, off_blse, off_blse2, bwd_bytes;
 };
 
 // Fills the plan; returns false for an unsupported problem.
@@ -72,8 +74,11 @@ struct BwdArgs {
   const float* mass;   // [B, k]    (mass norm only)
   float* dX;           // [T, d]
   float* dP;           // [k, d]
-  void* Gq;            // [B, k, d] G = dS (or dS / mass) in the input dtype
-  float* cv;           // [B, k]    G[j] . S[j] (mass norm) or 0
+  void* Gq;            // [B, kp, d] G = dS (or dS / mass) in the input dtype, rows >= k zero
+  float* cv;           // [B, kp]   G[j] . S[j] (mass norm) or 0
+  float* cvs;          // [B, kp]   -cv (bf16 dX pass)
+  void* Pq;            // [kp, d]   P with zero rows from k on (bf16 path)
+  int kp;
   float* delta;        // [T]
   float* dpp;          // [Gb, k, d] dP partial per segment
   uint32_t* status;
