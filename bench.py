@@ -297,6 +297,40 @@ def main():
         "kernel_avg_ms": {n: round(v, 5) for n, v in kern_ms.items()},
         "wall_s_timed_region": round(wall, 4),
     }
+    # Query/key projections of Eq. (6) folded into the prototype table: the
+    # fold and its backward for this workload's k and d (not part of the step:
+    # the step's P is the folded table).
+    gw = torch.Generator().manual_seed(1)
+    Wq = (torch.randn(d, d, generator=gw) / d ** 0.5).to(dev)
+    Wk = (torch.randn(d, d, generator=gw) / d ** 0.5).to(dev)
+    Peff = torch.empty_like(prob.P)
+    fws = torch.empty(int(sa.load().sa_fold_workspace_size(k, d)), dtype=torch.uint8, device=dev)
+    def graph_timed(fn, n=20):
+        # n calls captured in one HIP graph, so that host-side call overhead
+        # (larger than these small kernels) stays out of the measurement
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            fn()
+        st.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        return timed(g.replay, 5) / n
+
+    ms_fold = graph_timed(lambda: sa.fold_prototypes(prob.P, Wq, Wk, P_eff=Peff))
+    ms_fold_bwd = graph_timed(lambda: sa.fold_prototypes_backward(prob.P, Wq, Wk, dP, workspace=fws))
+    # two k x d x d products forward (Q, P_eff), five backward (Q, dQ, dP,
+    # dW_Q, dW_K), 2 flops per multiply-add
+    fold_flop, fold_bwd_flop = 4.0 * k * d * d, 10.0 * k * d * d
+    out["projections"] = {
+        "fold_us": round(ms_fold * 1e3, 2), "fold_backward_us": round(ms_fold_bwd * 1e3, 2),
+        "fold_gflops": round(fold_flop / (ms_fold * 1e-3) / 1e9, 1),
+        "fold_backward_gflops": round(fold_bwd_flop / (ms_fold_bwd * 1e-3) / 1e9, 1)}
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

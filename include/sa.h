@@ -183,6 +183,47 @@ sa_status sa_backward_profiled(const sa_problem* problem, const int64_t* offsets
                                float* dX, float* dP, void* ws, size_t ws_bytes,
                                void* stream, sa_profile* prof);
 
+/*
+ * Query and key projections (SequenceO1 reading notes, section 3.1, Eq. (6):
+ * Z = (P W_Q)(X W_K)^T / sqrt(d), with W_Q, W_K in R^{d x d}).  Because
+ * (P W_Q)(X W_K)^T = (P W_Q W_K^T) X^T, the projected affinities are the
+ * kernel's affinities of the folded table
+ *     P_eff = P W_Q W_K^T,
+ * so sa_forward(X, P_eff) computes the sketch of Eq. (6)-(9) with the
+ * projections; the aggregation still sums the unprojected X (Eq. (9)).
+ *
+ *  k, d    : 1 <= k <= 2048; d in {32, 64, 128}.
+ *  dtype   : dtype of P and P_eff (SA_BF16: P_eff is rounded to bf16 once,
+ *            from fp32 accumulation; SA_F32: fp32 throughout).
+ *  P       : [k, d] (dtype) device.
+ *  Wq, Wk  : float [d, d] device, row-major (row = input feature).
+ *  P_eff   : [k, d] (dtype) device, written; must not overlap P.
+ * All pointers 16-byte aligned, caller-owned.  Enqueued on `stream`; returns
+ * at once.  Errors (synchronous): SA_ERR_NULL_ARG, SA_ERR_BAD_SHAPE,
+ * SA_ERR_BAD_DTYPE, SA_ERR_MISALIGNED, SA_ERR_HIP.
+ */
+sa_status sa_fold_prototypes(int k, int d, sa_dtype dtype, const void* P, const float* Wq,
+                             const float* Wk, void* P_eff, void* stream);
+
+/*
+ * Backward of the fold.  Given dP_eff = dL/dP_eff (float [k, d], e.g. the dP
+ * that sa_backward returns for P_eff), writes, with M = W_Q W_K^T:
+ *     dP   = dP_eff M^T            float [k, d]
+ *     dW_Q = P^T dP_eff W_K        float [d, d]
+ *     dW_K = dP_eff^T P W_Q        float [d, d]
+ * (all overwritten).  dW_Q and dW_K are sums over the k rows taken in a fixed
+ * order, so repeated calls give identical bits.  `ws` is a device workspace of
+ * at least sa_fold_workspace_size(k, d) bytes (per-workgroup partial sums of
+ * dW_Q and dW_K); sa_fold_workspace_size returns 0 for unsupported (k, d).
+ * Other arguments as for sa_fold_prototypes; errors as there, plus
+ * SA_ERR_WORKSPACE_TOO_SMALL.
+ */
+size_t sa_fold_workspace_size(int k, int d);
+sa_status sa_fold_prototypes_backward(int k, int d, sa_dtype dtype, const void* P,
+                                      const float* Wq, const float* Wk, const float* dP_eff,
+                                      float* dP, float* dWq, float* dWk, void* ws,
+                                      size_t ws_bytes, void* stream);
+
 /* Waits for `stream`, then reports whether a kernel of the last call that
  * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS) or not
  * (SA_OK).  SA_ERR_HIP if the wait or the read fails. */

@@ -239,6 +239,46 @@ sa_status sa_backward_profiled(const sa_problem* pr, const int64_t* offsets_dev,
   return v;
 }
 
+static sa_status fold_check(int k, int d, sa_dtype dtype) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_BAD_DTYPE;
+  if (k < 1 || k > 2048 || !(d == 32 || d == 64 || d == 128)) return SA_ERR_BAD_SHAPE;
+  return SA_OK;
+}
+
+size_t sa_fold_workspace_size(int k, int d) {
+  if (k < 1 || k > 2048 || !(d == 32 || d == 64 || d == 128)) return 0;
+  return fold_workspace_bytes(k, d);
+}
+
+sa_status sa_fold_prototypes(int k, int d, sa_dtype dtype, const void* P, const float* Wq,
+                             const float* Wk, void* P_eff, void* stream) {
+  const sa_status v = fold_check(k, d, dtype);
+  if (v != SA_OK) return v;
+  if (P == nullptr || Wq == nullptr || Wk == nullptr || P_eff == nullptr) return SA_ERR_NULL_ARG;
+  if (!aligned16(P) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(P_eff))
+    return SA_ERR_MISALIGNED;
+  const hipError_t e = launch_fold(k, d, (int)dtype, P, Wq, Wk, P_eff, (hipStream_t)stream);
+  return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+sa_status sa_fold_prototypes_backward(int k, int d, sa_dtype dtype, const void* P,
+                                      const float* Wq, const float* Wk, const float* dP_eff,
+                                      float* dP, float* dWq, float* dWk, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  const sa_status v = fold_check(k, d, dtype);
+  if (v != SA_OK) return v;
+  if (P == nullptr || Wq == nullptr || Wk == nullptr || dP_eff == nullptr || dP == nullptr ||
+      dWq == nullptr || dWk == nullptr || ws == nullptr)
+    return SA_ERR_NULL_ARG;
+  if (!aligned16(P) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(dP_eff) || !aligned16(dP) ||
+      !aligned16(dWq) || !aligned16(dWk) || !aligned16(ws))
+    return SA_ERR_MISALIGNED;
+  if (ws_bytes < sa_fold_workspace_size(k, d)) return SA_ERR_WORKSPACE_TOO_SMALL;
+  const hipError_t e = launch_fold_backward(k, d, (int)dtype, P, Wq, Wk, dP_eff, dP, dWq, dWk,
+                                            (float*)ws, (hipStream_t)stream);
+  return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
 sa_status sa_get_device_status(const void* ws, void* stream) {
   if (ws == nullptr) return SA_ERR_NULL_ARG;
   hipStream_t st = (hipStream_t)stream;

@@ -112,6 +112,14 @@ inline void prof_end(Prof* p, hipStream_t st) {
 }
 
 hipError_t launch_stats_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
+// P_eff = P W_Q W_K^T and its backward.
+hipError_t launch_fold(int k, int d, int dtype, const void* P, const float* Wq, const float* Wk,
+                       void* Peff, hipStream_t st);
+hipError_t launch_fold_backward(int k, int d, int dtype, const void* P, const float* Wq,
+                                const float* Wk, const float* G, float* dP, float* dWq,
+                                float* dWk, float* parts, hipStream_t st);
+// Workspace of the fold's backward: per-workgroup parts of dW_Q and dW_K.
+size_t fold_workspace_bytes(int k, int d);
 hipError_t launch_stats_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st, Prof* prof);

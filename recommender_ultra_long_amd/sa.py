@@ -39,7 +39,8 @@ SA_PROFILE_MAX_KERNELS = 8
 
 EXPORTED = ("sa_version", "sa_status_string", "sa_validate", "sa_workspace_size",
             "sa_forward", "sa_backward", "sa_forward_profiled", "sa_backward_profiled",
-            "sa_get_device_status")
+            "sa_get_device_status", "sa_fold_workspace_size", "sa_fold_prototypes",
+            "sa_fold_prototypes_backward")
 
 
 class SaProblem(ctypes.Structure):
@@ -95,6 +96,13 @@ def load():
                                          ctypes.POINTER(SaProfile)]
     lib.sa_get_device_status.restype = i32
     lib.sa_get_device_status.argtypes = [vp, vp]
+    lib.sa_fold_workspace_size.restype = sz
+    lib.sa_fold_workspace_size.argtypes = [i32, i32]
+    lib.sa_fold_prototypes.restype = i32
+    lib.sa_fold_prototypes.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.sa_fold_prototypes_backward.restype = i32
+    lib.sa_fold_prototypes_backward.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                sz, vp]
     _lib = lib
     return lib
 
@@ -229,6 +237,44 @@ def sa_backward(offsets, X, P, dS, lse=None, S=None, mass=None, mass_norm=False,
     if st != SA_OK:
         raise SAError(st, "sa_backward")
     return dX, dP
+
+
+def _dtype_code(dtype):
+    return {torch.float32: SA_F32, torch.bfloat16: SA_BF16}.get(dtype, 99)
+
+
+def fold_prototypes(P, Wq, Wk, P_eff=None, stream=None):
+    """Calls sa_fold_prototypes: P_eff = P W_Q W_K^T ([k, d], P's dtype), the
+    prototype table whose affinities are Eq. (6)'s projected ones."""
+    lib = load()
+    k, d = P.shape
+    if P_eff is None:
+        P_eff = torch.empty_like(P)
+    st = lib.sa_fold_prototypes(int(k), int(d), _dtype_code(P.dtype), _ptr(P), _ptr(Wq), _ptr(Wk),
+                                _ptr(P_eff), _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_fold_prototypes")
+    return P_eff
+
+
+def fold_prototypes_backward(P, Wq, Wk, dP_eff, workspace=None, stream=None):
+    """Calls sa_fold_prototypes_backward.  Returns (dP [k, d], dW_Q [d, d],
+    dW_K [d, d]), all float32."""
+    lib = load()
+    k, d = P.shape
+    dev = P.device
+    dP = torch.empty((k, d), dtype=torch.float32, device=dev)
+    dWq = torch.empty((d, d), dtype=torch.float32, device=dev)
+    dWk = torch.empty((d, d), dtype=torch.float32, device=dev)
+    ws_bytes = int(lib.sa_fold_workspace_size(int(k), int(d)))
+    ws = _workspace(ws_bytes, dev, workspace)
+    st = lib.sa_fold_prototypes_backward(int(k), int(d), _dtype_code(P.dtype), _ptr(P), _ptr(Wq),
+                                         _ptr(Wk), _ptr(dP_eff), _ptr(dP), _ptr(dWq), _ptr(dWk),
+                                         _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
+                                         _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_fold_prototypes_backward")
+    return dP, dWq, dWk
 
 
 def sa_get_device_status(workspace, stream=None):

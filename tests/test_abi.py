@@ -135,3 +135,33 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sa, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         sa.load()
+
+
+def test_fold_argument_errors_are_synchronous():
+    lib = sa.load()
+    buf = ctypes.create_string_buffer(64)   # host memory, 16-byte alignment not required here
+    vp = ctypes.c_void_p
+    # backward workspace: Q and dQ (k x d) and two d x d partial sums per
+    # 128-row slice
+    assert lib.sa_fold_workspace_size(1024, 128) == (2 * 1024 * 128 + 2 * 8 * 128 * 128) * 4
+    assert lib.sa_fold_workspace_size(129, 32) == (2 * 129 * 32 + 2 * 2 * 32 * 32) * 4
+    assert lib.sa_fold_workspace_size(0, 128) == 0
+    assert lib.sa_fold_workspace_size(1024, 96) == 0
+    assert lib.sa_fold_workspace_size(4096, 64) == 0
+    nul = vp(None)
+    # shape and dtype errors come first, with null pointers (no HIP call)
+    assert lib.sa_fold_prototypes(0, 128, sa.SA_BF16, nul, nul, nul, nul, nul) == sa.SA_ERR_BAD_SHAPE
+    assert lib.sa_fold_prototypes(64, 48, sa.SA_BF16, nul, nul, nul, nul, nul) == sa.SA_ERR_BAD_SHAPE
+    assert lib.sa_fold_prototypes(64, 64, 7, nul, nul, nul, nul, nul) == sa.SA_ERR_BAD_DTYPE
+    assert lib.sa_fold_prototypes(64, 64, sa.SA_F32, nul, nul, nul, nul, nul) == sa.SA_ERR_NULL_ARG
+    assert lib.sa_fold_prototypes_backward(64, 64, sa.SA_F32, nul, nul, nul, nul, nul, nul, nul, nul, 0,
+                                           nul) == sa.SA_ERR_NULL_ARG
+    # misaligned pointer
+    odd = vp(ctypes.addressof(buf) | 1)
+    assert lib.sa_fold_prototypes(64, 64, sa.SA_F32, odd, odd, odd, odd, nul) == sa.SA_ERR_MISALIGNED
+    assert lib.sa_fold_prototypes_backward(64, 64, sa.SA_F32, odd, odd, odd, odd, odd, odd, odd, odd,
+                                           1 << 20, nul) == sa.SA_ERR_MISALIGNED
+    # workspace too small (aligned host addresses; the size check precedes any launch)
+    al = vp((ctypes.addressof(buf) + 15) & ~15)
+    assert lib.sa_fold_prototypes_backward(64, 64, sa.SA_F32, al, al, al, al, al, al, al, al, 16,
+                                           nul) == sa.SA_ERR_WORKSPACE_TOO_SMALL
