@@ -71,7 +71,7 @@ def _kernel_algorithmic(name, k, d, T):
     return 0.0, 0.0
 
 
-def _traffic_for(kernel, src_hash):
+def _traffic_for(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -82,7 +82,7 @@ def _traffic_for(kernel, src_hash):
     except (OSError, ValueError):
         return None
     ent = data.get("kernels", {}).get(kernel)
-    if not ent or ent.get("source_sha256") != src_hash:
+    if not ent or ent.get("source_sha256") != _source_hash(kernel):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -113,7 +113,7 @@ def _parse_traffic(fetch_csv, write_csv):
 
     f_scale = COPY_BYTES / copy_reading(fetch)
     w_scale = COPY_BYTES / copy_reading(write)
-    out = {"source_sha256": _source_hash(), "copy_bytes": COPY_BYTES,
+    out = {"copy_bytes": COPY_BYTES,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     for name in fetch:
         short = name.split("(")[0].replace("void ", "").split("::")[-1].split("<")[0]
@@ -121,7 +121,9 @@ def _parse_traffic(fetch_csv, write_csv):
             continue
         fb = statistics.median(fetch[name]) * f_scale
         wb = statistics.median(write.get(name, [0.0])) * w_scale
-        ent = out["kernels"].setdefault(short, {"source_sha256": out["source_sha256"]})
+        if short not in KERNEL_SOURCES:
+            continue
+        ent = out["kernels"].setdefault(short, {"source_sha256": _source_hash(short)})
         ent["fetch_bytes_per_launch"] = fb
         ent["write_bytes_per_launch"] = wb
         ent["hbm_bytes_per_launch"] = fb + wb
@@ -130,12 +132,28 @@ def _parse_traffic(fetch_csv, write_csv):
     print(json.dumps(out, indent=1))
 
 
-def _source_hash():
+# Source file of each profiled kernel.  A kernel's counters stay valid while
+# its own file, the shared device header and the launch plan (the API file
+# and the kernel declarations) are unchanged.
+KERNEL_SOURCES = {
+    "sa_stats_bf16": "sa_fwd_bf16.hip", "sa_agg_bf16": "sa_fwd_bf16.hip",
+    "sa_stats_f32": "sa_fwd_f32.hip", "sa_agg_f32": "sa_fwd_f32.hip",
+    "sa_reduce_kernel": "sa_reduce.hip",
+    "sa_bwd_prep": "sa_bwd.hip", "sa_bwdx_bf16": "sa_bwd.hip", "sa_bwdp_bf16": "sa_bwd.hip",
+    "sa_bwdx_f32": "sa_bwd.hip", "sa_bwdp_f32": "sa_bwd.hip", "sa_dp_reduce": "sa_bwd.hip",
+}
+SHARED_SOURCES = ("sa_device.h", "sa_kernels.h", "sa_api.cpp")
+
+
+def _source_hash(kernel):
+    """sha256 over the files that determine one kernel's code and launch."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recommender_ultra_long_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
-        if fn.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, fn), "rb").read())
+    own = KERNEL_SOURCES.get(kernel)
+    files = sorted(SHARED_SOURCES) + ([own] if own else [])
+    for fn in files:
+        h.update(fn.encode())
+        h.update(open(os.path.join(csrc, fn), "rb").read())
     return h.hexdigest()
 
 
@@ -260,7 +278,7 @@ def main():
         return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": _traffic_for(name, _source_hash()),
+                "traffic": _traffic_for(name),
                 "avg_launch_ms": round(ms, 5), "algorithmic_flop": fl,
                 "algorithmic_bytes": by,
                 "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1)}

@@ -8,13 +8,14 @@
 // regrouped so that every product is k x d x d).
 //
 // The products are small (at most 2048 x 128 x 128, fp32 on the vector ALU):
-// their cost is load latency, not arithmetic.  So every weight matrix is
-// brought into LDS with one batch of loads (the second one prefetched into
-// registers while the first product runs), and the row products work on
-// 16-row tiles so that k = 1024 already spreads over 64 workgroups.
+// their cost is load latency and LDS reads, not arithmetic.  So every weight
+// matrix is brought into LDS with one batch of loads (the second one
+// prefetched into registers while the first product runs), and the row
+// products work on tiles of 4 rows (8 at d = 32) so that k = 1024 spreads
+// over 256 workgroups.
 //
-// Row kernels (grid = ceil(k / 16)): each row of Q, dQ, P_eff and dP depends
-// only on the same row of P and G.  The d x d gradients sum over all k rows:
+// Row kernels (grid = ceil(k / rows per tile)): each row of Q, dQ, P_eff and
+// dP depends only on the same row of P and G.  The d x d gradients sum over all k rows:
 // the gram kernel splits the rows into 128-row slices, one workgroup per
 // (32 x 32 output tile, gradient, slice), and sa_fold_sum adds the slices in
 // slice order, so results do not depend on scheduling.
@@ -23,7 +24,11 @@
 
 namespace sa {
 
-constexpr int kFoldRows = 16;      // rows per row-kernel workgroup
+// Rows per row-kernel workgroup: as few as keep all 256 threads busy (one
+// output column per thread and 256 / D rows per pass), at least 4, so that
+// small k still spreads over many compute units.
+template <int D>
+constexpr int fold_rows() { return 256 / D > 4 ? 256 / D : 4; }
 constexpr int kGramRows = 128;     // rows per gram slice
 constexpr int kGramTile = 32;      // gram output tile edge
 
@@ -62,12 +67,12 @@ __device__ __forceinline__ void store_w(const FoldW<D>& r, float (*sW)[D + 1]) {
   }
 }
 
-// Rows r0 .. r0 + kFoldRows - 1 of a k x D matrix into LDS as fp32 (rows at
-// or beyond k read as zero).
+// Rows r0 .. r0 + fold_rows<D>() - 1 of a k x D matrix into LDS as fp32
+// (rows at or beyond k read as zero).
 template <typename T, int D>
 __device__ __forceinline__ void load_rows(const T* __restrict__ src, int r0, int k,
                                           float (*dst)[D + 4]) {
-  for (int i = threadIdx.x; i < kFoldRows * D; i += 256) {
+  for (int i = threadIdx.x; i < fold_rows<D>() * D; i += 256) {
     const int r = i / D, c = i % D;
     dst[r][c] = r0 + r < k ? (float)src[(int64_t)(r0 + r) * D + c] : 0.f;
   }
@@ -80,7 +85,7 @@ __device__ __forceinline__ void load_rows(const T* __restrict__ src, int r0, int
 template <int D, bool WT>
 __device__ __forceinline__ void rows_times_w(const float (*In)[D + 4], const float (*W)[D + 1],
                                              float* acc) {
-  constexpr int RS = 256 / D, NR = kFoldRows / RS;
+  constexpr int RS = 256 / D, NR = fold_rows<D>() / RS;
   const int n = threadIdx.x % D, rr = threadIdx.x / D;
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i] = 0.f;
@@ -100,17 +105,17 @@ __device__ __forceinline__ void rows_times_w(const float (*In)[D + 4], const flo
   }
 }
 
-// grid = ceil(k / kFoldRows); block 256.
+// grid = ceil(k / fold_rows<D>()); block 256.
 template <typename PT, int D>
 __global__ __launch_bounds__(256) void sa_fold_fwd(const PT* __restrict__ P,
                                                    const float* __restrict__ Wq,
                                                    const float* __restrict__ Wk,
                                                    PT* __restrict__ Peff, int k) {
-  constexpr int RS = 256 / D, NR = kFoldRows / RS;
+  constexpr int RB = fold_rows<D>(), RS = 256 / D, NR = RB / RS;
   __shared__ float sW[D][D + 1];
-  __shared__ __align__(16) float sP[kFoldRows][D + 4];
-  __shared__ __align__(16) float sQ[kFoldRows][D + 4];
-  const int r0 = blockIdx.x * kFoldRows;
+  __shared__ __align__(16) float sP[RB][D + 4];
+  __shared__ __align__(16) float sQ[RB][D + 4];
+  const int r0 = blockIdx.x * RB;
   const int n = threadIdx.x % D, rr = threadIdx.x / D;
   FoldW<D> wr;
   fetch_w<D>(Wq, wr);
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256) void sa_fold_fwd(const PT* __restrict__ P,
   }
 }
 
-// grid = ceil(k / kFoldRows); block 256.  Writes dP and the workspace rows
+// grid = ceil(k / fold_rows<D>()); block 256.  Writes dP and the workspace rows
 // Q = P W_Q and dQ = G W_K that the gram kernel reads.
 template <typename PT, int D>
 __global__ __launch_bounds__(256) void sa_fold_bwd_rows(const PT* __restrict__ P,
@@ -143,12 +148,12 @@ __global__ __launch_bounds__(256) void sa_fold_bwd_rows(const PT* __restrict__ P
                                                         float* __restrict__ dP,
                                                         float* __restrict__ Qw,
                                                         float* __restrict__ dQw, int k) {
-  constexpr int RS = 256 / D, NR = kFoldRows / RS;
+  constexpr int RB = fold_rows<D>(), RS = 256 / D, NR = RB / RS;
   __shared__ float sW[D][D + 1];
-  __shared__ __align__(16) float sP[kFoldRows][D + 4];
-  __shared__ __align__(16) float sG[kFoldRows][D + 4];
-  __shared__ __align__(16) float sdQ[kFoldRows][D + 4];
-  const int r0 = blockIdx.x * kFoldRows;
+  __shared__ __align__(16) float sP[RB][D + 4];
+  __shared__ __align__(16) float sG[RB][D + 4];
+  __shared__ __align__(16) float sdQ[RB][D + 4];
+  const int r0 = blockIdx.x * RB;
   const int n = threadIdx.x % D, rr = threadIdx.x / D;
   FoldW<D> wr;
   fetch_w<D>(Wk, wr);
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(256) void sa_fold_gram(const PT* __restrict__ P,
                                                     const float* __restrict__ dQw,
                                                     float* __restrict__ parts, int k) {
   constexpr int T = kGramTile, TPR = D / T;
-  __shared__ float sL[kGramRows][T + 1];
+  __shared__ __align__(16) float sL[kGramRows][T + 4];
   __shared__ float sR[kGramRows][T + 1];
   const int a0 = (blockIdx.x / TPR) * T, b0 = (blockIdx.x % TPR) * T;
   const int which = blockIdx.y, z = blockIdx.z;
@@ -215,20 +220,22 @@ __global__ __launch_bounds__(256) void sa_fold_gram(const PT* __restrict__ P,
     sR[r][c] = rv[j];
   }
   __syncthreads();
-  constexpr int NA = T * T / 256;                      // outputs per thread
-  const int b = threadIdx.x % T, a = threadIdx.x / T;  // rows a + (256 / T) i
-  float acc[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i] = 0.f;
-#pragma unroll 4
+  // thread t: output column b = t % T, rows a = 4 (t / T) .. + 3
+  const int b = threadIdx.x % T, a = 4 * (threadIdx.x / T);
+  static_assert(T * T / 256 == 4, "four outputs per thread");
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
   for (int r = 0; r < kGramRows; ++r) {
     const float x = sR[r][b];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) acc[i] = fmaf(sL[r][a + (256 / T) * i], x, acc[i]);
+    const float4 l = *reinterpret_cast<const float4*>(&sL[r][a]);
+    acc[0] = fmaf(l.x, x, acc[0]);
+    acc[1] = fmaf(l.y, x, acc[1]);
+    acc[2] = fmaf(l.z, x, acc[2]);
+    acc[3] = fmaf(l.w, x, acc[3]);
   }
   float* part = parts + (int64_t)(2 * z + which) * D * D;
 #pragma unroll
-  for (int i = 0; i < NA; ++i) part[(int64_t)(a0 + a + (256 / T) * i) * D + b0 + b] = acc[i];
+  for (int i = 0; i < 4; ++i) part[(int64_t)(a0 + a + i) * D + b0 + b] = acc[i];
 }
 
 // dW_Q and dW_K: the slices' parts added in slice order.
@@ -244,13 +251,16 @@ __global__ __launch_bounds__(256) void sa_fold_sum(const float* __restrict__ par
   (which == 0 ? dWq : dWk)[e] = s;
 }
 
-static unsigned fold_row_blocks(int k) { return (unsigned)((k + kFoldRows - 1) / kFoldRows); }
+template <int D>
+static unsigned fold_row_blocks(int k) {
+  return (unsigned)((k + fold_rows<D>() - 1) / fold_rows<D>());
+}
 static int fold_slices(int k) { return (k + kGramRows - 1) / kGramRows; }
 
 template <typename PT, int D>
 static hipError_t fold_t(int k, const void* P, const float* Wq, const float* Wk, void* Peff,
                          hipStream_t st) {
-  hipLaunchKernelGGL((sa_fold_fwd<PT, D>), dim3(fold_row_blocks(k)), dim3(256), 0, st,
+  hipLaunchKernelGGL((sa_fold_fwd<PT, D>), dim3(fold_row_blocks<D>(k)), dim3(256), 0, st,
                      (const PT*)P, Wq, Wk, (PT*)Peff, k);
   return hipGetLastError();
 }
@@ -262,7 +272,7 @@ static hipError_t fold_backward_t(int k, const void* P, const float* Wq, const f
   float* Qw = ws;
   float* dQw = Qw + (size_t)k * D;
   float* parts = dQw + (size_t)k * D;
-  hipLaunchKernelGGL((sa_fold_bwd_rows<PT, D>), dim3(fold_row_blocks(k)), dim3(256), 0, st,
+  hipLaunchKernelGGL((sa_fold_bwd_rows<PT, D>), dim3(fold_row_blocks<D>(k)), dim3(256), 0, st,
                      (const PT*)P, Wq, Wk, G, dP, Qw, dQw, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
