@@ -15,19 +15,32 @@ from __future__ import annotations
 import math
 
 
+def _tables(P, B):
+    """One table per user: P is k rows (shared by all users) or B tables of k
+    rows (user u uses P[u])."""
+    if isinstance(P[0][0], (list, tuple)):
+        if len(P) != B:
+            raise ValueError("need one table per user")
+        return [[[float(v) for v in row] for row in tab] for tab in P]
+    shared = [[float(v) for v in row] for row in P]
+    return [shared] * B
+
+
 def brute_forward(offsets, X, P, mass_norm=False):
     """offsets: list of ints (B+1); X: list of T rows (lists of d floats);
-    P: list of k rows.  Returns (S [B][k][d], lse [T], mass [B][k])."""
+    P: list of k rows, or a list of B such tables (one per user).
+    Returns (S [B][k][d], lse [T], mass [B][k])."""
     X = [[float(v) for v in row] for row in X]
-    P = [[float(v) for v in row] for row in P]
-    k = len(P)
-    d = len(P[0])
-    c = 1.0 / math.sqrt(d)
     B = len(offsets) - 1
+    tables = _tables(P, B)
+    k = len(tables[0])
+    d = len(tables[0][0])
+    c = 1.0 / math.sqrt(d)
     S = [[[0.0] * d for _ in range(k)] for _ in range(B)]
     mass = [[0.0] * k for _ in range(B)]
     lse = [0.0] * len(X)
     for u in range(B):
+        P = tables[u]
         toks = list(range(offsets[u], offsets[u + 1]))
         # A[j][t] for the tokens of this user
         A = {}

@@ -5,7 +5,10 @@ benchmark's CPU-baseline leg may use this module.  It imports nothing from the
 product package and shares no code with the HIP library.
 
 Notation (SequenceO1 reading notes, section 3.1): X is one user's history,
-n x d, rows x_i; P is the prototype table, k x d, rows p_j (Eq. 5).  The pages
+n x d, rows x_i; P is the prototype table, k x d, rows p_j (Eq. 5), shared by
+all users; or, in the refinement layers of section 3.3, Eq. (12)-(14), one
+table per user (the user's own sketch, projected, serves as the queries).  The
+pages
 call the affinity matrix S and the sketch X~; here the affinities are Z and the
 sketch is S, matching the C interface.
 
@@ -80,32 +83,47 @@ def affinities(P, Xu):
     return (P @ Xu.T) / np.sqrt(d)
 
 
+def _user_tables(P, B):
+    """P as one table per user: a shared [k, d] table (reading notes Eq. (5):
+    the prototypes are global) is used by every user; a [B, k, d] stack gives
+    user u its own table P[u] (the refinement layers of section 3.3,
+    Eq. (12)-(14), whose queries are the user's own sketch).  Returns (tables, per_user)."""
+    P = _as64(P)
+    if P.ndim == 2:
+        return [P] * B, False
+    if P.ndim == 3 and P.shape[0] == B:
+        return [P[u] for u in range(B)], True
+    raise ValueError("P must be [k, d] or [B, k, d]")
+
+
 def sa_forward_ref(offsets, X, P, mass_norm=False):
     """Sketch Attention forward over a CSR-ragged batch.
 
     offsets : int64 [B+1], offsets[0] = 0, non-decreasing, offsets[B] = T.
     X       : [T, d] histories of all users, concatenated (any float dtype;
               upcast exactly to float64).
-    P       : [k, d] prototypes shared by every user.
+    P       : [k, d] prototypes shared by every user, or [B, k, d] with one
+              table per user.
     Returns (S [B, k, d], lse [T], mass [B, k]), all float64.
     """
     X = _as64(X)
-    P = _as64(P)
     T, d = X.shape
-    k = P.shape[0]
     off = _check_offsets(offsets, T)
     B = off.size - 1
+    tables, _ = _user_tables(P, B)
+    k = tables[0].shape[0]
     S = np.zeros((B, k, d))
     mass = np.zeros((B, k))
     lse = np.zeros(T)
     for u in range(B):
         lo, hi = int(off[u]), int(off[u + 1])
+        Pu = tables[u]
         U = np.zeros((k, d))
         mu = np.zeros(k)
         for c0 in range(lo, hi, _CHUNK):
             c1 = min(hi, c0 + _CHUNK)
             Xc = X[c0:c1]
-            A, l = prototype_softmax(affinities(P, Xc))
+            A, l = prototype_softmax(affinities(Pu, Xc))
             lse[c0:c1] = l
             U += A @ Xc              # Eq. (9)
             mu += A.sum(axis=1)
@@ -119,7 +137,7 @@ def sa_forward_ref(offsets, X, P, mass_norm=False):
 
 
 def sa_backward_ref(offsets, X, P, dS, mass_norm=False):
-    """Gradients of L = sum(dS * S) with respect to X and the shared P.
+    """Gradients of L = sum(dS * S) with respect to X and P.
 
     The chain rule through the forward above, one user at a time:
       plain sum:   G = dS,  c = 0
@@ -130,24 +148,28 @@ def sa_backward_ref(offsets, X, P, dS, mass_norm=False):
       delta_i    = sum_j A[j, i] dA[j, i]      (softmax over prototypes)
       dZ[j, i]   = A[j, i] (dA[j, i] - delta_i)
       dX_i       = g_i + (1/sqrt d) sum_j dZ[j, i] p_j      (Eq. 6)
-      dP        += (1/sqrt d) sum_i dZ[j, i] x_i, summed over all users
-    Returns (dX [T, d], dP [k, d]) in float64.
+      dP_u       = (1/sqrt d) sum_i dZ[j, i] x_i over the user's tokens
+    A shared table's gradient is the sum of the users' dP_u; a per-user stack
+    [B, k, d] gets dP[u] = dP_u.
+    Returns (dX [T, d], dP [k, d] or [B, k, d]) in float64.
     """
     X = _as64(X)
-    P = _as64(P)
     dS = _as64(dS)
     T, d = X.shape
-    k = P.shape[0]
     off = _check_offsets(offsets, T)
     B = off.size - 1
+    tables, per_user = _user_tables(P, B)
+    k = tables[0].shape[0]
     if dS.shape != (B, k, d):
         raise ValueError("dS must be [B, k, d]")
     S, _, mass = sa_forward_ref(off, X, P, mass_norm)
     scale = 1.0 / np.sqrt(d)
     dX = np.zeros((T, d))
-    dP = np.zeros((k, d))
+    dP = np.zeros((B, k, d)) if per_user else np.zeros((k, d))
     for u in range(B):
         lo, hi = int(off[u]), int(off[u + 1])
+        Pu = tables[u]
+        dPu = dP[u] if per_user else dP
         if mass_norm:
             mu = mass[u]
             G = np.zeros((k, d))
@@ -160,13 +182,13 @@ def sa_backward_ref(offsets, X, P, dS, mass_norm=False):
         for c0 in range(lo, hi, _CHUNK):
             c1 = min(hi, c0 + _CHUNK)
             Xc = X[c0:c1]
-            A, _ = prototype_softmax(affinities(P, Xc))
+            A, _ = prototype_softmax(affinities(Pu, Xc))
             dA = G @ Xc.T - cvec[:, None]
             g = A.T @ G
             delta = np.einsum("ji,ji->i", A, dA)
             dZ = A * (dA - delta[None, :])
-            dX[c0:c1] = g + scale * (dZ.T @ P)
-            dP += scale * (dZ @ Xc)
+            dX[c0:c1] = g + scale * (dZ.T @ Pu)
+            dPu += scale * (dZ @ Xc)
     return dX, dP
 
 
