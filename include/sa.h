@@ -71,8 +71,16 @@ typedef enum {
 
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
 
-/* Problem flags. */
-enum { SA_FLAG_MASS_NORM = 1u };
+/* Problem flags.
+ *  SA_FLAG_MASS_NORM: S[j] is the mass-normalised (weighted-mean) sketch.
+ *  SA_FLAG_PER_USER_PROTOTYPES: every user has its own prototype table.  P is
+ *    then [B, k, d] (user u's table at P + u k d) instead of one shared
+ *    [k, d] table, and sa_backward's dP is [B, k, d] with dP[u] the gradient
+ *    of user u's table (instead of the sum over users).  This is the form of
+ *    the refinement layers (SequenceO1 reading notes, section 3.3,
+ *    Eq. (12)-(14)), whose queries are the user's own sketch from the layer
+ *    before. */
+enum { SA_FLAG_MASS_NORM = 1u, SA_FLAG_PER_USER_PROTOTYPES = 2u };
 
 /* Operation selector for sa_workspace_size. */
 enum { SA_OP_FORWARD = 0, SA_OP_BACKWARD = 1 };
@@ -112,7 +120,8 @@ size_t sa_workspace_size(const sa_problem* problem, int op);
  *  offsets_dev : int64 [B+1] device; offsets[0] = 0, non-decreasing,
  *                offsets[B] = total_tokens.
  *  X           : [T, d] (dtype) device.
- *  P           : [k, d] (dtype) device, shared by all users.
+ *  P           : [k, d] (dtype) device, shared by all users; or [B, k, d]
+ *                with SA_FLAG_PER_USER_PROTOTYPES (user u uses P[u]).
  *  S           : float [B, k, d] device, written.
  *  lse         : float [T] device, written; may be NULL (kept in workspace).
  *  mass        : float [B, k] device, written; may be NULL.
@@ -132,7 +141,9 @@ sa_status sa_forward(const sa_problem* problem, const int64_t* offsets_dev,
  * Backward.  Given dS = dL/dS (float [B, k, d]), writes
  *   dX = dL/dX  (float [T, d], overwritten) and
  *   dP = dL/dP  (float [k, d], overwritten; summed over all users because
- *                the prototypes are shared).
+ *                the prototypes are shared; with SA_FLAG_PER_USER_PROTOTYPES
+ *                float [B, k, d], dP[u] from user u's tokens alone, zero for
+ *                an empty user).
  * The softmax weights are recomputed tile by tile from X, P and lse; lse is
  * the forward's output (float [T]) or NULL, in which case it is recomputed.
  * With SA_FLAG_MASS_NORM, S and mass from the forward are required (float

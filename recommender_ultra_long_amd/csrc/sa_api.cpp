@@ -11,12 +11,14 @@ namespace sa {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* p) {
+bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, bool per_user,
+               Plan* p) {
   if (B < 1 || k < 1 || k > 2048 || !(d == 32 || d == 64 || d == 128)) return false;
   if (T < 0 || T >= ((int64_t)1 << 36)) return false;
   if (dtype != 0 && dtype != 1) return false;
   memset(p, 0, sizeof(*p));
   p->B = B; p->k = k; p->d = d; p->T = T; p->dtype = dtype; p->mass_norm = mass_norm;
+  p->per_user = per_user;
   // Segments: about one prototype-stationary workgroup per compute unit, and
   // never more segments than tokens, so that every segment is non-empty.
   auto segments = [T](int nchunks) {
@@ -32,6 +34,9 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* 
   p->bchunk = dtype == 1 ? kChunkBf16 : kChunkF32Bwd;
   p->bnchunks = (k + p->bchunk - 1) / p->bchunk;
   p->Gb = segments(p->bnchunks);
+  // dP partials: one per segment (shared P, summed over users), or one per
+  // (segment, user) piece with per-user tables.
+  p->bslots = per_user ? (int64_t)p->Gb + B - 1 : (int64_t)p->Gb;
 
   const size_t Tn = (size_t)T;
   size_t off = 0;
@@ -49,9 +54,9 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* 
   p->off_G = off; off = align256(off + (size_t)B * kp * d * esz);
   p->off_cv = off; off = align256(off + (size_t)B * kp * 4);
   p->off_cvs = off; off = align256(off + (size_t)B * kp * 4);
-  p->off_Pq = off; off = align256(off + kp * d * 2);
+  p->off_Pq = off; off = align256(off + (per_user ? (size_t)B : 1u) * kp * d * 2);
   p->off_delta = off; off = align256(off + Tn * 4);
-  p->off_dpp = off; off = align256(off + (size_t)p->Gb * k * d * 4);
+  p->off_dpp = off; off = align256(off + (size_t)p->bslots * k * d * 4);
   p->off_blse = off; off = align256(off + Tn * 4);
   p->off_blse2 = off; off = align256(off + (Tn + 1) * 4);
   p->bwd_bytes = off;
@@ -86,7 +91,8 @@ const char* sa_status_string(sa_status s) {
 sa_status sa_validate(const sa_problem* pr, const int64_t* offsets_host) {
   if (pr == nullptr) return SA_ERR_NULL_ARG;
   if (pr->dtype != SA_F32 && pr->dtype != SA_BF16) return SA_ERR_BAD_DTYPE;
-  if ((pr->flags & ~(uint32_t)SA_FLAG_MASS_NORM) != 0u) return SA_ERR_UNSUPPORTED;
+  if ((pr->flags & ~(uint32_t)(SA_FLAG_MASS_NORM | SA_FLAG_PER_USER_PROTOTYPES)) != 0u)
+    return SA_ERR_UNSUPPORTED;
   if (pr->batch < 1 || pr->k < 1 || pr->k > 2048) return SA_ERR_BAD_SHAPE;
   if (!(pr->d == 32 || pr->d == 64 || pr->d == 128)) return SA_ERR_BAD_SHAPE;
   if (pr->total_tokens < 0 || pr->total_tokens >= ((int64_t)1 << 36)) return SA_ERR_BAD_SHAPE;
@@ -102,7 +108,8 @@ size_t sa_workspace_size(const sa_problem* pr, int op) {
   if (sa_validate(pr, nullptr) != SA_OK) return 0;
   Plan p;
   if (!make_plan(pr->batch, pr->k, pr->d, pr->total_tokens, (int)pr->dtype,
-                 (pr->flags & SA_FLAG_MASS_NORM) != 0u, &p))
+                 (pr->flags & SA_FLAG_MASS_NORM) != 0u,
+                 (pr->flags & SA_FLAG_PER_USER_PROTOTYPES) != 0u, &p))
     return 0;
   if (op == SA_OP_FORWARD) return p.fwd_bytes;
   if (op == SA_OP_BACKWARD) return p.bwd_bytes;
@@ -122,7 +129,8 @@ static sa_status forward_impl(const sa_problem* pr, const int64_t* offsets_dev, 
     return SA_ERR_MISALIGNED;
   Plan p;
   const bool mn = (pr->flags & SA_FLAG_MASS_NORM) != 0u;
-  if (!make_plan(pr->batch, pr->k, pr->d, pr->total_tokens, (int)pr->dtype, mn, &p))
+  const bool pu = (pr->flags & SA_FLAG_PER_USER_PROTOTYPES) != 0u;
+  if (!make_plan(pr->batch, pr->k, pr->d, pr->total_tokens, (int)pr->dtype, mn, pu, &p))
     return SA_ERR_BAD_SHAPE;
   if (ws_bytes < p.fwd_bytes) return SA_ERR_WORKSPACE_TOO_SMALL;
 
@@ -131,6 +139,7 @@ static sa_status forward_impl(const sa_problem* pr, const int64_t* offsets_dev, 
   a.offsets = offsets_dev;
   a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
   a.X = X; a.P = P;
+  a.pstride = pu ? (int64_t)p.k * p.d : 0;
   a.lse = lse ? lse : (float*)(w + p.off_lse);
   a.lse2 = (float*)(w + p.off_lse2);
   a.S = S; a.mass = mass;
@@ -161,7 +170,8 @@ static sa_status backward_impl(const sa_problem* pr, const int64_t* offsets_dev,
       (S && !aligned16(S)) || (mass && !aligned16(mass)))
     return SA_ERR_MISALIGNED;
   Plan p;
-  if (!make_plan(pr->batch, pr->k, pr->d, pr->total_tokens, (int)pr->dtype, mn, &p))
+  const bool pu = (pr->flags & SA_FLAG_PER_USER_PROTOTYPES) != 0u;
+  if (!make_plan(pr->batch, pr->k, pr->d, pr->total_tokens, (int)pr->dtype, mn, pu, &p))
     return SA_ERR_BAD_SHAPE;
   if (ws_bytes < p.bwd_bytes) return SA_ERR_WORKSPACE_TOO_SMALL;
 
@@ -170,6 +180,7 @@ static sa_status backward_impl(const sa_problem* pr, const int64_t* offsets_dev,
   a.offsets = offsets_dev;
   a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
   a.X = X; a.P = P; a.dS = dS;
+  a.pstride = pu ? (int64_t)p.k * p.d : 0;
   a.lse_ws = (float*)(w + p.off_blse);
   a.lse2 = (float*)(w + p.off_blse2);
   a.recompute_lse = lse == nullptr ? 1 : 0;
@@ -184,7 +195,7 @@ static sa_status backward_impl(const sa_problem* pr, const int64_t* offsets_dev,
   a.delta = (float*)(w + p.off_delta);
   a.dpp = (float*)(w + p.off_dpp);
   a.status = (uint32_t*)(w + p.off_status);
-  a.Gb = p.Gb; a.bnchunks = p.bnchunks;
+  a.Gb = p.Gb; a.bnchunks = p.bnchunks; a.bslots = p.bslots;
   a.mass_norm = mn ? 1 : 0;
   hipError_t e = launch_bwd(a, (int)pr->dtype, (hipStream_t)stream, prof);
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;

@@ -36,15 +36,16 @@ namespace sa {
 //   [0, nbg)          one group of D/4 threads per (user, prototype) row: G in
 //                     the input dtype, cv, and -cv (when cvs is not null);
 //   [nbg, nbg + nbq)  Pq = P with zero rows k .. kp - 1, 16 bytes per thread
-//                     (bf16 only);
+//                     (bf16 only); one copy per user (pq_users = B, user u's
+//                     table at P + u pstride) or one shared copy (pq_users = 1);
 //   from nbg + nbq    lse2 = lse log2(e), with the +inf sentinel at index T.
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void sa_bwd_prep(
     const float* __restrict__ dS, const float* __restrict__ S, const float* __restrict__ mass,
     int B, int k, int kp, int mass_norm, float scale, OutT* __restrict__ Gq,
     float* __restrict__ cv, float* __restrict__ cvs, unsigned nbg, const bf16* __restrict__ P,
-    bf16* __restrict__ Pq, unsigned nbq, const float* __restrict__ lse, int64_t T,
-    float* __restrict__ lse2) {
+    int64_t pstride, int pq_users, bf16* __restrict__ Pq, unsigned nbq,
+    const float* __restrict__ lse, int64_t T, float* __restrict__ lse2) {
   if (blockIdx.x >= nbg + nbq) {
     const int64_t i = (int64_t)(blockIdx.x - nbg - nbq) * 256 + threadIdx.x;
     if (i < T) lse2[i] = lse[i] * kLog2e;
@@ -54,11 +55,14 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(
   if (blockIdx.x >= nbg) {
     constexpr int UPR = D / 8;   // 16-byte units per row
     const int64_t unit = (int64_t)(blockIdx.x - nbg) * 256 + threadIdx.x;
-    const int row = (int)(unit / UPR), part = (int)(unit % UPR);
-    if (row < kp) {
+    const int64_t row = unit / UPR;                    // over pq_users x kp rows
+    const int part = (int)(unit % UPR);
+    if (row < (int64_t)pq_users * kp) {
+      const int64_t u = row / kp;
+      const int j = (int)(row % kp);
       bf16x8 v = {};
-      if (row < k) v = *(const bf16x8*)(P + (int64_t)row * D + 8 * part);
-      *(bf16x8*)(Pq + (int64_t)row * D + 8 * part) = v;
+      if (j < k) v = *(const bf16x8*)(P + u * pstride + (int64_t)j * D + 8 * part);
+      *(bf16x8*)(Pq + row * D + 8 * part) = v;
     }
     return;
   }
@@ -124,9 +128,9 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(
 template <int D>
 __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
-    const bf16* __restrict__ Pq, const bf16* __restrict__ Gq, const float* __restrict__ cvn,
-    int kp, int64_t T, float alpha, float scale, const float* __restrict__ lse,
-    float* __restrict__ dX, float* __restrict__ delta_out) {
+    const bf16* __restrict__ Pq, int64_t pq_ustride, const bf16* __restrict__ Gq,
+    const float* __restrict__ cvn, int kp, int64_t T, float alpha, float scale,
+    const float* __restrict__ lse, float* __restrict__ dX, float* __restrict__ delta_out) {
   constexpr int NW = 8;                   // waves
   static_assert(NW * 32 == kBwdxTokensBf16, "");
   constexpr int KS = D / 16, DB = D / 32, U = D / 8;
@@ -196,6 +200,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const bool mine = tok >= ulo && tok < uhi;
     const float lsh = mine ? l2 : INFINITY;
     const bf16* Gu = Gq + (int64_t)u * kp * D;
+    const bf16* Pu = Pq + (int64_t)u * pq_ustride;   // the user's table (or the shared one)
     const float* cvu = cvn + (int64_t)u * kp;
 
     // Chunk q of the stream: q < nch is stage-1 chunk q (P, G, -cv), then
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
 #pragma unroll
         for (int j = 0; j < XI; ++j) {
           if (UPW >= 64 || lane < UPW) {
-            lds_copy16(Pq, goff + cgo[j], dst + j * 1024);
+            lds_copy16(Pu, goff + cgo[j], dst + j * 1024);
             lds_copy16(Gu, goff + cgo[j], dst + GOFF + j * 1024);
           }
         }
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
         const uint32_t goff = (uint32_t)(q < 2 * nch ? q - nch : 0) * MB;
 #pragma unroll
         for (int j = 0; j < XI; ++j)
-          if (UPW >= 64 || lane < UPW) lds_copy16(Pq, goff + cgo[j], dst + j * 1024);
+          if (UPW >= 64 || lane < UPW) lds_copy16(Pu, goff + cgo[j], dst + j * 1024);
       }
     };
     // After chunk q: wait until chunk q + 1 has landed (q + 2 may still be in
@@ -408,17 +413,20 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
 // prototypes, the tiling and copy pipeline of the forward aggregation:
 // 32-token tiles copied global -> LDS (X, lse2, delta) six tiles ahead into
 // eight buffers, a barrier after every second tile.  Per tile: Z^T and dA'^T
-// (matrix cores), dZ (vector ALU), dP^T += X^T dZ^T (matrix cores).  The
-// partial spans the whole segment, across users (P is shared).
+// (matrix cores), dZ (vector ALU), dP^T += X^T dZ^T (matrix cores).  With a
+// shared P the partial spans the whole segment, across users (slot s).  With
+// one table per user (PU, user u's at P + u pstride) each (segment, user)
+// piece has its own partial (slot s + u), and a user change reloads the
+// prototype rows.
 //
 // lse2 holds the log-sum-exp in log2 units with lse2[T] = +inf, which rows
 // past the end of a tile read (weight 0, so dZ = 0).
-template <int D, int NW>
+template <int D, int NW, bool PU>
 __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
-    const bf16* __restrict__ P, const bf16* __restrict__ Gq, const float* __restrict__ cv, int k,
-    int kp, int64_t T, int G, float alpha, const float* __restrict__ lse2,
-    const float* __restrict__ delta, float* __restrict__ dpp) {
+    const bf16* __restrict__ P, int64_t pstride, const bf16* __restrict__ Gq,
+    const float* __restrict__ cv, int k, int kp, int64_t T, int G, float alpha,
+    const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dpp) {
   constexpr int KS = D / 16;             // reduction steps over d
   constexpr int DB = D / 32;             // 32-row blocks of the transposed partial
   constexpr int U = D / 8;               // 16-byte units per token row
@@ -450,18 +458,37 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
 
   // B operands: pw[ks] = P[proto][16 ks + 8h .. +7], gw likewise for the
   // current user's G (row stride kp); cw = cv[user][proto].
+  const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
+  TileWalker<TILE> cw_;                // tile being computed
+  cw_.start(offsets, B, lo, hi);
+
   bf16x8 pw[KS], gw[KS];
   float cw;
+  auto load_prototype = [&](const bf16* Pu) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) pw[ks] = *(const bf16x8*)(P + (int64_t)prow * D + 16 * ks + 8 * h);
+    for (int ks = 0; ks < KS; ++ks)
+      pw[ks] = *(const bf16x8*)(Pu + (int64_t)prow * D + 16 * ks + 8 * h);
+  };
+  load_prototype(PU && cw_.valid ? P + (int64_t)cw_.user * pstride : P);
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  // acc[db] register i is dP[proto][d = 32 db + crow(i, h)] / c.
+  auto flush = [&](int64_t slot) {
+    if (proto < k) {
+      float* dst = dpp + (slot * k + proto) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+          *(f32x4*)(dst + 32 * db + 8 * g + 4 * h) = v;
+        }
+    }
+  };
 
-  const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
-  TileWalker<TILE> cw_;                // tile being computed
-  cw_.start(offsets, B, lo, hi);
+  int guser = -1;
   if (cw_.valid) {
     TileWalker<TILE> qw = cw_;         // next tile to copy
 
@@ -497,7 +524,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
       if (valid) qw.advance();
     };
 
-    int guser = cw_.user;
+    guser = cw_.user;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * kp + prow) * D + 16 * ks + 8 * h);
@@ -530,11 +557,24 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
       copy_next((t + AHEAD) & (NBUF - 1));
       if (cw_.user != guser) {
         // A new user: its G rows and cv (rare; waits for the loads here).
+        if constexpr (PU) {
+          // The finished piece's partial; then nothing stays in flight, so
+          // the vmcnt counts below hold as at the start.
+          flush((int64_t)s + guser);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+          wait_vmem_all();
+        }
         guser = cw_.user;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * kp + prow) * D + 16 * ks + 8 * h);
         cw = cv[(int64_t)guser * kp + prow];
+        if constexpr (PU) {
+          load_prototype(P + (int64_t)guser * pstride);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(pw[ks]));
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(gw[ks]));
         asm volatile("" ::"v"(cw));
@@ -588,18 +628,10 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
     }
     wait_vmcnt<0>();   // no copy left in flight
   }
-  // Flush this segment's partial: acc[db] register i is
-  // dP[proto][d = 32 db + crow(i, h)] / c.
-  if (proto < k) {
-    float* dst = dpp + ((int64_t)s * k + proto) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
-        *(f32x4*)(dst + 32 * db + 8 * g + 4 * h) = v;
-      }
-  }
+  // This segment's partial (shared P: every segment writes its slot), or the
+  // last piece's.
+  if (!PU) flush(s);
+  else if (guser >= 0) flush((int64_t)s + guser);
 }
 
 
@@ -609,7 +641,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
 template <int D>
 __global__ __launch_bounds__(256) void sa_bwdx_f32(
     const int64_t* __restrict__ offsets, int B, const float* __restrict__ X,
-    const float* __restrict__ P, const float* __restrict__ Gq, const float* __restrict__ cv, int k,
+    const float* __restrict__ P, int64_t pstride, const float* __restrict__ Gq,
+    const float* __restrict__ cv, int k,
     int64_t T, float alpha, float scale, const float* __restrict__ lse, float* __restrict__ dX,
     float* __restrict__ delta_out) {
   constexpr int PC = 32, DS = D / 8;
@@ -634,6 +667,7 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
     const bool mine = tok >= ulo && tok < uhi;
     const float lsh = mine ? l2 : INFINITY;
     const float* Gu = Gq + (int64_t)u * k * D;
+    const float* Pu = P + (int64_t)u * pstride;   // the user's table (or the shared one)
     float g[DS], aa[DS], bb[DS];
 #pragma unroll
     for (int e = 0; e < DS; ++e) { g[e] = 0.f; aa[e] = 0.f; bb[e] = 0.f; }
@@ -643,7 +677,7 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
       for (int i = tid; i < PC * D; i += 256) {
         const int r = i / D, c = i % D;
         const bool v = p0 + r < k;
-        sP[r][c] = v ? P[(int64_t)(p0 + r) * D + c] : 0.f;
+        sP[r][c] = v ? Pu[(int64_t)(p0 + r) * D + c] : 0.f;
         sG[r][c] = v ? Gu[(int64_t)(p0 + r) * D + c] : 0.f;
       }
       if (tid < PC) sC[tid] = p0 + tid < k ? cv[(int64_t)u * k + p0 + tid] : 0.f;
@@ -682,11 +716,14 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
 
 // fp32 dP pass.  grid = (Gb, ceil(k / 32)); block 256: thread (j = t / 8,
 // q = t % 8) owns prototype j, columns q D/8 .. +D/8 of the partial, and
-// computes the weights of tokens 4q .. 4q+3 of each 32-token tile.
+// computes the weights of tokens 4q .. 4q+3 of each 32-token tile.  With one
+// table per user (pstride != 0) each (segment, user) piece writes its own
+// partial (slot s + u) and a user change reloads the table's rows.
 template <int D>
 __global__ __launch_bounds__(256) void sa_bwdp_f32(
     const int64_t* __restrict__ offsets, int B, const float* __restrict__ X,
-    const float* __restrict__ P, const float* __restrict__ Gq, const float* __restrict__ cv, int k,
+    const float* __restrict__ P, int64_t pstride, const float* __restrict__ Gq,
+    const float* __restrict__ cv, int k,
     int64_t T, int G, float alpha, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dpp) {
   constexpr int PC = kChunkF32Bwd, TILE = 32, DS = D / 8;
@@ -699,13 +736,16 @@ __global__ __launch_bounds__(256) void sa_bwdp_f32(
   const int j = tid >> 3, q = tid & 7;
   const int s = blockIdx.x;
   const int p0 = blockIdx.y * PC;
-  for (int i = tid; i < PC * D; i += 256) {
-    const int r = i / D, c = i % D;
-    sP[r][c] = (p0 + r < k) ? P[(int64_t)(p0 + r) * D + c] : 0.f;
-  }
   float acc[DS];
 #pragma unroll
   for (int e = 0; e < DS; ++e) acc[e] = 0.f;
+  auto flush = [&](int64_t slot) {
+    if (p0 + j < k) {
+      float* dst = dpp + (slot * k + p0 + j) * D + q * DS;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) dst[e] = acc[e];
+    }
+  };
 
   const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
   TileWalker<TILE> cur;
@@ -714,7 +754,19 @@ __global__ __launch_bounds__(256) void sa_bwdp_f32(
   while (cur.valid) {
     __syncthreads();
     if (cur.user != loaded_user) {
+      if (pstride != 0 && loaded_user >= 0) {
+        flush((int64_t)s + loaded_user);   // the finished piece
+#pragma unroll
+        for (int e = 0; e < DS; ++e) acc[e] = 0.f;
+      }
       const float* Gu = Gq + (int64_t)cur.user * k * D;
+      if (pstride != 0 || loaded_user < 0) {
+        const float* Pu = P + (int64_t)cur.user * pstride;
+        for (int i = tid; i < PC * D; i += 256) {
+          const int r = i / D, c = i % D;
+          sP[r][c] = (p0 + r < k) ? Pu[(int64_t)(p0 + r) * D + c] : 0.f;
+        }
+      }
       for (int i = tid; i < PC * D; i += 256) {
         const int r = i / D, c = i % D;
         sG[r][c] = (p0 + r < k) ? Gu[(int64_t)(p0 + r) * D + c] : 0.f;
@@ -753,11 +805,8 @@ __global__ __launch_bounds__(256) void sa_bwdp_f32(
     }
     cur.advance();
   }
-  if (p0 + j < k) {
-    float* dst = dpp + ((int64_t)s * k + p0 + j) * D + q * DS;
-#pragma unroll
-    for (int e = 0; e < DS; ++e) dst[e] = acc[e];
-  }
+  if (pstride == 0) flush(s);
+  else if (loaded_user >= 0) flush((int64_t)s + loaded_user);
 }
 
 // ----------------------------------------------------------------------------
@@ -800,8 +849,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
   const float scale = 1.0f / sqrtf((float)D);
   const float alpha = scale * kLog2e;
   hipError_t e;
+  const bool pu = a.pstride != 0;
   if (a.recompute_lse && a.T > 0) {
     FwdArgs f = {};
+    f.offsets = a.offsets; f.B = a.B; f.pstride = a.pstride;
     f.X = a.X; f.P = a.P; f.k = a.k; f.d = a.d; f.T = a.T; f.lse = a.lse_ws;
     f.lse2 = dtype == 1 ? a.lse2 : nullptr;
     e = dtype == 1 ? launch_stats_bf16(f, st, prof) : launch_stats_f32(f, st, prof);
@@ -813,18 +864,22 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
   const int64_t rows = (int64_t)a.B * a.kp;
   const unsigned nbg = (unsigned)((rows * (D / 4) + 255) / 256);
   const bool bf = dtype == 1;
-  const unsigned nbq = bf ? (unsigned)(((int64_t)a.kp * (D / 8) + 255) / 256) : 0u;
+  const int pq_users = pu ? a.B : 1;
+  const unsigned nbq =
+      bf ? (unsigned)(((int64_t)pq_users * a.kp * (D / 8) + 255) / 256) : 0u;
   const bool lse2 = bf && a.T > 0 && !a.recompute_lse;
   const unsigned nbl = lse2 ? (unsigned)((a.T + 1 + 255) / 256) : 0u;
   prof_begin(prof, "sa_bwd_prep", st);
   if (bf)
     hipLaunchKernelGGL((sa_bwd_prep<bf16, D>), dim3(nbg + nbq + nbl), dim3(256), 0, st, a.dS, a.S,
                        a.mass, a.B, a.k, a.kp, a.mass_norm, scale, (bf16*)a.Gq, a.cv, a.cvs, nbg,
-                       (const bf16*)a.P, (bf16*)a.Pq, nbq, a.lse, a.T, a.lse2);
+                       (const bf16*)a.P, a.pstride, pq_users, (bf16*)a.Pq, nbq, a.lse, a.T,
+                       a.lse2);
   else
     hipLaunchKernelGGL((sa_bwd_prep<float, D>), dim3(nbg), dim3(256), 0, st, a.dS, a.S, a.mass,
                        a.B, a.k, a.kp, a.mass_norm, scale, (float*)a.Gq, a.cv, (float*)nullptr,
-                       nbg, (const bf16*)nullptr, (bf16*)nullptr, 0u, a.lse, a.T, a.lse2);
+                       nbg, (const bf16*)nullptr, (int64_t)0, 1, (bf16*)nullptr, 0u, a.lse, a.T,
+                       a.lse2);
   e = hipGetLastError();
   prof_end(prof, st);
   if (e != hipSuccess) return e;
@@ -833,16 +888,23 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
       const unsigned nbx = (unsigned)((a.T + kBwdxTokensBf16 - 1) / kBwdxTokensBf16);
       prof_begin(prof, "sa_bwdx_bf16", st);
       hipLaunchKernelGGL(sa_bwdx_bf16<D>, dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st, a.offsets,
-                         a.B, (const bf16*)a.X, (const bf16*)a.Pq, (const bf16*)a.Gq, a.cvs, a.kp, a.T,
+                         a.B, (const bf16*)a.X, (const bf16*)a.Pq,
+                         pu ? (int64_t)a.kp * D : (int64_t)0, (const bf16*)a.Gq, a.cvs, a.kp, a.T,
                          alpha, scale, a.lse, a.dX, a.delta);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
       prof_begin(prof, "sa_bwdp_bf16", st);
-      hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves>), dim3(a.Gb, a.bnchunks), dim3(64 * kBwdpWaves),
-                         0, st, a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.P,
-                         (const bf16*)a.Gq, a.cv, a.k, a.kp, a.T, a.Gb, alpha, a.lse2, a.delta,
-                         a.dpp);
+      if (pu)
+        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, true>), dim3(a.Gb, a.bnchunks),
+                           dim3(64 * kBwdpWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
+                           (const bf16*)a.P, a.pstride, (const bf16*)a.Gq, a.cv, a.k, a.kp, a.T,
+                           a.Gb, alpha, a.lse2, a.delta, a.dpp);
+      else
+        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, false>), dim3(a.Gb, a.bnchunks),
+                           dim3(64 * kBwdpWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
+                           (const bf16*)a.P, (int64_t)0, (const bf16*)a.Gq, a.cv, a.k, a.kp, a.T,
+                           a.Gb, alpha, a.lse2, a.delta, a.dpp);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
@@ -850,20 +912,23 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
       const unsigned nbx = (unsigned)((a.T + kBwdxTokensF32 - 1) / kBwdxTokensF32);
       prof_begin(prof, "sa_bwdx_f32", st);
       hipLaunchKernelGGL(sa_bwdx_f32<D>, dim3(nbx), dim3(256), 0, st, a.offsets, a.B,
-                         (const float*)a.X, (const float*)a.P, (const float*)a.Gq, a.cv, a.k, a.T,
-                         alpha, scale, a.lse, a.dX, a.delta);
+                         (const float*)a.X, (const float*)a.P, a.pstride, (const float*)a.Gq,
+                         a.cv, a.k, a.T, alpha, scale, a.lse, a.dX, a.delta);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
       prof_begin(prof, "sa_bwdp_f32", st);
       hipLaunchKernelGGL(sa_bwdp_f32<D>, dim3(a.Gb, a.bnchunks), dim3(256), 0, st, a.offsets, a.B,
-                         (const float*)a.X, (const float*)a.P, (const float*)a.Gq, a.cv, a.k, a.T,
-                         a.Gb, alpha, a.lse, a.delta, a.dpp);
+                         (const float*)a.X, (const float*)a.P, a.pstride, (const float*)a.Gq,
+                         a.cv, a.k, a.T, a.Gb, alpha, a.lse, a.delta, a.dpp);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
     }
   }
+  if (pu)   // dP[u] = c (sum of user u's pieces), like the forward's sketch
+    return launch_piece_sum(a.offsets, a.B, a.k, a.d, a.T, a.Gb, a.dpp, scale, a.dP, a.status, st,
+                            prof);
   const int64_t kd = (int64_t)a.k * a.d;
   prof_begin(prof, "sa_dp_reduce", st);
   hipLaunchKernelGGL(sa_dp_reduce, dim3((unsigned)((kd + 255) / 256)), dim3(256), 0, st,

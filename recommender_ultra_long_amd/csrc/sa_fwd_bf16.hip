@@ -33,12 +33,17 @@ namespace sa {
 // Block: 256 threads = 4 waves; wave w handles tokens blk*256 + 64w .. +63 as
 // two 32-token MFMA tiles.  Prototypes are streamed in chunks of 64 rows
 // through LDS in MFMA fragment order, double buffered via registers.
-template <int D>
+// With one table per user (PU), the block makes one pass over the prototypes
+// per user among its tokens, with that user's table, and each pass writes the
+// statistics of its user's tokens only.
+template <int D, bool PU>
 __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__ X,
                                                      const bf16* __restrict__ P, int k,
                                                      int64_t T, float alpha, float scale,
                                                      float* __restrict__ lse_out,
-                                                     float* __restrict__ lse2_out) {
+                                                     float* __restrict__ lse2_out,
+                                                     const int64_t* __restrict__ offsets, int B,
+                                                     int64_t pstride) {
   constexpr int KS = D / 16;            // 16-wide reduction steps over d
   constexpr int PCH = 64;               // prototypes per LDS chunk
   constexpr int NPIECE = PCH * D / 8;   // 16-byte pieces per chunk
@@ -66,6 +71,7 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
   // ((pt KS + ks) 64 + L) is lane L's A operand for prototype tile pt and
   // step ks, i.e. P[p0 + 32 pt + L % 32][16 ks + 8 (L / 32) .. +7].  Consecutive
   // lanes write consecutive 16-byte slots (no LDS bank conflicts).
+  const bf16* Pu = P;                    // the current user's table
   auto load_chunk = [&](int p0, bf16x8 (&reg)[PPT]) {
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       const int ks = rem / 64, L = rem % 64;
       const int row = p0 + pt * 32 + (L & 31);
       const int cp = 2 * ks + (L >> 5);
-      if (row < k) reg[e] = *(const bf16x8*)(P + (int64_t)row * D + 8 * cp);
+      if (row < k) reg[e] = *(const bf16x8*)(Pu + (int64_t)row * D + 8 * cp);
       else reg[e] = bf16x8{};
     }
   };
@@ -125,68 +131,92 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
     }
   };
 
-  // Software pipeline over prototype tiles: the products of tile p are
-  // issued in the same straight-line block as the vector work on tile p - 1,
-  // so the matrix cores and the vector ALU overlap.  All chunks but the last
-  // are full; q starts as an all -inf tile, whose fold changes nothing.
-  bf16x8 pre[PPT];
-  load_chunk(0, pre);
-  store_chunk(0, pre);
-  __syncthreads();
-  const int nch = (k + PCH - 1) / PCH;
-  f32x16 q0, q1;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
-  static_assert(PCH == 64, "two prototype tiles per chunk");
-  for (int ci = 0; ci + 1 < nch; ++ci) {
-    load_chunk((ci + 1) * PCH, pre);
-    const int buf = ci & 1;
-    // The two tiles of the chunk swap roles with q, so nothing is copied.
-    f32x16 c0, c1;
-    products(buf, 0, c0, c1);
-    fold(q0, 0);
-    fold(q1, 1);
-    products(buf, 1, q0, q1);
-    fold(c0, 0);
-    fold(c1, 1);
-    store_chunk(buf ^ 1, pre);
+  // One pass over all prototypes of table Pu; writes the statistics of the
+  // tokens in [ulo, uhi).
+  auto run_pass = [&](int64_t ulo, int64_t uhi) {
+    m[0] = m[1] = -INFINITY;
+    l[0] = l[1] = 0.f;
+    // Software pipeline over prototype tiles: the products of tile p are
+    // issued in the same straight-line block as the vector work on tile p - 1,
+    // so the matrix cores and the vector ALU overlap.  All chunks but the last
+    // are full; q starts as an all -inf tile, whose fold changes nothing.
+    bf16x8 pre[PPT];
+    load_chunk(0, pre);
+    store_chunk(0, pre);
     __syncthreads();
-  }
-  {
-    // Last chunk: tiles may be partial or past k; padding rows drop out as
-    // -inf.
-    const int ci = nch - 1, buf = ci & 1;
+    const int nch = (k + PCH - 1) / PCH;
+    f32x16 q0, q1;
 #pragma unroll
-    for (int pt = 0; pt < PCH / 32; ++pt) {
-      const int pbase = ci * PCH + pt * 32;
-      if (pbase >= k) break;             // uniform across the block
+    for (int i = 0; i < 16; ++i) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
+    static_assert(PCH == 64, "two prototype tiles per chunk");
+    for (int ci = 0; ci + 1 < nch; ++ci) {
+      load_chunk((ci + 1) * PCH, pre);
+      const int buf = ci & 1;
+      // The two tiles of the chunk swap roles with q, so nothing is copied.
       f32x16 c0, c1;
-      products(buf, pt, c0, c1);
+      products(buf, 0, c0, c1);
       fold(q0, 0);
       fold(q1, 1);
-      q0 = c0;
-      q1 = c1;
-      if (pbase + 32 > k) {
+      products(buf, 1, q0, q1);
+      fold(c0, 0);
+      fold(c1, 1);
+      store_chunk(buf ^ 1, pre);
+      __syncthreads();
+    }
+    {
+      // Last chunk: tiles may be partial or past k; padding rows drop out as
+      // -inf.
+      const int ci = nch - 1, buf = ci & 1;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (pbase + crow(i, h) >= k) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
+      for (int pt = 0; pt < PCH / 32; ++pt) {
+        const int pbase = ci * PCH + pt * 32;
+        if (pbase >= k) break;             // uniform across the block
+        f32x16 c0, c1;
+        products(buf, pt, c0, c1);
+        fold(q0, 0);
+        fold(q1, 1);
+        q0 = c0;
+        q1 = c1;
+        if (pbase + 32 > k) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (pbase + crow(i, h) >= k) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
+        }
+      }
+      fold(q0, 0);
+      fold(q1, 1);
+    }
+
+    // Lanes l and l ^ 32 saw disjoint halves of the prototypes of one token.
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const float mo = shfl_xor32(m[tt]), lo = shfl_xor32(l[tt]);
+      const float M = fmaxf(m[tt], mo);
+      const float Ma = M * alpha;
+      const float L = l[tt] * exp2_fast(fmaf(m[tt], alpha, -Ma)) + lo * exp2_fast(fmaf(mo, alpha, -Ma));
+      const int64_t tok = tok0 + tt * 32 + l32;
+      if (h == 0 && tok >= ulo && tok < uhi) {
+        lse_out[tok] = M * scale + __logf(L);
+        if (lse2_out != nullptr) lse2_out[tok] = Ma + __log2f(L);
       }
     }
-    fold(q0, 0);
-    fold(q1, 1);
-  }
+  };
 
-  // Lanes l and l ^ 32 saw disjoint halves of the prototypes of one token.
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const float mo = shfl_xor32(m[tt]), lo = shfl_xor32(l[tt]);
-    const float M = fmaxf(m[tt], mo);
-    const float Ma = M * alpha;
-    const float L = l[tt] * exp2_fast(fmaf(m[tt], alpha, -Ma)) + lo * exp2_fast(fmaf(mo, alpha, -Ma));
-    const int64_t tok = tok0 + tt * 32 + l32;
-    if (h == 0 && tok < T) {
-      lse_out[tok] = M * scale + __logf(L);
-      if (lse2_out != nullptr) lse2_out[tok] = Ma + __log2f(L);
+  if constexpr (!PU) {
+    run_pass(0, T);
+  } else {
+    // One pass per user among this block's tokens, with that user's table.
+    const int64_t b0 = (int64_t)blockIdx.x * 256;
+    const int64_t b1 = b0 + 256 < T ? b0 + 256 : T;
+    for (int u = first_user_after(offsets, B, b0);; ++u) {
+      const int64_t ulo = clamp64(uload64(offsets + u), b0, b1);
+      const int64_t uhi = clamp64(uload64(offsets + u + 1), ulo, b1);
+      if (uhi > ulo) {
+        Pu = P + (int64_t)u * pstride;
+        run_pass(ulo, uhi);
+      }
+      if (uhi >= b1 || u + 1 >= B) break;
+      __syncthreads();   // the last pass's LDS reads are done before the next store
     }
   }
   // Sentinel read by the aggregation pass for rows past the end of a tile.
@@ -209,10 +239,15 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
 //
 // lse2 holds the per-token log-sum-exp in log2 units, with lse2[T] = +inf:
 // rows of a tile past its end read that entry and get weight 0.
-template <int D, bool MASS, int NW, int PT>
+//
+// With one table per user (PU, user u's table at P + u pstride), every piece
+// after the segment's first reloads the prototype rows and recomputes the
+// affinities of its first tile (the step before computed them with the
+// previous user's table).
+template <int D, bool MASS, int NW, int PT, bool PU>
 __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
-    const bf16* __restrict__ P, int k, int64_t T, int G, float alpha,
+    const bf16* __restrict__ P, int64_t pstride, int k, int64_t T, int G, float alpha,
     const float* __restrict__ lse2, float* __restrict__ part, float* __restrict__ pmass) {
   constexpr int KS = D / 16;             // reduction steps of the affinity product
   constexpr int DB = D / 32;             // 32-row blocks of the transposed sketch
@@ -241,22 +276,25 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
   const uint32_t sl0 = lds_addr((const SA_LDS void*)&sL[0][0]);
   const SA_LDS char* lds = (const SA_LDS char*)0;
 
-  // Prototype rows as B operands of Z^T = X P^T: pw[pt][ks] holds
-  // P[pw0 + 32 pt + l32][16 ks + 8h .. +7].
-  bf16x8 pw[PT][KS];
-#pragma unroll
-  for (int pt = 0; pt < PT; ++pt) {
-    const int row = pw0 + pt * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      pw[pt][ks] = row < k ? *(const bf16x8*)(P + (int64_t)row * D + 16 * ks + 8 * h) : bf16x8{};
-  }
-
   const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
   TileWalker<TILE> cw;                 // tile being computed
   cw.start(offsets, B, lo, hi);
   if (!cw.valid) return;
   TileWalker<TILE> qw = cw;            // next tile to copy
+
+  // Prototype rows as B operands of Z^T = X P^T: pw[pt][ks] holds
+  // P[pw0 + 32 pt + l32][16 ks + 8h .. +7] (of the piece's user's table).
+  bf16x8 pw[PT][KS];
+  auto load_prototypes = [&](const bf16* Pu) {
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      const int row = pw0 + pt * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        pw[pt][ks] = row < k ? *(const bf16x8*)(Pu + (int64_t)row * D + 16 * ks + 8 * h) : bf16x8{};
+    }
+  };
+  load_prototypes(PU ? P + (int64_t)cw.user * pstride : P);
 
   // Copy geometry.  Copy instruction j of this wave moves units
   // v0 .. v0 + 63 of the tile, v0 = wave UPW + 64 j; the lane's unit v sits in
@@ -340,6 +378,29 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
   // tiles.  The accumulators are only touched by the matrix cores inside the
   // inner loop, and flushed once per piece.
   while (cw.valid) {
+    if constexpr (PU) {
+      if (t > 0) {
+        // A later piece: the next user's rows.  No load is in flight here (the
+        // previous flush waited for all), and tile t's buffer is complete and
+        // published (the previous step read it).
+        load_prototypes(P + (int64_t)cw.user * pstride);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(pw[pt][ks]));
+        wait_vmcnt<0>();
+        const SA_LDS char* xs = lds + sx0 + (t & (NBUF - 1)) * XBYTES;
+        bf16x8 a0[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a0[ks] = *(const SA_LDS bf16x8*)(xs + aoff[ks]);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          znext[pt] = mfma32(a0[0], pw[pt][0], f32x16{});
+#pragma unroll
+          for (int ks = 1; ks < KS; ++ks) znext[pt] = mfma32(a0[ks], pw[pt][ks], znext[pt]);
+        }
+      }
+    }
     const int64_t slot = (int64_t)s + cw.user;
     f32x16 acc[PT][DB];
 #pragma unroll
@@ -459,8 +520,14 @@ static hipError_t launch_stats_bf16_t(const FwdArgs& a, hipStream_t st, Prof* pr
   const float alpha = scale * kLog2e;
   const unsigned nb = (unsigned)((a.T + 255) / 256);
   prof_begin(prof, "sa_stats_bf16", st);
-  hipLaunchKernelGGL(sa_stats_bf16<D>, dim3(nb), dim3(256), 0, st, (const bf16*)a.X,
-                     (const bf16*)a.P, a.k, a.T, alpha, scale, a.lse, a.lse2);
+  if (a.pstride != 0)
+    hipLaunchKernelGGL((sa_stats_bf16<D, true>), dim3(nb), dim3(256), 0, st, (const bf16*)a.X,
+                       (const bf16*)a.P, a.k, a.T, alpha, scale, a.lse, a.lse2, a.offsets, a.B,
+                       a.pstride);
+  else
+    hipLaunchKernelGGL((sa_stats_bf16<D, false>), dim3(nb), dim3(256), 0, st, (const bf16*)a.X,
+                       (const bf16*)a.P, a.k, a.T, alpha, scale, a.lse, a.lse2, a.offsets, a.B,
+                       (int64_t)0);
   const hipError_t e = hipGetLastError();
   prof_end(prof, st);
   return e;
@@ -475,14 +542,26 @@ static hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t st, Prof* prof
     hipError_t e = launch_stats_bf16_t<D>(a, st, prof);
     if (e != hipSuccess) return e;
     prof_begin(prof, "sa_agg_bf16", st);
-    if (a.mass_norm || a.mass != nullptr)
-      hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, PT>), dim3(a.G, a.nchunks),
-                         dim3(64 * kAggWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
-                         (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse2, a.part, a.pmass);
+    const bool ms = a.mass_norm || a.mass != nullptr, pu = a.pstride != 0;
+    const dim3 grid(a.G, a.nchunks), block(64 * kAggWaves);
+    const bf16* X = (const bf16*)a.X;
+    const bf16* P = (const bf16*)a.P;
+    if (ms && pu)
+      hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, PT, true>), grid, block, 0, st,
+                         a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
+                         a.pmass);
+    else if (ms)
+      hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, PT, false>), grid, block, 0, st,
+                         a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
+                         a.pmass);
+    else if (pu)
+      hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, PT, true>), grid, block, 0, st,
+                         a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
+                         a.pmass);
     else
-      hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, PT>), dim3(a.G, a.nchunks),
-                         dim3(64 * kAggWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
-                         (const bf16*)a.P, a.k, a.T, a.G, alpha, a.lse2, a.part, a.pmass);
+      hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, PT, false>), grid, block, 0, st,
+                         a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
+                         a.pmass);
     e = hipGetLastError();
     prof_end(prof, st);
     if (e != hipSuccess) return e;

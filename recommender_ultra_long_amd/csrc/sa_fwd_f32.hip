@@ -9,25 +9,20 @@
 
 namespace sa {
 
-// Pass 1: one token per thread, prototypes streamed through LDS 32 at a time.
+// Log-sum-exp of the thread's token x over the k rows of table Pu, which the
+// block streams through LDS 32 rows at a time (every thread of the block must
+// call it).
 template <int D>
-__global__ __launch_bounds__(256) void sa_stats_f32(const float* __restrict__ X,
-                                                    const float* __restrict__ P, int k, int64_t T,
-                                                    float alpha, float scale,
-                                                    float* __restrict__ lse_out) {
+__device__ float table_lse(const float* __restrict__ Pu, int k, const float (&x)[D], float alpha,
+                           float scale, float (*sP)[D]) {
   constexpr int PC = 32;
-  __shared__ float sP[PC][D];
   const int tid = threadIdx.x;
-  const int64_t tok = (int64_t)blockIdx.x * 256 + tid;
-  float x[D];
-#pragma unroll
-  for (int e = 0; e < D; ++e) x[e] = tok < T ? X[tok * D + e] : 0.f;
   float m = -INFINITY, l = 0.f;
   for (int p0 = 0; p0 < k; p0 += PC) {
     __syncthreads();
     for (int q = tid; q < PC * D; q += 256) {
       const int r = q / D, c = q % D;
-      sP[r][c] = (p0 + r < k) ? P[(int64_t)(p0 + r) * D + c] : 0.f;
+      sP[r][c] = (p0 + r < k) ? Pu[(int64_t)(p0 + r) * D + c] : 0.f;
     }
     __syncthreads();
     const int np = k - p0 < PC ? k - p0 : PC;
@@ -49,15 +44,53 @@ __global__ __launch_bounds__(256) void sa_stats_f32(const float* __restrict__ X,
     l = fmaf(l, exp2_fast(fmaf(m, alpha, -ma)), s);
     m = mnew;
   }
-  if (tok < T) lse_out[tok] = m * scale + __logf(l);
+  return m * scale + __logf(l);
+}
+
+// Pass 1: one token per thread, prototypes streamed through LDS 32 at a time.
+// With one table per user (user u's table at P + u pstride, pstride != 0),
+// the block makes one pass per user among its tokens and each token keeps
+// the result of its own user's pass.
+template <int D>
+__global__ __launch_bounds__(256) void sa_stats_f32(const float* __restrict__ X,
+                                                    const float* __restrict__ P, int k, int64_t T,
+                                                    float alpha, float scale,
+                                                    float* __restrict__ lse_out,
+                                                    const int64_t* __restrict__ offsets, int B,
+                                                    int64_t pstride) {
+  __shared__ float sP[32][D];
+  const int64_t b0 = (int64_t)blockIdx.x * 256;
+  const int64_t b1 = b0 + 256 < T ? b0 + 256 : T;
+  const int64_t tok = b0 + threadIdx.x;
+  float x[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) x[e] = tok < T ? X[tok * D + e] : 0.f;
+  if (pstride == 0) {
+    const float v = table_lse<D>(P, k, x, alpha, scale, sP);
+    if (tok < T) lse_out[tok] = v;
+    return;
+  }
+  for (int u = first_user_after(offsets, B, b0);; ++u) {
+    const int64_t ulo = clamp64(uload64(offsets + u), b0, b1);
+    const int64_t uhi = clamp64(uload64(offsets + u + 1), ulo, b1);
+    if (uhi > ulo) {
+      // (table_lse starts every chunk with a barrier, so the previous pass's
+      // LDS reads are done before sP is refilled)
+      const float v = table_lse<D>(P + (int64_t)u * pstride, k, x, alpha, scale, sP);
+      if (tok >= ulo && tok < uhi) lse_out[tok] = v;
+    }
+    if (uhi >= b1 || u + 1 >= B) break;
+  }
 }
 
 // Pass 2: grid = (G, nchunks), block 256.  Workgroup owns 64 prototypes;
-// thread t owns prototype t / 4 and columns (t % 4) D/4 .. +D/4 of U.
+// thread t owns prototype t / 4 and columns (t % 4) D/4 .. +D/4 of U.  With
+// one table per user, the workgroup's rows of it are reloaded at a user change.
 template <int D>
 __global__ __launch_bounds__(256) void sa_agg_f32(const int64_t* __restrict__ offsets, int B,
                                                   const float* __restrict__ X,
-                                                  const float* __restrict__ P, int k, int64_t T,
+                                                  const float* __restrict__ P, int64_t pstride,
+                                                  int k, int64_t T,
                                                   int G, float alpha,
                                                   const float* __restrict__ lse,
                                                   float* __restrict__ part,
@@ -74,11 +107,6 @@ __global__ __launch_bounds__(256) void sa_agg_f32(const int64_t* __restrict__ of
   const int s = blockIdx.x;
   const int p0 = blockIdx.y * PC;
 
-  for (int i = tid; i < PC * D; i += 256) {
-    const int r = i / D, c = i % D;
-    sP[r][c] = (p0 + r < k) ? P[(int64_t)(p0 + r) * D + c] : 0.f;
-  }
-
   const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
   TileWalker<TILE> cur;
   cur.start(offsets, B, lo, hi);
@@ -87,9 +115,18 @@ __global__ __launch_bounds__(256) void sa_agg_f32(const int64_t* __restrict__ of
 #pragma unroll
   for (int e = 0; e < DQ; ++e) acc[e] = 0.f;
   float ms = 0.f;
+  int table = -1;   // user whose table is in sP (any user's, with a shared P)
 
   while (cur.valid) {
     __syncthreads();
+    if (table < 0 || (pstride != 0 && cur.user != table)) {
+      table = cur.user;
+      const float* Pu = P + (int64_t)table * pstride;
+      for (int i = tid; i < PC * D; i += 256) {
+        const int r = i / D, c = i % D;
+        sP[r][c] = (p0 + r < k) ? Pu[(int64_t)(p0 + r) * D + c] : 0.f;
+      }
+    }
     for (int i = tid; i < TILE * D; i += 256) {
       const int r = i / D, c = i % D;
       sX[r][c] = (cur.t0 + r < cur.t1) ? X[(cur.t0 + r) * D + c] : 0.f;
@@ -139,7 +176,7 @@ static hipError_t launch_stats_f32_t(const FwdArgs& a, hipStream_t st, Prof* pro
   const unsigned nb = (unsigned)((a.T + 255) / 256);
   prof_begin(prof, "sa_stats_f32", st);
   hipLaunchKernelGGL(sa_stats_f32<D>, dim3(nb), dim3(256), 0, st, (const float*)a.X,
-                     (const float*)a.P, a.k, a.T, alpha, scale, a.lse);
+                     (const float*)a.P, a.k, a.T, alpha, scale, a.lse, a.offsets, a.B, a.pstride);
   const hipError_t e = hipGetLastError();
   prof_end(prof, st);
   return e;
@@ -154,8 +191,8 @@ static hipError_t launch_fwd_f32_t(const FwdArgs& a, hipStream_t st, Prof* prof)
     if (e != hipSuccess) return e;
     prof_begin(prof, "sa_agg_f32", st);
     hipLaunchKernelGGL(sa_agg_f32<D>, dim3(a.G, a.nchunks), dim3(256), 0, st, a.offsets, a.B,
-                       (const float*)a.X, (const float*)a.P, a.k, a.T, a.G, alpha, a.lse, a.part,
-                       a.pmass);
+                       (const float*)a.X, (const float*)a.P, a.pstride, a.k, a.T, a.G, alpha,
+                       a.lse, a.part, a.pmass);
     e = hipGetLastError();
     prof_end(prof, st);
     if (e != hipSuccess) return e;

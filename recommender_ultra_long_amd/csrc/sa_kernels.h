@@ -28,11 +28,13 @@ struct Plan {
   int64_t T;
   int dtype;            // 0 = fp32, 1 = bf16
   bool mass_norm;
+  bool per_user;        // P is [B, k, d] (one table per user), dP likewise
   // forward
   int chunk, nchunks, G;
   int64_t nslots;       // G + B - 1 partial slots
   // backward (dP pass)
   int bchunk, bnchunks, Gb;
+  int64_t bslots;       // dP partial slots: Gb, or Gb + B - 1 with per-user tables
   int kp;               // row stride of G and cv: k rounded up to the dX chunk (bf16), else k
   // forward workspace layout (byte offsets)
   size_t off_status, off_lse, off_lse2, off_part, off_pmass, fwd_bytes;
@@ -41,7 +43,8 @@ struct Plan {
 };
 
 // Fills the plan; returns false for an unsupported problem.
-bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, Plan* p);
+bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, bool per_user,
+               Plan* p);
 
 struct FwdArgs {
   const int64_t* offsets;
@@ -49,6 +52,7 @@ struct FwdArgs {
   int64_t T;
   const void* X;
   const void* P;
+  int64_t pstride;     // elements between users' tables: 0 (shared P) or k d
   float* lse;          // [T] (caller's buffer or workspace)
   float* lse2;         // [T + 1] log2-unit lse and +inf sentinel, or nullptr (bf16 stats only)
   float* S;            // [B, k, d]
@@ -66,6 +70,7 @@ struct BwdArgs {
   int64_t T;
   const void* X;
   const void* P;
+  int64_t pstride;     // elements between users' tables: 0 (shared P) or k d
   const float* dS;     // [B, k, d]
   const float* lse;    // [T] (caller's, or lse_ws after recomputation)
   float* lse_ws;       // [T]
@@ -73,16 +78,17 @@ struct BwdArgs {
   const float* S;      // [B, k, d] (mass norm only)
   const float* mass;   // [B, k]    (mass norm only)
   float* dX;           // [T, d]
-  float* dP;           // [k, d]
+  float* dP;           // [k, d], or [B, k, d] with per-user tables
   void* Gq;            // [B, kp, d] G = dS (or dS / mass) in the input dtype, rows >= k zero
   float* cv;           // [B, kp]   G[j] . S[j] (mass norm) or 0
   float* cvs;          // [B, kp]   -cv (bf16 dX pass)
-  void* Pq;            // [kp, d]   P with zero rows from k on (bf16 path)
+  void* Pq;            // [kp, d] (or [B, kp, d] per user): P with zero rows from k on (bf16)
   int kp;
   float* delta;        // [T]
-  float* dpp;          // [Gb, k, d] dP partial per segment
+  float* dpp;          // [bslots, k, d] dP partial per segment (per piece with per-user tables)
   uint32_t* status;
   int Gb, bnchunks;
+  int64_t bslots;
   int mass_norm;
   int recompute_lse;
 };
@@ -124,6 +130,11 @@ hipError_t launch_stats_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof);
+// out[u] = scale * sum of user u's piece partials (slot s + u of segment s of
+// G), in piece order; also checks the offsets.  Per-user dP.
+hipError_t launch_piece_sum(const int64_t* offsets, int B, int k, int d, int64_t T, int G,
+                            const float* parts, float scale, float* out, uint32_t* status,
+                            hipStream_t st, Prof* prof);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t st, Prof* prof);
 
 }  // namespace sa

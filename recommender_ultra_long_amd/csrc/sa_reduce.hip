@@ -18,7 +18,8 @@ namespace sa {
 __global__ __launch_bounds__(256) void sa_reduce_kernel(
     const int64_t* __restrict__ offsets, int B, int k, int d, int64_t T, int G,
     const float* __restrict__ part, const float* __restrict__ pmass, int use_mass,
-    float* __restrict__ S, float* __restrict__ mass, int mass_norm, uint32_t* __restrict__ status) {
+    float* __restrict__ S, float* __restrict__ mass, int mass_norm, float out_scale,
+    uint32_t* __restrict__ status) {
   __shared__ f32x4 red[4][64];
   __shared__ float redm[4][64];
   const int u = blockIdx.x;
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(256) void sa_reduce_kernel(
     const float inv = mu > 0.f ? 1.0f / mu : 0.f;
     acc = mu > 0.f ? acc * inv : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  if (out_scale != 1.0f) acc = acc * out_scale;
   *(f32x4*)(S + (int64_t)u * kd + e) = acc;
   if (mass != nullptr && (e % d) == 0) mass[(int64_t)u * k + j] = mu;
 }
@@ -80,7 +82,21 @@ hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof) {
   const int use_mass = (a.mass_norm || a.mass != nullptr) ? 1 : 0;
   prof_begin(prof, "sa_reduce", st);
   hipLaunchKernelGGL(sa_reduce_kernel, dim3(a.B, gy), dim3(256), 0, st, a.offsets, a.B, a.k, a.d,
-                     a.T, a.G, a.part, a.pmass, use_mass, a.S, a.mass, a.mass_norm, a.status);
+                     a.T, a.G, a.part, a.pmass, use_mass, a.S, a.mass, a.mass_norm, 1.0f,
+                     a.status);
+  const hipError_t e = hipGetLastError();
+  prof_end(prof, st);
+  return e;
+}
+
+hipError_t launch_piece_sum(const int64_t* offsets, int B, int k, int d, int64_t T, int G,
+                            const float* parts, float scale, float* out, uint32_t* status,
+                            hipStream_t st, Prof* prof) {
+  const int64_t kd = (int64_t)k * d;
+  const unsigned gy = (unsigned)((kd + 255) / 256);
+  prof_begin(prof, "sa_reduce", st);
+  hipLaunchKernelGGL(sa_reduce_kernel, dim3(B, gy), dim3(256), 0, st, offsets, B, k, d, T, G,
+                     parts, (const float*)nullptr, 0, out, (float*)nullptr, 0, scale, status);
   const hipError_t e = hipGetLastError();
   prof_end(prof, st);
   return e;

@@ -32,6 +32,7 @@ SA_ERR_HIP = 8
 SA_F32 = 0
 SA_BF16 = 1
 SA_FLAG_MASS_NORM = 1
+SA_FLAG_PER_USER_PROTOTYPES = 2
 SA_OP_FORWARD = 0
 SA_OP_BACKWARD = 1
 
@@ -115,11 +116,20 @@ def status_string(status):
     return load().sa_status_string(int(status)).decode()
 
 
-def make_problem(batch, k, d, total_tokens, dtype, mass_norm=False):
+def make_problem(batch, k, d, total_tokens, dtype, mass_norm=False, per_user=False):
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}.get(dtype, 99)
-    return SaProblem(int(batch), int(k), int(d), int(total_tokens), int(dtype),
-                     SA_FLAG_MASS_NORM if mass_norm else 0)
+    flags = (SA_FLAG_MASS_NORM if mass_norm else 0) | (SA_FLAG_PER_USER_PROTOTYPES if per_user else 0)
+    return SaProblem(int(batch), int(k), int(d), int(total_tokens), int(dtype), flags)
+
+
+def _tables(P, B):
+    """(k, per_user) for a shared [k, d] table or a [B, k, d] stack."""
+    if P.dim() == 2:
+        return P.shape[0], False
+    if P.dim() == 3 and P.shape[0] == B:
+        return P.shape[1], True
+    raise ValueError(f"P must be [k, d] or [{B}, k, d], got {tuple(P.shape)}")
 
 
 def validate(problem, offsets_host=None):
@@ -182,16 +192,16 @@ class KernelTimer:
 def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, workspace=None,
                stream=None, want_lse=True, want_mass=True, timer=None):
     """Calls sa_forward.  offsets: int64 [B+1] (device tensor, or host array
-    copied to X's device); X [T, d] and P [k, d] float32 or bfloat16 on the
-    GPU.  Returns (S [B, k, d] f32, lse [T] f32 or None, mass [B, k] f32 or
-    None)."""
+    copied to X's device); X [T, d] and P float32 or bfloat16 on the GPU, P
+    either [k, d] (shared) or [B, k, d] (one table per user).  Returns
+    (S [B, k, d] f32, lse [T] f32 or None, mass [B, k] f32 or None)."""
     lib = load()
     dev = P.device
     off = _device_offsets(offsets, dev)
     B = off.numel() - 1
     T, d = X.shape
-    k = P.shape[0]
-    pr = make_problem(B, k, d, T, X.dtype, mass_norm)
+    k, per_user = _tables(P, B)
+    pr = make_problem(B, k, d, T, X.dtype, mass_norm, per_user)
     if S is None:
         S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
     if lse is None and want_lse:
@@ -213,18 +223,19 @@ def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, work
 
 def sa_backward(offsets, X, P, dS, lse=None, S=None, mass=None, mass_norm=False, dX=None,
                 dP=None, workspace=None, stream=None, timer=None):
-    """Calls sa_backward.  Returns (dX [T, d] f32, dP [k, d] f32)."""
+    """Calls sa_backward.  Returns (dX [T, d] f32, dP f32 shaped like P:
+    [k, d] summed over users, or [B, k, d] per user)."""
     lib = load()
     dev = P.device
     off = _device_offsets(offsets, dev)
     B = off.numel() - 1
     T, d = X.shape
-    k = P.shape[0]
-    pr = make_problem(B, k, d, T, X.dtype, mass_norm)
+    k, per_user = _tables(P, B)
+    pr = make_problem(B, k, d, T, X.dtype, mass_norm, per_user)
     if dX is None:
         dX = torch.empty((T, d), dtype=torch.float32, device=dev)
     if dP is None:
-        dP = torch.empty((k, d), dtype=torch.float32, device=dev)
+        dP = torch.empty(tuple(P.shape), dtype=torch.float32, device=dev)
     ws_bytes = workspace_size(pr, SA_OP_BACKWARD)
     ws = _workspace(ws_bytes, dev, workspace)
     args = (ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(dS), _ptr(lse), _ptr(S),

@@ -136,7 +136,7 @@ class Problem:
     workload: Workload
     offsets: np.ndarray          # int64 [B+1], host
     X: torch.Tensor              # [T, d] f32 or bf16
-    P: torch.Tensor              # [k, d] same dtype as X
+    P: torch.Tensor              # [k, d] (or [B, k, d] per user), same dtype as X
     dS: torch.Tensor | None      # [B, k, d] f32
     mass_norm: bool
 
@@ -147,11 +147,12 @@ class Problem:
 
 def make_inputs(lengths, k, d, dtype="bf16", device="cpu", seed=0, wid=0,
                 x_kind="normal", p_std=None, with_dS=False, mass_norm=False,
-                workload=None) -> Problem:
+                workload=None, per_user_p=False) -> Problem:
     """Build a Problem for arbitrary lengths.
 
     p_std defaults to d**-0.5 (P ~ N(0, 1/d)); a larger value gives sharper
     logits (the standard deviation of each affinity is p_std when X ~ N(0, 1)).
+    per_user_p draws one k x d table per user (P is then [B, k, d]).
     """
     lengths = np.asarray(lengths, dtype=np.int64)
     off = offsets_from_lengths(lengths)
@@ -177,7 +178,8 @@ def make_inputs(lengths, k, d, dtype="bf16", device="cpu", seed=0, wid=0,
     else:
         raise ValueError(x_kind)
     gp = _gen(device, _seed_for(seed, wid, "P"))
-    P = (torch.randn((k, d), generator=gp, device=device, dtype=torch.float32) * p_std).to(tdt)
+    pshape = (int(lengths.size), k, d) if per_user_p else (k, d)
+    P = (torch.randn(pshape, generator=gp, device=device, dtype=torch.float32) * p_std).to(tdt)
     dS = None
     if with_dS:
         gd = _gen(device, _seed_for(seed, wid, "dS"))

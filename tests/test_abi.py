@@ -57,7 +57,9 @@ def test_validate_shapes_and_dtypes():
     assert sa.validate(_p(total_tokens=1 << 36)) == sa.SA_ERR_BAD_SHAPE
     assert sa.validate(_p(dtype=7)) == sa.SA_ERR_BAD_DTYPE
     pr = _p()
-    pr.flags = 2
+    pr.flags = sa.SA_FLAG_MASS_NORM | sa.SA_FLAG_PER_USER_PROTOTYPES
+    assert sa.validate(pr) == sa.SA_OK
+    pr.flags = 4
     assert sa.validate(pr) == sa.SA_ERR_UNSUPPORTED
 
 
@@ -73,6 +75,12 @@ def test_workspace_size():
     f = sa.workspace_size(_p(), sa.SA_OP_FORWARD)
     b = sa.workspace_size(_p(), sa.SA_OP_BACKWARD)
     assert f > 0 and b > 0 and f % 256 == 0 and b % 256 == 0
+    # per-user tables: the forward needs nothing more; the backward holds a
+    # padded copy of every user's table and a dP partial per piece
+    pu = _p()
+    pu.flags = sa.SA_FLAG_PER_USER_PROTOTYPES
+    assert sa.workspace_size(pu, sa.SA_OP_FORWARD) == f
+    assert sa.workspace_size(pu, sa.SA_OP_BACKWARD) > b
     assert sa.workspace_size(_p(k=0), sa.SA_OP_FORWARD) == 0
     assert sa.workspace_size(_p(), 5) == 0
     # grows with the token count (the per-token lse and backward buffers)
