@@ -203,7 +203,9 @@ sa_status sa_backward_profiled(const sa_problem* problem, const int64_t* offsets
  * so sa_forward(X, P_eff) computes the sketch of Eq. (6)-(9) with the
  * projections; the aggregation still sums the unprojected X (Eq. (9)).
  *
- *  k, d    : 1 <= k <= 2048; d in {32, 64, 128}.
+ *  k, d    : rows of P and P_eff, 1 <= k <= 2^24: a shared table's k, or
+ *            B k for the stacked per-user tables of SA_FLAG_PER_USER_PROTOTYPES
+ *            (one W_Q, W_K for all users); d in {32, 64, 128}.
  *  dtype   : dtype of P and P_eff (SA_BF16: P_eff is rounded to bf16 once,
  *            from fp32 accumulation; SA_F32: fp32 throughout).
  *  P       : [k, d] (dtype) device.

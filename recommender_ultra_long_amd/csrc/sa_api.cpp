@@ -250,14 +250,18 @@ sa_status sa_backward_profiled(const sa_problem* pr, const int64_t* offsets_dev,
   return v;
 }
 
+static bool fold_shape_ok(int rows, int d) {
+  return rows >= 1 && rows <= (1 << 24) && (d == 32 || d == 64 || d == 128);
+}
+
 static sa_status fold_check(int k, int d, sa_dtype dtype) {
   if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_BAD_DTYPE;
-  if (k < 1 || k > 2048 || !(d == 32 || d == 64 || d == 128)) return SA_ERR_BAD_SHAPE;
+  if (!fold_shape_ok(k, d)) return SA_ERR_BAD_SHAPE;
   return SA_OK;
 }
 
 size_t sa_fold_workspace_size(int k, int d) {
-  if (k < 1 || k > 2048 || !(d == 32 || d == 64 || d == 128)) return 0;
+  if (!fold_shape_ok(k, d)) return 0;
   return fold_workspace_bytes(k, d);
 }
 

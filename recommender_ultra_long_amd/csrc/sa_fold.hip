@@ -7,7 +7,8 @@
 // (dW_Q = dM W_K and dW_K = dM^T W_Q for M = W_Q W_K^T and dM = P^T G,
 // regrouped so that every product is k x d x d).
 //
-// The products are small (at most 2048 x 128 x 128, fp32 on the vector ALU):
+// The products are small (k x 128 x 128 with k in the thousands for a shared
+// table; fp32 on the vector ALU):
 // their cost is load latency and LDS reads, not arithmetic.  So every weight
 // matrix is brought into LDS with one batch of loads (the second one
 // prefetched into registers while the first product runs), and the row
@@ -16,9 +17,11 @@
 //
 // Row kernels (grid = ceil(k / rows per tile)): each row of Q, dQ, P_eff and
 // dP depends only on the same row of P and G.  The d x d gradients sum over all k rows:
-// the gram kernel splits the rows into 128-row slices, one workgroup per
-// (32 x 32 output tile, gradient, slice), and sa_fold_sum adds the slices in
-// slice order, so results do not depend on scheduling.
+// the gram kernel splits the rows into at most 256 slices (whole 128-row
+// sub-chunks), one workgroup per (32 x 32 output tile, gradient, slice), and
+// sa_fold_sum adds the slices in slice order, so results do not depend on
+// scheduling.  The rows can be one shared table (k) or the stacked tables of
+// all users (B k rows, one W_Q and W_K for all).
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -29,7 +32,8 @@ namespace sa {
 // small k still spreads over many compute units.
 template <int D>
 constexpr int fold_rows() { return 256 / D > 4 ? 256 / D : 4; }
-constexpr int kGramRows = 128;     // rows per gram slice
+constexpr int kGramRows = 128;     // rows per gram sub-chunk (a slice is a whole number of them)
+constexpr int kMaxSlices = 256;    // at most this many slices (partial sums) per gradient
 constexpr int kGramTile = 32;      // gram output tile edge
 
 template <int D>
@@ -187,51 +191,55 @@ __global__ __launch_bounds__(256) void sa_fold_bwd_rows(const PT* __restrict__ P
   }
 }
 
-// grid = ((D / 32)^2, 2, ceil(k / kGramRows)); block 256.  blockIdx.y = 0:
-// slice part of dW_Q = P^T dQ; 1: of dW_K = G^T Q.  The 32 x 32 output tile
-// (a0, b0) sums the slice's rows; parts[(z * 2 + y) * D * D + a * D + b].
+// grid = ((D / 32)^2, 2, slices); block 256.  blockIdx.y = 0: slice part of
+// dW_Q = P^T dQ; 1: of dW_K = G^T Q.  Slice z is rows [z span, (z+1) span),
+// taken in 128-row sub-chunks in order; the 32 x 32 output tile (a0, b0) sums
+// them into parts[(z * 2 + y) * D * D + a * D + b].
 template <typename PT, int D>
 __global__ __launch_bounds__(256) void sa_fold_gram(const PT* __restrict__ P,
                                                     const float* __restrict__ G,
                                                     const float* __restrict__ Qw,
                                                     const float* __restrict__ dQw,
-                                                    float* __restrict__ parts, int k) {
+                                                    float* __restrict__ parts, int k, int span) {
   constexpr int T = kGramTile, TPR = D / T;
   __shared__ __align__(16) float sL[kGramRows][T + 4];
   __shared__ float sR[kGramRows][T + 1];
   const int a0 = (blockIdx.x / TPR) * T, b0 = (blockIdx.x % TPR) * T;
   const int which = blockIdx.y, z = blockIdx.z;
-  const int row0 = z * kGramRows;
   const float* R = which == 0 ? dQw : Qw;
   constexpr int PER = kGramRows * T / 256;
-  float lv[PER], rv[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = threadIdx.x + 256 * j, r = e / T, c = e % T;
-    const bool in = row0 + r < k;
-    const int64_t g = (int64_t)(row0 + r) * D;
-    lv[j] = in ? (which == 0 ? (float)P[g + a0 + c] : G[g + a0 + c]) : 0.f;
-    rv[j] = in ? R[g + b0 + c] : 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = threadIdx.x + 256 * j, r = e / T, c = e % T;
-    sL[r][c] = lv[j];
-    sR[r][c] = rv[j];
-  }
-  __syncthreads();
   // thread t: output column b = t % T, rows a = 4 (t / T) .. + 3
   const int b = threadIdx.x % T, a = 4 * (threadIdx.x / T);
   static_assert(T * T / 256 == 4, "four outputs per thread");
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int end = (z + 1) * span < k ? (z + 1) * span : k;
+  for (int row0 = z * span; row0 < end; row0 += kGramRows) {
+    float lv[PER], rv[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = threadIdx.x + 256 * j, r = e / T, c = e % T;
+      const bool in = row0 + r < end;
+      const int64_t g = (int64_t)(row0 + r) * D;
+      lv[j] = in ? (which == 0 ? (float)P[g + a0 + c] : G[g + a0 + c]) : 0.f;
+      rv[j] = in ? R[g + b0 + c] : 0.f;
+    }
+    __syncthreads();   // the previous sub-chunk's LDS reads are done
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = threadIdx.x + 256 * j, r = e / T, c = e % T;
+      sL[r][c] = lv[j];
+      sR[r][c] = rv[j];
+    }
+    __syncthreads();
 #pragma unroll 8
-  for (int r = 0; r < kGramRows; ++r) {
-    const float x = sR[r][b];
-    const float4 l = *reinterpret_cast<const float4*>(&sL[r][a]);
-    acc[0] = fmaf(l.x, x, acc[0]);
-    acc[1] = fmaf(l.y, x, acc[1]);
-    acc[2] = fmaf(l.z, x, acc[2]);
-    acc[3] = fmaf(l.w, x, acc[3]);
+    for (int r = 0; r < kGramRows; ++r) {
+      const float x = sR[r][b];
+      const float4 l = *reinterpret_cast<const float4*>(&sL[r][a]);
+      acc[0] = fmaf(l.x, x, acc[0]);
+      acc[1] = fmaf(l.y, x, acc[1]);
+      acc[2] = fmaf(l.z, x, acc[2]);
+      acc[3] = fmaf(l.w, x, acc[3]);
+    }
   }
   float* part = parts + (int64_t)(2 * z + which) * D * D;
 #pragma unroll
@@ -255,7 +263,14 @@ template <int D>
 static unsigned fold_row_blocks(int k) {
   return (unsigned)((k + fold_rows<D>() - 1) / fold_rows<D>());
 }
-static int fold_slices(int k) { return (k + kGramRows - 1) / kGramRows; }
+// Rows per gram slice (a multiple of kGramRows, so that at most kMaxSlices
+// slices cover k rows) and the number of slices.
+static int fold_span(int k) {
+  const int chunks = (k + kGramRows - 1) / kGramRows;
+  const int ns = chunks < kMaxSlices ? chunks : kMaxSlices;
+  return (chunks + ns - 1) / ns * kGramRows;
+}
+static int fold_slices(int k) { return (k + fold_span(k) - 1) / fold_span(k); }
 
 template <typename PT, int D>
 static hipError_t fold_t(int k, const void* P, const float* Wq, const float* Wk, void* Peff,
@@ -279,7 +294,7 @@ static hipError_t fold_backward_t(int k, const void* P, const float* Wq, const f
   const int ns = fold_slices(k);
   constexpr int tiles = (D / kGramTile) * (D / kGramTile);
   hipLaunchKernelGGL((sa_fold_gram<PT, D>), dim3(tiles, 2, (unsigned)ns), dim3(256), 0, st,
-                     (const PT*)P, G, Qw, dQw, parts, k);
+                     (const PT*)P, G, Qw, dQw, parts, k, fold_span(k));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sa_fold_sum, dim3((unsigned)((2 * D * D + 255) / 256)), dim3(256), 0, st,

@@ -155,7 +155,11 @@ def test_fold_argument_errors_are_synchronous():
     assert lib.sa_fold_workspace_size(129, 32) == (2 * 129 * 32 + 2 * 2 * 32 * 32) * 4
     assert lib.sa_fold_workspace_size(0, 128) == 0
     assert lib.sa_fold_workspace_size(1024, 96) == 0
-    assert lib.sa_fold_workspace_size(4096, 64) == 0
+    # stacked per-user tables: up to 2^24 rows, at most 256 slices
+    assert lib.sa_fold_workspace_size(4096, 64) == (2 * 4096 * 64 + 2 * 32 * 64 * 64) * 4
+    assert lib.sa_fold_workspace_size(256 * 1024, 128) == (2 * 262144 * 128 + 2 * 256 * 128 * 128) * 4
+    assert lib.sa_fold_workspace_size(40000, 128) == (2 * 40000 * 128 + 2 * 157 * 128 * 128) * 4
+    assert lib.sa_fold_workspace_size((1 << 24) + 1, 32) == 0
     nul = vp(None)
     # shape and dtype errors come first, with null pointers (no HIP call)
     assert lib.sa_fold_prototypes(0, 128, sa.SA_BF16, nul, nul, nul, nul, nul) == sa.SA_ERR_BAD_SHAPE

@@ -10,7 +10,7 @@ import torch
 from oracle.projections import fold_prototypes_backward_ref, fold_prototypes_ref
 from oracle.sa_ref import sa_backward_ref, sa_forward_ref
 from recommender_ultra_long_amd import sa
-from sa_testutil import TOL_BF16, rel_err, say
+from sa_testutil import TOL_BF16, TOL_F32, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,24 @@ def test_fold_backward_parity(dtype, k, d):
     for name, a, b in (("dP", dP, rP), ("dWq", dWq, rWq), ("dWk", dWk, rWk)):
         e = rel_err(a.cpu().numpy(), b)
         assert e <= TOL_FOLD_F32, f"{name} rel err {e:.3e}"
+
+
+@pytest.mark.parametrize("rows", [32 * 1024, 40000])
+def test_fold_of_stacked_user_tables(rows):
+    # the refinement layers fold every user's table with one W_Q, W_K: B k rows
+    # in one call (the gram slices then span several 128-row sub-chunks)
+    say(f"case fold stacked rows={rows} d=128")
+    P, Wq, Wk = _inputs(rows, rows, 128, torch.bfloat16)
+    G = torch.randn(rows, 128, generator=torch.Generator().manual_seed(rows + 1))
+    Peff = sa.fold_prototypes(P.cuda(), Wq.cuda(), Wk.cuda())
+    dP, dWq, dWk = sa.fold_prototypes_backward(P.cuda(), Wq.cuda(), Wk.cuda(), G.cuda())
+    torch.cuda.synchronize()
+    P64 = P.float().numpy()
+    assert rel_err(Peff.float().cpu().numpy(), fold_prototypes_ref(P64, Wq.numpy(), Wk.numpy())) <= TOL_FOLD_BF16
+    rP, rWq, rWk = fold_prototypes_backward_ref(P64, Wq.numpy(), Wk.numpy(), G.numpy())
+    for name, a, b in (("dP", dP, rP), ("dWq", dWq, rWq), ("dWk", dWk, rWk)):
+        e = rel_err(a.cpu().numpy(), b)
+        assert e <= TOL_F32, f"{name} rel err {e:.3e}"
 
 
 def test_fold_backward_is_deterministic():
