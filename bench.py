@@ -13,7 +13,7 @@ on the launch stream by the library's profiled entry points), the forward
 alone against the bf16 matrix-core peak, and the float64 CPU oracle timed on
 a bounded sample of the same input.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-per-user]
 """
 
 import argparse
@@ -40,6 +40,10 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-user", action="store_true",
+                    help="skip the shared-vs-per-user table timing on the 32-user batch "
+                         "(profiling runs skip it so that kernel statistics cover the step "
+                         "workload only)")
     ap.add_argument("--profile-reps", type=int, default=None,
                     help="calls timed per kernel (default: --steps)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -188,6 +192,46 @@ def _cpu_baseline(prob, budget_s=15.0):
             "sample": f"first {n} tokens of the {T}-token user, sa_forward_ref + sa_backward_ref "
                       f"(float64 numpy), {t:.1f} s on {os.cpu_count()} host CPUs",
             "seconds": t, "tokens": n}
+
+
+def _per_user_timing(sa, synth, timed, dev):
+    """Forward + backward on the 32-user ragged batch (lengths uniform in
+    [10,000, 100,000], k = 1024, d = 128, bf16) with one shared table and with
+    one table per user (the refinement layers' form): the cost of per-user
+    tables.  Not part of the step."""
+    import torch
+    prob = synth.make_workload("backward32_k1024", device=dev, with_dS=True)
+    B = len(prob.offsets) - 1
+    k, d = prob.workload.k, prob.workload.d
+    T = prob.total_tokens
+    off = torch.as_tensor(prob.offsets, device=dev)
+    g = torch.Generator(device=dev).manual_seed(7)
+    Pu = (torch.randn((B, k, d), generator=g, device=dev) / d ** 0.5).to(prob.X.dtype)
+    res = {"workload": f"{B} users, lengths uniform[10000, 100000], k={k}, d={d}, bf16",
+           "tokens": T}
+    for name, P in (("shared", prob.P), ("per_user", Pu)):
+        per_user = P.dim() == 3
+        pr = sa.make_problem(B, k, d, T, prob.X.dtype, False, per_user)
+        wsf = torch.empty(sa.workspace_size(pr, sa.SA_OP_FORWARD), dtype=torch.uint8, device=dev)
+        wsb = torch.empty(sa.workspace_size(pr, sa.SA_OP_BACKWARD), dtype=torch.uint8, device=dev)
+        S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((T,), dtype=torch.float32, device=dev)
+        dX = torch.empty((T, d), dtype=torch.float32, device=dev)
+        dP = torch.empty(tuple(P.shape), dtype=torch.float32, device=dev)
+
+        def step(P=P, wsf=wsf, wsb=wsb, S=S, lse=lse, dX=dX, dP=dP):
+            sa.sa_forward(off, prob.X, P, False, S=S, lse=lse, mass=None, workspace=wsf,
+                          want_mass=False)
+            sa.sa_backward(off, prob.X, P, prob.dS, lse, dX=dX, dP=dP, workspace=wsb)
+
+        step()
+        ms = timed(step, 3)
+        res[name + "_ms"] = round(ms, 3)
+        res[name + "_tokens_per_s"] = round(T / (ms * 1e-3), 1)
+    res["per_user_over_shared"] = round(res["per_user_ms"] / res["shared_ms"], 4)
+    del prob, Pu
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -349,6 +393,8 @@ def main():
         "fold_us": round(ms_fold * 1e3, 2), "fold_backward_us": round(ms_fold_bwd * 1e3, 2),
         "fold_gflops": round(fold_flop / (ms_fold * 1e-3) / 1e9, 1),
         "fold_backward_gflops": round(fold_bwd_flop / (ms_fold_bwd * 1e-3) / 1e9, 1)}
+    if not args.no_per_user:
+        out["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
