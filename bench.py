@@ -41,9 +41,9 @@ def _parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-user", action="store_true",
-                    help="skip the shared-vs-per-user table timing on the 32-user batch "
-                         "(profiling runs skip it so that kernel statistics cover the step "
-                         "workload only)")
+                    help="skip the timings on the 32-user batch (shared vs per-user tables, "
+                         "the stacked block); profiling runs skip them so that kernel "
+                         "statistics cover the step workload only")
     ap.add_argument("--profile-reps", type=int, default=None,
                     help="calls timed per kernel (default: --steps)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -234,6 +234,51 @@ def _per_user_timing(sa, synth, timed, dev):
     return res
 
 
+def _block_timing(sa, synth, timed, dev, n_layers=2):
+    """The stacked block (N_sa = 2 refinement layers, Eq. 12-16), forward and
+    backward, on the 32-user ragged batch (lengths uniform in [10,000,
+    100,000], k = 1024, d = 128, bf16 history): the pages' configuration of
+    the user-side sketch.  Not part of the step."""
+    import torch
+    prob = synth.make_workload("backward32_k1024", device=dev, with_dS=False)
+    B = len(prob.offsets) - 1
+    k, d = prob.workload.k, prob.workload.d
+    T = prob.total_tokens
+    off = torch.as_tensor(prob.offsets, device=dev)
+    g = torch.Generator(device=dev).manual_seed(11)
+    rn = lambda *shape, s=1.0: torch.randn(shape, generator=g, device=dev) * s
+    P0 = rn(k, d, s=d ** -0.5)
+    layers = [dict(Wq=rn(d, d, s=d ** -0.5), Wk=rn(d, d, s=d ** -0.5), ln1_g=1 + rn(d, s=0.1),
+                   ln1_b=rn(d, s=0.1), W1=rn(d, 2 * d, s=d ** -0.5), W3=rn(d, 2 * d, s=d ** -0.5),
+                   W2=rn(2 * d, d, s=(2 * d) ** -0.5), ln2_g=1 + rn(d, s=0.1), ln2_b=rn(d, s=0.1))
+              for _ in range(n_layers)]
+    dout = rn(B, k, d)
+    out = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+    ws = sa.block_workspace(B + 1, k, d, T, prob.X.dtype, n_layers, dev)
+    dX = torch.empty((T, d), dtype=torch.float32, device=dev)
+    dP0 = torch.empty((k, d), dtype=torch.float32, device=dev)
+    grads = [{n: torch.empty_like(v) for n, v in L.items()} for L in layers]
+
+    def fwd():
+        sa.block_forward(off, prob.X, P0, layers, out=out, workspace=ws)
+
+    def step():
+        fwd()
+        sa.block_backward(off, prob.X, P0, layers, dout, ws, dX=dX, dP0=dP0, grads=grads)
+
+    step()
+    ms_f = timed(fwd, 3)
+    ms = timed(step, 3)
+    res = {"workload": f"{B} users, lengths uniform[10000, 100000], k={k}, d={d}, bf16, "
+                       f"{n_layers} layers",
+           "tokens": T, "forward_ms": round(ms_f, 3), "forward_backward_ms": round(ms, 3),
+           "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "workspace_GB": round(ws.numel() / 1e9, 3)}
+    del prob, ws, dX
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = _parse()
     if args.parse_traffic:
@@ -395,6 +440,7 @@ def main():
         "fold_backward_gflops": round(fold_bwd_flop / (ms_fold_bwd * 1e-3) / 1e9, 1)}
     if not args.no_per_user:
         out["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
+        out["block"] = _block_timing(sa, synth, timed, dev)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

@@ -237,6 +237,80 @@ sa_status sa_fold_prototypes_backward(int k, int d, sa_dtype dtype, const void* 
                                       float* dP, float* dWq, float* dWk, void* ws,
                                       size_t ws_bytes, void* stream);
 
+/*
+ * The stacked Sketch Attention block (SequenceO1 reading notes, section 3.3,
+ * Eq. (12)-(16)): starting from the shared table, X~(0) = P0, each of the
+ * n_layers layers computes, per user,
+ *     X^     = SA(X, X~ W_Q W_K^T)            Eq. (12)-(14), plain-sum sketch
+ *     X-     = LN1(X~ + X^)                    Eq. (15)
+ *     X~'    = LN2(X- + FFN(X-))               Eq. (16)
+ * with FFN(x) = (silu(x W1) * (x W3)) W2, the SwiGLU FFN of hidden width 2d
+ * (W1, W3: [d, 2d], W2: [2d, d], no biases), and LN(v) = (v - mean) /
+ * sqrt(var + 1e-5) * g + b over the d features of a row (biased variance).
+ * Layer 0's queries are the shared table; later layers' queries are each
+ * user's own rows (SA_FLAG_PER_USER_PROTOTYPES inside).  The output is X~ of
+ * the last layer, float [B, k, d].
+ *
+ * All parameters are float32 device arrays, row-major.  The sketch products
+ * run in the problem's dtype (X and the folded tables in bf16 with fp32
+ * accumulation for SA_BF16); everything else is fp32.
+ *
+ *  problem  : as for sa_forward; flags must be 0 (the block's sketch is the
+ *             plain sum of Eq. (14), and it manages per-user tables itself).
+ *  n_layers : 1 .. 8 (the pages use 2).
+ *  X        : [T, d] (dtype); P0: float [k, d]; out: float [B, k, d].
+ *  layers   : host array of n_layers parameter sets (device pointers).
+ *  ws       : device workspace of sa_block_workspace_size(problem, n_layers)
+ *             bytes.  sa_block_forward leaves in it the activations that
+ *             sa_block_backward reads: a backward must use the workspace of
+ *             the forward on the same inputs, untouched in between.
+ * Errors as for sa_forward (SA_ERR_UNSUPPORTED for flags or n_layers out of
+ * range).
+ */
+typedef struct {
+  const float* Wq;      /* [d, d]   */
+  const float* Wk;      /* [d, d]   */
+  const float* ln1_g;   /* [d]      */
+  const float* ln1_b;   /* [d]      */
+  const float* W1;      /* [d, 2d]  */
+  const float* W3;      /* [d, 2d]  */
+  const float* W2;      /* [2d, d]  */
+  const float* ln2_g;   /* [d]      */
+  const float* ln2_b;   /* [d]      */
+} sa_block_layer;
+
+/* Gradients of one layer's parameters (device pointers, same shapes as
+ * sa_block_layer; all overwritten). */
+typedef struct {
+  float* Wq;
+  float* Wk;
+  float* ln1_g;
+  float* ln1_b;
+  float* W1;
+  float* W3;
+  float* W2;
+  float* ln2_g;
+  float* ln2_b;
+} sa_block_layer_grad;
+
+size_t sa_block_workspace_size(const sa_problem* problem, int n_layers);
+sa_status sa_block_forward(const sa_problem* problem, int n_layers, const int64_t* offsets_dev,
+                           const void* X, const float* P0, const sa_block_layer* layers,
+                           float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the block: given dout = dL/dout (float [B, k, d]), writes
+ * dX = dL/dX (float [T, d]), dP0 = dL/dP0 (float [k, d]) and every layer's
+ * parameter gradients (all overwritten).  Weight and layer-norm gradients
+ * sum over all users' rows in a fixed order (deterministic).  `ws` must hold
+ * the state left by sa_block_forward for the same problem, X, P0 and layers.
+ */
+sa_status sa_block_backward(const sa_problem* problem, int n_layers, const int64_t* offsets_dev,
+                            const void* X, const float* P0, const sa_block_layer* layers,
+                            const float* dout, float* dX, float* dP0,
+                            const sa_block_layer_grad* grads, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* Waits for `stream`, then reports whether a kernel of the last call that
  * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS) or not
  * (SA_OK).  SA_ERR_HIP if the wait or the read fails. */

@@ -63,6 +63,51 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, bool p
   return true;
 }
 
+FwdArgs fwd_args(const Plan& p, char* w, const int64_t* offsets, const void* X, const void* P,
+                 int64_t pstride, float* S, float* lse, float* mass) {
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.offsets = offsets;
+  a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
+  a.X = X; a.P = P; a.pstride = pstride;
+  a.lse = lse ? lse : (float*)(w + p.off_lse);
+  a.lse2 = (float*)(w + p.off_lse2);
+  a.S = S; a.mass = mass;
+  a.part = (float*)(w + p.off_part);
+  a.pmass = (float*)(w + p.off_pmass);
+  a.status = (uint32_t*)(w + p.off_status);
+  a.G = p.G; a.nchunks = p.nchunks;
+  a.mass_norm = p.mass_norm ? 1 : 0;
+  return a;
+}
+
+BwdArgs bwd_args(const Plan& p, char* w, const int64_t* offsets, const void* X, const void* P,
+                 int64_t pstride, const float* dS, const float* lse, const float* S,
+                 const float* mass, float* dX, float* dP) {
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.offsets = offsets;
+  a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
+  a.X = X; a.P = P; a.pstride = pstride; a.dS = dS;
+  a.lse_ws = (float*)(w + p.off_blse);
+  a.lse2 = (float*)(w + p.off_blse2);
+  a.recompute_lse = lse == nullptr ? 1 : 0;
+  a.lse = lse ? lse : a.lse_ws;
+  a.S = S; a.mass = mass;
+  a.dX = dX; a.dP = dP; a.acc_dx = 0;
+  a.Gq = (void*)(w + p.off_G);
+  a.cv = (float*)(w + p.off_cv);
+  a.cvs = (float*)(w + p.off_cvs);
+  a.Pq = (void*)(w + p.off_Pq);
+  a.kp = p.kp;
+  a.delta = (float*)(w + p.off_delta);
+  a.dpp = (float*)(w + p.off_dpp);
+  a.status = (uint32_t*)(w + p.off_status);
+  a.Gb = p.Gb; a.bnchunks = p.bnchunks; a.bslots = p.bslots;
+  a.mass_norm = p.mass_norm ? 1 : 0;
+  return a;
+}
+
 }  // namespace sa
 
 using namespace sa;
@@ -134,20 +179,8 @@ static sa_status forward_impl(const sa_problem* pr, const int64_t* offsets_dev, 
     return SA_ERR_BAD_SHAPE;
   if (ws_bytes < p.fwd_bytes) return SA_ERR_WORKSPACE_TOO_SMALL;
 
-  char* w = (char*)ws;
-  FwdArgs a;
-  a.offsets = offsets_dev;
-  a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
-  a.X = X; a.P = P;
-  a.pstride = pu ? (int64_t)p.k * p.d : 0;
-  a.lse = lse ? lse : (float*)(w + p.off_lse);
-  a.lse2 = (float*)(w + p.off_lse2);
-  a.S = S; a.mass = mass;
-  a.part = (float*)(w + p.off_part);
-  a.pmass = (float*)(w + p.off_pmass);
-  a.status = (uint32_t*)(w + p.off_status);
-  a.G = p.G; a.nchunks = p.nchunks;
-  a.mass_norm = mn ? 1 : 0;
+  const FwdArgs a = fwd_args(p, (char*)ws, offsets_dev, X, P, pu ? (int64_t)p.k * p.d : 0, S,
+                             lse, mass);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = pr->dtype == SA_BF16 ? launch_fwd_bf16(a, st, prof) : launch_fwd_f32(a, st, prof);
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
@@ -175,28 +208,8 @@ static sa_status backward_impl(const sa_problem* pr, const int64_t* offsets_dev,
     return SA_ERR_BAD_SHAPE;
   if (ws_bytes < p.bwd_bytes) return SA_ERR_WORKSPACE_TOO_SMALL;
 
-  char* w = (char*)ws;
-  BwdArgs a;
-  a.offsets = offsets_dev;
-  a.B = p.B; a.k = p.k; a.d = p.d; a.T = p.T;
-  a.X = X; a.P = P; a.dS = dS;
-  a.pstride = pu ? (int64_t)p.k * p.d : 0;
-  a.lse_ws = (float*)(w + p.off_blse);
-  a.lse2 = (float*)(w + p.off_blse2);
-  a.recompute_lse = lse == nullptr ? 1 : 0;
-  a.lse = lse ? lse : a.lse_ws;
-  a.S = S; a.mass = mass;
-  a.dX = dX; a.dP = dP;
-  a.Gq = (void*)(w + p.off_G);
-  a.cv = (float*)(w + p.off_cv);
-  a.cvs = (float*)(w + p.off_cvs);
-  a.Pq = (void*)(w + p.off_Pq);
-  a.kp = p.kp;
-  a.delta = (float*)(w + p.off_delta);
-  a.dpp = (float*)(w + p.off_dpp);
-  a.status = (uint32_t*)(w + p.off_status);
-  a.Gb = p.Gb; a.bnchunks = p.bnchunks; a.bslots = p.bslots;
-  a.mass_norm = mn ? 1 : 0;
+  const BwdArgs a = bwd_args(p, (char*)ws, offsets_dev, X, P, pu ? (int64_t)p.k * p.d : 0, dS,
+                             lse, S, mass, dX, dP);
   hipError_t e = launch_bwd(a, (int)pr->dtype, (hipStream_t)stream, prof);
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }

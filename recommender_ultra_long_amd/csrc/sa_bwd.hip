@@ -130,7 +130,8 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ Pq, int64_t pq_ustride, const bf16* __restrict__ Gq,
     const float* __restrict__ cvn, int kp, int64_t T, float alpha, float scale,
-    const float* __restrict__ lse, float* __restrict__ dX, float* __restrict__ delta_out) {
+    const float* __restrict__ lse, float* __restrict__ dX, int acc_dx,
+    float* __restrict__ delta_out) {
   constexpr int NW = 8;                   // waves
   static_assert(NW * 32 == kBwdxTokensBf16, "");
   constexpr int KS = D / 16, DB = D / 32, U = D / 8;
@@ -403,7 +404,10 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
       const int row = q * RPI + rr;
       const int64_t t = r0 + wave * 32 + row;
       const f32x4 v = st[row * (D / 4) + (cc ^ sw(row))];
-      if (t >= ulo && t < uhi) *(f32x4*)(dX + t * D + 4 * cc) = v;
+      if (t >= ulo && t < uhi) {
+        f32x4* dst = (f32x4*)(dX + t * D + 4 * cc);
+        *dst = acc_dx ? *dst + v : v;   // acc_dx: add to the caller's dX
+      }
     }
   }
 }
@@ -644,7 +648,7 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
     const float* __restrict__ P, int64_t pstride, const float* __restrict__ Gq,
     const float* __restrict__ cv, int k,
     int64_t T, float alpha, float scale, const float* __restrict__ lse, float* __restrict__ dX,
-    float* __restrict__ delta_out) {
+    int acc_dx, float* __restrict__ delta_out) {
   constexpr int PC = 32, DS = D / 8;
   __shared__ float sP[PC][D + 4];
   __shared__ float sG[PC][D + 4];
@@ -708,7 +712,11 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
     }
     if (mine) {
 #pragma unroll
-      for (int e = 0; e < DS; ++e) dX[tok * D + q * DS + e] = g[e] + scale * (bb[e] - dsum * aa[e]);
+      for (int e = 0; e < DS; ++e) {
+        const float v = g[e] + scale * (bb[e] - dsum * aa[e]);
+        float* dst = dX + tok * D + q * DS + e;
+        *dst = acc_dx ? *dst + v : v;   // acc_dx: add to the caller's dX
+      }
       if (q == 0) delta_out[tok] = dsum;
     }
   }
@@ -890,7 +898,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
       hipLaunchKernelGGL(sa_bwdx_bf16<D>, dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st, a.offsets,
                          a.B, (const bf16*)a.X, (const bf16*)a.Pq,
                          pu ? (int64_t)a.kp * D : (int64_t)0, (const bf16*)a.Gq, a.cvs, a.kp, a.T,
-                         alpha, scale, a.lse, a.dX, a.delta);
+                         alpha, scale, a.lse, a.dX, a.acc_dx, a.delta);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
@@ -913,7 +921,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
       prof_begin(prof, "sa_bwdx_f32", st);
       hipLaunchKernelGGL(sa_bwdx_f32<D>, dim3(nbx), dim3(256), 0, st, a.offsets, a.B,
                          (const float*)a.X, (const float*)a.P, a.pstride, (const float*)a.Gq,
-                         a.cv, a.k, a.T, alpha, scale, a.lse, a.dX, a.delta);
+                         a.cv, a.k, a.T, alpha, scale, a.lse, a.dX, a.acc_dx, a.delta);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;

@@ -109,12 +109,13 @@ __device__ __forceinline__ void rows_times_w(const float (*In)[D + 4], const flo
   }
 }
 
-// grid = ceil(k / fold_rows<D>()); block 256.
-template <typename PT, int D>
+// grid = ceil(k / fold_rows<D>()); block 256.  P_eff is written in OT (the
+// sketch's input dtype), rounded once from the fp32 result.
+template <typename PT, typename OT, int D>
 __global__ __launch_bounds__(256) void sa_fold_fwd(const PT* __restrict__ P,
                                                    const float* __restrict__ Wq,
                                                    const float* __restrict__ Wk,
-                                                   PT* __restrict__ Peff, int k) {
+                                                   OT* __restrict__ Peff, int k) {
   constexpr int RB = fold_rows<D>(), RS = 256 / D, NR = RB / RS;
   __shared__ float sW[D][D + 1];
   __shared__ __align__(16) float sP[RB][D + 4];
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void sa_fold_fwd(const PT* __restrict__ P,
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     const int r = r0 + rr + RS * i;
-    if (r < k) Peff[(int64_t)r * D + n] = (PT)acc[i];
+    if (r < k) Peff[(int64_t)r * D + n] = (OT)acc[i];
   }
 }
 
@@ -272,12 +273,25 @@ static int fold_span(int k) {
 }
 static int fold_slices(int k) { return (k + fold_span(k) - 1) / fold_span(k); }
 
-template <typename PT, int D>
+template <typename PT, int D, typename OT = PT>
 static hipError_t fold_t(int k, const void* P, const float* Wq, const float* Wk, void* Peff,
                          hipStream_t st) {
-  hipLaunchKernelGGL((sa_fold_fwd<PT, D>), dim3(fold_row_blocks<D>(k)), dim3(256), 0, st,
-                     (const PT*)P, Wq, Wk, (PT*)Peff, k);
+  hipLaunchKernelGGL((sa_fold_fwd<PT, OT, D>), dim3(fold_row_blocks<D>(k)), dim3(256), 0, st,
+                     (const PT*)P, Wq, Wk, (OT*)Peff, k);
   return hipGetLastError();
+}
+
+hipError_t launch_fold_from_f32(int k, int d, int out_dtype, const float* P, const float* Wq,
+                                const float* Wk, void* Peff, hipStream_t st) {
+  switch (d) {
+    case 32: return out_dtype == 1 ? fold_t<float, 32, bf16>(k, P, Wq, Wk, Peff, st)
+                                   : fold_t<float, 32>(k, P, Wq, Wk, Peff, st);
+    case 64: return out_dtype == 1 ? fold_t<float, 64, bf16>(k, P, Wq, Wk, Peff, st)
+                                   : fold_t<float, 64>(k, P, Wq, Wk, Peff, st);
+    case 128: return out_dtype == 1 ? fold_t<float, 128, bf16>(k, P, Wq, Wk, Peff, st)
+                                    : fold_t<float, 128>(k, P, Wq, Wk, Peff, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename PT, int D>

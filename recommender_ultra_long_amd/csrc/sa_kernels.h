@@ -78,6 +78,7 @@ struct BwdArgs {
   const float* S;      // [B, k, d] (mass norm only)
   const float* mass;   // [B, k]    (mass norm only)
   float* dX;           // [T, d]
+  int acc_dx;          // 1: add to dX instead of overwriting it
   float* dP;           // [k, d], or [B, k, d] with per-user tables
   void* Gq;            // [B, kp, d] G = dS (or dS / mass) in the input dtype, rows >= k zero
   float* cv;           // [B, kp]   G[j] . S[j] (mass norm) or 0
@@ -124,8 +125,36 @@ hipError_t launch_fold(int k, int d, int dtype, const void* P, const float* Wq, 
 hipError_t launch_fold_backward(int k, int d, int dtype, const void* P, const float* Wq,
                                 const float* Wk, const float* G, float* dP, float* dWq,
                                 float* dWk, float* parts, hipStream_t st);
-// Workspace of the fold's backward: per-workgroup parts of dW_Q and dW_K.
+// The fold of an fp32 table, P_eff written in out_dtype (0 fp32, 1 bf16).
+hipError_t launch_fold_from_f32(int k, int d, int out_dtype, const float* P, const float* Wq,
+                                const float* Wk, void* Peff, hipStream_t st);
+// Workspace of the fold's backward: Q, dQ and per-slice parts of dW_Q, dW_K.
 size_t fold_workspace_bytes(int k, int d);
+
+// Dense pieces of the stacked block (sa_block.hip), fp32.
+hipError_t launch_gemm(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
+                       float* C, int ldc, int M, int N, int K, int slices, int accumulate,
+                       hipStream_t st);
+hipError_t launch_sum_slices(const float* parts, int nslices, int64_t n, const float* init,
+                             float* out, hipStream_t st);
+hipError_t launch_ln_fwd(int d, const float* a, const float* res, int64_t res_rows, int64_t R,
+                         const float* g, const float* b, float* y, float* mean, float* rstd,
+                         hipStream_t st);
+hipError_t launch_ln_bwd(int d, const float* dy, const float* a, const float* res,
+                         int64_t res_rows, int64_t R, const float* mean, const float* rstd,
+                         const float* g, float* dv, int acc_dv, float* part, int nblk,
+                         hipStream_t st);
+hipError_t launch_swiglu_fwd(const float* U1, const float* U3, int64_t n, float* G,
+                             hipStream_t st);
+hipError_t launch_swiglu_bwd(const float* dG, const float* U1, const float* U3, int64_t n,
+                             float* dU1, float* dU3, hipStream_t st);
+
+// Argument blocks of the sketch kernels for a plan and a workspace (sa_api.cpp).
+FwdArgs fwd_args(const Plan& p, char* ws, const int64_t* offsets, const void* X, const void* P,
+                 int64_t pstride, float* S, float* lse, float* mass);
+BwdArgs bwd_args(const Plan& p, char* ws, const int64_t* offsets, const void* X, const void* P,
+                 int64_t pstride, const float* dS, const float* lse, const float* S,
+                 const float* mass, float* dX, float* dP);
 hipError_t launch_stats_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st, Prof* prof);

@@ -41,13 +41,21 @@ SA_PROFILE_MAX_KERNELS = 8
 EXPORTED = ("sa_version", "sa_status_string", "sa_validate", "sa_workspace_size",
             "sa_forward", "sa_backward", "sa_forward_profiled", "sa_backward_profiled",
             "sa_get_device_status", "sa_fold_workspace_size", "sa_fold_prototypes",
-            "sa_fold_prototypes_backward")
+            "sa_fold_prototypes_backward", "sa_block_workspace_size", "sa_block_forward",
+            "sa_block_backward")
+
+# Parameter names of one layer of the stacked block, in sa_block_layer order.
+BLOCK_LAYER_KEYS = ("Wq", "Wk", "ln1_g", "ln1_b", "W1", "W3", "W2", "ln2_g", "ln2_b")
 
 
 class SaProblem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("k", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("total_tokens", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("flags", ctypes.c_uint32)]
+
+
+class SaBlockLayer(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in BLOCK_LAYER_KEYS]
 
 
 class SaProfile(ctypes.Structure):
@@ -104,6 +112,14 @@ def load():
     lib.sa_fold_prototypes_backward.restype = i32
     lib.sa_fold_prototypes_backward.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 sz, vp]
+    lib.sa_block_workspace_size.restype = sz
+    lib.sa_block_workspace_size.argtypes = [pp, i32]
+    lib.sa_block_forward.restype = i32
+    lib.sa_block_forward.argtypes = [pp, i32, vp, vp, vp, ctypes.POINTER(SaBlockLayer), vp, vp, sz,
+                                     vp]
+    lib.sa_block_backward.restype = i32
+    lib.sa_block_backward.argtypes = [pp, i32, vp, vp, vp, ctypes.POINTER(SaBlockLayer), vp, vp, vp,
+                                      ctypes.POINTER(SaBlockLayer), vp, sz, vp]
     _lib = lib
     return lib
 
@@ -286,6 +302,75 @@ def fold_prototypes_backward(P, Wq, Wk, dP_eff, workspace=None, stream=None):
     if st != SA_OK:
         raise SAError(st, "sa_fold_prototypes_backward")
     return dP, dWq, dWk
+
+
+def _layer_array(layers):
+    """ctypes array of SaBlockLayer from a list of dicts of device tensors
+    keyed by BLOCK_LAYER_KEYS (the same struct layout serves the gradients)."""
+    arr = (SaBlockLayer * len(layers))()
+    for i, L in enumerate(layers):
+        for name in BLOCK_LAYER_KEYS:
+            setattr(arr[i], name, _ptr(L[name]))
+    return arr
+
+
+def block_workspace(offsets_len, k, d, T, dtype, n_layers, device):
+    pr = make_problem(offsets_len - 1, k, d, T, dtype)
+    nbytes = int(load().sa_block_workspace_size(ctypes.byref(pr), int(n_layers)))
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def block_forward(offsets, X, P0, layers, out=None, workspace=None, stream=None):
+    """Calls sa_block_forward: the stacked block (Eq. 12-16) over a CSR batch.
+    X [T, d] (f32 or bf16), P0 [k, d] f32, layers: list of dicts of f32 device
+    tensors keyed by BLOCK_LAYER_KEYS.  Returns (out [B, k, d] f32, workspace);
+    pass the same workspace to block_backward."""
+    lib = load()
+    dev = P0.device
+    off = _device_offsets(offsets, dev)
+    B = off.numel() - 1
+    T, d = X.shape
+    k = P0.shape[0]
+    pr = make_problem(B, k, d, T, X.dtype)
+    if out is None:
+        out = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else block_workspace(B + 1, k, d, T, X.dtype,
+                                                                 len(layers), dev)
+    arr = _layer_array(layers)
+    st = lib.sa_block_forward(ctypes.byref(pr), len(layers), _ptr(off), _ptr(X), _ptr(P0), arr,
+                              _ptr(out), _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
+                              _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_block_forward")
+    return out, ws
+
+
+def block_backward(offsets, X, P0, layers, dout, workspace, dX=None, dP0=None, grads=None,
+                   stream=None):
+    """Calls sa_block_backward with the workspace of the matching
+    block_forward.  Returns (dX [T, d], dP0 [k, d], grads: list of dicts like
+    layers), all f32."""
+    lib = load()
+    dev = P0.device
+    off = _device_offsets(offsets, dev)
+    B = off.numel() - 1
+    T, d = X.shape
+    k = P0.shape[0]
+    pr = make_problem(B, k, d, T, X.dtype)
+    if dX is None:
+        dX = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if dP0 is None:
+        dP0 = torch.empty((k, d), dtype=torch.float32, device=dev)
+    if grads is None:
+        grads = [{name: torch.empty_like(L[name]) for name in BLOCK_LAYER_KEYS} for L in layers]
+    st = lib.sa_block_backward(ctypes.byref(pr), len(layers), _ptr(off), _ptr(X), _ptr(P0),
+                               _layer_array(layers), _ptr(dout), _ptr(dX), _ptr(dP0),
+                               _layer_array(grads), _ptr(workspace),
+                               ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                               _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_block_backward")
+    return dX, dP0, grads
 
 
 def sa_get_device_status(workspace, stream=None):
