@@ -40,6 +40,9 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--part", choices=("all", "block"), default="all",
+                    help="block: time only the stacked block on the 32-user batch and print "
+                         "its JSON (for profiling the block's kernels alone)")
     ap.add_argument("--no-per-user", action="store_true",
                     help="skip the timings on the 32-user batch (shared vs per-user tables, "
                          "the stacked block); profiling runs skip them so that kernel "
@@ -293,6 +296,19 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.part == "block":
+        def timed_block(fn, reps):
+            st = torch.cuda.current_stream()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(st)
+            for _ in range(reps):
+                fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+        print(json.dumps({"block": _block_timing(sa, synth, timed_block, dev)}))
+        return
     prob = synth.make_workload(args.workload, device=dev, with_dS=True)
     w = prob.workload
     T, k, d = prob.total_tokens, w.k, w.d
