@@ -79,8 +79,16 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
  *    of user u's table (instead of the sum over users).  This is the form of
  *    the refinement layers (SequenceO1 reading notes, section 3.3,
  *    Eq. (12)-(14)), whose queries are the user's own sketch from the layer
- *    before. */
-enum { SA_FLAG_MASS_NORM = 1u, SA_FLAG_PER_USER_PROTOTYPES = 2u };
+ *    before.
+ *  SA_FLAG_TOKEN_WISE: the vanilla-attention baseline of Table 1 (reading
+ *    notes, sections 3.5 and 7.1): the same affinities normalised over each
+ *    user's tokens instead of over the prototypes,
+ *        A[j,i] = exp Z[j,i] / sum_i' exp Z[j,i'],  S[j] = sum_i A[j,i] x_i,
+ *    with lse per user and prototype: lse[u,j] = log sum_i exp Z[j,i]
+ *    (float [B, k]; -inf for an empty user, whose S is 0).  sa_forward's lse
+ *    argument is then [B, k] and mass must be NULL; sa_backward requires the
+ *    forward's S and lse.  Not combinable with the other two flags. */
+enum { SA_FLAG_MASS_NORM = 1u, SA_FLAG_PER_USER_PROTOTYPES = 2u, SA_FLAG_TOKEN_WISE = 4u };
 
 /* Operation selector for sa_workspace_size. */
 enum { SA_OP_FORWARD = 0, SA_OP_BACKWARD = 1 };

@@ -45,6 +45,8 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, bool p
   p->off_lse2 = off; off = align256(off + (Tn + 1) * 4);
   p->off_part = off; off = align256(off + (size_t)p->nslots * k * d * 4);
   p->off_pmass = off; off = align256(off + (size_t)p->nslots * k * 4);
+  p->off_pl = off; off = align256(off + (size_t)p->nslots * k * 4);
+  p->off_tlse = off; off = align256(off + (size_t)B * k * 4);
   p->fwd_bytes = off;
 
   const size_t esz = dtype == 1 ? 2 : 4;
@@ -75,6 +77,7 @@ FwdArgs fwd_args(const Plan& p, char* w, const int64_t* offsets, const void* X, 
   a.S = S; a.mass = mass;
   a.part = (float*)(w + p.off_part);
   a.pmass = (float*)(w + p.off_pmass);
+  a.pl = (float*)(w + p.off_pl);
   a.status = (uint32_t*)(w + p.off_status);
   a.G = p.G; a.nchunks = p.nchunks;
   a.mass_norm = p.mass_norm ? 1 : 0;
@@ -136,7 +139,12 @@ const char* sa_status_string(sa_status s) {
 sa_status sa_validate(const sa_problem* pr, const int64_t* offsets_host) {
   if (pr == nullptr) return SA_ERR_NULL_ARG;
   if (pr->dtype != SA_F32 && pr->dtype != SA_BF16) return SA_ERR_BAD_DTYPE;
-  if ((pr->flags & ~(uint32_t)(SA_FLAG_MASS_NORM | SA_FLAG_PER_USER_PROTOTYPES)) != 0u)
+  const uint32_t known = SA_FLAG_MASS_NORM | SA_FLAG_PER_USER_PROTOTYPES | SA_FLAG_TOKEN_WISE;
+  if ((pr->flags & ~known) != 0u) return SA_ERR_UNSUPPORTED;
+  // Token-wise weights already sum to one per prototype (no mass
+  // normalisation), and that variant takes one shared table.
+  if ((pr->flags & SA_FLAG_TOKEN_WISE) != 0u &&
+      (pr->flags & (SA_FLAG_MASS_NORM | SA_FLAG_PER_USER_PROTOTYPES)) != 0u)
     return SA_ERR_UNSUPPORTED;
   if (pr->batch < 1 || pr->k < 1 || pr->k > 2048) return SA_ERR_BAD_SHAPE;
   if (!(pr->d == 32 || pr->d == 64 || pr->d == 128)) return SA_ERR_BAD_SHAPE;
@@ -179,9 +187,16 @@ static sa_status forward_impl(const sa_problem* pr, const int64_t* offsets_dev, 
     return SA_ERR_BAD_SHAPE;
   if (ws_bytes < p.fwd_bytes) return SA_ERR_WORKSPACE_TOO_SMALL;
 
+  hipStream_t st = (hipStream_t)stream;
+  if ((pr->flags & SA_FLAG_TOKEN_WISE) != 0u) {
+    if (mass != nullptr) return SA_ERR_UNSUPPORTED;   // every row of weights sums to one
+    const FwdArgs a = fwd_args(p, (char*)ws, offsets_dev, X, P, 0, S,
+                               lse ? lse : (float*)((char*)ws + p.off_tlse), nullptr);
+    const hipError_t e = launch_tok_fwd(a, (int)pr->dtype, st, prof);
+    return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+  }
   const FwdArgs a = fwd_args(p, (char*)ws, offsets_dev, X, P, pu ? (int64_t)p.k * p.d : 0, S,
                              lse, mass);
-  hipStream_t st = (hipStream_t)stream;
   hipError_t e = pr->dtype == SA_BF16 ? launch_fwd_bf16(a, st, prof) : launch_fwd_f32(a, st, prof);
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }

@@ -37,7 +37,7 @@ struct Plan {
   int64_t bslots;       // dP partial slots: Gb, or Gb + B - 1 with per-user tables
   int kp;               // row stride of G and cv: k rounded up to the dX chunk (bf16), else k
   // forward workspace layout (byte offsets)
-  size_t off_status, off_lse, off_lse2, off_part, off_pmass, fwd_bytes;
+  size_t off_status, off_lse, off_lse2, off_part, off_pmass, off_pl, off_tlse, fwd_bytes;
   // backward workspace layout (byte offsets)
   size_t off_G, off_cv, off_cvs, off_Pq, off_delta, off_dpp, off_blse, off_blse2, bwd_bytes;
 };
@@ -58,7 +58,8 @@ struct FwdArgs {
   float* S;            // [B, k, d]
   float* mass;         // [B, k] or nullptr
   float* part;         // [nslots, k, d]
-  float* pmass;        // [nslots, k]
+  float* pmass;        // [nslots, k] (token-wise: per-slot running maxima)
+  float* pl;           // [nslots, k] token-wise: per-slot sums of weights
   uint32_t* status;    // device status word
   int G, nchunks;
   int mass_norm;
@@ -159,6 +160,8 @@ hipError_t launch_stats_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof);
+// Token-wise normalisation (sa_tok.hip): S [B, k, d] and lse [B, k].
+hipError_t launch_tok_fwd(const FwdArgs& a, int dtype, hipStream_t st, Prof* prof);
 // out[u] = scale * sum of user u's piece partials (slot s + u of segment s of
 // G), in piece order; also checks the offsets.  Per-user dP.
 hipError_t launch_piece_sum(const int64_t* offsets, int B, int k, int d, int64_t T, int G,

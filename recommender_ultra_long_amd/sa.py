@@ -33,6 +33,7 @@ SA_F32 = 0
 SA_BF16 = 1
 SA_FLAG_MASS_NORM = 1
 SA_FLAG_PER_USER_PROTOTYPES = 2
+SA_FLAG_TOKEN_WISE = 4
 SA_OP_FORWARD = 0
 SA_OP_BACKWARD = 1
 
@@ -132,10 +133,12 @@ def status_string(status):
     return load().sa_status_string(int(status)).decode()
 
 
-def make_problem(batch, k, d, total_tokens, dtype, mass_norm=False, per_user=False):
+def make_problem(batch, k, d, total_tokens, dtype, mass_norm=False, per_user=False,
+                 token_wise=False):
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}.get(dtype, 99)
-    flags = (SA_FLAG_MASS_NORM if mass_norm else 0) | (SA_FLAG_PER_USER_PROTOTYPES if per_user else 0)
+    flags = ((SA_FLAG_MASS_NORM if mass_norm else 0) | (SA_FLAG_PER_USER_PROTOTYPES if per_user else 0)
+             | (SA_FLAG_TOKEN_WISE if token_wise else 0))
     return SaProblem(int(batch), int(k), int(d), int(total_tokens), int(dtype), flags)
 
 
@@ -235,6 +238,29 @@ def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, work
     if st != SA_OK:
         raise SAError(st, "sa_forward")
     return S, lse, mass
+
+
+def tokenwise_forward(offsets, X, P, S=None, lse=None, workspace=None, stream=None):
+    """Calls sa_forward with SA_FLAG_TOKEN_WISE (the vanilla-attention baseline:
+    softmax over each user's tokens).  Returns (S [B, k, d] f32, lse [B, k] f32)."""
+    lib = load()
+    dev = P.device
+    off = _device_offsets(offsets, dev)
+    B = off.numel() - 1
+    T, d = X.shape
+    k = P.shape[0]
+    pr = make_problem(B, k, d, T, X.dtype, token_wise=True)
+    if S is None:
+        S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, k), dtype=torch.float32, device=dev)
+    ws = _workspace(workspace_size(pr, SA_OP_FORWARD), dev, workspace)
+    st = lib.sa_forward(ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(S), _ptr(lse), None,
+                        _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
+                        _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_forward (token-wise)")
+    return S, lse
 
 
 def sa_backward(offsets, X, P, dS, lse=None, S=None, mass=None, mass_norm=False, dX=None,

@@ -59,7 +59,14 @@ def test_validate_shapes_and_dtypes():
     pr = _p()
     pr.flags = sa.SA_FLAG_MASS_NORM | sa.SA_FLAG_PER_USER_PROTOTYPES
     assert sa.validate(pr) == sa.SA_OK
-    pr.flags = 4
+    pr.flags = sa.SA_FLAG_TOKEN_WISE
+    assert sa.validate(pr) == sa.SA_OK
+    # token-wise weights already sum to one; that variant takes a shared table
+    pr.flags = sa.SA_FLAG_TOKEN_WISE | sa.SA_FLAG_MASS_NORM
+    assert sa.validate(pr) == sa.SA_ERR_UNSUPPORTED
+    pr.flags = sa.SA_FLAG_TOKEN_WISE | sa.SA_FLAG_PER_USER_PROTOTYPES
+    assert sa.validate(pr) == sa.SA_ERR_UNSUPPORTED
+    pr.flags = 8
     assert sa.validate(pr) == sa.SA_ERR_UNSUPPORTED
 
 
