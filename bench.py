@@ -454,6 +454,25 @@ def main():
         "fold_us": round(ms_fold * 1e3, 2), "fold_backward_us": round(ms_fold_bwd * 1e3, 2),
         "fold_gflops": round(fold_flop / (ms_fold * 1e-3) / 1e9, 1),
         "fold_backward_gflops": round(fold_bwd_flop / (ms_fold_bwd * 1e-3) / 1e9, 1)}
+    # The token-wise normalised variant (the vanilla-attention baseline of
+    # Table 1) on the step's own workload: one pass forward (4 k d matrix
+    # flops per token, no statistics pass), single-stage dX pass backward.
+    Stw = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+    lsetw = torch.empty((B, k), dtype=torch.float32, device=dev)
+    prt = sa.make_problem(B, k, d, T, prob.X.dtype, token_wise=True)
+    wsf_t = torch.empty(sa.workspace_size(prt, sa.SA_OP_FORWARD), dtype=torch.uint8, device=dev)
+    wsb_t = torch.empty(sa.workspace_size(prt, sa.SA_OP_BACKWARD), dtype=torch.uint8, device=dev)
+    tw_fwd = lambda: sa.tokenwise_forward(off, prob.X, prob.P, S=Stw, lse=lsetw, workspace=wsf_t)
+    tw_bwd = lambda: sa.tokenwise_backward(off, prob.X, prob.P, prob.dS, Stw, lsetw, dX=dX, dP=dP,
+                                           workspace=wsb_t)
+    tw_fwd()
+    tw_bwd()
+    ms_tf = timed(tw_fwd, reps)
+    ms_tb = timed(tw_bwd, reps)
+    out["token_wise"] = {
+        "forward_ms": round(ms_tf, 5), "backward_ms": round(ms_tb, 5),
+        "forward_frac_bf16_peak": round(fwd_flop / (ms_tf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(T / ((ms_tf + ms_tb) * 1e-3), 1)}
     if not args.no_per_user:
         out["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
         out["block"] = _block_timing(sa, synth, timed, dev)

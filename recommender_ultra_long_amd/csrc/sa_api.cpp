@@ -61,6 +61,7 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, bool p
   p->off_dpp = off; off = align256(off + (size_t)p->bslots * k * d * 4);
   p->off_blse = off; off = align256(off + Tn * 4);
   p->off_blse2 = off; off = align256(off + (Tn + 1) * 4);
+  p->off_tlse2 = off; off = align256(off + (size_t)B * kp * 4);
   p->bwd_bytes = off;
   return true;
 }
@@ -108,6 +109,8 @@ BwdArgs bwd_args(const Plan& p, char* w, const int64_t* offsets, const void* X, 
   a.status = (uint32_t*)(w + p.off_status);
   a.Gb = p.Gb; a.bnchunks = p.bnchunks; a.bslots = p.bslots;
   a.mass_norm = p.mass_norm ? 1 : 0;
+  a.tokwise = 0;
+  a.tlse2 = (float*)(w + p.off_tlse2);
   return a;
 }
 
@@ -223,8 +226,11 @@ static sa_status backward_impl(const sa_problem* pr, const int64_t* offsets_dev,
     return SA_ERR_BAD_SHAPE;
   if (ws_bytes < p.bwd_bytes) return SA_ERR_WORKSPACE_TOO_SMALL;
 
-  const BwdArgs a = bwd_args(p, (char*)ws, offsets_dev, X, P, pu ? (int64_t)p.k * p.d : 0, dS,
-                             lse, S, mass, dX, dP);
+  const bool tw = (pr->flags & SA_FLAG_TOKEN_WISE) != 0u;
+  if (tw && (S == nullptr || lse == nullptr)) return SA_ERR_NULL_ARG;   // D_j = dS_j . S_j
+  BwdArgs a = bwd_args(p, (char*)ws, offsets_dev, X, P, pu ? (int64_t)p.k * p.d : 0, dS, lse, S,
+                       mass, dX, dP);
+  a.tokwise = tw ? 1 : 0;
   hipError_t e = launch_bwd(a, (int)pr->dtype, (hipStream_t)stream, prof);
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }

@@ -38,16 +38,29 @@ namespace sa {
 //   [nbg, nbg + nbq)  Pq = P with zero rows k .. kp - 1, 16 bytes per thread
 //                     (bf16 only); one copy per user (pq_users = B, user u's
 //                     table at P + u pstride) or one shared copy (pq_users = 1);
-//   from nbg + nbq    lse2 = lse log2(e), with the +inf sentinel at index T.
+//   from nbg + nbq    lse2 = lse log2(e), with the +inf sentinel at index T;
+//                     token-wise (mode 2): per (user, prototype), rows of
+//                     stride kp, +inf on padding rows.
+// mode: 0 plain sum (G = dS, cv = 0), 1 mass normalisation (G = dS / mu,
+// cv = G . S), 2 token-wise normalisation (G = dS, cv = G . S).
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void sa_bwd_prep(
     const float* __restrict__ dS, const float* __restrict__ S, const float* __restrict__ mass,
-    int B, int k, int kp, int mass_norm, float scale, OutT* __restrict__ Gq,
+    int B, int k, int kp, int mode, float scale, OutT* __restrict__ Gq,
     float* __restrict__ cv, float* __restrict__ cvs, unsigned nbg, const bf16* __restrict__ P,
     int64_t pstride, int pq_users, bf16* __restrict__ Pq, unsigned nbq,
     const float* __restrict__ lse, int64_t T, float* __restrict__ lse2) {
   if (blockIdx.x >= nbg + nbq) {
     const int64_t i = (int64_t)(blockIdx.x - nbg - nbq) * 256 + threadIdx.x;
+    if (mode == 2) {
+      // token-wise: per (user, prototype) rows of stride kp, +inf for padding
+      if (i < (int64_t)B * kp) {
+        const int64_t u = i / kp;
+        const int j = (int)(i % kp);
+        lse2[i] = j < k ? lse[u * k + j] * kLog2e : INFINITY;
+      }
+      return;
+    }
     if (i < T) lse2[i] = lse[i] * kLog2e;
     else if (i == T) lse2[i] = INFINITY;
     return;
@@ -79,10 +92,14 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(
   float c = 0.f;
   if (live) {
     g = *(const f32x4*)(dS + r * D + 4 * part);
-    if (mass_norm) {
+    if (mode == 1) {
       const float mu = mass[r];
       const float inv = mu > 0.f ? 1.0f / mu : 0.f;
       g = mu > 0.f ? g * inv : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (mode != 0) {
+      // cv = G . S: the mass-normalised sketch's rows, or, token-wise, the
+      // softmax term D_j = sum_i A_ji dA_ji = dS_j . S_j
       const f32x4 sv = *(const f32x4*)(S + r * D + 4 * part);
       c = g[0] * sv[0] + g[1] * sv[1] + g[2] * sv[2] + g[3] * sv[3];
     }
@@ -125,13 +142,18 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(
 // resident as B operands); the A operands of the accumulation are
 // transpose-read from LDS.  dX goes out through LDS so that every store
 // covers whole token rows.
-template <int D>
+//
+// Token-wise normalisation (TW): the weights A_ji = exp(z_ji - lse_j) use the
+// prototype's statistic, streamed with each chunk beside -cv (= -D_j); with
+// w'_ji = c A_ji (dA'_ji - D_j) = c dZ_ji there is no per-token coupling, so
+// stage 1 alone gives dX_i = sum_j (A_ji G_j + w'_ji p_j), and no delta.
+template <int D, bool TW>
 __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ Pq, int64_t pq_ustride, const bf16* __restrict__ Gq,
     const float* __restrict__ cvn, int kp, int64_t T, float alpha, float scale,
-    const float* __restrict__ lse, float* __restrict__ dX, int acc_dx,
-    float* __restrict__ delta_out) {
+    const float* __restrict__ lse, const float* __restrict__ lq2, float* __restrict__ dX,
+    int acc_dx, float* __restrict__ delta_out) {
   constexpr int NW = 8;                   // waves
   static_assert(NW * 32 == kBwdxTokensBf16, "");
   constexpr int KS = D / 16, DB = D / 32, U = D / 8;
@@ -142,7 +164,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
   constexpr int UPW = CU / NW;            // units per wave per matrix
   static_assert(UPW < 64 || UPW % 64 == 0, "");
   constexpr int XI = (UPW + 63) / 64;     // copy instructions per wave per matrix
-  constexpr int L1 = 2 * XI + 1;          // loads per wave per stage-1 chunk
+  constexpr int L1 = 2 * XI + 1 + (TW ? 1 : 0);   // loads per wave per stage-1 chunk
   constexpr int L2 = XI;                  // loads per wave per stage-2 chunk
   constexpr int CW = PCH / NW;            // cv entries copied per wave
   constexpr uint32_t MB = PCH * D * 2;    // bytes of one matrix chunk
@@ -153,6 +175,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
   static_assert(NW * 32 * D * 4 <= NB * CB, "dX staging fits in the chunk buffers");
   __shared__ __attribute__((aligned(16))) bf16 sbuf[NB * 2 * PCH * D];
   __shared__ __attribute__((aligned(16))) float sC[NB][PCH];
+  __shared__ __attribute__((aligned(16))) float sQ[TW ? NB : 1][PCH];   // TW: lse2 per prototype
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -161,13 +184,14 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
   const int64_t tok = r0 + wave * 32 + l32;
   const uint32_t sb0 = lds_addr((const SA_LDS void*)&sbuf[0]);
   const uint32_t sc0 = lds_addr((const SA_LDS void*)&sC[0][0]);
+  const uint32_t sq0 = lds_addr((const SA_LDS void*)&sQ[0][0]);
   const SA_LDS char* lds = (const SA_LDS char*)0;
 
   bf16x8 xb[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     xb[ks] = tok < r1 ? *(const bf16x8*)(X + tok * D + 16 * ks + 8 * h) : bf16x8{};
-  const float l2 = tok < r1 ? lse[tok] * kLog2e : INFINITY;
+  const float l2 = (!TW && tok < r1) ? lse[tok] * kLog2e : INFINITY;
 
   // Copy geometry (per matrix): instruction j of this wave moves units
   // v0 .. v0 + 63, v0 = wave UPW + 64 j; unit v is row v / U at stored
@@ -203,6 +227,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const bf16* Gu = Gq + (int64_t)u * kp * D;
     const bf16* Pu = Pq + (int64_t)u * pq_ustride;   // the user's table (or the shared one)
     const float* cvu = cvn + (int64_t)u * kp;
+    const float* lqu = TW ? lq2 + (int64_t)u * kp : nullptr;
 
     // Chunk q of the stream: q < nch is stage-1 chunk q (P, G, -cv), then
     // stage-2 chunk q - nch (P), then copies of chunk 0 that are never read.
@@ -220,6 +245,10 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
         }
         if (lane < CW)
           lds_copy4v(cvu + q * PCH + wave * CW + lane, sc0 + ((q & (NB - 1)) * PCH + wave * CW) * 4);
+        if constexpr (TW) {
+          if (lane < CW)
+            lds_copy4v(lqu + q * PCH + wave * CW + lane, sq0 + ((q & (NB - 1)) * PCH + wave * CW) * 4);
+        }
       } else {
         const uint32_t goff = (uint32_t)(q < 2 * nch ? q - nch : 0) * MB;
 #pragma unroll
@@ -273,6 +302,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     for (int q = 0; q < nch; ++q) {
       const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
       const uint32_t cb = sc0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
+      const uint32_t qb = sq0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         const uint32_t tbuf = buf + pt * TB;
@@ -311,13 +341,19 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
         fence();
         bf16x8 abf[2], wbf[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          // A <= 1 for real prototypes; the clamp keeps padded ones finite.
-          const float a = __builtin_amdgcn_fmed3f(exp2_fast(fmaf(z[i], alpha, -lsh)), 0.f, 1.f);
-          const float w = a * (da[i] * scale);
-          ssum += w;
-          abf[i >> 3][i & 7] = (bf16)a;
-          wbf[i >> 3][i & 7] = (bf16)w;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 l4 = {lsh, lsh, lsh, lsh};
+          if constexpr (TW) l4 = *(const SA_LDS f32x4*)(lds + qb + pt * 128 + 32 * g4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g4 + r;
+            // A <= 1 for real prototypes; the clamp keeps padded ones finite.
+            const float a = __builtin_amdgcn_fmed3f(exp2_fast(fmaf(z[i], alpha, -l4[r])), 0.f, 1.f);
+            const float w = a * (da[i] * scale);
+            if constexpr (!TW) ssum += w;
+            abf[i >> 3][i & 7] = (bf16)a;
+            wbf[i >> 3][i & 7] = (bf16)w;
+          }
         }
         // acc^T (d x tokens) += G^T A + P^T w'.  K slot j of half h in block
         // kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
@@ -336,9 +372,9 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
       advance(q);
     }
 
-    // Stage 2: acc^T += P^T (-s A).
+    // Stage 2: acc^T += P^T (-s A) (not with token-wise weights).
     const float s = ssum + shfl_xor32(ssum);   // c delta of this lane's token
-    for (int q = nch; q < 2 * nch; ++q) {
+    for (int q = nch; q < (TW ? nch : 2 * nch); ++q) {
       const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
@@ -391,7 +427,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
                          acc[db][4 * g4 + 3]};
         st[l32 * (D / 4) + ((8 * db + 2 * g4 + h) ^ sw(l32))] = v;
       }
-    if (mine && h == 0) delta_out[tok] = s / scale;
+    if (!TW && mine && h == 0) delta_out[tok] = s / scale;
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
     // Each store instruction writes 64 x 16 bytes = 256 / D whole rows.
     constexpr int RPI = 256 / D;
@@ -425,12 +461,18 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
 //
 // lse2 holds the log-sum-exp in log2 units with lse2[T] = +inf, which rows
 // past the end of a tile read (weight 0, so dZ = 0).
-template <int D, int NW, bool PU>
+//
+// Token-wise normalisation (TW): the weights use the prototype's statistic,
+// lq2[user][proto] (a lane register, reloaded with G at a user change), dZ =
+// A (dA' - D_j) has no per-token term, and rows past a tile's end are masked
+// by the tile's row count (no per-token copies at all).
+template <int D, int NW, bool PU, bool TW>
 __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ P, int64_t pstride, const bf16* __restrict__ Gq,
     const float* __restrict__ cv, int k, int kp, int64_t T, int G, float alpha,
-    const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dpp) {
+    const float* __restrict__ lse2, const float* __restrict__ delta,
+    const float* __restrict__ lq2, float* __restrict__ dpp) {
   constexpr int KS = D / 16;             // reduction steps over d
   constexpr int DB = D / 32;             // 32-row blocks of the transposed partial
   constexpr int U = D / 8;               // 16-byte units per token row
@@ -443,7 +485,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
   constexpr int XI = (UPW + 63) / 64;    // X copy instructions per wave per tile
   constexpr int LPW = TILE / NW;         // lse and delta entries copied by each wave
   constexpr int NBUF = 8, AHEAD = 6;
-  constexpr int L = XI + 2;              // loads per wave per tile
+  constexpr int L = XI + (TW ? 0 : 2);   // loads per wave per tile
   constexpr uint32_t XBYTES = TILE * D * 2;
 
   __shared__ __attribute__((aligned(16))) bf16 sX[NBUF][TILE * D];
@@ -467,7 +509,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
   cw_.start(offsets, B, lo, hi);
 
   bf16x8 pw[KS], gw[KS];
-  float cw;
+  float cw, lj = 0.f;   // cv (or D_j) and, token-wise, lse2 of the lane's prototype
   auto load_prototype = [&](const bf16* Pu) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -520,7 +562,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
           lds_copy16(xb, (uint32_t)(r * D * 2) + ccol[j],
                      sx0 + b * XBYTES + (uint32_t)(wave * UPW + j * 64) * 16);
       }
-      if (lane < LPW) {
+      if (!TW && lane < LPW) {
         const bool in = lrow < nr;
         lds_copy4v(in ? lse2 + base + lrow : lse2 + T, sl0 + (b * TILE + wave * LPW) * 4);
         lds_copy4v(delta + base + (in ? lrow : 0), sd0 + (b * TILE + wave * LPW) * 4);
@@ -533,13 +575,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
     for (int ks = 0; ks < KS; ++ks)
       gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * kp + prow) * D + 16 * ks + 8 * h);
     cw = cv[(int64_t)guser * kp + prow];
+    if constexpr (TW) lj = lq2[(int64_t)guser * kp + prow];
 #pragma unroll
     for (int b = 0; b < AHEAD; ++b) copy_next(b);
     // The compiler must see the waits for the operand loads above here, not
     // inside the loop (where they would also wait for every copy in flight).
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(pw[ks]), "v"(gw[ks]));
-    asm volatile("" ::"v"(cw));
+    asm volatile("" ::"v"(cw), "v"(lj));
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -574,6 +617,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
         for (int ks = 0; ks < KS; ++ks)
           gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * kp + prow) * D + 16 * ks + 8 * h);
         cw = cv[(int64_t)guser * kp + prow];
+        if constexpr (TW) lj = lq2[(int64_t)guser * kp + prow];
         if constexpr (PU) {
           load_prototype(P + (int64_t)guser * pstride);
 #pragma unroll
@@ -581,7 +625,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(gw[ks]));
-        asm volatile("" ::"v"(cw));
+        asm volatile("" ::"v"(cw), "v"(lj));
       }
 
       const SA_LDS char* xs = lds + sx0 + buf * XBYTES;
@@ -594,19 +638,28 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
         da = mfma32(a, gw[ks], da);
       }
       // dZ = A (dA' - cv - delta); register i of a lane is token crow(i, h).
-      const SA_LDS char* ls = lds + sl0 + buf * (TILE * 4) + lqoff;
-      const SA_LDS char* ds = lds + sd0 + buf * (TILE * 4) + lqoff;
-      f32x4 lq[4], dq[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lq[g] = *(const SA_LDS f32x4*)(ls + 32 * g);
-        dq[g] = *(const SA_LDS f32x4*)(ds + 32 * g);
-      }
       bf16x8 zbf[2];
+      if constexpr (TW) {
+        const int nr = (int)(cw_.t1 - cw_.t0);   // valid rows of this tile
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float a = exp2_fast(fmaf(z[i], alpha, -lq[i >> 2][i & 3]));
-        zbf[i >> 3][i & 7] = (bf16)(a * (da[i] - cw - dq[i >> 2][i & 3]));
+        for (int i = 0; i < 16; ++i) {
+          const float a = crow(i, h) < nr ? exp2_fast(fmaf(z[i], alpha, -lj)) : 0.f;
+          zbf[i >> 3][i & 7] = (bf16)(a * (da[i] - cw));
+        }
+      } else {
+        const SA_LDS char* ls = lds + sl0 + buf * (TILE * 4) + lqoff;
+        const SA_LDS char* ds = lds + sd0 + buf * (TILE * 4) + lqoff;
+        f32x4 lq[4], dq[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          lq[g] = *(const SA_LDS f32x4*)(ls + 32 * g);
+          dq[g] = *(const SA_LDS f32x4*)(ds + 32 * g);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = exp2_fast(fmaf(z[i], alpha, -lq[i >> 2][i & 3]));
+          zbf[i >> 3][i & 7] = (bf16)(a * (da[i] - cw - dq[i >> 2][i & 3]));
+        }
       }
       // dP^T (d x prototypes) += X^T (d x tokens) dZ^T (tokens x prototypes).
 #pragma unroll
@@ -642,17 +695,21 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
 // ----------------------------------------------------------------------------
 // fp32 dX pass.  grid = ceil(T / 32); block 256 = 32 tokens x 8 threads, each
 // thread owning D/8 columns.  Prototypes stream through LDS 32 at a time.
+// tw: token-wise normalisation, A_ji = exp2(z alpha - lse2_j) with the
+// prototype's statistic (lse [B, k], natural log), cv = D_j, and
+// dX_i = sum_j (A_ji G_j + c dZ_ji p_j) with no per-token term.
 template <int D>
 __global__ __launch_bounds__(256) void sa_bwdx_f32(
     const int64_t* __restrict__ offsets, int B, const float* __restrict__ X,
     const float* __restrict__ P, int64_t pstride, const float* __restrict__ Gq,
     const float* __restrict__ cv, int k,
-    int64_t T, float alpha, float scale, const float* __restrict__ lse, float* __restrict__ dX,
-    int acc_dx, float* __restrict__ delta_out) {
+    int64_t T, float alpha, float scale, const float* __restrict__ lse, int tw,
+    float* __restrict__ dX, int acc_dx, float* __restrict__ delta_out) {
   constexpr int PC = 32, DS = D / 8;
   __shared__ float sP[PC][D + 4];
   __shared__ float sG[PC][D + 4];
   __shared__ float sC[PC];
+  __shared__ float sQ[PC];   // tw: lse2 of the chunk's prototypes
   const int tid = threadIdx.x;
   const int q = tid & 7;
   const int64_t r0 = (int64_t)blockIdx.x * kBwdxTokensF32;
@@ -661,7 +718,7 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
   float x[DS];
 #pragma unroll
   for (int e = 0; e < DS; ++e) x[e] = tok < r1 ? X[tok * D + q * DS + e] : 0.f;
-  const float l2 = tok < r1 ? lse[tok] * kLog2e : INFINITY;
+  const float l2 = (!tw && tok < r1) ? lse[tok] * kLog2e : INFINITY;
 
   int u = first_user_after(offsets, B, r0);
   for (; u < B; ++u) {
@@ -685,6 +742,7 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
         sG[r][c] = v ? Gu[(int64_t)(p0 + r) * D + c] : 0.f;
       }
       if (tid < PC) sC[tid] = p0 + tid < k ? cv[(int64_t)u * k + p0 + tid] : 0.f;
+      if (tw && tid < PC) sQ[tid] = p0 + tid < k ? lse[(int64_t)u * k + p0 + tid] * kLog2e : INFINITY;
       __syncthreads();
       const int np = k - p0 < PC ? k - p0 : PC;
       for (int j = 0; j < np; ++j) {
@@ -699,7 +757,7 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
           pz += __shfl_xor(pz, off, 64);
           pg += __shfl_xor(pg, off, 64);
         }
-        const float a = exp2_fast(fmaf(pz, alpha, -lsh));
+        const float a = exp2_fast(fmaf(pz, alpha, -(tw ? sQ[j] : lsh)));
         const float w = a * (pg - sC[j]);
         dsum += w;
 #pragma unroll
@@ -713,11 +771,11 @@ __global__ __launch_bounds__(256) void sa_bwdx_f32(
     if (mine) {
 #pragma unroll
       for (int e = 0; e < DS; ++e) {
-        const float v = g[e] + scale * (bb[e] - dsum * aa[e]);
+        const float v = g[e] + scale * (tw ? bb[e] : bb[e] - dsum * aa[e]);
         float* dst = dX + tok * D + q * DS + e;
         *dst = acc_dx ? *dst + v : v;   // acc_dx: add to the caller's dX
       }
-      if (q == 0) delta_out[tok] = dsum;
+      if (q == 0 && !tw) delta_out[tok] = dsum;
     }
   }
 }
@@ -733,13 +791,13 @@ __global__ __launch_bounds__(256) void sa_bwdp_f32(
     const float* __restrict__ P, int64_t pstride, const float* __restrict__ Gq,
     const float* __restrict__ cv, int k,
     int64_t T, int G, float alpha, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dpp) {
+    int tw, float* __restrict__ dpp) {
   constexpr int PC = kChunkF32Bwd, TILE = 32, DS = D / 8;
   __shared__ float sP[PC][D + 1];
   __shared__ float sG[PC][D + 1];
   __shared__ float sX[TILE][D + 1];
   __shared__ float sZ[PC][TILE + 1];
-  __shared__ float sL[TILE], sDl[TILE], sC[PC];
+  __shared__ float sL[TILE], sDl[TILE], sC[PC], sQ[PC];
   const int tid = threadIdx.x;
   const int j = tid >> 3, q = tid & 7;
   const int s = blockIdx.x;
@@ -780,17 +838,20 @@ __global__ __launch_bounds__(256) void sa_bwdp_f32(
         sG[r][c] = (p0 + r < k) ? Gu[(int64_t)(p0 + r) * D + c] : 0.f;
       }
       if (tid < PC) sC[tid] = p0 + tid < k ? cv[(int64_t)cur.user * k + p0 + tid] : 0.f;
+      if (tw && tid < PC)
+        sQ[tid] = p0 + tid < k ? lse[(int64_t)cur.user * k + p0 + tid] * kLog2e : INFINITY;
       loaded_user = cur.user;
     }
     for (int i = tid; i < TILE * D; i += 256) {
       const int r = i / D, c = i % D;
       sX[r][c] = (cur.t0 + r < cur.t1) ? X[(cur.t0 + r) * D + c] : 0.f;
     }
-    if (tid < TILE) {
+    if (!tw && tid < TILE) {
       const bool in = cur.t0 + tid < cur.t1;
       sL[tid] = in ? lse[cur.t0 + tid] * kLog2e : INFINITY;
       sDl[tid] = in ? delta[cur.t0 + tid] : 0.f;
     }
+    const int nr = (int)(cur.t1 - cur.t0);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -801,8 +862,13 @@ __global__ __launch_bounds__(256) void sa_bwdp_f32(
         z = fmaf(sP[j][e], sX[tt][e], z);
         ga = fmaf(sG[j][e], sX[tt][e], ga);
       }
-      const float a = exp2_fast(fmaf(z, alpha, -sL[tt]));
-      sZ[j][tt] = a * (ga - sC[j] - sDl[tt]);
+      if (tw) {
+        const float a = tt < nr ? exp2_fast(fmaf(z, alpha, -sQ[j])) : 0.f;
+        sZ[j][tt] = a * (ga - sC[j]);
+      } else {
+        const float a = exp2_fast(fmaf(z, alpha, -sL[tt]));
+        sZ[j][tt] = a * (ga - sC[j] - sDl[tt]);
+      }
     }
     __syncthreads();
 #pragma unroll 4
@@ -858,7 +924,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
   const float alpha = scale * kLog2e;
   hipError_t e;
   const bool pu = a.pstride != 0;
-  if (a.recompute_lse && a.T > 0) {
+  const bool tw = a.tokwise != 0;   // token-wise normalisation: lse is [B, k], S required
+  if (a.recompute_lse && a.T > 0 && !tw) {
     FwdArgs f = {};
     f.offsets = a.offsets; f.B = a.B; f.pstride = a.pstride;
     f.X = a.X; f.P = a.P; f.k = a.k; f.d = a.d; f.T = a.T; f.lse = a.lse_ws;
@@ -875,17 +942,20 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
   const int pq_users = pu ? a.B : 1;
   const unsigned nbq =
       bf ? (unsigned)(((int64_t)pq_users * a.kp * (D / 8) + 255) / 256) : 0u;
-  const bool lse2 = bf && a.T > 0 && !a.recompute_lse;
-  const unsigned nbl = lse2 ? (unsigned)((a.T + 1 + 255) / 256) : 0u;
+  const bool lse2 = bf && a.T > 0 && (tw || !a.recompute_lse);
+  const int64_t nl = tw ? (int64_t)a.B * a.kp : a.T + 1;
+  const unsigned nbl = lse2 ? (unsigned)((nl + 255) / 256) : 0u;
+  const int mode = tw ? 2 : (a.mass_norm ? 1 : 0);
+  float* lse2_out = tw ? a.tlse2 : a.lse2;
   prof_begin(prof, "sa_bwd_prep", st);
   if (bf)
     hipLaunchKernelGGL((sa_bwd_prep<bf16, D>), dim3(nbg + nbq + nbl), dim3(256), 0, st, a.dS, a.S,
-                       a.mass, a.B, a.k, a.kp, a.mass_norm, scale, (bf16*)a.Gq, a.cv, a.cvs, nbg,
+                       a.mass, a.B, a.k, a.kp, mode, scale, (bf16*)a.Gq, a.cv, a.cvs, nbg,
                        (const bf16*)a.P, a.pstride, pq_users, (bf16*)a.Pq, nbq, a.lse, a.T,
-                       a.lse2);
+                       lse2_out);
   else
     hipLaunchKernelGGL((sa_bwd_prep<float, D>), dim3(nbg), dim3(256), 0, st, a.dS, a.S, a.mass,
-                       a.B, a.k, a.kp, a.mass_norm, scale, (float*)a.Gq, a.cv, (float*)nullptr,
+                       a.B, a.k, a.kp, mode, scale, (float*)a.Gq, a.cv, (float*)nullptr,
                        nbg, (const bf16*)nullptr, (int64_t)0, 1, (bf16*)nullptr, 0u, a.lse, a.T,
                        a.lse2);
   e = hipGetLastError();
@@ -895,24 +965,37 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
     if (bf) {
       const unsigned nbx = (unsigned)((a.T + kBwdxTokensBf16 - 1) / kBwdxTokensBf16);
       prof_begin(prof, "sa_bwdx_bf16", st);
-      hipLaunchKernelGGL(sa_bwdx_bf16<D>, dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st, a.offsets,
-                         a.B, (const bf16*)a.X, (const bf16*)a.Pq,
-                         pu ? (int64_t)a.kp * D : (int64_t)0, (const bf16*)a.Gq, a.cvs, a.kp, a.T,
-                         alpha, scale, a.lse, a.dX, a.acc_dx, a.delta);
+      if (tw)
+        hipLaunchKernelGGL((sa_bwdx_bf16<D, true>), dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st,
+                           a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.Pq, (int64_t)0,
+                           (const bf16*)a.Gq, a.cvs, a.kp, a.T, alpha, scale, a.lse,
+                           (const float*)a.tlse2, a.dX, a.acc_dx, a.delta);
+      else
+        hipLaunchKernelGGL((sa_bwdx_bf16<D, false>), dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st,
+                           a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.Pq,
+                           pu ? (int64_t)a.kp * D : (int64_t)0, (const bf16*)a.Gq, a.cvs, a.kp,
+                           a.T, alpha, scale, a.lse, (const float*)nullptr, a.dX, a.acc_dx,
+                           a.delta);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
       prof_begin(prof, "sa_bwdp_bf16", st);
-      if (pu)
-        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, true>), dim3(a.Gb, a.bnchunks),
-                           dim3(64 * kBwdpWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
-                           (const bf16*)a.P, a.pstride, (const bf16*)a.Gq, a.cv, a.k, a.kp, a.T,
-                           a.Gb, alpha, a.lse2, a.delta, a.dpp);
+      const dim3 pg(a.Gb, a.bnchunks), pb(64 * kBwdpWaves);
+      if (tw)
+        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, false, true>), pg, pb, 0, st, a.offsets,
+                           a.B, (const bf16*)a.X, (const bf16*)a.P, (int64_t)0, (const bf16*)a.Gq,
+                           a.cv, a.k, a.kp, a.T, a.Gb, alpha, a.lse2, a.delta,
+                           (const float*)a.tlse2, a.dpp);
+      else if (pu)
+        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, true, false>), pg, pb, 0, st, a.offsets,
+                           a.B, (const bf16*)a.X, (const bf16*)a.P, a.pstride, (const bf16*)a.Gq,
+                           a.cv, a.k, a.kp, a.T, a.Gb, alpha, a.lse2, a.delta,
+                           (const float*)nullptr, a.dpp);
       else
-        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, false>), dim3(a.Gb, a.bnchunks),
-                           dim3(64 * kBwdpWaves), 0, st, a.offsets, a.B, (const bf16*)a.X,
-                           (const bf16*)a.P, (int64_t)0, (const bf16*)a.Gq, a.cv, a.k, a.kp, a.T,
-                           a.Gb, alpha, a.lse2, a.delta, a.dpp);
+        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, false, false>), pg, pb, 0, st, a.offsets,
+                           a.B, (const bf16*)a.X, (const bf16*)a.P, (int64_t)0, (const bf16*)a.Gq,
+                           a.cv, a.k, a.kp, a.T, a.Gb, alpha, a.lse2, a.delta,
+                           (const float*)nullptr, a.dpp);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
@@ -921,14 +1004,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
       prof_begin(prof, "sa_bwdx_f32", st);
       hipLaunchKernelGGL(sa_bwdx_f32<D>, dim3(nbx), dim3(256), 0, st, a.offsets, a.B,
                          (const float*)a.X, (const float*)a.P, a.pstride, (const float*)a.Gq,
-                         a.cv, a.k, a.T, alpha, scale, a.lse, a.dX, a.acc_dx, a.delta);
+                         a.cv, a.k, a.T, alpha, scale, a.lse, tw ? 1 : 0, a.dX, a.acc_dx,
+                         a.delta);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
       prof_begin(prof, "sa_bwdp_f32", st);
       hipLaunchKernelGGL(sa_bwdp_f32<D>, dim3(a.Gb, a.bnchunks), dim3(256), 0, st, a.offsets, a.B,
                          (const float*)a.X, (const float*)a.P, a.pstride, (const float*)a.Gq,
-                         a.cv, a.k, a.T, a.Gb, alpha, a.lse, a.delta, a.dpp);
+                         a.cv, a.k, a.T, a.Gb, alpha, a.lse, a.delta, tw ? 1 : 0, a.dpp);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;

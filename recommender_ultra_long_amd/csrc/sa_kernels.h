@@ -39,7 +39,8 @@ struct Plan {
   // forward workspace layout (byte offsets)
   size_t off_status, off_lse, off_lse2, off_part, off_pmass, off_pl, off_tlse, fwd_bytes;
   // backward workspace layout (byte offsets)
-  size_t off_G, off_cv, off_cvs, off_Pq, off_delta, off_dpp, off_blse, off_blse2, bwd_bytes;
+  size_t off_G, off_cv, off_cvs, off_Pq, off_delta, off_dpp, off_blse, off_blse2, off_tlse2,
+      bwd_bytes;
 };
 
 // Fills the plan; returns false for an unsupported problem.
@@ -93,6 +94,8 @@ struct BwdArgs {
   int64_t bslots;
   int mass_norm;
   int recompute_lse;
+  int tokwise;         // token-wise normalisation: lse is [B, k] and S is required
+  float* tlse2;        // [B, kp] token-wise: log2-unit lse per prototype (bf16 path)
 };
 
 // Optional per-kernel timing: when ev is non-null, the launchers record

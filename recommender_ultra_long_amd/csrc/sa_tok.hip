@@ -183,12 +183,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_tok_fwd_bf16(
       bf16x8 abf[PT][2];
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
+        if (nr < TILE) {   // the last tile of a piece: rows past its end weigh 0
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (crow(i, h) >= nr) z[pt][i] = -INFINITY;
+        }
         float tm = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (crow(i, h) >= nr) z[pt][i] = -INFINITY;
-          tm = fmaxf(tm, z[pt][i]);
-        }
+        for (int i = 0; i < 16; ++i) tm = fmaxf(tm, z[pt][i]);
         tm = fmaxf(tm, shfl_xor32(tm));            // both halves of the prototype
         const bool need = tm > mrun[pt] + tau_raw;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -345,8 +347,11 @@ __global__ __launch_bounds__(256) void sa_tok_fwd_f32(const int64_t* __restrict_
 }
 
 // ----------------------------------------------------------------------------
-// grid = (B, ceil(k d / 1024)); block 256; thread -> 4 consecutive elements
-// of S[u] (one prototype).  Pieces of user u are slots s0 + u .. s1 + u.
+// grid = (B, ceil(k d / 256)); block 256 = 4 waves; lane -> 4 consecutive
+// elements of S[u] (one prototype).  Pieces of user u are slots s0 + u ..
+// s1 + u.  Every wave finds the maximum M over the pieces; wave w then adds
+// pieces w, w + 4, ... (eight loads in flight) and the four wave sums are
+// added in wave order, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void sa_tok_reduce(const int64_t* __restrict__ offsets, int B,
                                                      int k, int d, int64_t T, int G, float scale,
                                                      float alpha, const float* __restrict__ part,
@@ -354,33 +359,58 @@ __global__ __launch_bounds__(256) void sa_tok_reduce(const int64_t* __restrict__
                                                      const float* __restrict__ pl,
                                                      float* __restrict__ S, float* __restrict__ lse,
                                                      uint32_t* __restrict__ status) {
+  __shared__ f32x4 red[4][64];
+  __shared__ float redl[4][64];
   const int u = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (blockIdx.y == 0 && u == 0) check_offsets_block(offsets, B, T, status, kStatusOk, kStatusBadOffsets);
   const int64_t kd = (int64_t)k * d;
-  const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
-  if (e >= kd) return;
-  const int j = (int)(e / d);
+  const int64_t e = ((int64_t)blockIdx.y * 64 + lane) * 4;
+  const bool live = e < kd;
+  const int j = live ? (int)(e / d) : 0;
   const int64_t lo = clamp64(uload64(offsets + u), 0, T);
   const int64_t hi = clamp64(uload64(offsets + u + 1), lo, T);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float out_lse = -INFINITY;
-  if (hi > lo) {
+  float Ls = 0.f, M = -INFINITY;
+  if (hi > lo && live) {
     const int s0 = seg_of(T, G, lo), s1 = seg_of(T, G, hi - 1);
+    const int n = s1 - s0 + 1;
     const int64_t b0 = (int64_t)s0 + u;
-    float M = -INFINITY;
-    for (int q = 0; q <= s1 - s0; ++q) M = fmaxf(M, pm[(b0 + q) * k + j]);
-    float Ls = 0.f;
-    for (int q = 0; q <= s1 - s0; ++q) {
-      const int64_t sl = b0 + q;
-      const float f = exp2_fast((pm[sl * k + j] - M) * alpha);
-      Ls = fmaf(pl[sl * k + j], f, Ls);
-      acc += *(const f32x4*)(part + sl * kd + e) * f;
+    for (int q = 0; q < n; ++q) M = fmaxf(M, pm[(b0 + q) * k + j]);
+    int q = wave;
+    for (; q + 28 < n; q += 32) {
+      f32x4 v[8];
+      float f[8], lv[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int64_t sl = b0 + q + 4 * r;
+        v[r] = *(const f32x4*)(part + sl * kd + e);
+        f[r] = pm[sl * k + j];
+        lv[r] = pl[sl * k + j];
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float w = exp2_fast((f[r] - M) * alpha);
+        acc += v[r] * w;
+        Ls = fmaf(lv[r], w, Ls);
+      }
     }
-    acc = acc * (1.0f / Ls);
-    out_lse = M * scale + __logf(Ls);
+    for (; q < n; q += 4) {
+      const int64_t sl = b0 + q;
+      const float w = exp2_fast((pm[sl * k + j] - M) * alpha);
+      acc += *(const f32x4*)(part + sl * kd + e) * w;
+      Ls = fmaf(pl[sl * k + j], w, Ls);
+    }
   }
-  *(f32x4*)(S + (int64_t)u * kd + e) = acc;
-  if (e % d == 0) lse[(int64_t)u * k + j] = out_lse;
+  red[wave][lane] = acc;
+  redl[wave][lane] = Ls;
+  __syncthreads();
+  if (wave != 0 || !live) return;
+  acc = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+  Ls = ((redl[0][lane] + redl[1][lane]) + redl[2][lane]) + redl[3][lane];
+  const bool any = hi > lo;
+  *(f32x4*)(S + (int64_t)u * kd + e) = any ? acc * (1.0f / Ls) : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (e % d == 0) lse[(int64_t)u * k + j] = any ? M * scale + __logf(Ls) : -INFINITY;
 }
 
 // ----------------------------------------------------------------------------
@@ -412,7 +442,7 @@ static hipError_t tok_fwd_t(const FwdArgs& a, int dtype, hipStream_t st, Prof* p
   }
   const int64_t kd = (int64_t)a.k * a.d;
   prof_begin(prof, "sa_tok_reduce", st);
-  hipLaunchKernelGGL(sa_tok_reduce, dim3(a.B, (unsigned)((kd + 1023) / 1024)), dim3(256), 0, st,
+  hipLaunchKernelGGL(sa_tok_reduce, dim3(a.B, (unsigned)((kd + 255) / 256)), dim3(256), 0, st,
                      a.offsets, a.B, a.k, a.d, a.T, a.G, scale, alpha, a.part, pm, pl, a.S, a.lse,
                      a.status);
   const hipError_t e = hipGetLastError();

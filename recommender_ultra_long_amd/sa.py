@@ -263,6 +263,29 @@ def tokenwise_forward(offsets, X, P, S=None, lse=None, workspace=None, stream=No
     return S, lse
 
 
+def tokenwise_backward(offsets, X, P, dS, S, lse, dX=None, dP=None, workspace=None, stream=None):
+    """Calls sa_backward with SA_FLAG_TOKEN_WISE, given the token-wise
+    forward's S [B, k, d] and lse [B, k].  Returns (dX [T, d], dP [k, d])."""
+    lib = load()
+    dev = P.device
+    off = _device_offsets(offsets, dev)
+    B = off.numel() - 1
+    T, d = X.shape
+    k = P.shape[0]
+    pr = make_problem(B, k, d, T, X.dtype, token_wise=True)
+    if dX is None:
+        dX = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if dP is None:
+        dP = torch.empty((k, d), dtype=torch.float32, device=dev)
+    ws = _workspace(workspace_size(pr, SA_OP_BACKWARD), dev, workspace)
+    st = lib.sa_backward(ctypes.byref(pr), _ptr(off), _ptr(X), _ptr(P), _ptr(dS), _ptr(lse), _ptr(S),
+                         None, _ptr(dX), _ptr(dP), _ptr(ws),
+                         ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_backward (token-wise)")
+    return dX, dP
+
+
 def sa_backward(offsets, X, P, dS, lse=None, S=None, mass=None, mass_norm=False, dX=None,
                 dP=None, workspace=None, stream=None, timer=None):
     """Calls sa_backward.  Returns (dX [T, d] f32, dP f32 shaped like P:

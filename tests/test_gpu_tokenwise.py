@@ -1,13 +1,14 @@
 """GPU parity of the token-wise normalised sketch (SA_FLAG_TOKEN_WISE, the
 vanilla-attention baseline of Table 1; SequenceO1 reading notes, sections 3.5
 and 7.1) against the float64 oracle (oracle/tokenwise.py): max|gpu - ref| /
-max|ref| per user for S, <= 1e-4 (fp32) and <= 2e-2 (bf16); lse absolute."""
+max|ref| per user for S and dX, over the tensor for dP, <= 1e-4 (fp32) and
+<= 2e-2 (bf16); lse absolute."""
 
 import numpy as np
 import pytest
 import torch
 
-from oracle.tokenwise import tokenwise_forward_ref
+from oracle.tokenwise import tokenwise_backward_ref, tokenwise_forward_ref
 from recommender_ultra_long_amd import sa, synth
 from sa_testutil import TOL_BF16, TOL_F32, TOL_LSE_ABS, rel_err, say
 
@@ -60,3 +61,40 @@ def test_tokenwise_long_user_many_segments():
     S, lse = sa.tokenwise_forward(torch.as_tensor(prob.offsets, device="cuda"), prob.X, prob.P)
     torch.cuda.synchronize()
     _check(prob, S, lse, TOL_BF16)
+
+
+def _check_backward(prob, dS, dX, dP, tol):
+    X64, P64 = synth.to_f64(prob.X), synth.to_f64(prob.P)
+    dXr, dPr = tokenwise_backward_ref(prob.offsets, X64, P64, synth.to_f64(dS))
+    e = rel_err(dP.cpu().numpy(), dPr)
+    assert e <= tol, f"dP rel err {e:.3e}"
+    for u in range(len(prob.offsets) - 1):
+        lo, hi = int(prob.offsets[u]), int(prob.offsets[u + 1])
+        if hi > lo:
+            e = rel_err(dX[lo:hi].cpu().numpy(), dXr[lo:hi])
+            assert e <= tol, f"user {u}: dX rel err {e:.3e}"
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("k", [1, 100, 300])
+def test_tokenwise_backward(dtype, tol, d, k):
+    lengths = [0, 1, 31, 33, 700, 0, 2500, 5]
+    say(f"case tokenwise backward dtype={dtype} d={d} k={k}")
+    prob = synth.make_inputs(lengths, k, d, dtype, device="cuda", seed=k + d, wid=530, with_dS=True)
+    off = torch.as_tensor(prob.offsets, device="cuda")
+    S, lse = sa.tokenwise_forward(off, prob.X, prob.P)
+    dX, dP = sa.tokenwise_backward(off, prob.X, prob.P, prob.dS, S, lse)
+    torch.cuda.synchronize()
+    _check_backward(prob, prob.dS, dX, dP, tol)
+
+
+def test_tokenwise_backward_long_user():
+    say("case tokenwise backward 100k user")
+    prob = synth.make_inputs([100000, 3000], 1024, 128, "bf16", device="cuda", seed=2, wid=540,
+                             with_dS=True)
+    off = torch.as_tensor(prob.offsets, device="cuda")
+    S, lse = sa.tokenwise_forward(off, prob.X, prob.P)
+    dX, dP = sa.tokenwise_backward(off, prob.X, prob.P, prob.dS, S, lse)
+    torch.cuda.synchronize()
+    _check_backward(prob, prob.dS, dX, dP, TOL_BF16)
