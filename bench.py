@@ -282,6 +282,40 @@ def _block_timing(sa, synth, timed, dev, n_layers=2):
     return res
 
 
+def _action_timing(sa, timed, dev, T=1781264, d=128, n_types=8, T_bwd=100000):
+    """The action-side SwiGLU fusion of Eq. 20 (x = e + FFN_SwiGLU([e; a]),
+    hidden width 2d): the fused matrix-core forward over the 32-user batch's
+    1,781,264 events (bf16 item embeddings, 8 action types), and the fp32
+    backward over 100,000 events.  Not part of the step."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(13)
+    rn = lambda *shape, s=1.0: torch.randn(shape, generator=g, device=dev) * s
+    e = rn(T, d).to(torch.bfloat16)
+    types = torch.randint(0, n_types, (T,), generator=g, device=dev, dtype=torch.int32)
+    A = rn(n_types, d, s=0.7)
+    W1, W3 = rn(2 * d, 2 * d, s=(2 * d) ** -0.5), rn(2 * d, 2 * d, s=(2 * d) ** -0.5)
+    W2 = rn(2 * d, d, s=(2 * d) ** -0.5)
+    x = torch.empty_like(e)
+    ws = sa._action_ws(d, e.dtype, T, n_types, sa.SA_OP_FORWARD, dev, None)
+    fwd = lambda: sa.action_fusion_forward(e, types, A, W1, W3, W2, x=x, workspace=ws)
+    fwd()
+    ms = timed(fwd, 5)
+    flop = 12.0 * d * d * T            # per event: e W1e, e W3e (2 * 2 d^2 each), G W2 (4 d^2)
+    res = {"forward_events": T, "forward_ms": round(ms, 4),
+           "forward_tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+           "forward_frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del ws
+    eb, tb, dx = e[:T_bwd], types[:T_bwd], rn(T_bwd, d)
+    wsb = sa._action_ws(d, e.dtype, T_bwd, n_types, sa.SA_OP_BACKWARD, dev, None)
+    bwd = lambda: sa.action_fusion_backward(eb, tb, A, W1, W3, W2, dx, workspace=wsb)
+    bwd()
+    res["backward_events"] = T_bwd
+    res["backward_ms"] = round(timed(bwd, 3), 4)
+    del e, x, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = _parse()
     if args.parse_traffic:
@@ -476,6 +510,7 @@ def main():
     if not args.no_per_user:
         out["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
         out["block"] = _block_timing(sa, synth, timed, dev)
+        out["action_fusion"] = _action_timing(sa, timed, dev)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

@@ -319,6 +319,37 @@ sa_status sa_block_backward(const sa_problem* problem, int n_layers, const int64
                             const sa_block_layer_grad* grads, void* ws, size_t ws_bytes,
                             void* stream);
 
+/*
+ * Action-side SwiGLU fusion (SequenceO1 reading notes, section 3.6,
+ * Eq. (20)): the history rows the sketch consumes,
+ *     x_i = e_i + (silu(v_i W1) * (v_i W3)) W2,   v_i = [e_i; A[t_i]],
+ * from item embeddings e (the history's dtype) and action types t_i that
+ * index an action table A (float [n_types, d]).  W1, W3: float [2d, 2d]
+ * (rows 0 .. d-1 act on e, rows d .. 2d-1 on the action row), W2: float
+ * [2d, d]; hidden width 2d, no biases.
+ *
+ *  d       : 32, 64 or 128;  T: events, 0 <= T <= 2^30;  1 <= n_types <= 16.
+ *  dtype   : of e and x.  SA_BF16 runs the fused matrix-core kernel (bf16
+ *            products, fp32 accumulation); SA_F32 is fp32 throughout.
+ *  types   : int32 [T] device (values outside [0, n_types) are clamped).
+ *  x       : [T, d] (dtype) device, written; the sketch's X.
+ *  ws      : sa_action_fusion_workspace_size(d, dtype, T, n_types, op) bytes.
+ * Backward: given dx = dL/dx (float [T, d], e.g. sa_backward's dX), writes
+ * de (float [T, d]), dA (float [n_types, d]), dW1, dW3 (float [2d, 2d]) and
+ * dW2 (float [2d, d]), all overwritten; the weight and table gradients sum
+ * over events in a fixed order.  Errors as for the fold.
+ */
+size_t sa_action_fusion_workspace_size(int d, sa_dtype dtype, int64_t T, int n_types, int op);
+sa_status sa_action_fusion_forward(int d, sa_dtype dtype, int64_t T, int n_types, const void* e,
+                                   const int32_t* types, const float* A, const float* W1,
+                                   const float* W3, const float* W2, void* x, void* ws,
+                                   size_t ws_bytes, void* stream);
+sa_status sa_action_fusion_backward(int d, sa_dtype dtype, int64_t T, int n_types, const void* e,
+                                    const int32_t* types, const float* A, const float* W1,
+                                    const float* W3, const float* W2, const float* dx, float* de,
+                                    float* dA, float* dW1, float* dW3, float* dW2, void* ws,
+                                    size_t ws_bytes, void* stream);
+
 /* Waits for `stream`, then reports whether a kernel of the last call that
  * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS) or not
  * (SA_OK).  SA_ERR_HIP if the wait or the read fails. */

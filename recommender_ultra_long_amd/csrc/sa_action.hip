@@ -1,0 +1,308 @@
+// sa_action.hip — the action-side SwiGLU fusion that builds the history rows
+// (SequenceO1 reading notes, section 3.6, Eq. (20)):
+//     x_i = e_i + (silu(v_i W1) * (v_i W3)) W2,   v_i = [e_i; a_{t_i}],
+// e_i the item embedding, a_t row t of the action table A (one row per
+// action type), W1, W3 in R^{2d x 2d}, W2 in R^{2d x d} (hidden width H = 2d).
+//
+// The action half of the first products depends only on the type, so
+//     v W1 = e W1e + T1[t],   T1 = A W1a   (W1 = [W1e; W1a]),
+// and the per-type rows T1, T3 (n_types x H, computed once per call) replace
+// the second half of the product: each event costs 12 d^2 flops instead of 20.
+//
+// sa_action_prep:   W1e^T, W3e^T, W2^T in bf16 (matrix-core operands) and
+//                   T1, T3 in fp32.
+// sa_action_fwd<D>: persistent workgroups over 32-event tiles, 4 waves, all
+//                   products on the matrix cores (bf16 in, fp32 accumulate),
+//                   computed transposed so that each product's result feeds
+//                   the next without a relayout:
+//                     U^T = W1e^T e^T   (weights as A operands, kept in
+//                                        registers; events as B operands)
+//                     G   = silu(U1^T + T1) * (U3^T + T3)   -> LDS [event][H]
+//                     x^T = W2^T G^T    (W2^T from LDS, G^T read back as
+//                                        B operands), + e, stored in the
+//                                        history's dtype.
+//                   Wave w computes hidden rows [w H/4, (w+1) H/4) of U and
+//                   output rows [32 w, 32 w + 32) of x.
+#include "sa_device.h"
+#include "sa_kernels.h"
+
+namespace sa {
+
+constexpr int kActionMaxTypes = 16;
+
+// Block b < nw: element i = b 256 + t of the transposed bf16 weights;
+// blocks from nw: T1 / T3 entries.
+//   W1eT[h][c] = W1[c][h], W3eT likewise (c < D, h < H); W2T[o][h] = W2[h][o];
+//   T1[t][h] = sum_c A[t][c] W1[D + c][h], T3 likewise.
+template <int D>
+__global__ __launch_bounds__(256) void sa_action_prep(const float* __restrict__ A, int n_types,
+                                                      const float* __restrict__ W1,
+                                                      const float* __restrict__ W3,
+                                                      const float* __restrict__ W2,
+                                                      bf16* __restrict__ W1eT, bf16* __restrict__ W3eT,
+                                                      bf16* __restrict__ W2T, float* __restrict__ T1,
+                                                      float* __restrict__ T3, int nw) {
+  constexpr int H = 2 * D;
+  if ((int)blockIdx.x < nw) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < H * D) {
+      const int h = i / D, c = i % D;            // W1eT / W3eT entry (h, c)
+      W1eT[i] = (bf16)W1[c * H + h];
+      W3eT[i] = (bf16)W3[c * H + h];
+      const int o = i / H, hh = i % H;           // W2T entry (o, hh)
+      W2T[i] = (bf16)W2[hh * D + o];
+    }
+    return;
+  }
+  const int i = (blockIdx.x - nw) * 256 + threadIdx.x;
+  if (i >= n_types * H) return;
+  const int t = i / H, h = i % H;
+  float s1 = 0.f, s3 = 0.f;
+  for (int c = 0; c < D; ++c) {
+    const float a = A[t * D + c];
+    s1 = fmaf(a, W1[(D + c) * H + h], s1);
+    s3 = fmaf(a, W3[(D + c) * H + h], s3);
+  }
+  T1[i] = s1;
+  T3[i] = s3;
+}
+
+template <typename ET>
+__device__ __forceinline__ bf16x8 load8_bf16(const ET* p) {
+  if constexpr (sizeof(ET) == 2) {
+    return *(const bf16x8*)p;
+  } else {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+    bf16x8 r;
+    r[0] = (bf16)a[0]; r[1] = (bf16)a[1]; r[2] = (bf16)a[2]; r[3] = (bf16)a[3];
+    r[4] = (bf16)b[0]; r[5] = (bf16)b[1]; r[6] = (bf16)b[2]; r[7] = (bf16)b[3];
+    return r;
+  }
+}
+
+// grid: persistent, ntiles = ceil(T / 32) tiles of 32 events; block 256.
+template <int D, typename ET>
+__global__ __launch_bounds__(256, 1) void sa_action_fwd(const ET* __restrict__ e,
+                                                        const int32_t* __restrict__ types,
+                                                        int n_types, int64_t T,
+                                                        const bf16* __restrict__ W1eT,
+                                                        const bf16* __restrict__ W3eT,
+                                                        const bf16* __restrict__ W2T,
+                                                        const float* __restrict__ T1,
+                                                        const float* __restrict__ T3,
+                                                        ET* __restrict__ x) {
+  constexpr int H = 2 * D;
+  constexpr int KS = D / 16;               // K steps of the first products (over d)
+  constexpr int KH = H / 16;               // K steps of the second product (over H)
+  constexpr int MT = H / 32;               // 32-row hidden tiles (2, 4, 8)
+  constexpr int NW = 4;
+  constexpr int TPW = MT / NW > 0 ? MT / NW : 1;   // hidden tiles per wave
+  constexpr int OT = D / 32;               // 32-row output tiles (1, 2, 4)
+  constexpr int GROW = H + 8;              // bf16 per LDS row of G and W2^T (16-byte pad:
+                                           // rows of 32 lanes fall on distinct banks)
+  __shared__ __attribute__((aligned(16))) bf16 sW2[D * GROW];       // W2^T [out][H]
+  __shared__ __attribute__((aligned(16))) bf16 sG[32 * GROW];       // G [event][H]
+  __shared__ float sT1[kActionMaxTypes * H], sT3[kActionMaxTypes * H];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  for (int i = tid; i < D * H / 8; i += 256) {
+    const int row = i / (H / 8), c8 = i % (H / 8);
+    *(bf16x8*)(sW2 + row * GROW + 8 * c8) = ((const bf16x8*)W2T)[i];
+  }
+  for (int i = tid; i < n_types * H; i += 256) {
+    sT1[i] = T1[i];
+    sT3[i] = T3[i];
+  }
+  // This wave's hidden tiles (waves past MT have none when H < 128).
+  const bool has_hidden = wave * TPW < MT;
+  bf16x8 w1[TPW][KS], w3[TPW][KS];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int row = (wave * TPW + m) * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      w1[m][ks] = has_hidden ? *(const bf16x8*)(W1eT + row * D + 16 * ks + 8 * h) : bf16x8{};
+      w3[m][ks] = has_hidden ? *(const bf16x8*)(W3eT + row * D + 16 * ks + 8 * h) : bf16x8{};
+    }
+  }
+  __syncthreads();
+
+  const int64_t ntiles = (T + 31) / 32;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t ev = tile * 32 + l32;            // this lane's event
+    const bool valid = ev < T;
+    const int ty = valid ? types[ev] : 0;
+    const int tcl = ty < 0 ? 0 : (ty >= n_types ? n_types - 1 : ty);   // clamped type
+    // e^T as B operands: eb[ks] = e[ev][16 ks + 8h .. +7].
+    bf16x8 eb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      eb[ks] = valid ? load8_bf16(e + ev * D + 16 * ks + 8 * h) : bf16x8{};
+    if (has_hidden) {
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        f32x16 u1 = f32x16{}, u3 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u1 = mfma32(w1[m][ks], eb[ks], u1);
+          u3 = mfma32(w3[m][ks], eb[ks], u3);
+        }
+        // Register i: hidden row hb + crow(i, h), this lane's event.
+        const int hb = (wave * TPW + m) * 32;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16 gv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g4 + r, hr = hb + crow(i, h);
+            const float a1 = u1[i] + sT1[tcl * H + hr];
+            const float a3 = u3[i] + sT3[tcl * H + hr];
+            gv[r] = (bf16)(a1 / (1.0f + __expf(-a1)) * a3);
+          }
+          bf16* dst = sG + l32 * GROW + hb + 8 * g4 + 4 * h;
+          *(uint2*)dst = *(const uint2*)gv;
+        }
+      }
+    }
+    __syncthreads();
+    // x^T rows [32 wave, +32): A = W2^T rows from LDS, B = G^T from LDS.
+    if (wave < OT) {
+      f32x16 xo = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < KH; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(sW2 + (32 * wave + l32) * GROW + 16 * kb + 8 * h);
+        const bf16x8 b = *(const bf16x8*)(sG + l32 * GROW + 16 * kb + 8 * h);
+        xo = mfma32(a, b, xo);
+      }
+      // Register i: output column 32 wave + crow(i, h) of this lane's event.
+      if (valid) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int c = 32 * wave + 8 * g4 + 4 * h;
+          ET* dst = x + ev * D + c;
+          const ET* src = e + ev * D + c;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[r] = (ET)((float)src[r] + xo[4 * g4 + r]);
+        }
+      }
+    }
+    __syncthreads();   // sG is rewritten by the next tile
+  }
+}
+
+hipError_t launch_action_fwd(int d, int dtype, int64_t T, int n_types, const void* e,
+                             const int32_t* types, const float* A, const float* W1,
+                             const float* W3, const float* W2, void* prep, void* x,
+                             hipStream_t st) {
+  if (n_types < 1 || n_types > kActionMaxTypes) return hipErrorInvalidValue;
+  const int H = 2 * d;
+  bf16* W1eT = (bf16*)prep;
+  bf16* W3eT = W1eT + H * d;
+  bf16* W2T = W3eT + H * d;
+  float* T1 = (float*)(W2T + H * d);
+  float* T3 = T1 + kActionMaxTypes * H;
+  const int nw = (H * d + 255) / 256;
+  const int nt = (n_types * H + 255) / 256;
+  const int64_t ntiles = (T + 31) / 32;
+  const unsigned grid = (unsigned)(ntiles < 512 ? (ntiles > 0 ? ntiles : 1) : 512);
+#define SA_ACTION_CASE(DD)                                                                       \
+  case DD:                                                                                      \
+    hipLaunchKernelGGL(sa_action_prep<DD>, dim3(nw + nt), dim3(256), 0, st, A, n_types, W1, W3, \
+                       W2, W1eT, W3eT, W2T, T1, T3, nw);                                         \
+    if (T <= 0) break;                                                                          \
+    if (dtype == 1)                                                                             \
+      hipLaunchKernelGGL((sa_action_fwd<DD, bf16>), dim3(grid), dim3(256), 0, st,                \
+                         (const bf16*)e, types, n_types, T, W1eT, W3eT, W2T, T1, T3, (bf16*)x);  \
+    else                                                                                        \
+      hipLaunchKernelGGL((sa_action_fwd<DD, float>), dim3(grid), dim3(256), 0, st,               \
+                         (const float*)e, types, n_types, T, W1eT, W3eT, W2T, T1, T3,            \
+                         (float*)x);                                                             \
+    break;
+  switch (d) {
+    SA_ACTION_CASE(32)
+    SA_ACTION_CASE(64)
+    SA_ACTION_CASE(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef SA_ACTION_CASE
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Backward helpers (the products themselves are sa_gemm_f32).
+// V = [e; A[t]] as fp32 rows of width 2D.
+template <typename ET>
+__global__ __launch_bounds__(256) void sa_action_build_v(const ET* __restrict__ e,
+                                                         const int32_t* __restrict__ types,
+                                                         int n_types, const float* __restrict__ A,
+                                                         int d, int64_t T, float* __restrict__ V) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * 2 * d) return;
+  const int64_t ev = i / (2 * d);
+  const int c = (int)(i % (2 * d));
+  if (c < d) {
+    V[i] = (float)e[ev * d + c];
+  } else {
+    int t = types[ev];
+    t = t < 0 ? 0 : (t >= n_types ? n_types - 1 : t);
+    V[i] = A[t * d + (c - d)];
+  }
+}
+
+// de = dx + dV[:, :d]; and this block's per-type sums of dV[:, d:] over its
+// events (in event order), part[(blk n_types + t) d + c].  Thread c < d of a
+// block owns column c.
+__global__ __launch_bounds__(256) void sa_action_dedA(const float* __restrict__ dx,
+                                                      const float* __restrict__ dV,
+                                                      const int32_t* __restrict__ types,
+                                                      int n_types, int d, int64_t T, int64_t epb,
+                                                      float* __restrict__ de,
+                                                      float* __restrict__ part) {
+  __shared__ float acc[kActionMaxTypes * 128];
+  const int c = threadIdx.x;
+  const int64_t e0 = (int64_t)blockIdx.x * epb;
+  const int64_t e1 = e0 + epb < T ? e0 + epb : T;
+  if (c < d)
+    for (int t = 0; t < n_types; ++t) acc[t * d + c] = 0.f;
+  if (c < d) {
+    for (int64_t ev = e0; ev < e1; ++ev) {
+      de[ev * d + c] = dx[ev * d + c] + dV[ev * 2 * d + c];
+      int t = types[ev];
+      t = t < 0 ? 0 : (t >= n_types ? n_types - 1 : t);
+      acc[t * d + c] += dV[ev * 2 * d + d + c];
+    }
+    for (int t = 0; t < n_types; ++t)
+      part[((int64_t)blockIdx.x * n_types + t) * d + c] = acc[t * d + c];
+  }
+}
+
+hipError_t launch_action_build_v(int d, int dtype, int64_t T, int n_types, const void* e,
+                                 const int32_t* types, const float* A, float* V, hipStream_t st) {
+  const int64_t n = T * 2 * d;
+  if (n <= 0) return hipSuccess;
+  const unsigned nb = (unsigned)((n + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(sa_action_build_v<bf16>, dim3(nb), dim3(256), 0, st, (const bf16*)e, types,
+                       n_types, A, d, T, V);
+  else
+    hipLaunchKernelGGL(sa_action_build_v<float>, dim3(nb), dim3(256), 0, st, (const float*)e,
+                       types, n_types, A, d, T, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_action_dedA(int d, int64_t T, int n_types, const float* dx, const float* dV,
+                              const int32_t* types, float* de, float* part, int nblk,
+                              hipStream_t st) {
+  if (n_types < 1 || n_types > kActionMaxTypes || d > 128) return hipErrorInvalidValue;
+  const int64_t epb = (T + nblk - 1) / nblk;
+  hipLaunchKernelGGL(sa_action_dedA, dim3(nblk), dim3(256), 0, st, dx, dV, types, n_types, d, T,
+                     epb > 0 ? epb : 1, de, part);
+  return hipGetLastError();
+}
+
+size_t action_prep_bytes(int d) {
+  const size_t H = 2 * (size_t)d;
+  return 3 * H * d * 2 + 2 * (size_t)kActionMaxTypes * H * 4;
+}
+
+}  // namespace sa

@@ -153,6 +153,19 @@ hipError_t launch_swiglu_fwd(const float* U1, const float* U3, int64_t n, float*
 hipError_t launch_swiglu_bwd(const float* dG, const float* U1, const float* U3, int64_t n,
                              float* dU1, float* dU3, hipStream_t st);
 
+// Action-side SwiGLU fusion (sa_action.hip).
+constexpr int kActionTypesMax = 16;
+hipError_t launch_action_fwd(int d, int dtype, int64_t T, int n_types, const void* e,
+                             const int32_t* types, const float* A, const float* W1,
+                             const float* W3, const float* W2, void* prep, void* x,
+                             hipStream_t st);
+size_t action_prep_bytes(int d);
+hipError_t launch_action_build_v(int d, int dtype, int64_t T, int n_types, const void* e,
+                                 const int32_t* types, const float* A, float* V, hipStream_t st);
+hipError_t launch_action_dedA(int d, int64_t T, int n_types, const float* dx, const float* dV,
+                              const int32_t* types, float* de, float* part, int nblk,
+                              hipStream_t st);
+
 // Argument blocks of the sketch kernels for a plan and a workspace (sa_api.cpp).
 FwdArgs fwd_args(const Plan& p, char* ws, const int64_t* offsets, const void* X, const void* P,
                  int64_t pstride, float* S, float* lse, float* mass);

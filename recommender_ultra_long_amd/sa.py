@@ -43,7 +43,8 @@ EXPORTED = ("sa_version", "sa_status_string", "sa_validate", "sa_workspace_size"
             "sa_forward", "sa_backward", "sa_forward_profiled", "sa_backward_profiled",
             "sa_get_device_status", "sa_fold_workspace_size", "sa_fold_prototypes",
             "sa_fold_prototypes_backward", "sa_block_workspace_size", "sa_block_forward",
-            "sa_block_backward")
+            "sa_block_backward", "sa_action_fusion_workspace_size", "sa_action_fusion_forward",
+            "sa_action_fusion_backward")
 
 # Parameter names of one layer of the stacked block, in sa_block_layer order.
 BLOCK_LAYER_KEYS = ("Wq", "Wk", "ln1_g", "ln1_b", "W1", "W3", "W2", "ln2_g", "ln2_b")
@@ -121,6 +122,13 @@ def load():
     lib.sa_block_backward.restype = i32
     lib.sa_block_backward.argtypes = [pp, i32, vp, vp, vp, ctypes.POINTER(SaBlockLayer), vp, vp, vp,
                                       ctypes.POINTER(SaBlockLayer), vp, sz, vp]
+    i64 = ctypes.c_int64
+    lib.sa_action_fusion_workspace_size.restype = sz
+    lib.sa_action_fusion_workspace_size.argtypes = [i32, i32, i64, i32, i32]
+    lib.sa_action_fusion_forward.restype = i32
+    lib.sa_action_fusion_forward.argtypes = [i32, i32, i64, i32] + [vp] * 7 + [vp, sz, vp]
+    lib.sa_action_fusion_backward.restype = i32
+    lib.sa_action_fusion_backward.argtypes = [i32, i32, i64, i32] + [vp] * 12 + [vp, sz, vp]
     _lib = lib
     return lib
 
@@ -420,6 +428,52 @@ def block_backward(offsets, X, P0, layers, dout, workspace, dX=None, dP0=None, g
     if st != SA_OK:
         raise SAError(st, "sa_block_backward")
     return dX, dP0, grads
+
+
+def _action_ws(d, dtype, T, n_types, op, device, workspace):
+    n = int(load().sa_action_fusion_workspace_size(int(d), _dtype_code(dtype), int(T), int(n_types),
+                                                   int(op)))
+    return _workspace(n, device, workspace)
+
+
+def action_fusion_forward(e, types, A, W1, W3, W2, x=None, workspace=None, stream=None):
+    """Calls sa_action_fusion_forward: x = e + SwiGLU([e; A[types]]) (Eq. 20).
+    e [T, d] f32 or bf16, types int32 [T], A [n_types, d], W1, W3 [2d, 2d],
+    W2 [2d, d] f32.  Returns x [T, d] in e's dtype."""
+    lib = load()
+    T, d = e.shape
+    n_types = A.shape[0]
+    if x is None:
+        x = torch.empty_like(e)
+    ws = _action_ws(d, e.dtype, T, n_types, SA_OP_FORWARD, e.device, workspace)
+    st = lib.sa_action_fusion_forward(int(d), _dtype_code(e.dtype), int(T), int(n_types), _ptr(e),
+                                      _ptr(types), _ptr(A), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(x),
+                                      _ptr(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
+                                      _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_action_fusion_forward")
+    return x
+
+
+def action_fusion_backward(e, types, A, W1, W3, W2, dx, workspace=None, stream=None):
+    """Calls sa_action_fusion_backward.  Returns (de [T, d], dA, dW1, dW3,
+    dW2), all f32."""
+    lib = load()
+    T, d = e.shape
+    n_types = A.shape[0]
+    dev = e.device
+    de = torch.empty((T, d), dtype=torch.float32, device=dev)
+    dA, dW1, dW3, dW2 = (torch.empty_like(t) for t in (A, W1, W3, W2))
+    ws = _action_ws(d, e.dtype, T, n_types, SA_OP_BACKWARD, dev, workspace)
+    st = lib.sa_action_fusion_backward(int(d), _dtype_code(e.dtype), int(T), int(n_types), _ptr(e),
+                                       _ptr(types), _ptr(A), _ptr(W1), _ptr(W3), _ptr(W2),
+                                       _ptr(dx), _ptr(de), _ptr(dA), _ptr(dW1), _ptr(dW3),
+                                       _ptr(dW2), _ptr(ws),
+                                       ctypes.c_size_t(ws.numel() * ws.element_size()),
+                                       _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_action_fusion_backward")
+    return de, dA, dW1, dW3, dW2
 
 
 def sa_get_device_status(workspace, stream=None):
