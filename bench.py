@@ -13,7 +13,7 @@ on the launch stream by the library's profiled entry points), the forward
 alone against the bf16 matrix-core peak, and the float64 CPU oracle timed on
 a bounded sample of the same input.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-per-user]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--step-only]
 """
 
 import argparse
@@ -43,10 +43,10 @@ def _parse():
     ap.add_argument("--part", choices=("all", "block"), default="all",
                     help="block: time only the stacked block on the 32-user batch and print "
                          "its JSON (for profiling the block's kernels alone)")
-    ap.add_argument("--no-per-user", action="store_true",
-                    help="skip the timings on the 32-user batch (shared vs per-user tables, "
-                         "the stacked block); profiling runs skip them so that kernel "
-                         "statistics cover the step workload only")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step only: skip the token-wise, per-user, stacked-block and "
+                         "action-fusion timings (profiling runs use this, so that the kernel "
+                         "statistics cover the step's kernels alone)")
     ap.add_argument("--profile-reps", type=int, default=None,
                     help="calls timed per kernel (default: --steps)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -94,6 +94,16 @@ def _traffic_for(kernel):
     return ent.get("hbm_bytes_per_launch")
 
 
+def _short_name(name):
+    """Kernel name without namespace, template arguments and parameters; the
+    profiler reports some instantiations mangled (_ZN2sa<len><name>...)."""
+    import re
+    m = re.match(r"_ZN2sa(\d+)(\w+)", name)
+    if m:
+        return m.group(2)[:int(m.group(1))]
+    return name.split("(")[0].replace("void ", "").split("::")[-1].split("<")[0]
+
+
 def _parse_traffic(fetch_csv, write_csv):
     """Scale the per-dispatch FETCH_SIZE / WRITE_SIZE readings (KiB) of every
     Sketch Attention kernel by the factor that maps the calibration copy's
@@ -123,7 +133,7 @@ def _parse_traffic(fetch_csv, write_csv):
     out = {"copy_bytes": COPY_BYTES,
            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     for name in fetch:
-        short = name.split("(")[0].replace("void ", "").split("::")[-1].split("<")[0]
+        short = _short_name(name)
         if not short.startswith("sa_"):
             continue
         fb = statistics.median(fetch[name]) * f_scale
@@ -316,6 +326,37 @@ def _action_timing(sa, timed, dev, T=1781264, d=128, n_types=8, T_bwd=100000):
     return res
 
 
+def _extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop):
+    """Timings beside the step (not part of it): the token-wise normalised
+    variant on the step's workload, shared vs per-user tables and the stacked
+    block on the 32-user batch, and the action-side fusion."""
+    import torch
+    ex = {}
+    # The token-wise normalised variant (the vanilla-attention baseline of
+    # Table 1) on the step's own workload: one pass forward (4 k d matrix
+    # flops per token, no statistics pass), single-stage dX pass backward.
+    Stw = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+    lsetw = torch.empty((B, k), dtype=torch.float32, device=dev)
+    prt = sa.make_problem(B, k, d, T, prob.X.dtype, token_wise=True)
+    wsf_t = torch.empty(sa.workspace_size(prt, sa.SA_OP_FORWARD), dtype=torch.uint8, device=dev)
+    wsb_t = torch.empty(sa.workspace_size(prt, sa.SA_OP_BACKWARD), dtype=torch.uint8, device=dev)
+    tw_fwd = lambda: sa.tokenwise_forward(off, prob.X, prob.P, S=Stw, lse=lsetw, workspace=wsf_t)
+    tw_bwd = lambda: sa.tokenwise_backward(off, prob.X, prob.P, prob.dS, Stw, lsetw, dX=dX, dP=dP,
+                                           workspace=wsb_t)
+    tw_fwd()
+    tw_bwd()
+    ms_tf = timed(tw_fwd, reps)
+    ms_tb = timed(tw_bwd, reps)
+    ex["token_wise"] = {
+        "forward_ms": round(ms_tf, 5), "backward_ms": round(ms_tb, 5),
+        "forward_frac_bf16_peak": round(fwd_flop / (ms_tf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(T / ((ms_tf + ms_tb) * 1e-3), 1)}
+    ex["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
+    ex["block"] = _block_timing(sa, synth, timed, dev)
+    ex["action_fusion"] = _action_timing(sa, timed, dev)
+    return ex
+
+
 def main():
     args = _parse()
     if args.parse_traffic:
@@ -488,29 +529,8 @@ def main():
         "fold_us": round(ms_fold * 1e3, 2), "fold_backward_us": round(ms_fold_bwd * 1e3, 2),
         "fold_gflops": round(fold_flop / (ms_fold * 1e-3) / 1e9, 1),
         "fold_backward_gflops": round(fold_bwd_flop / (ms_fold_bwd * 1e-3) / 1e9, 1)}
-    # The token-wise normalised variant (the vanilla-attention baseline of
-    # Table 1) on the step's own workload: one pass forward (4 k d matrix
-    # flops per token, no statistics pass), single-stage dX pass backward.
-    Stw = torch.empty((B, k, d), dtype=torch.float32, device=dev)
-    lsetw = torch.empty((B, k), dtype=torch.float32, device=dev)
-    prt = sa.make_problem(B, k, d, T, prob.X.dtype, token_wise=True)
-    wsf_t = torch.empty(sa.workspace_size(prt, sa.SA_OP_FORWARD), dtype=torch.uint8, device=dev)
-    wsb_t = torch.empty(sa.workspace_size(prt, sa.SA_OP_BACKWARD), dtype=torch.uint8, device=dev)
-    tw_fwd = lambda: sa.tokenwise_forward(off, prob.X, prob.P, S=Stw, lse=lsetw, workspace=wsf_t)
-    tw_bwd = lambda: sa.tokenwise_backward(off, prob.X, prob.P, prob.dS, Stw, lsetw, dX=dX, dP=dP,
-                                           workspace=wsb_t)
-    tw_fwd()
-    tw_bwd()
-    ms_tf = timed(tw_fwd, reps)
-    ms_tb = timed(tw_bwd, reps)
-    out["token_wise"] = {
-        "forward_ms": round(ms_tf, 5), "backward_ms": round(ms_tb, 5),
-        "forward_frac_bf16_peak": round(fwd_flop / (ms_tf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "tokens_per_s": round(T / ((ms_tf + ms_tb) * 1e-3), 1)}
-    if not args.no_per_user:
-        out["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
-        out["block"] = _block_timing(sa, synth, timed, dev)
-        out["action_fusion"] = _action_timing(sa, timed, dev)
+    if not args.step_only:
+        out.update(_extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop))
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
