@@ -40,7 +40,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=("all", "block"), default="all",
+    ap.add_argument("--part", choices=("all", "block", "stca"), default="all",
                     help="block: time only the stacked block on the 32-user batch and print "
                          "its JSON (for profiling the block's kernels alone)")
     ap.add_argument("--step-only", action="store_true",
@@ -326,6 +326,41 @@ def _action_timing(sa, timed, dev, T=1781264, d=128, n_types=8, T_bwd=100000):
     return res
 
 
+def _stca_timing(sa, timed, dev, D=1024, h=16):
+    """The reordered single-query STCA attention of Eq. 24 at D = 1024,
+    h = 16: over each user's k = 1024 sketch rows with 40 targets per user
+    (32 users), and over a 10,000-event recent suffix with 300 targets per
+    user (8 users).  Core flops: 4 L D per (target, head) row (the score and
+    context reductions); projections: 6 D^2 per target.  Not part of the
+    step."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(17)
+    s = D ** -0.5
+    Wq, Wk, Wv = (torch.randn(D, D, generator=g, device=dev) * s for _ in range(3))
+    res = {"D": D, "heads": h}
+    for name, B, L, R in (("sketch_rows", 32, 1024, 40), ("recent_suffix", 8, 10000, 300)):
+        x_off = torch.arange(0, B + 1, device=dev, dtype=torch.int64) * L
+        t_off = torch.arange(0, B + 1, device=dev, dtype=torch.int64) * R
+        X = torch.randn(B * L, D, generator=g, device=dev).to(torch.bfloat16)
+        Q = torch.randn(B * R, D, generator=g, device=dev)
+        o = torch.empty((B * R, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B * R, h), dtype=torch.float32, device=dev)
+        ws = torch.empty(int(sa.load().sa_stca_workspace_size(D, h, B * R)), dtype=torch.uint8,
+                         device=dev)
+        fn = lambda: sa.stca_attention(x_off, X, t_off, Q, Wq, Wk, Wv, h, o=o, lse=lse, workspace=ws)
+        fn()
+        ms = timed(fn, 5)
+        core = 4.0 * L * D * B * R * h
+        proj = 6.0 * D * D * B * R
+        res[name] = {"users": B, "rows_per_user": L, "targets_per_user": R, "ms": round(ms, 4),
+                     "targets_per_s": round(B * R / (ms * 1e-3), 1),
+                     "core_gflop": round(core / 1e9, 2), "projection_gflop": round(proj / 1e9, 2),
+                     "tflops_all": round((core + proj) / (ms * 1e-3) / 1e12, 1)}
+        del X, Q, o, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def _extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop):
     """Timings beside the step (not part of it): the token-wise normalised
     variant on the step's workload, shared vs per-user tables and the stacked
@@ -354,6 +389,7 @@ def _extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop
     ex["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
     ex["block"] = _block_timing(sa, synth, timed, dev)
     ex["action_fusion"] = _action_timing(sa, timed, dev)
+    ex["stca"] = _stca_timing(sa, timed, dev)
     return ex
 
 
@@ -371,7 +407,7 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    if args.part == "block":
+    if args.part in ("block", "stca"):
         def timed_block(fn, reps):
             st = torch.cuda.current_stream()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -382,7 +418,10 @@ def main():
             b.record(st)
             torch.cuda.synchronize()
             return a.elapsed_time(b) / reps
-        print(json.dumps({"block": _block_timing(sa, synth, timed_block, dev)}))
+        if args.part == "block":
+            print(json.dumps({"block": _block_timing(sa, synth, timed_block, dev)}))
+        else:
+            print(json.dumps({"stca": _stca_timing(sa, timed_block, dev)}))
         return
     prob = synth.make_workload(args.workload, device=dev, with_dS=True)
     w = prob.workload

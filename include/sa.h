@@ -350,6 +350,35 @@ sa_status sa_action_fusion_backward(int d, sa_dtype dtype, int64_t T, int n_type
                                     float* dA, float* dW1, float* dW3, float* dW2, void* ws,
                                     size_t ws_bytes, void* stream);
 
+/*
+ * Reordered single-query STCA attention (SequenceO1 reading notes, section
+ * 5.1, Eq. (24)-(25)): each target r has one query q_r (width D) and attends,
+ * per head j (h heads of width d_h = D / h, head j = columns j d_h ..
+ * (j+1) d_h - 1 of W_Q, W_K, W_V), over the history rows of its user:
+ *     u     = (q_r W_Q[:, j]) W_K[:, j]^T                (width D)
+ *     alpha = softmax(X_u u / sqrt(d_h)),   o[r, j] = (alpha X_u) W_V[:, j]
+ * so X W_K and X W_V are never formed; the length-dependent work is the two
+ * reductions, 4 L D flops per head and target, on the matrix cores (X and u
+ * in bf16, fp32 accumulation).  The output projection and the FFN that
+ * follow in the pages' STCA are outside this call.
+ *
+ *  B           : users; x_off: int64 [B+1] device, rows of X per user;
+ *                t_off: int64 [B+1] device, targets (rows of Q and o) per user.
+ *  D, h        : D in {256, 512, 1024}, h divides D.
+ *  X           : bf16 [L, D] device (the sketch rows after the width adapter,
+ *                or the recent suffix); Q: float [R, D]; Wq, Wk, Wv: float [D, D].
+ *  o           : float [R, D], written (heads concatenated; 0 for a user
+ *                without rows); lse: float [R, h] or NULL (log-sum-exp of the
+ *                scaled scores, -inf for a user without rows).
+ *  ws          : sa_stca_workspace_size(D, h, R) bytes.
+ * Errors as for the fold.
+ */
+size_t sa_stca_workspace_size(int D, int h, int64_t R);
+sa_status sa_stca_attention(int B, int D, int h, int64_t L, int64_t R, const int64_t* x_off,
+                            const int64_t* t_off, const void* X, const float* Q, const float* Wq,
+                            const float* Wk, const float* Wv, float* o, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* Waits for `stream`, then reports whether a kernel of the last call that
  * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS) or not
  * (SA_OK).  SA_ERR_HIP if the wait or the read fails. */

@@ -25,26 +25,31 @@ namespace sa {
 constexpr float kLnEps = 1e-5f;
 
 // ----------------------------------------------------------------------------
-// C[m][n] (+)= sum_kk A(m, kk) B(kk, n) over kk in slice z, where
+// C[m][n] (+)= sum_kk A(m, kk) B(kk, n), where
 // A(m, kk) = TA ? A[kk lda + m] : A[m lda + kk] and
 // B(kk, n) = TB ? B[n ldb + kk] : B[kk ldb + n].
-// grid = (ceil(M / 64), ceil(N / 64), slices) (rows in x: M can be B k, far
-// beyond the 65535 limit of y and z); slice z covers kk in
-// [z kc, (z + 1) kc) and writes C + z M ldc.  Thread (tx, ty) = (t % 16, t / 16)
-// owns rows 4 ty .. +3 and columns 4 tx .. +3 of the tile.
+// grid = (ceil(M / 64), ceil(N / 64), Z) (rows in x: M can be B k, far
+// beyond the 65535 limit of y and z).  With zk = 1, z is a reduction slice:
+// it covers kk in [z kc, (z + 1) kc) and writes C + z M ldc.  With zk = 0, z
+// is a batch index: the product of A + z sA and B + z sB over all of K goes to
+// C + z sC.  Thread (tx, ty) = (t % 16, t / 16) owns rows 4 ty .. +3 and
+// columns 4 tx .. +3 of the tile.
 template <bool TA, bool TB>
 __global__ __launch_bounds__(256) void sa_gemm_f32(const float* __restrict__ A, int lda,
-                                                   const float* __restrict__ B, int ldb,
-                                                   float* __restrict__ C, int ldc, int M, int N,
-                                                   int K, int kc, int accumulate) {
+                                                   int64_t sA, const float* __restrict__ B,
+                                                   int ldb, int64_t sB, float* __restrict__ C,
+                                                   int ldc, int64_t sC, int M, int N, int K,
+                                                   int kc, int zk, int accumulate) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ __align__(16) float As[2][BK][BM + 4];
   __shared__ __align__(16) float Bs[2][BK][BN + 4];
   const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-  const int k0 = blockIdx.z * kc;
-  const int k1 = k0 + kc < K ? k0 + kc : K;
-  C += (int64_t)blockIdx.z * M * ldc;
+  const int k0 = zk ? (int)blockIdx.z * kc : 0;
+  const int k1 = zk ? (k0 + kc < K ? k0 + kc : K) : K;
+  A += (int64_t)blockIdx.z * sA;
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
 
   // Element e = tid + 256 i of a tile, laid out so that consecutive threads
   // read consecutive addresses of the source.
@@ -284,6 +289,24 @@ __global__ __launch_bounds__(256) void sa_swiglu_bwd(const float* __restrict__ d
 // Launchers.
 static unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+namespace {
+
+hipError_t gemm_dispatch(bool ta, bool tb, dim3 grid, const float* A, int lda, int64_t sA,
+                         const float* B, int ldb, int64_t sB, float* C, int ldc, int64_t sC, int M,
+                         int N, int K, int kc, int zk, int accumulate, hipStream_t st) {
+#define SA_GEMM_LAUNCH(TA_, TB_)                                                                  \
+  hipLaunchKernelGGL((sa_gemm_f32<TA_, TB_>), grid, dim3(256), 0, st, A, lda, sA, B, ldb, sB, C, \
+                     ldc, sC, M, N, K, kc, zk, accumulate)
+  if (!ta && !tb) SA_GEMM_LAUNCH(false, false);
+  else if (!ta && tb) SA_GEMM_LAUNCH(false, true);
+  else if (ta && !tb) SA_GEMM_LAUNCH(true, false);
+  else SA_GEMM_LAUNCH(true, true);
+#undef SA_GEMM_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_gemm(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
                        float* C, int ldc, int M, int N, int K, int slices, int accumulate,
                        hipStream_t st) {
@@ -292,19 +315,18 @@ hipError_t launch_gemm(bool ta, bool tb, const float* A, int lda, const float* B
   int kc = (K + slices - 1) / slices;
   kc = (kc + 15) / 16 * 16;
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)slices);
-  if (!ta && !tb)
-    hipLaunchKernelGGL((sa_gemm_f32<false, false>), grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc,
-                       M, N, K, kc, accumulate);
-  else if (!ta && tb)
-    hipLaunchKernelGGL((sa_gemm_f32<false, true>), grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc,
-                       M, N, K, kc, accumulate);
-  else if (ta && !tb)
-    hipLaunchKernelGGL((sa_gemm_f32<true, false>), grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc,
-                       M, N, K, kc, accumulate);
-  else
-    hipLaunchKernelGGL((sa_gemm_f32<true, true>), grid, dim3(256), 0, st, A, lda, B, ldb, C, ldc,
-                       M, N, K, kc, accumulate);
-  return hipGetLastError();
+  return gemm_dispatch(ta, tb, grid, A, lda, 0, B, ldb, 0, C, ldc, (int64_t)M * ldc, M, N, K, kc,
+                       1, accumulate, st);
+}
+
+hipError_t launch_gemm_batched(bool ta, bool tb, const float* A, int lda, int64_t sA,
+                               const float* B, int ldb, int64_t sB, float* C, int ldc, int64_t sC,
+                               int M, int N, int K, int batch, int accumulate, hipStream_t st) {
+  if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
+  if (batch > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)batch);
+  return gemm_dispatch(ta, tb, grid, A, lda, sA, B, ldb, sB, C, ldc, sC, M, N, K, K, 0, accumulate,
+                       st);
 }
 
 hipError_t launch_sum_slices(const float* parts, int nslices, int64_t n, const float* init,

@@ -139,6 +139,10 @@ size_t fold_workspace_bytes(int k, int d);
 hipError_t launch_gemm(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
                        float* C, int ldc, int M, int N, int K, int slices, int accumulate,
                        hipStream_t st);
+// Batch z of the product: A + z sA, B + z sB -> C + z sC, over all of K.
+hipError_t launch_gemm_batched(bool ta, bool tb, const float* A, int lda, int64_t sA,
+                               const float* B, int ldb, int64_t sB, float* C, int ldc, int64_t sC,
+                               int M, int N, int K, int batch, int accumulate, hipStream_t st);
 hipError_t launch_sum_slices(const float* parts, int nslices, int64_t n, const float* init,
                              float* out, hipStream_t st);
 hipError_t launch_ln_fwd(int d, const float* a, const float* res, int64_t res_rows, int64_t R,
@@ -165,6 +169,13 @@ hipError_t launch_action_build_v(int d, int dtype, int64_t T, int n_types, const
 hipError_t launch_action_dedA(int d, int64_t T, int n_types, const float* dx, const float* dV,
                               const int32_t* types, float* de, float* part, int nblk,
                               hipStream_t st);
+
+// Reordered single-query STCA attention core (sa_stca.hip).
+// U, X: bf16 device arrays.
+hipError_t launch_stca_core(int D, int h, int B, const int64_t* x_off, const int64_t* t_off,
+                            const void* U, const void* X, int64_t rows, float* C, float* lse,
+                            hipStream_t st);
+hipError_t launch_to_bf16(const float* a, int64_t n, void* b, hipStream_t st);
 
 // Argument blocks of the sketch kernels for a plan and a workspace (sa_api.cpp).
 FwdArgs fwd_args(const Plan& p, char* ws, const int64_t* offsets, const void* X, const void* P,

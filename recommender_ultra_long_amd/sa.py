@@ -44,7 +44,7 @@ EXPORTED = ("sa_version", "sa_status_string", "sa_validate", "sa_workspace_size"
             "sa_get_device_status", "sa_fold_workspace_size", "sa_fold_prototypes",
             "sa_fold_prototypes_backward", "sa_block_workspace_size", "sa_block_forward",
             "sa_block_backward", "sa_action_fusion_workspace_size", "sa_action_fusion_forward",
-            "sa_action_fusion_backward")
+            "sa_action_fusion_backward", "sa_stca_workspace_size", "sa_stca_attention")
 
 # Parameter names of one layer of the stacked block, in sa_block_layer order.
 BLOCK_LAYER_KEYS = ("Wq", "Wk", "ln1_g", "ln1_b", "W1", "W3", "W2", "ln2_g", "ln2_b")
@@ -129,6 +129,10 @@ def load():
     lib.sa_action_fusion_forward.argtypes = [i32, i32, i64, i32] + [vp] * 7 + [vp, sz, vp]
     lib.sa_action_fusion_backward.restype = i32
     lib.sa_action_fusion_backward.argtypes = [i32, i32, i64, i32] + [vp] * 12 + [vp, sz, vp]
+    lib.sa_stca_workspace_size.restype = sz
+    lib.sa_stca_workspace_size.argtypes = [i32, i32, i64]
+    lib.sa_stca_attention.restype = i32
+    lib.sa_stca_attention.argtypes = [i32, i32, i32, i64, i64] + [vp] * 9 + [vp, sz, vp]
     _lib = lib
     return lib
 
@@ -474,6 +478,33 @@ def action_fusion_backward(e, types, A, W1, W3, W2, dx, workspace=None, stream=N
     if st != SA_OK:
         raise SAError(st, "sa_action_fusion_backward")
     return de, dA, dW1, dW3, dW2
+
+
+def stca_attention(x_off, X, t_off, Q, Wq, Wk, Wv, h, o=None, lse=None, workspace=None,
+                   stream=None):
+    """Calls sa_stca_attention (Eq. 24): per target and head, softmax over the
+    target's user's rows of X.  x_off, t_off: int64 [B+1] (device); X bf16
+    [L, D]; Q, Wq, Wk, Wv f32.  Returns (o [R, D], lse [R, h])."""
+    lib = load()
+    dev = Q.device
+    xo = _device_offsets(x_off, dev)
+    to = _device_offsets(t_off, dev)
+    B = xo.numel() - 1
+    L, D = X.shape
+    R = Q.shape[0]
+    if o is None:
+        o = torch.empty((R, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((R, h), dtype=torch.float32, device=dev)
+    n = int(lib.sa_stca_workspace_size(int(D), int(h), int(R)))
+    ws = _workspace(n, dev, workspace)
+    st = lib.sa_stca_attention(int(B), int(D), int(h), int(L), int(R), _ptr(xo), _ptr(to), _ptr(X),
+                               _ptr(Q), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(o), _ptr(lse), _ptr(ws),
+                               ctypes.c_size_t(ws.numel() * ws.element_size()),
+                               _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_stca_attention")
+    return o, lse
 
 
 def sa_get_device_status(workspace, stream=None):
