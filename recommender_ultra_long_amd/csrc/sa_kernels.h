@@ -139,6 +139,13 @@ size_t fold_workspace_bytes(int k, int d);
 hipError_t launch_gemm(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
                        float* C, int ldc, int M, int N, int K, int slices, int accumulate,
                        hipStream_t st);
+// fp32 operands rounded to bf16 on the matrix cores, fp32 accumulation
+// (sa_gemm_mx.hip): C (fp32, or bf16 when out_bf16) = A B(k, n) per batch z,
+// A row-major, B(k, n) = tb ? B[n ldb + k] : B[k ldb + n].  K % 32 == 0 and
+// 16-byte aligned rows, else hipErrorInvalidValue.
+hipError_t launch_gemm_mx(bool tb, bool out_bf16, const float* A, int lda, int64_t sA,
+                          const float* B, int ldb, int64_t sB, void* C, int ldc, int64_t sC, int M,
+                          int N, int K, int batch, hipStream_t st);
 // Batch z of the product: A + z sA, B + z sB -> C + z sC, over all of K.
 hipError_t launch_gemm_batched(bool ta, bool tb, const float* A, int lda, int64_t sA,
                                const float* B, int ldb, int64_t sB, float* C, int ldc, int64_t sC,

@@ -81,16 +81,27 @@ sa_status sa_stca_attention(int B, int D, int h, int64_t L, int64_t R, const int
   float* C = (float*)(w + p.C);
   float* l = lse ? lse : (float*)(w + p.lse);
   // q W_Q, then per head u_j = (q W_Q)[:, j] W_K[:, j]^T (row r h + j of U),
-// all heads in one batched launch.
-  SA_TRY(launch_gemm(false, false, Q, D, Wq, D, Qp, D, (int)R, D, D, 1, 0, st));
-  SA_TRY(launch_gemm_batched(false, true, Qp, D, dh, Wk, D, dh, Uf, h * D, D, (int)R, D, dh, h, 0,
-                             st));
-  SA_TRY(launch_to_bf16(Uf, rows * D, w + p.U, st));
+  // all heads in one batched launch; o[:, j] = C[r, j] W_V[:, j] likewise.
+  // Head widths that are multiples of 32 run on the matrix cores with the
+  // operands rounded to bf16 (the precision the core consumes them in); other
+  // widths use the fp32 products.
+  if (dh % 32 == 0) {
+    SA_TRY(launch_gemm_mx(false, false, Q, D, 0, Wq, D, 0, Qp, D, 0, (int)R, D, D, 1, st));
+    SA_TRY(launch_gemm_mx(true, true, Qp, D, dh, Wk, D, dh, w + p.U, h * D, D, (int)R, D, dh, h,
+                          st));
+  } else {
+    SA_TRY(launch_gemm(false, false, Q, D, Wq, D, Qp, D, (int)R, D, D, 1, 0, st));
+    SA_TRY(launch_gemm_batched(false, true, Qp, D, dh, Wk, D, dh, Uf, h * D, D, (int)R, D, dh, h,
+                               0, st));
+    SA_TRY(launch_to_bf16(Uf, rows * D, w + p.U, st));
+  }
   // The length-dependent core: C[r, j] = softmax(X_u u_j / sqrt(d_h)) X_u.
   SA_TRY(launch_stca_core(D, h, B, x_off, t_off, w + p.U, X, rows, C, l, st));
-  // o[:, j] = C[r, j] W_V[:, j], all heads in one batched launch.
-  SA_TRY(launch_gemm_batched(false, false, C, h * D, D, Wv, D, dh, o, D, dh, (int)R, dh, D, h, 0,
-                             st));
+  if (dh % 32 == 0)
+    SA_TRY(launch_gemm_mx(false, false, C, h * D, D, Wv, D, dh, o, D, dh, (int)R, dh, D, h, st));
+  else
+    SA_TRY(launch_gemm_batched(false, false, C, h * D, D, Wv, D, dh, o, D, dh, (int)R, dh, D, h,
+                               0, st));
   return SA_OK;
 }
 
