@@ -2,10 +2,11 @@
 // (SequenceO1 reading notes, section 3.6, Eq. (20)): validation, workspace
 // layout and the launch sequence.  Host code only.
 //
-// bf16 histories: the fused matrix-core kernel of sa_action.hip.  fp32
-// histories (fp32 arithmetic throughout, like the sketch's fp32 path) and
-// the backward: the fp32 products of sa_block.hip on materialised
-// intermediates.
+// bf16 histories: the fused matrix-core kernel of sa_action.hip forward; the
+// backward on materialised intermediates with its products on the matrix
+// cores (fp32 operands rounded to bf16, fp32 accumulation, sa_gemm_mx.hip).
+// fp32 histories: fp32 arithmetic throughout, like the sketch's fp32 path
+// (the fp32 products of sa_block.hip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -70,6 +71,17 @@ bool a16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
     if (e_ != hipSuccess) return SA_ERR_HIP;    \
   } while (0)
 
+// The products of the materialised path: fp32 operands rounded to bf16 on the
+// matrix cores for bf16 histories (the sketch's own precision: bf16 in, fp32
+// accumulate), fp32 on the vector ALU for fp32 histories.
+hipError_t product(int dtype, bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
+                   float* C, int ldc, int M, int N, int K, int slices, int accumulate,
+                   hipStream_t st) {
+  if (dtype == SA_BF16)
+    return launch_gemm_mx_sliced(ta, tb, A, lda, B, ldb, C, ldc, M, N, K, slices, accumulate, st);
+  return launch_gemm(ta, tb, A, lda, B, ldb, C, ldc, M, N, K, slices, accumulate, st);
+}
+
 // U1 = V W1, U3 = V W3, G = silu(U1) U3 (fp32).
 sa_status fp32_hidden(int d, int dtype, int64_t T, int n_types, const void* e,
                       const int32_t* types, const float* A, const float* W1, const float* W3,
@@ -77,8 +89,10 @@ sa_status fp32_hidden(int d, int dtype, int64_t T, int n_types, const void* e,
   const int H = 2 * d;
   float* V = (float*)(w + p.V);
   SA_TRY(launch_action_build_v(d, dtype, T, n_types, e, types, A, V, st));
-  SA_TRY(launch_gemm(false, false, V, 2 * d, W1, H, (float*)(w + p.U1), H, (int)T, H, 2 * d, 1, 0, st));
-  SA_TRY(launch_gemm(false, false, V, 2 * d, W3, H, (float*)(w + p.U3), H, (int)T, H, 2 * d, 1, 0, st));
+  SA_TRY(product(dtype, false, false, V, 2 * d, W1, H, (float*)(w + p.U1), H, (int)T, H, 2 * d, 1,
+                 0, st));
+  SA_TRY(product(dtype, false, false, V, 2 * d, W3, H, (float*)(w + p.U3), H, (int)T, H, 2 * d, 1,
+                 0, st));
   SA_TRY(launch_swiglu_fwd((const float*)(w + p.U1), (const float*)(w + p.U3), T * H,
                            (float*)(w + p.G), st));
   return SA_OK;
@@ -168,17 +182,18 @@ sa_status sa_action_fusion_backward(int d, sa_dtype dtype, int64_t T, int n_type
   float* dU1 = (float*)(w + p.dU1);
   float* dU3 = (float*)(w + p.dU3);
   float* dV = (float*)(w + p.dV);
+  const int dt = (int)dtype;
   // dG = dx W2^T; dW2 = G^T dx.
-  SA_TRY(launch_gemm(false, true, dx, d, W2, d, dG, H, (int)T, H, d, 1, 0, st));
-  SA_TRY(launch_gemm(true, false, G, H, dx, d, parts, d, H, d, (int)T, ns, 0, st));
+  SA_TRY(product(dt, false, true, dx, d, W2, d, dG, H, (int)T, H, d, 1, 0, st));
+  SA_TRY(product(dt, true, false, G, H, dx, d, parts, d, H, d, (int)T, ns, 0, st));
   SA_TRY(launch_sum_slices(parts, ns, (int64_t)H * d, nullptr, dW2, st));
   // Through the SwiGLU; dV = dU1 W1^T + dU3 W3^T; dW1 = V^T dU1, dW3 = V^T dU3.
   SA_TRY(launch_swiglu_bwd(dG, U1, U3, T * H, dU1, dU3, st));
-  SA_TRY(launch_gemm(false, true, dU1, H, W1, H, dV, 2 * d, (int)T, 2 * d, H, 1, 0, st));
-  SA_TRY(launch_gemm(false, true, dU3, H, W3, H, dV, 2 * d, (int)T, 2 * d, H, 1, 1, st));
-  SA_TRY(launch_gemm(true, false, V, 2 * d, dU1, H, parts, H, 2 * d, H, (int)T, ns, 0, st));
+  SA_TRY(product(dt, false, true, dU1, H, W1, H, dV, 2 * d, (int)T, 2 * d, H, 1, 0, st));
+  SA_TRY(product(dt, false, true, dU3, H, W3, H, dV, 2 * d, (int)T, 2 * d, H, 1, 1, st));
+  SA_TRY(product(dt, true, false, V, 2 * d, dU1, H, parts, H, 2 * d, H, (int)T, ns, 0, st));
   SA_TRY(launch_sum_slices(parts, ns, (int64_t)2 * d * H, nullptr, dW1, st));
-  SA_TRY(launch_gemm(true, false, V, 2 * d, dU3, H, parts, H, 2 * d, H, (int)T, ns, 0, st));
+  SA_TRY(product(dt, true, false, V, 2 * d, dU3, H, parts, H, 2 * d, H, (int)T, ns, 0, st));
   SA_TRY(launch_sum_slices(parts, ns, (int64_t)2 * d * H, nullptr, dW3, st));
   // de = dx + dV[:, :d]; dA[t] = sum over events of type t of dV[:, d:].
   float* dAparts = (float*)(w + p.dAparts);

@@ -1,18 +1,26 @@
 // sa_gemm_mx.hip — dense products with fp32 operands rounded to bf16 on the
-// matrix cores (fp32 accumulation): the query, key and value projections of
-// the single-query STCA attention (SequenceO1 reading notes, section 5.1,
-// Eq. (24)), whose history and query rows enter its core in bf16 anyway.
+// matrix cores (fp32 accumulation).  They serve the products around the
+// sketch whose inputs enter the matrix cores in bf16 anyway: the query, key
+// and value projections of the single-query STCA attention (SequenceO1
+// reading notes, section 5.1, Eq. (24)) and the backward of the action-side
+// SwiGLU fusion (section 3.6, Eq. (20)) on bf16 histories.
 //
-// sa_gemm_mx<TB, OBF>: C[m][n] = sum_k A[m][k] B(k, n) for batch z, with
-//   A row-major (lda), B(k, n) = TB ? B[n ldb + k] : B[k ldb + n],
-//   A + z sA, B + z sB, C + z sC; C fp32 or (OBF) bf16, row-major (ldc).
+// sa_gemm_mx<TA, TB, OBF>: C (+)= op(A) op(B) with
+//   A(m, k) = TA ? A[k lda + m] : A[m lda + k],
+//   B(k, n) = TB ? B[n ldb + k] : B[k ldb + n],
+//   C fp32, or bf16 when OBF, row-major (ldc).
+// blockIdx.z is either a batch index (zk = 0: A + z sA, B + z sB, all of K)
+// or a reduction slice (zk = 1: k in [z kc, min((z + 1) kc, K))); either way
+// the output goes to C + z sC.
 // 64 x 64 output tile per workgroup of 4 waves (2 x 2 waves of 32 x 32), K in
 // steps of 32.  The operands are staged in LDS as [row][k] bf16 (row stride 40
 // elements, so 16 lanes reading one 16-byte column of 16 rows hit distinct
-// banks); the next four K steps are in flight in registers meanwhile.
-// Requires K % 32 == 0, 16-byte aligned rows (lda, ldb multiples of 4; N a
-// multiple of 4 when TB is false) — the launcher checks and reports
-// hipErrorInvalidValue otherwise.  M and N are bounds-checked.
+// banks); four K steps are in flight in registers meanwhile.  An operand
+// stored [row][k] is loaded 8 k-values per lane and needs K % 32 == 0; one
+// stored [k][row] is loaded as pairs of k rows, 4 values each, with the rows
+// past the end of K read clamped and zeroed, so K is free there.  Rows of A
+// (columns of C) past M (N) read row (column) 0 instead: they only feed
+// outputs that are never stored, so no load is conditional.
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -20,7 +28,9 @@ namespace sa {
 
 namespace {
 
-constexpr int kMxTile = 64, kMxK = 32, kMxStride = 40;
+constexpr int kMxTile = 64, kMxK = 32, kMxStride = 40, kMxPf = 4;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 to_bf16x8(const float4 a, const float4 b) {
   bf16x8 r;
@@ -29,88 +39,117 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float4 a, const float4 b) {
   return r;
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// One operand tile (64 rows x 32 k) of an fp32 matrix, staged into LDS as
+// [row][k] bf16.  KROW: the matrix is stored [k][row] (ld between k rows);
+// otherwise [row][k] (ld between rows).  `rows` bounds the row index.
+template <bool KROW>
+struct MxOperand {
+  const float* base;   // this thread's first element (row clamped)
+  int ld;
+  int row_s, k_s;      // staging position: LDS row and first k of this thread
+  float4 r[kMxPf][2];
 
-}  // namespace
-
-template <bool TB, bool OBF>
-__global__ __launch_bounds__(256) void sa_gemm_mx(const float* __restrict__ A, int lda, int64_t sA,
-                                                  const float* __restrict__ B, int ldb, int64_t sB,
-                                                  void* __restrict__ Cv, int ldc, int64_t sC, int M,
-                                                  int N, int K) {
-  __shared__ __attribute__((aligned(16))) bf16 As[2][kMxTile * kMxStride];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][kMxTile * kMxStride];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-  const int m0 = blockIdx.x * kMxTile, n0 = blockIdx.y * kMxTile;
-  A += (int64_t)blockIdx.z * sA;
-  B += (int64_t)blockIdx.z * sB;
-
-  // Staging geometry.  A (and B when TB): thread -> row t / 4, k 8 (t % 4) ..
-  // +7.  B when !TB: thread -> k rows 2 (t / 16), +1, columns 4 (t % 16) .. +3.
-  const int ar = tid >> 2, ak = (tid & 3) * 8;
-  const bool a_ok = m0 + ar < M;
-  const float* ap = A + (int64_t)(a_ok ? m0 + ar : 0) * lda + ak;
-  const int bkp = TB ? 0 : (tid >> 4) * 2, bn = TB ? 0 : (tid & 15) * 4;
-  const bool b_ok = TB ? (n0 + ar < N) : (n0 + bn < N);
-  const float* bp = TB ? B + (int64_t)(b_ok ? n0 + ar : 0) * ldb + ak
-                       : B + (int64_t)bkp * ldb + (b_ok ? n0 + bn : 0);
-
-  // NPF K steps in flight: register stage s holds K step kt while steps
-  // kt + 1 .. kt + NPF - 1 load; LDS is double-buffered.
-  constexpr int NPF = 4;
-  float4 ra[NPF][2], rb[NPF][2];
-  // Rows of A (columns of C) past M (N) read row (column) 0 instead: they only
-  // feed outputs that are never stored, so no load is conditional.
-  auto load = [&](int s, int k0) {
-    ra[s][0] = *(const float4*)(ap + k0);
-    ra[s][1] = *(const float4*)(ap + k0 + 4);
-    if (TB) {
-      rb[s][0] = *(const float4*)(bp + k0);
-      rb[s][1] = *(const float4*)(bp + k0 + 4);
+  __device__ void init(const float* m, int ldm, int row0, int rows, int tid) {
+    ld = ldm;
+    if (KROW) {
+      k_s = (tid >> 4) * 2;
+      row_s = (tid & 15) * 4;
+      const int row = row0 + row_s < rows ? row0 + row_s : 0;
+      base = m + row;
     } else {
-      rb[s][0] = *(const float4*)(bp + (int64_t)k0 * ldb);
-      rb[s][1] = *(const float4*)(bp + (int64_t)(k0 + 1) * ldb);
+      row_s = tid >> 2;
+      k_s = (tid & 3) * 8;
+      const int row = row0 + row_s < rows ? row0 + row_s : 0;
+      base = m + (int64_t)row * ld + k_s;
     }
-  };
-  auto store = [&](int s, int buf) {
-    *(bf16x8*)&As[buf][ar * kMxStride + ak] = to_bf16x8(ra[s][0], ra[s][1]);
-    if (TB) {
-      *(bf16x8*)&Bs[buf][ar * kMxStride + ak] = to_bf16x8(rb[s][0], rb[s][1]);
+  }
+  // K step at k0 into stage s; k1 bounds k (KROW only: rows past it are 0).
+  __device__ void load(int s, int k0, int k1) {
+    if (KROW) {
+      const int ka = k0 + k_s, kb = ka + 1;
+      const int kac = ka < k1 ? ka : k1 - 1, kbc = kb < k1 ? kb : k1 - 1;
+      const float4 va = *(const float4*)(base + (int64_t)kac * ld);
+      const float4 vb = *(const float4*)(base + (int64_t)kbc * ld);
+      const float4 z = {0.f, 0.f, 0.f, 0.f};
+      r[s][0] = ka < k1 ? va : z;
+      r[s][1] = kb < k1 ? vb : z;
     } else {
-      const float x0[4] = {rb[s][0].x, rb[s][0].y, rb[s][0].z, rb[s][0].w};
-      const float x1[4] = {rb[s][1].x, rb[s][1].y, rb[s][1].z, rb[s][1].w};
+      r[s][0] = *(const float4*)(base + k0);
+      r[s][1] = *(const float4*)(base + k0 + 4);
+    }
+  }
+  __device__ void store(int s, bf16* S) const {
+    if (KROW) {
+      const float x0[4] = {r[s][0].x, r[s][0].y, r[s][0].z, r[s][0].w};
+      const float x1[4] = {r[s][1].x, r[s][1].y, r[s][1].z, r[s][1].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         bf16x2 v;
         v[0] = (bf16)x0[i];
         v[1] = (bf16)x1[i];
-        *(bf16x2*)&Bs[buf][(bn + i) * kMxStride + bkp] = v;
+        *(bf16x2*)&S[(row_s + i) * kMxStride + k_s] = v;
       }
+    } else {
+      *(bf16x8*)&S[row_s * kMxStride + k_s] = to_bf16x8(r[s][0], r[s][1]);
     }
-  };
+  }
+};
+
+}  // namespace
+
+template <bool TA, bool TB, bool OBF>
+__global__ __launch_bounds__(256) void sa_gemm_mx(const float* __restrict__ A, int lda, int64_t sA,
+                                                  const float* __restrict__ B, int ldb, int64_t sB,
+                                                  void* __restrict__ Cv, int ldc, int64_t sC, int M,
+                                                  int N, int K, int kc, int zk, int accumulate) {
+  __shared__ __attribute__((aligned(16))) bf16 As[2][kMxTile * kMxStride];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[2][kMxTile * kMxStride];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int m0 = blockIdx.x * kMxTile, n0 = blockIdx.y * kMxTile;
+  const int z = blockIdx.z;
+  int kbeg = 0, kend = K;
+  if (zk) {
+    kbeg = z * kc;
+    kend = kbeg + kc < K ? kbeg + kc : K;
+  } else {
+    A += (int64_t)z * sA;
+    B += (int64_t)z * sB;
+  }
+
+  MxOperand<TA> a;     // A stored [k][m] when TA
+  MxOperand<!TB> b;    // B stored [k][n] when !TB
+  a.init(A, lda, m0, M, tid);
+  b.init(B, ldb, n0, N, tid);
 
   f32x16 acc = f32x16{};
-  const int nk = K / kMxK;
+  const int nk = kend > kbeg ? (kend - kbeg + kMxK - 1) / kMxK : 0;
 #pragma unroll
-  for (int s = 0; s < NPF; ++s)
-    if (s < nk) load(s, s * kMxK);
-  for (int kt0 = 0; kt0 < nk; kt0 += NPF) {
+  for (int s = 0; s < kMxPf; ++s)
+    if (s < nk) {
+      a.load(s, kbeg + s * kMxK, kend);
+      b.load(s, kbeg + s * kMxK, kend);
+    }
+  for (int kt0 = 0; kt0 < nk; kt0 += kMxPf) {
 #pragma unroll
-    for (int s = 0; s < NPF; ++s) {
+    for (int s = 0; s < kMxPf; ++s) {
       const int kt = kt0 + s;
       if (kt >= nk) break;
       const int buf = kt & 1;
       // Readers of this buffer (step kt - 2) finished before the barrier of
       // step kt - 1.
-      store(s, buf);
+      a.store(s, As[buf]);
+      b.store(s, Bs[buf]);
       __syncthreads();
-      if (kt + NPF < nk) load(s, (kt + NPF) * kMxK);
+      if (kt + kMxPf < nk) {
+        a.load(s, kbeg + (kt + kMxPf) * kMxK, kend);
+        b.load(s, kbeg + (kt + kMxPf) * kMxK, kend);
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = *(const bf16x8*)&As[buf][(wm + l32) * kMxStride + 16 * ks + 8 * h];
-        const bf16x8 b = *(const bf16x8*)&Bs[buf][(wn + l32) * kMxStride + 16 * ks + 8 * h];
-        acc = mfma32(a, b, acc);
+        const bf16x8 av = *(const bf16x8*)&As[buf][(wm + l32) * kMxStride + 16 * ks + 8 * h];
+        const bf16x8 bv = *(const bf16x8*)&Bs[buf][(wn + l32) * kMxStride + 16 * ks + 8 * h];
+        acc = mfma32(av, bv, acc);
       }
     }
   }
@@ -121,36 +160,77 @@ __global__ __launch_bounds__(256) void sa_gemm_mx(const float* __restrict__ A, i
     for (int i = 0; i < 16; ++i) {
       const int m = m0 + wm + crow(i, h);
       if (m < M) {
-        const int64_t o = (int64_t)blockIdx.z * sC + (int64_t)m * ldc + n;
-        if (OBF) ((bf16*)Cv)[o] = (bf16)acc[i];
-        else ((float*)Cv)[o] = acc[i];
+        const int64_t o = (int64_t)z * sC + (int64_t)m * ldc + n;
+        if (OBF) {
+          ((bf16*)Cv)[o] = (bf16)acc[i];
+        } else {
+          float* c = (float*)Cv + o;
+          *c = accumulate ? *c + acc[i] : acc[i];
+        }
       }
     }
   }
 }
 
+namespace {
+
+hipError_t mx_dispatch(bool ta, bool tb, bool obf, dim3 grid, const float* A, int lda, int64_t sA,
+                       const float* B, int ldb, int64_t sB, void* C, int ldc, int64_t sC, int M,
+                       int N, int K, int kc, int zk, int accumulate, hipStream_t st) {
+#define SA_MX(TA_, TB_, OBF_)                                                                   \
+  hipLaunchKernelGGL((sa_gemm_mx<TA_, TB_, OBF_>), grid, dim3(256), 0, st, A, lda, sA, B, ldb, \
+                     sB, C, ldc, sC, M, N, K, kc, zk, accumulate)
+  if (obf) {
+    if (ta || !tb) return hipErrorInvalidValue;   // bf16 output: the key product only
+    SA_MX(false, true, true);
+  } else if (!ta && !tb) SA_MX(false, false, false);
+  else if (!ta && tb) SA_MX(false, true, false);
+  else if (ta && !tb) SA_MX(true, false, false);
+  else SA_MX(true, true, false);
+#undef SA_MX
+  return hipGetLastError();
+}
+
+// Operands stored [row][k] need K % 32 == 0 (per slice too); all rows must be
+// 16-byte aligned, and so must the [k][row] operands' row extents.
+bool mx_shape_ok(bool ta, bool tb, const float* A, int lda, int64_t sA, const float* B, int ldb,
+                 int64_t sB, int M, int N, int K, int kc) {
+  const bool rowk_a = !ta, rowk_b = tb;
+  if ((rowk_a || rowk_b) && (K % kMxK != 0 || kc % kMxK != 0)) return false;
+  if (ta && M % 4 != 0) return false;
+  if (!tb && N % 4 != 0) return false;
+  return lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 && sB % 4 == 0 &&
+         ((uintptr_t)A & 15u) == 0 && ((uintptr_t)B & 15u) == 0;
+}
+
+}  // namespace
+
 hipError_t launch_gemm_mx(bool tb, bool out_bf16, const float* A, int lda, int64_t sA,
                           const float* B, int ldb, int64_t sB, void* C, int ldc, int64_t sC, int M,
                           int N, int K, int batch, hipStream_t st) {
   if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
-  const bool shape_ok = K % kMxK == 0 && lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 &&
-                        sB % 4 == 0 && (tb || N % 4 == 0) && batch <= 65535 &&
-                        ((uintptr_t)A & 15u) == 0 && ((uintptr_t)B & 15u) == 0;
-  if (!shape_ok) return hipErrorInvalidValue;
+  if (batch > 65535 || !mx_shape_ok(false, tb, A, lda, sA, B, ldb, sB, M, N, K, K))
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)((M + kMxTile - 1) / kMxTile), (unsigned)((N + kMxTile - 1) / kMxTile),
                   (unsigned)batch);
-#define SA_MX(TB_, OBF_)                                                                        \
-  hipLaunchKernelGGL((sa_gemm_mx<TB_, OBF_>), grid, dim3(256), 0, st, A, lda, sA, B, ldb, sB, C, \
-                     ldc, sC, M, N, K)
-  if (tb) {
-    if (out_bf16) SA_MX(true, true);
-    else SA_MX(true, false);
-  } else {
-    if (out_bf16) SA_MX(false, true);
-    else SA_MX(false, false);
-  }
-#undef SA_MX
-  return hipGetLastError();
+  return mx_dispatch(false, tb, out_bf16, grid, A, lda, sA, B, ldb, sB, C, ldc, sC, M, N, K, K, 0, 0,
+                     st);
+}
+
+hipError_t launch_gemm_mx_sliced(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
+                                 float* C, int ldc, int M, int N, int K, int slices, int accumulate,
+                                 hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (slices < 1) slices = 1;
+  int kc = (K + slices - 1) / slices;
+  kc = (kc + kMxK - 1) / kMxK * kMxK;
+  if (kc < kMxK) kc = kMxK;
+  if (slices > 65535 || !mx_shape_ok(ta, tb, A, lda, 0, B, ldb, 0, M, N, K, slices > 1 ? kc : K))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((M + kMxTile - 1) / kMxTile), (unsigned)((N + kMxTile - 1) / kMxTile),
+                  (unsigned)slices);
+  return mx_dispatch(ta, tb, false, grid, A, lda, 0, B, ldb, 0, C, ldc, (int64_t)M * ldc, M, N, K,
+                     kc, 1, accumulate, st);
 }
 
 }  // namespace sa

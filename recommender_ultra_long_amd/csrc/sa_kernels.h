@@ -146,6 +146,12 @@ hipError_t launch_gemm(bool ta, bool tb, const float* A, int lda, const float* B
 hipError_t launch_gemm_mx(bool tb, bool out_bf16, const float* A, int lda, int64_t sA,
                           const float* B, int ldb, int64_t sB, void* C, int ldc, int64_t sC, int M,
                           int N, int K, int batch, hipStream_t st);
+// The same with A(m, k) = ta ? A[k lda + m] : A[m lda + k] and the
+// reduction split into `slices` slices written to C + z M ldc (accumulate:
+// C += instead of C =); K is free when both operands are stored [k][row].
+hipError_t launch_gemm_mx_sliced(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
+                                 float* C, int ldc, int M, int N, int K, int slices, int accumulate,
+                                 hipStream_t st);
 // Batch z of the product: A + z sA, B + z sB -> C + z sC, over all of K.
 hipError_t launch_gemm_batched(bool ta, bool tb, const float* A, int lda, int64_t sA,
                                const float* B, int ldb, int64_t sB, float* C, int ldc, int64_t sC,

@@ -48,8 +48,9 @@ def test_action_fusion_forward_backward(dtype, tol, d, T):
                                     W3.double().numpy(), W2.double().numpy(), dx.double().numpy())
     for name, a, b in zip(("de", "dA", "dW1", "dW3", "dW2"), grads, rg):
         eg = rel_err(a.cpu().numpy(), b)
-        # the backward is fp32 for both dtypes (its inputs are exact copies)
-        assert eg <= TOL_F32, f"{name} rel err {eg:.3e}"
+        # fp32 histories: fp32 throughout; bf16 histories: the backward's
+        # products take bf16 operands with fp32 accumulation
+        assert eg <= tol, f"{name} rel err {eg:.3e}"
 
 
 def test_action_fusion_one_type_equals_shared_row():
