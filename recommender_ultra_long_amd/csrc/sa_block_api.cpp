@@ -93,6 +93,17 @@ bool block_plan(const sa_problem* pr, int L, BlockPlan* bp) {
 
 bool a16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 
+// The FFN products of Eq. (16) and their gradients: fp32 operands rounded to
+// bf16 on the matrix cores when the sketch runs in bf16 (bf16 in, fp32
+// accumulate, as the sketch), fp32 on the vector ALU otherwise.
+hipError_t product(int dtype, bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
+                   float* C, int ldc, int M, int N, int K, int slices, int accumulate,
+                   hipStream_t st) {
+  if (dtype == SA_BF16)
+    return launch_gemm_mx_sliced(ta, tb, A, lda, B, ldb, C, ldc, M, N, K, slices, accumulate, st);
+  return launch_gemm(ta, tb, A, lda, B, ldb, C, ldc, M, N, K, slices, accumulate, st);
+}
+
 sa_status check_common(const sa_problem* pr, int L, const int64_t* offsets, const void* X,
                        const float* P0, const sa_block_layer* layers, void* ws) {
   const sa_status v = sa_validate(pr, nullptr);
@@ -171,10 +182,10 @@ sa_status sa_block_forward(const sa_problem* pr, int L, const int64_t* offsets, 
     SA_TRY(launch_ln_fwd(d, xh, q, q_rows, R, p.ln1_g, p.ln1_b, xbar, (float*)(w + b.mean1),
                          (float*)(w + b.rstd1), st));
     // Eq. (16): LN2(X- + FFN(X-)), FFN = (silu(X- W1) * (X- W3)) W2.
-    SA_TRY(launch_gemm(false, false, xbar, d, p.W1, 2 * d, u1, 2 * d, (int)R, 2 * d, d, 1, 0, st));
-    SA_TRY(launch_gemm(false, false, xbar, d, p.W3, 2 * d, u3, 2 * d, (int)R, 2 * d, d, 1, 0, st));
+    SA_TRY(product(dt, false, false, xbar, d, p.W1, 2 * d, u1, 2 * d, (int)R, 2 * d, d, 1, 0, st));
+    SA_TRY(product(dt, false, false, xbar, d, p.W3, 2 * d, u3, 2 * d, (int)R, 2 * d, d, 1, 0, st));
     SA_TRY(launch_swiglu_fwd(u1, u3, R * 2 * d, G, st));
-    SA_TRY(launch_gemm(false, false, G, 2 * d, p.W2, d, F, d, (int)R, d, 2 * d, 1, 0, st));
+    SA_TRY(product(dt, false, false, G, 2 * d, p.W2, d, F, d, (int)R, d, 2 * d, 1, 0, st));
     SA_TRY(launch_ln_fwd(d, xbar, F, R, R, p.ln2_g, p.ln2_b, y, (float*)(w + b.mean2),
                          (float*)(w + b.rstd2), st));
     q = y;
@@ -241,17 +252,17 @@ sa_status sa_block_backward(const sa_problem* pr, int L, const int64_t* offsets,
     SA_TRY(launch_sum_slices(lnparts + (size_t)kLnBlocks * d, kLnBlocks, d, nullptr, g.ln2_b, st));
     // FFN: dG = dF W2^T, dW2 = G^T dF (G recomputed), then the SwiGLU.
     SA_TRY(launch_swiglu_fwd(u1, u3, R * 2 * d, G, st));
-    SA_TRY(launch_gemm(false, true, dxbar, d, p.W2, d, dG, 2 * d, (int)R, 2 * d, d, 1, 0, st));
-    SA_TRY(launch_gemm(true, false, G, 2 * d, dxbar, d, wparts, d, 2 * d, d, (int)R, ns, 0, st));
+    SA_TRY(product(dt, false, true, dxbar, d, p.W2, d, dG, 2 * d, (int)R, 2 * d, d, 1, 0, st));
+    SA_TRY(product(dt, true, false, G, 2 * d, dxbar, d, wparts, d, 2 * d, d, (int)R, ns, 0, st));
     SA_TRY(launch_sum_slices(wparts, ns, (int64_t)2 * d * d, nullptr, g.W2, st));
     SA_TRY(launch_swiglu_bwd(dG, u1, u3, R * 2 * d, dU1, dU3, st));
-    SA_TRY(launch_gemm(true, false, xbar, d, dU1, 2 * d, wparts, 2 * d, d, 2 * d, (int)R, ns, 0, st));
+    SA_TRY(product(dt, true, false, xbar, d, dU1, 2 * d, wparts, 2 * d, d, 2 * d, (int)R, ns, 0, st));
     SA_TRY(launch_sum_slices(wparts, ns, (int64_t)2 * d * d, nullptr, g.W1, st));
-    SA_TRY(launch_gemm(true, false, xbar, d, dU3, 2 * d, wparts, 2 * d, d, 2 * d, (int)R, ns, 0, st));
+    SA_TRY(product(dt, true, false, xbar, d, dU3, 2 * d, wparts, 2 * d, d, 2 * d, (int)R, ns, 0, st));
     SA_TRY(launch_sum_slices(wparts, ns, (int64_t)2 * d * d, nullptr, g.W3, st));
     // dL/dX- = dF (residual) + dU1 W1^T + dU3 W3^T.
-    SA_TRY(launch_gemm(false, true, dU1, 2 * d, p.W1, 2 * d, dxbar, d, (int)R, d, 2 * d, 1, 1, st));
-    SA_TRY(launch_gemm(false, true, dU3, 2 * d, p.W3, 2 * d, dxbar, d, (int)R, d, 2 * d, 1, 1, st));
+    SA_TRY(product(dt, false, true, dU1, 2 * d, p.W1, 2 * d, dxbar, d, (int)R, d, 2 * d, 1, 1, st));
+    SA_TRY(product(dt, false, true, dU3, 2 * d, p.W3, 2 * d, dxbar, d, (int)R, d, 2 * d, 1, 1, st));
     // LN1: dr1 = dL/d(X~ + X^); dg1, db1.
     SA_TRY(launch_ln_bwd(d, dxbar, xh, q, q_rows, R, (const float*)(w + b.mean1),
                          (const float*)(w + b.rstd1), p.ln1_g, dr1, 0, lnparts, kLnBlocks, st));
