@@ -184,3 +184,45 @@ def test_fold_argument_errors_are_synchronous():
     al = vp((ctypes.addressof(buf) + 15) & ~15)
     assert lib.sa_fold_prototypes_backward(64, 64, sa.SA_F32, al, al, al, al, al, al, al, al, 16,
                                            nul) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_stca_argument_errors_are_synchronous():
+    # Reordered single-query STCA (Eq. 24): shape, pointer, alignment and
+    # workspace checks all return before any HIP call, so they run on the CPU.
+    lib = sa.load()
+    a256 = lambda v: (v + 255) // 256 * 256
+    D, h, R = 1024, 16, 40
+    want = (a256(R * D * 4) + a256(R * h * D * 4) + a256(R * h * D * 2) + a256(R * h * D * 4)
+            + a256(R * h * 4))
+    assert lib.sa_stca_workspace_size(D, h, R) == want
+    assert lib.sa_stca_workspace_size(128, 4, R) == 0          # D not in {256, 512, 1024}
+    assert lib.sa_stca_workspace_size(256, 3, R) == 0          # heads must divide D
+    assert lib.sa_stca_workspace_size(256, 0, R) == 0
+    assert lib.sa_stca_workspace_size(256, 4, -1) == 0
+    buf = ctypes.create_string_buffer(256)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    vp = ctypes.c_void_p
+    ok = vp(al)
+    nul = vp(None)
+
+    def call(B=2, D=256, h=4, L=10, R=3, x_off=ok, t_off=ok, X=ok, Q=ok, Wq=ok, Wk=ok, Wv=ok,
+             o=ok, lse=nul, ws=ok, ws_bytes=1 << 40):
+        return lib.sa_stca_attention(B, D, h, L, R, x_off, t_off, X, Q, Wq, Wk, Wv, o, lse, ws,
+                                     ctypes.c_size_t(ws_bytes), nul)
+
+    assert call(D=128) == sa.SA_ERR_BAD_SHAPE
+    assert call(h=5) == sa.SA_ERR_BAD_SHAPE
+    assert call(B=0) == sa.SA_ERR_BAD_SHAPE
+    assert call(L=-1) == sa.SA_ERR_BAD_SHAPE
+    assert call(x_off=nul) == sa.SA_ERR_NULL_ARG
+    assert call(Wk=nul) == sa.SA_ERR_NULL_ARG
+    assert call(ws=nul) == sa.SA_ERR_NULL_ARG
+    assert call(X=nul) == sa.SA_ERR_NULL_ARG                 # rows present, no X
+    assert call(Q=nul) == sa.SA_ERR_NULL_ARG                 # targets present, no queries
+    assert call(o=nul) == sa.SA_ERR_NULL_ARG
+    odd = vp(al + 4)
+    assert call(Wq=odd) == sa.SA_ERR_MISALIGNED
+    assert call(t_off=vp(al + 4)) == sa.SA_ERR_MISALIGNED    # int64 offsets: 8-byte alignment
+    assert call(ws_bytes=16) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+    # no targets: nothing to compute, nothing enqueued
+    assert call(R=0, Q=nul, o=nul) == sa.SA_OK

@@ -62,3 +62,17 @@ def test_stca_many_targets_sharp_scores():
                                Wv.double().numpy(), h)
     e = rel_err(o.cpu().numpy()[sel], ro)
     assert e <= TOL_BF16, f"o rel err {e:.3e}"
+
+
+def test_stca_users_without_history():
+    # every target's user has no rows: o = 0 and lse = -inf throughout
+    say("case stca no history rows")
+    D, h = 512, 8
+    x_off, X, t_off, Q, (Wq, Wk, Wv) = _case(11, [0, 0, 0], [2, 0, 3], D, h)
+    X = torch.zeros(16, D, dtype=torch.bfloat16)              # L = 0: no row is read
+    o, lse = sa.stca_attention(torch.as_tensor(x_off, device="cuda"), X.cuda(),
+                               torch.as_tensor(t_off, device="cuda"), Q.cuda(), Wq.cuda(),
+                               Wk.cuda(), Wv.cuda(), h)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0
+    assert bool(torch.all(torch.isneginf(lse)).item())
