@@ -201,10 +201,19 @@ def _cpu_baseline(prob, budget_s=15.0):
     t0 = run(n0)
     n = int(min(T, max(n0, n0 * budget_s / max(t0, 1e-6))))
     t = run(n) if n != n0 else t0
-    return {"value": n / t, "unit": "history tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} tokens of the {T}-token user, sa_forward_ref + sa_backward_ref "
-                      f"(float64 numpy), {t:.1f} s on {os.cpu_count()} host CPUs",
-            "seconds": t, "tokens": n}
+    # A whole workload that takes well under the budget is run again until
+    # about budget_s seconds of work have been timed.
+    passes = 1
+    while n == T and t < 0.6 * budget_s:
+        t += run(n)
+        passes += 1
+    what = (f"first {n} tokens of the {T}-token user" if n < T
+            else f"the whole {T}-token user, {passes} passes")
+    return {"value": n * passes / t, "unit": "history tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{what}, sa_forward_ref + sa_backward_ref (float64 numpy), {t:.1f} s on "
+                      f"{os.cpu_count()} host CPUs",
+            "seconds": t, "tokens": n * passes}
 
 
 def _per_user_timing(sa, synth, timed, dev):
