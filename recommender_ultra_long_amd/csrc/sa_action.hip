@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256, 1) void sa_action_fwd(const ET* __restrict__ e
                                            // rows of 32 lanes fall on distinct banks)
   __shared__ __attribute__((aligned(16))) bf16 sW2[D * GROW];       // W2^T [out][H]
   __shared__ __attribute__((aligned(16))) bf16 sG[32 * GROW];       // G [event][H]
-  __shared__ float sT1[kActionMaxTypes * H], sT3[kActionMaxTypes * H];
+  __shared__ __attribute__((aligned(16))) float sT1[kActionMaxTypes * H];
+  __shared__ __attribute__((aligned(16))) float sT3[kActionMaxTypes * H];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   for (int i = tid; i < D * H / 8; i += 256) {
@@ -141,23 +142,37 @@ __global__ __launch_bounds__(256, 1) void sa_action_fwd(const ET* __restrict__ e
     if (has_hidden) {
 #pragma unroll
       for (int m = 0; m < TPW; ++m) {
-        f32x16 u1 = f32x16{}, u3 = f32x16{};
+        // Register i: hidden row hb + crow(i, h), this lane's event.  The
+        // products start from the event type's rows of T1 and T3 (4
+        // consecutive hidden rows per register group).
+        const int hb = (wave * TPW + m) * 32;
+        f32x16 u1, u3;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int hr = tcl * H + hb + 8 * g4 + 4 * h;
+          const f32x4 t1 = *(const f32x4*)&sT1[hr], t3 = *(const f32x4*)&sT3[hr];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            u1[4 * g4 + r] = t1[r];
+            u3[4 * g4 + r] = t3[r];
+          }
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           u1 = mfma32(w1[m][ks], eb[ks], u1);
           u3 = mfma32(w3[m][ks], eb[ks], u3);
         }
-        // Register i: hidden row hb + crow(i, h), this lane's event.
-        const int hb = (wave * TPW + m) * 32;
+        // silu(a1) a3 = a1 a3 / (1 + exp(-a1)), with the hardware reciprocal
+        // (the result is rounded to bf16).
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           bf16 gv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int i = 4 * g4 + r, hr = hb + crow(i, h);
-            const float a1 = u1[i] + sT1[tcl * H + hr];
-            const float a3 = u3[i] + sT3[tcl * H + hr];
-            gv[r] = (bf16)(a1 / (1.0f + __expf(-a1)) * a3);
+            const int i = 4 * g4 + r;
+            const float a1 = u1[i], a3 = u3[i];
+            const float den = 1.0f + exp2_fast(a1 * -kLog2e);
+            gv[r] = (bf16)(a1 * a3 * __builtin_amdgcn_rcpf(den));
           }
           bf16* dst = sG + l32 * GROW + hb + 8 * g4 + 4 * h;
           *(uint2*)dst = *(const uint2*)gv;
