@@ -62,3 +62,17 @@ def test_action_fusion_one_type_equals_shared_row():
     ref = action_fusion_ref(e.double().numpy(), np.zeros(500, dtype=np.int64), A.double().numpy(),
                             W1.double().numpy(), W3.double().numpy(), W2.double().numpy())
     assert rel_err(x.double().cpu().numpy(), ref) <= TOL_BF16
+
+
+def test_action_fusion_backward_is_deterministic():
+    # the weight gradients are split over the events and summed in slice
+    # order: two calls agree bit for bit
+    say("case action fusion determinism")
+    e, types, A, W1, W3, W2 = _inputs(3, 40000, 128, 8, torch.bfloat16)
+    dx = torch.randn(40000, 128, generator=torch.Generator().manual_seed(4))
+    dev = [t.cuda() for t in (e, types, A, W1, W3, W2)]
+    g1 = sa.action_fusion_backward(*dev, dx.cuda())
+    g2 = sa.action_fusion_backward(*dev, dx.cuda())
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)

@@ -76,3 +76,16 @@ def test_stca_users_without_history():
     torch.cuda.synchronize()
     assert torch.count_nonzero(o).item() == 0
     assert bool(torch.all(torch.isneginf(lse)).item())
+
+
+def test_stca_is_deterministic():
+    # no atomics anywhere: two calls on the same inputs agree bit for bit
+    say("case stca determinism")
+    D, h = 1024, 16
+    x_off, X, t_off, Q, (Wq, Wk, Wv) = _case(5, [3000, 17, 900], [7, 3, 40], D, h)
+    args = (torch.as_tensor(x_off, device="cuda"), X.cuda(), torch.as_tensor(t_off, device="cuda"),
+            Q.cuda(), Wq.cuda(), Wk.cuda(), Wv.cuda(), h)
+    o1, l1 = sa.stca_attention(*args)
+    o2, l2 = sa.stca_attention(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
