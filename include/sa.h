@@ -371,6 +371,12 @@ sa_status sa_action_fusion_backward(int d, sa_dtype dtype, int64_t T, int n_type
  *                without rows); lse: float [R, h] or NULL (log-sum-exp of the
  *                scaled scores, -inf for a user without rows).
  *  ws          : sa_stca_workspace_size(D, h, R) bytes.
+ * x_off must be nondecreasing in [0, L] and t_off nondecreasing in [0, R]
+ * with t_off[B] = R.  The kernels clamp every user's row range to [0, L] and
+ * map every target to a user in [0, B), so malformed offsets give wrong
+ * numbers but never an access outside X, Q or o; they are not reported.
+ * The query, key and value products round their fp32 operands to bf16 on
+ * the matrix cores when d_h is a multiple of 32 and run in fp32 otherwise.
  * Errors as for the fold.
  */
 size_t sa_stca_workspace_size(int D, int h, int64_t R);

@@ -186,8 +186,8 @@ hipError_t launch_action_dedA(int d, int64_t T, int n_types, const float* dx, co
 // Reordered single-query STCA attention core (sa_stca.hip).
 // U, X: bf16 device arrays.
 hipError_t launch_stca_core(int D, int h, int B, const int64_t* x_off, const int64_t* t_off,
-                            const void* U, const void* X, int64_t rows, float* C, float* lse,
-                            hipStream_t st);
+                            const void* U, const void* X, int64_t L, int64_t rows, float* C,
+                            float* lse, hipStream_t st);
 hipError_t launch_to_bf16(const float* a, int64_t n, void* b, hipStream_t st);
 
 // Argument blocks of the sketch kernels for a plan and a workspace (sa_api.cpp).

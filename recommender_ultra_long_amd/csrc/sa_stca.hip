@@ -74,7 +74,8 @@ template <int DW>
 __global__ __launch_bounds__(512, 1) void sa_stca_core(const int64_t* __restrict__ x_off,
                                                       const int64_t* __restrict__ t_off, int B,
                                                       int h, const bf16* __restrict__ U,
-                                                      const bf16* __restrict__ X, int64_t rows,
+                                                      const bf16* __restrict__ X,
+                                                      int64_t nrows_x, int64_t rows,
                                                       float alpha, float scale,
                                                       float* __restrict__ C,
                                                       float* __restrict__ lse) {
@@ -177,7 +178,10 @@ __global__ __launch_bounds__(512, 1) void sa_stca_core(const int64_t* __restrict
   const int u_last = user_of_target<true>(t_off, B, qlast / h);
   for (int u = u_first; u <= u_last; ++u) {
     if (uload64(t_off + u) == uload64(t_off + u + 1)) continue;   // no targets here
-    const int64_t xlo = uload64(x_off + u), xhi = uload64(x_off + u + 1);
+    // Row ranges are clamped to the nrows_x rows of X: corrupt offsets give
+    // wrong numbers, never an access outside X.
+    const int64_t xlo = clamp64(uload64(x_off + u), 0, nrows_x);
+    const int64_t xhi = clamp64(uload64(x_off + u + 1), xlo, nrows_x);
     if (xlo >= xhi) continue;
     const bool mine = ruser == u;
     const int nt = (int)((xhi - xlo + 31) / 32);
@@ -304,8 +308,8 @@ __global__ __launch_bounds__(512, 1) void sa_stca_core(const int64_t* __restrict
 }
 
 hipError_t launch_stca_core(int D, int h, int B, const int64_t* x_off, const int64_t* t_off,
-                            const void* Uv, const void* Xv, int64_t rows, float* C, float* lse,
-                            hipStream_t st) {
+                            const void* Uv, const void* Xv, int64_t L, int64_t rows, float* C,
+                            float* lse, hipStream_t st) {
   const bf16* U = (const bf16*)Uv;
   const bf16* X = (const bf16*)Xv;
   if (rows <= 0) return hipSuccess;
@@ -314,9 +318,9 @@ hipError_t launch_stca_core(int D, int h, int B, const int64_t* x_off, const int
   const float alpha = scale * kLog2e;
   const dim3 grid((unsigned)((rows + 31) / 32));
   switch (D) {
-    case 256: hipLaunchKernelGGL(sa_stca_core<32>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, rows, alpha, scale, C, lse); break;
-    case 512: hipLaunchKernelGGL(sa_stca_core<64>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, rows, alpha, scale, C, lse); break;
-    case 1024: hipLaunchKernelGGL(sa_stca_core<128>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, rows, alpha, scale, C, lse); break;
+    case 256: hipLaunchKernelGGL(sa_stca_core<32>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, L, rows, alpha, scale, C, lse); break;
+    case 512: hipLaunchKernelGGL(sa_stca_core<64>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, L, rows, alpha, scale, C, lse); break;
+    case 1024: hipLaunchKernelGGL(sa_stca_core<128>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, L, rows, alpha, scale, C, lse); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

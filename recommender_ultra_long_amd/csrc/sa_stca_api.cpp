@@ -96,7 +96,7 @@ sa_status sa_stca_attention(int B, int D, int h, int64_t L, int64_t R, const int
     SA_TRY(launch_to_bf16(Uf, rows * D, w + p.U, st));
   }
   // The length-dependent core: C[r, j] = softmax(X_u u_j / sqrt(d_h)) X_u.
-  SA_TRY(launch_stca_core(D, h, B, x_off, t_off, w + p.U, X, rows, C, l, st));
+  SA_TRY(launch_stca_core(D, h, B, x_off, t_off, w + p.U, X, L, rows, C, l, st));
   if (dh % 32 == 0)
     SA_TRY(launch_gemm_mx(false, false, C, h * D, D, Wv, D, dh, o, D, dh, (int)R, dh, D, h, st));
   else
