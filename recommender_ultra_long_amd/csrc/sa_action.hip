@@ -251,49 +251,62 @@ __global__ __launch_bounds__(256) void sa_action_build_v(const ET* __restrict__ 
                                                          const int32_t* __restrict__ types,
                                                          int n_types, const float* __restrict__ A,
                                                          int d, int64_t T, float* __restrict__ V) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * 2 * d) return;
-  const int64_t ev = i / (2 * d);
-  const int c = (int)(i % (2 * d));
+  // Thread -> 4 consecutive columns of one row of V = [e | A[type]] (d % 4 == 0).
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int qpr = d / 2;                         // float4 per row of V (2d / 4)
+  if (i4 >= T * qpr) return;
+  const int64_t ev = i4 / qpr;
+  const int c = (int)(i4 % qpr) * 4;
+  f32x4 v;
   if (c < d) {
-    V[i] = (float)e[ev * d + c];
+    const ET* src = e + ev * d + c;
+    v = f32x4{(float)src[0], (float)src[1], (float)src[2], (float)src[3]};
   } else {
     int t = types[ev];
     t = t < 0 ? 0 : (t >= n_types ? n_types - 1 : t);
-    V[i] = A[t * d + (c - d)];
+    v = *(const f32x4*)(A + t * d + (c - d));
   }
+  *(f32x4*)(V + ev * 2 * d + c) = v;
 }
 
 // de = dx + dV[:, :d]; and this block's per-type sums of dV[:, d:] over its
-// events (in event order), part[(blk n_types + t) d + c].  Thread c < d of a
-// block owns column c.
+// events, part[(blk n_types + t) d + c].  The block's threads form sub-rows
+// of d / 4 threads (4 columns each); sub-row r takes events e0 + r,
+// e0 + r + SR, ... in order into its own LDS accumulators, which are then
+// added in sub-row order (a fixed order: the sums are deterministic).
 __global__ __launch_bounds__(256) void sa_action_dedA(const float* __restrict__ dx,
                                                       const float* __restrict__ dV,
                                                       const int32_t* __restrict__ types,
                                                       int n_types, int d, int64_t T, int64_t epb,
                                                       float* __restrict__ de,
                                                       float* __restrict__ part) {
-  __shared__ float acc[kActionMaxTypes * 128];
-  const int c = threadIdx.x;
+  __shared__ f32x4 acc[256 * kActionMaxTypes];   // [sub-row][type][quad]
+  const int qpr = d / 4, sr_n = 256 / qpr;
+  const int tid = threadIdx.x, q = tid % qpr, sr = tid / qpr;
   const int64_t e0 = (int64_t)blockIdx.x * epb;
   const int64_t e1 = e0 + epb < T ? e0 + epb : T;
-  if (c < d)
-    for (int t = 0; t < n_types; ++t) acc[t * d + c] = 0.f;
-  if (c < d) {
-    for (int64_t ev = e0; ev < e1; ++ev) {
-      de[ev * d + c] = dx[ev * d + c] + dV[ev * 2 * d + c];
-      int t = types[ev];
-      t = t < 0 ? 0 : (t >= n_types ? n_types - 1 : t);
-      acc[t * d + c] += dV[ev * 2 * d + d + c];
-    }
-    for (int t = 0; t < n_types; ++t)
-      part[((int64_t)blockIdx.x * n_types + t) * d + c] = acc[t * d + c];
+  f32x4* mine = acc + sr * n_types * qpr + q;
+  for (int t = 0; t < n_types; ++t) mine[t * qpr] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t ev = e0 + sr; ev < e1; ev += sr_n) {
+    const f32x4 a = *(const f32x4*)(dx + ev * d + 4 * q);
+    const f32x4 b = *(const f32x4*)(dV + ev * 2 * d + 4 * q);
+    const f32x4 g = *(const f32x4*)(dV + ev * 2 * d + d + 4 * q);
+    *(f32x4*)(de + ev * d + 4 * q) = a + b;
+    int t = types[ev];
+    t = t < 0 ? 0 : (t >= n_types ? n_types - 1 : t);
+    mine[t * qpr] += g;
+  }
+  __syncthreads();
+  for (int o = tid; o < n_types * qpr; o += 256) {
+    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < sr_n; ++r) sum += acc[r * n_types * qpr + o];
+    *(f32x4*)(part + (int64_t)blockIdx.x * n_types * d + 4 * (int64_t)o) = sum;
   }
 }
 
 hipError_t launch_action_build_v(int d, int dtype, int64_t T, int n_types, const void* e,
                                  const int32_t* types, const float* A, float* V, hipStream_t st) {
-  const int64_t n = T * 2 * d;
+  const int64_t n = T * (d / 2);                  // float4 of V
   if (n <= 0) return hipSuccess;
   const unsigned nb = (unsigned)((n + 255) / 256);
   if (dtype == 1)

@@ -120,16 +120,41 @@ __global__ __launch_bounds__(256) void sa_gemm_f32(const float* __restrict__ A, 
   }
 }
 
-// out[i] = (init ? init[i] : 0) + sum_s parts[s n + i], s in increasing order.
+// out[i] = (init ? init[i] : 0) + sum_s parts[s n + i].  Four running sums
+// take slices z = 4 m + r (r = 0..3, m increasing) and are combined as
+// ((s0 + s1) + (s2 + s3)): a fixed order, so the result is deterministic, with
+// four independent load/add chains per thread.
 __global__ __launch_bounds__(256) void sa_sum_slices(const float* __restrict__ parts, int nslices,
                                                      int64_t n, const float* __restrict__ init,
                                                      float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  float s = init != nullptr ? init[i] : 0.f;
-#pragma unroll 4
-  for (int z = 0; z < nslices; ++z) s += parts[(int64_t)z * n + i];
-  out[i] = s;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  const float* p = parts + i;
+  int z = 0;
+  for (; z + 15 < nslices; z += 16) {   // sixteen loads in flight
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = p[(int64_t)(z + r) * n];
+#pragma unroll
+    for (int r = 0; r < 16; r += 4) {
+      s0 += v[r];
+      s1 += v[r + 1];
+      s2 += v[r + 2];
+      s3 += v[r + 3];
+    }
+  }
+  for (; z + 3 < nslices; z += 4) {
+    s0 += p[(int64_t)z * n];
+    s1 += p[(int64_t)(z + 1) * n];
+    s2 += p[(int64_t)(z + 2) * n];
+    s3 += p[(int64_t)(z + 3) * n];
+  }
+  if (z < nslices) s0 += p[(int64_t)z * n];
+  if (z + 1 < nslices) s1 += p[(int64_t)(z + 1) * n];
+  if (z + 2 < nslices) s2 += p[(int64_t)(z + 2) * n];
+  const float s = (s0 + s1) + (s2 + s3);
+  out[i] = init != nullptr ? init[i] + s : s;
 }
 
 // ----------------------------------------------------------------------------
