@@ -269,39 +269,202 @@ __global__ __launch_bounds__(256) void sa_action_build_v(const ET* __restrict__ 
   *(f32x4*)(V + ev * 2 * d + c) = v;
 }
 
-// de = dx + dV[:, :d]; and this block's per-type sums of dV[:, d:] over its
-// events, part[(blk n_types + t) d + c].  The block's threads form sub-rows
-// of d / 4 threads (4 columns each); sub-row r takes events e0 + r,
-// e0 + r + SR, ... in order into its own LDS accumulators, which are then
-// added in sub-row order (a fixed order: the sums are deterministic).
-__global__ __launch_bounds__(256) void sa_action_dedA(const float* __restrict__ dx,
-                                                      const float* __restrict__ dV,
-                                                      const int32_t* __restrict__ types,
-                                                      int n_types, int d, int64_t T, int64_t epb,
-                                                      float* __restrict__ de,
-                                                      float* __restrict__ part) {
+// ----------------------------------------------------------------------------
+// Backward helpers without the materialised history rows.  With
+// V = [e | A[type]], the products over V split into e W?e plus the per-type
+// rows T? = A W?a, and every sum over the action half of V becomes a sum over
+// the events of each type (rank n_types).
+
+// E32 = fp32(e), 8 values per thread.
+__global__ __launch_bounds__(256) void sa_action_e32(const bf16* __restrict__ e, int64_t n8,
+                                                     float* __restrict__ E32) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const bf16x8 v = *(const bf16x8*)(e + 8 * i);
+  *(f32x4*)(E32 + 8 * i) = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  *(f32x4*)(E32 + 8 * i + 4) = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+}
+
+__device__ __forceinline__ float act_logistic(float u) {
+  return __builtin_amdgcn_rcpf(1.0f + exp2_fast(u * -kLog2e));
+}
+
+// a1 = U1' + T1[type], a3 = U3' + T3[type] (4 columns per thread, H columns
+// per row).  fwd: G = silu(a1) a3.  bwd: dU1 = dG a3 s (1 + a1 (1 - s)),
+// dU3 = dG a1 s, s = logistic(a1).
+template <bool BWD>
+__global__ __launch_bounds__(256) void sa_action_swiglu_t(const float* __restrict__ dG,
+                                                          const float* __restrict__ U1,
+                                                          const float* __restrict__ U3,
+                                                          const int32_t* __restrict__ types,
+                                                          const float* __restrict__ T1,
+                                                          const float* __restrict__ T3,
+                                                          int n_types, int H, int64_t n4,
+                                                          float* __restrict__ out1,
+                                                          float* __restrict__ out3) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const int q = H / 4;
+  const int64_t ev = i / q;
+  const int c = (int)(i % q) * 4;
+  int t = types[ev];
+  t = t < 0 ? 0 : (t >= n_types ? n_types - 1 : t);
+  const f32x4 a1 = *(const f32x4*)(U1 + 4 * i) + *(const f32x4*)(T1 + t * H + c);
+  const f32x4 a3 = *(const f32x4*)(U3 + 4 * i) + *(const f32x4*)(T3 + t * H + c);
+  f32x4 s;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] = act_logistic(a1[r]);
+  if (!BWD) {
+    *(f32x4*)(out1 + 4 * i) = a1 * s * a3;
+  } else {
+    const f32x4 g = *(const f32x4*)(dG + 4 * i);
+    *(f32x4*)(out1 + 4 * i) = g * a3 * s * (1.0f + a1 * (1.0f - s));
+    *(f32x4*)(out3 + 4 * i) = g * a1 * s;
+  }
+}
+
+// Per-type sums of the rows of X [T, ncol] (ncol in {64, 128, 256, 512,
+// 1024}): this block's events, part[(blk n_types + t) ncol + c].  Sub-rows of
+// ncol / 4 threads take events e0 + r, e0 + r + SR, ... in order into their
+// own LDS accumulators, added in sub-row order (deterministic).
+__global__ __launch_bounds__(256) void sa_action_type_sums(const float* __restrict__ X,
+                                                           const int32_t* __restrict__ types,
+                                                           int n_types, int ncol, int64_t T,
+                                                           int64_t epb, float* __restrict__ part) {
   __shared__ f32x4 acc[256 * kActionMaxTypes];   // [sub-row][type][quad]
-  const int qpr = d / 4, sr_n = 256 / qpr;
+  const int qpr = ncol / 4, sr_n = 256 / qpr;
   const int tid = threadIdx.x, q = tid % qpr, sr = tid / qpr;
   const int64_t e0 = (int64_t)blockIdx.x * epb;
   const int64_t e1 = e0 + epb < T ? e0 + epb : T;
   f32x4* mine = acc + sr * n_types * qpr + q;
   for (int t = 0; t < n_types; ++t) mine[t * qpr] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t ev = e0 + sr; ev < e1; ev += sr_n) {
-    const f32x4 a = *(const f32x4*)(dx + ev * d + 4 * q);
-    const f32x4 b = *(const f32x4*)(dV + ev * 2 * d + 4 * q);
-    const f32x4 g = *(const f32x4*)(dV + ev * 2 * d + d + 4 * q);
-    *(f32x4*)(de + ev * d + 4 * q) = a + b;
-    int t = types[ev];
-    t = t < 0 ? 0 : (t >= n_types ? n_types - 1 : t);
-    mine[t * qpr] += g;
+  auto clampt = [&](int t) { return t < 0 ? 0 : (t >= n_types ? n_types - 1 : t); };
+  int64_t ev = e0 + sr;
+  for (; ev + 3 * sr_n < e1; ev += 4 * sr_n) {   // four events' loads in flight
+    f32x4 g[4];
+    int t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      g[j] = *(const f32x4*)(X + (ev + j * sr_n) * ncol + 4 * q);
+      t[j] = types[ev + j * sr_n];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mine[clampt(t[j]) * qpr] += g[j];
   }
+  for (; ev < e1; ev += sr_n) mine[clampt(types[ev]) * qpr] += *(const f32x4*)(X + ev * ncol + 4 * q);
   __syncthreads();
   for (int o = tid; o < n_types * qpr; o += 256) {
     f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < sr_n; ++r) sum += acc[r * n_types * qpr + o];
-    *(f32x4*)(part + (int64_t)blockIdx.x * n_types * d + 4 * (int64_t)o) = sum;
+    *(f32x4*)(part + (int64_t)blockIdx.x * n_types * ncol + 4 * (int64_t)o) = sum;
   }
+}
+
+// The rank-n_types products of the backward, one thread per output:
+//   mode 0: T1 = A W1a, T3 = A W3a                       ([n_types, H] each)
+//   mode 1: dA = S1 W1a^T + S3 W3a^T                      ([n_types, d])
+//           dW1[d + c][h] = sum_t A[t][c] S1[t][h], dW3 likewise ([d, H] each)
+// with W1a, W3a the rows d .. 2d - 1 of W1, W3 ([2d, H]).
+__global__ __launch_bounds__(256) void sa_action_small(int mode, int d, int n_types,
+                                                       const float* __restrict__ A,
+                                                       const float* __restrict__ W1,
+                                                       const float* __restrict__ W3,
+                                                       const float* __restrict__ S1,
+                                                       const float* __restrict__ S3,
+                                                       float* __restrict__ T1,
+                                                       float* __restrict__ T3,
+                                                       float* __restrict__ dA,
+                                                       float* __restrict__ dW1,
+                                                       float* __restrict__ dW3) {
+  const int H = 2 * d;
+  const float* W1a = W1 + (int64_t)d * H;
+  const float* W3a = W3 + (int64_t)d * H;
+  int i = blockIdx.x * 256 + threadIdx.x;
+  if (mode == 0) {
+    if (i >= n_types * H) return;
+    const int t = i / H, h = i % H;
+    // d is a multiple of 8: eight terms' loads in flight, eight partial sums.
+    float s1[8] = {}, s3[8] = {};
+    for (int c = 0; c < d; c += 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float a = A[t * d + c + j];
+        s1[j] = fmaf(a, W1a[(c + j) * H + h], s1[j]);
+        s3[j] = fmaf(a, W3a[(c + j) * H + h], s3[j]);
+      }
+    }
+    T1[i] = ((s1[0] + s1[1]) + (s1[2] + s1[3])) + ((s1[4] + s1[5]) + (s1[6] + s1[7]));
+    T3[i] = ((s3[0] + s3[1]) + (s3[2] + s3[3])) + ((s3[4] + s3[5]) + (s3[6] + s3[7]));
+    return;
+  }
+  if (i < n_types * d) {
+    const int t = i / d, c = i % d;
+    const f32x4* s1r = (const f32x4*)(S1 + t * H);
+    const f32x4* s3r = (const f32x4*)(S3 + t * H);
+    const f32x4* w1r = (const f32x4*)(W1a + (int64_t)c * H);
+    const f32x4* w3r = (const f32x4*)(W3a + (int64_t)c * H);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int h4 = 0; h4 < H / 4; ++h4) s += s1r[h4] * w1r[h4] + s3r[h4] * w3r[h4];
+    dA[i] = (s[0] + s[1]) + (s[2] + s[3]);
+    return;
+  }
+  i -= n_types * d;
+  if (i >= d * H) return;
+  const int c = i / H, h = i % H;
+  float s1 = 0.f, s3 = 0.f;
+  for (int t = 0; t < n_types; ++t) {
+    const float a = A[t * d + c];
+    s1 = fmaf(a, S1[t * H + h], s1);
+    s3 = fmaf(a, S3[t * H + h], s3);
+  }
+  dW1[(int64_t)d * H + i] = s1;
+  dW3[(int64_t)d * H + i] = s3;
+}
+
+hipError_t launch_action_small(int mode, int d, int n_types, const float* A, const float* W1,
+                               const float* W3, const float* S1, const float* S3, float* T1,
+                               float* T3, float* dA, float* dW1, float* dW3, hipStream_t st) {
+  const int H = 2 * d;
+  const int n = mode == 0 ? n_types * H : n_types * d + d * H;
+  hipLaunchKernelGGL(sa_action_small, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, mode, d,
+                     n_types, A, W1, W3, S1, S3, T1, T3, dA, dW1, dW3);
+  return hipGetLastError();
+}
+
+hipError_t launch_action_e32(const void* e, int64_t n, float* E32, hipStream_t st) {
+  const int64_t n8 = n / 8;                      // n = T d, d % 8 == 0
+  if (n8 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sa_action_e32, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                     (const bf16*)e, n8, E32);
+  return hipGetLastError();
+}
+
+hipError_t launch_action_swiglu(bool bwd, const float* dG, const float* U1, const float* U3,
+                                const int32_t* types, const float* T1, const float* T3,
+                                int n_types, int H, int64_t T, float* out1, float* out3,
+                                hipStream_t st) {
+  const int64_t n4 = T * (H / 4);
+  if (n4 <= 0) return hipSuccess;
+  const unsigned nb = (unsigned)((n4 + 255) / 256);
+  if (bwd)
+    hipLaunchKernelGGL(sa_action_swiglu_t<true>, dim3(nb), dim3(256), 0, st, dG, U1, U3, types, T1,
+                       T3, n_types, H, n4, out1, out3);
+  else
+    hipLaunchKernelGGL(sa_action_swiglu_t<false>, dim3(nb), dim3(256), 0, st, dG, U1, U3, types,
+                       T1, T3, n_types, H, n4, out1, out3);
+  return hipGetLastError();
+}
+
+hipError_t launch_action_type_sums(const float* X, const int32_t* types, int n_types, int ncol,
+                                   int64_t T, float* part, int nblk, hipStream_t st) {
+  if (n_types < 1 || n_types > kActionMaxTypes || ncol % 4 != 0 || ncol > 1024 ||
+      256 % (ncol / 4) != 0)
+    return hipErrorInvalidValue;
+  const int64_t epb = (T + nblk - 1) / nblk;
+  hipLaunchKernelGGL(sa_action_type_sums, dim3(nblk), dim3(256), 0, st, X, types, n_types, ncol, T,
+                     epb > 0 ? epb : 1, part);
+  return hipGetLastError();
 }
 
 hipError_t launch_action_build_v(int d, int dtype, int64_t T, int n_types, const void* e,
@@ -315,16 +478,6 @@ hipError_t launch_action_build_v(int d, int dtype, int64_t T, int n_types, const
   else
     hipLaunchKernelGGL(sa_action_build_v<float>, dim3(nb), dim3(256), 0, st, (const float*)e,
                        types, n_types, A, d, T, V);
-  return hipGetLastError();
-}
-
-hipError_t launch_action_dedA(int d, int64_t T, int n_types, const float* dx, const float* dV,
-                              const int32_t* types, float* de, float* part, int nblk,
-                              hipStream_t st) {
-  if (n_types < 1 || n_types > kActionMaxTypes || d > 128) return hipErrorInvalidValue;
-  const int64_t epb = (T + nblk - 1) / nblk;
-  hipLaunchKernelGGL(sa_action_dedA, dim3(nblk), dim3(256), 0, st, dx, dV, types, n_types, d, T,
-                     epb > 0 ? epb : 1, de, part);
   return hipGetLastError();
 }
 

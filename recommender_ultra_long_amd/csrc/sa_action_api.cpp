@@ -17,7 +17,7 @@
 namespace sa {
 namespace {
 
-constexpr int kDedABlocks = 256;      // event blocks of the per-type dA partial sums
+constexpr int kTypeBlocks = 256;      // event blocks of the per-type partial sums
 constexpr int kMaxSlices = 64;        // reduction slices of a weight-gradient product
 
 size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -32,33 +32,43 @@ int slices_for(int64_t T) {
   return (int)(s < 1 ? 1 : (s > kMaxSlices ? kMaxSlices : s));
 }
 
-// Workspace of the fp32 composition: V [T, 2d], U1, U3, G [T, 2d] (H = 2d),
-// then F (forward) or dG, dU1, dU3, dV (backward), slices and dA partials.
+// Forward workspace (fp32 histories): V [T, 2d], U1, U3, G [T, H] (H = 2d), F
+// [T, d].  Backward: E (fp32 e, bf16 histories), U1' = E W1e, U3' = E W3e,
+// G, dG, dU1, dU3 [T, H], the weight-gradient slices, the per-type partial
+// sums, S1, S3 (per-type sums of dU1, dU3) and T1, T3 (= A W1a, A W3a).
 struct ActionPlan {
-  size_t prep, V, U1, U3, G, F, dG, dU1, dU3, dV, parts, dAparts, fwd_bf16, fwd_f32, bwd;
+  size_t prep, V, U1, U3, G, F, fwd_bf16, fwd_f32;
+  size_t bE, bU1, bU3, bG, bdG, bdU1, bdU3, bparts, btparts, bS1, bS3, bT1, bT3, bwd;
 };
 
 ActionPlan action_plan(int d, int64_t T, int n_types) {
   ActionPlan p;
   memset(&p, 0, sizeof(p));
-  const size_t Tn = (size_t)T, H = 2 * (size_t)d;
+  const size_t Tn = (size_t)T, H = 2 * (size_t)d, nt = (size_t)n_types;
   size_t off = 0;
   p.prep = off; off = a256(off + action_prep_bytes(d));
   p.fwd_bf16 = off;
+  const size_t base = off;
   p.V = off; off = a256(off + Tn * 2 * d * 4);
   p.U1 = off; off = a256(off + Tn * H * 4);
   p.U3 = off; off = a256(off + Tn * H * 4);
   p.G = off; off = a256(off + Tn * H * 4);
-  const size_t common = off;
   p.F = off; off = a256(off + Tn * d * 4);
   p.fwd_f32 = off;
-  off = common;
-  p.dG = off; off = a256(off + Tn * H * 4);
-  p.dU1 = off; off = a256(off + Tn * H * 4);
-  p.dU3 = off; off = a256(off + Tn * H * 4);
-  p.dV = off; off = a256(off + Tn * 2 * d * 4);
-  p.parts = off; off = a256(off + (size_t)slices_for(T) * 2 * d * H * 4);
-  p.dAparts = off; off = a256(off + (size_t)kDedABlocks * n_types * d * 4);
+  off = base;
+  p.bE = off; off = a256(off + Tn * d * 4);
+  p.bU1 = off; off = a256(off + Tn * H * 4);
+  p.bU3 = off; off = a256(off + Tn * H * 4);
+  p.bG = off; off = a256(off + Tn * H * 4);
+  p.bdG = off; off = a256(off + Tn * H * 4);
+  p.bdU1 = off; off = a256(off + Tn * H * 4);
+  p.bdU3 = off; off = a256(off + Tn * H * 4);
+  p.bparts = off; off = a256(off + (size_t)slices_for(T) * d * H * 4);
+  p.btparts = off; off = a256(off + (size_t)kTypeBlocks * nt * H * 4);
+  p.bS1 = off; off = a256(off + nt * H * 4);
+  p.bS3 = off; off = a256(off + nt * H * 4);
+  p.bT1 = off; off = a256(off + nt * H * 4);
+  p.bT3 = off; off = a256(off + nt * H * 4);
   p.bwd = off;
   return p;
 }
@@ -167,38 +177,59 @@ sa_status sa_action_fusion_backward(int d, sa_dtype dtype, int64_t T, int n_type
   const ActionPlan p = action_plan(d, T, n_types);
   char* w = (char*)ws;
   hipStream_t st = (hipStream_t)stream;
-  const int H = 2 * d;
+  const int H = 2 * d, dt = (int)dtype, nt = n_types;
   const int ns = slices_for(T);
-  float* parts = (float*)(w + p.parts);
+  // With V = [e | A[type]]: U1 = e W1e + T1[type] (T1 = A W1a), likewise U3;
+  // de = dx + dU1 W1e^T + dU3 W3e^T; dA = S1 W1a^T + S3 W3a^T and
+  // dW1 = [e^T dU1 ; A^T S1], dW3 likewise, with S1[t], S3[t] the sums of the
+  // rows of dU1, dU3 over the events of type t.  V is never formed.
+  const float* E = dtype == SA_BF16 ? (const float*)(w + p.bE) : (const float*)e;
+  float* U1 = (float*)(w + p.bU1);
+  float* U3 = (float*)(w + p.bU3);
+  float* G = (float*)(w + p.bG);
+  float* dG = (float*)(w + p.bdG);
+  float* dU1 = (float*)(w + p.bdU1);
+  float* dU3 = (float*)(w + p.bdU3);
+  float* parts = (float*)(w + p.bparts);
+  float* tparts = (float*)(w + p.btparts);
+  float* S1 = (float*)(w + p.bS1);
+  float* S3 = (float*)(w + p.bS3);
+  float* T1 = (float*)(w + p.bT1);
+  float* T3 = (float*)(w + p.bT3);
+  SA_TRY(launch_action_small(0, d, nt, A, W1, W3, nullptr, nullptr, T1, T3, nullptr, nullptr,
+                             nullptr, st));
   if (T > 0) {
-    const sa_status v = fp32_hidden(d, (int)dtype, T, n_types, e, types, A, W1, W3, w, p, st);
-    if (v != SA_OK) return v;
+    if (dtype == SA_BF16) SA_TRY(launch_action_e32(e, T * d, (float*)(w + p.bE), st));
+    SA_TRY(product(dt, false, false, E, d, W1, H, U1, H, (int)T, H, d, 1, 0, st));
+    SA_TRY(product(dt, false, false, E, d, W3, H, U3, H, (int)T, H, d, 1, 0, st));
+    SA_TRY(launch_action_swiglu(false, nullptr, U1, U3, types, T1, T3, nt, H, T, G, nullptr, st));
+    // dG = dx W2^T.
+    SA_TRY(product(dt, false, true, dx, d, W2, d, dG, H, (int)T, H, d, 1, 0, st));
+    SA_TRY(launch_action_swiglu(true, dG, U1, U3, types, T1, T3, nt, H, T, dU1, dU3, st));
+    // de = dx + dU1 W1e^T + dU3 W3e^T.
+    if (dtype == SA_BF16) {
+      SA_TRY(launch_gemm_mx_sliced(false, true, dU1, H, W1, H, de, d, (int)T, d, H, 1, 0, st, dx));
+    } else {
+      SA_TRY(launch_sum_slices(dx, 1, T * d, nullptr, de, st));
+      SA_TRY(launch_gemm(false, true, dU1, H, W1, H, de, d, (int)T, d, H, 1, 1, st));
+    }
+    SA_TRY(product(dt, false, true, dU3, H, W3, H, de, d, (int)T, d, H, 1, 1, st));
   }
-  const float* V = (const float*)(w + p.V);
-  const float* U1 = (const float*)(w + p.U1);
-  const float* U3 = (const float*)(w + p.U3);
-  const float* G = (const float*)(w + p.G);
-  float* dG = (float*)(w + p.dG);
-  float* dU1 = (float*)(w + p.dU1);
-  float* dU3 = (float*)(w + p.dU3);
-  float* dV = (float*)(w + p.dV);
-  const int dt = (int)dtype;
-  // dG = dx W2^T; dW2 = G^T dx.
-  SA_TRY(product(dt, false, true, dx, d, W2, d, dG, H, (int)T, H, d, 1, 0, st));
+  // dW2 = G^T dx (zero without events).
   SA_TRY(product(dt, true, false, G, H, dx, d, parts, d, H, d, (int)T, ns, 0, st));
   SA_TRY(launch_sum_slices(parts, ns, (int64_t)H * d, nullptr, dW2, st));
-  // Through the SwiGLU; dV = dU1 W1^T + dU3 W3^T; dW1 = V^T dU1, dW3 = V^T dU3.
-  SA_TRY(launch_swiglu_bwd(dG, U1, U3, T * H, dU1, dU3, st));
-  SA_TRY(product(dt, false, true, dU1, H, W1, H, dV, 2 * d, (int)T, 2 * d, H, 1, 0, st));
-  SA_TRY(product(dt, false, true, dU3, H, W3, H, dV, 2 * d, (int)T, 2 * d, H, 1, 1, st));
-  SA_TRY(product(dt, true, false, V, 2 * d, dU1, H, parts, H, 2 * d, H, (int)T, ns, 0, st));
-  SA_TRY(launch_sum_slices(parts, ns, (int64_t)2 * d * H, nullptr, dW1, st));
-  SA_TRY(product(dt, true, false, V, 2 * d, dU3, H, parts, H, 2 * d, H, (int)T, ns, 0, st));
-  SA_TRY(launch_sum_slices(parts, ns, (int64_t)2 * d * H, nullptr, dW3, st));
-  // de = dx + dV[:, :d]; dA[t] = sum over events of type t of dV[:, d:].
-  float* dAparts = (float*)(w + p.dAparts);
-  SA_TRY(launch_action_dedA(d, T, n_types, dx, dV, types, de, dAparts, kDedABlocks, st));
-  SA_TRY(launch_sum_slices(dAparts, kDedABlocks, (int64_t)n_types * d, nullptr, dA, st));
+  // S1, S3; dA = S1 W1a^T + S3 W3a^T.
+  SA_TRY(launch_action_type_sums(dU1, types, nt, H, T, tparts, kTypeBlocks, st));
+  SA_TRY(launch_sum_slices(tparts, kTypeBlocks, (int64_t)nt * H, nullptr, S1, st));
+  SA_TRY(launch_action_type_sums(dU3, types, nt, H, T, tparts, kTypeBlocks, st));
+  SA_TRY(launch_sum_slices(tparts, kTypeBlocks, (int64_t)nt * H, nullptr, S3, st));
+  // dA and the action rows of dW1, dW3 (A^T S1, A^T S3); then their event rows
+  // E^T dU1, E^T dU3.
+  SA_TRY(launch_action_small(1, d, nt, A, W1, W3, S1, S3, nullptr, nullptr, dA, dW1, dW3, st));
+  SA_TRY(product(dt, true, false, E, d, dU1, H, parts, H, d, H, (int)T, ns, 0, st));
+  SA_TRY(launch_sum_slices(parts, ns, (int64_t)d * H, nullptr, dW1, st));
+  SA_TRY(product(dt, true, false, E, d, dU3, H, parts, H, d, H, (int)T, ns, 0, st));
+  SA_TRY(launch_sum_slices(parts, ns, (int64_t)d * H, nullptr, dW3, st));
   return SA_OK;
 }
 

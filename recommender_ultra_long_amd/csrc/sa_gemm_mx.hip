@@ -9,6 +9,8 @@
 //   A(m, k) = TA ? A[k lda + m] : A[m lda + k],
 //   B(k, n) = TB ? B[n ldb + k] : B[k ldb + n],
 //   C fp32, or bf16 when OBF, row-major (ldc).
+// With C0 (one slice, not accumulating) the output is C0 + op(A) op(B), C0
+// laid out like C.
 // blockIdx.z is either a batch index (zk = 0: A + z sA, B + z sB, all of K)
 // or a reduction slice (zk = 1: k in [z kc, min((z + 1) kc, K))); either way
 // the output goes to C + z sC.
@@ -101,7 +103,8 @@ template <bool TA, bool TB, bool OBF>
 __global__ __launch_bounds__(256) void sa_gemm_mx(const float* __restrict__ A, int lda, int64_t sA,
                                                   const float* __restrict__ B, int ldb, int64_t sB,
                                                   void* __restrict__ Cv, int ldc, int64_t sC, int M,
-                                                  int N, int K, int kc, int zk, int accumulate) {
+                                                  int N, int K, int kc, int zk, int accumulate,
+                                                  const float* __restrict__ C0) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][kMxTile * kMxStride];
   __shared__ __attribute__((aligned(16))) bf16 Bs[2][kMxTile * kMxStride];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(256) void sa_gemm_mx(const float* __restrict__ A, i
           ((bf16*)Cv)[o] = (bf16)acc[i];
         } else {
           float* c = (float*)Cv + o;
-          *c = accumulate ? *c + acc[i] : acc[i];
+          *c = accumulate ? *c + acc[i] : (C0 != nullptr ? C0[o] + acc[i] : acc[i]);
         }
       }
     }
@@ -176,10 +179,11 @@ namespace {
 
 hipError_t mx_dispatch(bool ta, bool tb, bool obf, dim3 grid, const float* A, int lda, int64_t sA,
                        const float* B, int ldb, int64_t sB, void* C, int ldc, int64_t sC, int M,
-                       int N, int K, int kc, int zk, int accumulate, hipStream_t st) {
+                       int N, int K, int kc, int zk, int accumulate, const float* C0,
+                       hipStream_t st) {
 #define SA_MX(TA_, TB_, OBF_)                                                                   \
   hipLaunchKernelGGL((sa_gemm_mx<TA_, TB_, OBF_>), grid, dim3(256), 0, st, A, lda, sA, B, ldb, \
-                     sB, C, ldc, sC, M, N, K, kc, zk, accumulate)
+                     sB, C, ldc, sC, M, N, K, kc, zk, accumulate, C0)
   if (obf) {
     if (ta || !tb) return hipErrorInvalidValue;   // bf16 output: the key product only
     SA_MX(false, true, true);
@@ -214,23 +218,24 @@ hipError_t launch_gemm_mx(bool tb, bool out_bf16, const float* A, int lda, int64
   const dim3 grid((unsigned)((M + kMxTile - 1) / kMxTile), (unsigned)((N + kMxTile - 1) / kMxTile),
                   (unsigned)batch);
   return mx_dispatch(false, tb, out_bf16, grid, A, lda, sA, B, ldb, sB, C, ldc, sC, M, N, K, K, 0, 0,
-                     st);
+                     nullptr, st);
 }
 
 hipError_t launch_gemm_mx_sliced(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
                                  float* C, int ldc, int M, int N, int K, int slices, int accumulate,
-                                 hipStream_t st) {
+                                 hipStream_t st, const float* init) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (slices < 1) slices = 1;
   int kc = (K + slices - 1) / slices;
   kc = (kc + kMxK - 1) / kMxK * kMxK;
   if (kc < kMxK) kc = kMxK;
-  if (slices > 65535 || !mx_shape_ok(ta, tb, A, lda, 0, B, ldb, 0, M, N, K, slices > 1 ? kc : K))
+  if (slices > 65535 || !mx_shape_ok(ta, tb, A, lda, 0, B, ldb, 0, M, N, K, slices > 1 ? kc : K) ||
+      (init != nullptr && (slices != 1 || accumulate)))
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((M + kMxTile - 1) / kMxTile), (unsigned)((N + kMxTile - 1) / kMxTile),
                   (unsigned)slices);
   return mx_dispatch(ta, tb, false, grid, A, lda, 0, B, ldb, 0, C, ldc, (int64_t)M * ldc, M, N, K,
-                     kc, 1, accumulate, st);
+                     kc, 1, accumulate, init, st);
 }
 
 }  // namespace sa

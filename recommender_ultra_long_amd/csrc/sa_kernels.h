@@ -149,9 +149,10 @@ hipError_t launch_gemm_mx(bool tb, bool out_bf16, const float* A, int lda, int64
 // The same with A(m, k) = ta ? A[k lda + m] : A[m lda + k] and the
 // reduction split into `slices` slices written to C + z M ldc (accumulate:
 // C += instead of C =); K is free when both operands are stored [k][row].
+// init (one slice, not accumulating): C = init + op(A) op(B).
 hipError_t launch_gemm_mx_sliced(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
                                  float* C, int ldc, int M, int N, int K, int slices, int accumulate,
-                                 hipStream_t st);
+                                 hipStream_t st, const float* init = nullptr);
 // Batch z of the product: A + z sA, B + z sB -> C + z sC, over all of K.
 hipError_t launch_gemm_batched(bool ta, bool tb, const float* A, int lda, int64_t sA,
                                const float* B, int ldb, int64_t sB, float* C, int ldc, int64_t sC,
@@ -179,9 +180,21 @@ hipError_t launch_action_fwd(int d, int dtype, int64_t T, int n_types, const voi
 size_t action_prep_bytes(int d);
 hipError_t launch_action_build_v(int d, int dtype, int64_t T, int n_types, const void* e,
                                  const int32_t* types, const float* A, float* V, hipStream_t st);
-hipError_t launch_action_dedA(int d, int64_t T, int n_types, const float* dx, const float* dV,
-                              const int32_t* types, float* de, float* part, int nblk,
-                              hipStream_t st);
+// Backward without V: E32 = fp32(e) (bf16 e, T d values); the SwiGLU with the
+// type rows added on the fly (bwd: dU1, dU3 from dG; fwd: G into out1); the
+// per-type row sums of X [T, ncol] per block (part [nblk, n_types, ncol]).
+hipError_t launch_action_e32(const void* e, int64_t n, float* E32, hipStream_t st);
+hipError_t launch_action_swiglu(bool bwd, const float* dG, const float* U1, const float* U3,
+                                const int32_t* types, const float* T1, const float* T3,
+                                int n_types, int H, int64_t T, float* out1, float* out3,
+                                hipStream_t st);
+hipError_t launch_action_type_sums(const float* X, const int32_t* types, int n_types, int ncol,
+                                   int64_t T, float* part, int nblk, hipStream_t st);
+// mode 0: T1 = A W1a, T3 = A W3a; mode 1: dA = S1 W1a^T + S3 W3a^T and the
+// action rows of dW1, dW3 (A^T S1, A^T S3).
+hipError_t launch_action_small(int mode, int d, int n_types, const float* A, const float* W1,
+                               const float* W3, const float* S1, const float* S3, float* T1,
+                               float* T3, float* dA, float* dW1, float* dW3, hipStream_t st);
 
 // Reordered single-query STCA attention core (sa_stca.hip).
 // U, X: bf16 device arrays.
