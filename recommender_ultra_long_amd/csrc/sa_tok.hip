@@ -361,6 +361,7 @@ __global__ __launch_bounds__(256) void sa_tok_reduce(const int64_t* __restrict__
                                                      uint32_t* __restrict__ status) {
   __shared__ f32x4 red[4][64];
   __shared__ float redl[4][64];
+  __shared__ float redm[4][64];
   const int u = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (blockIdx.y == 0 && u == 0) check_offsets_block(offsets, B, T, status, kStatusOk, kStatusBadOffsets);
@@ -372,11 +373,28 @@ __global__ __launch_bounds__(256) void sa_tok_reduce(const int64_t* __restrict__
   const int64_t hi = clamp64(uload64(offsets + u + 1), lo, T);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float Ls = 0.f, M = -INFINITY;
-  if (hi > lo && live) {
-    const int s0 = seg_of(T, G, lo), s1 = seg_of(T, G, hi - 1);
-    const int n = s1 - s0 + 1;
-    const int64_t b0 = (int64_t)s0 + u;
-    for (int q = 0; q < n; ++q) M = fmaxf(M, pm[(b0 + q) * k + j]);
+  const bool work = hi > lo && live;
+  const int s0 = work ? seg_of(T, G, lo) : 0, s1 = work ? seg_of(T, G, hi - 1) : -1;
+  const int n = s1 - s0 + 1;                     // pieces of user u (0 without work)
+  const int64_t b0 = (int64_t)s0 + u;
+  // The maximum over the pieces: wave w takes pieces w, w + 4, ... with eight
+  // loads in flight; the four wave maxima meet in LDS.
+  {
+    float Mw = -INFINITY;
+    int q = wave;
+    for (; q + 28 < n; q += 32) {
+      float t8[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) t8[r] = pm[(b0 + q + 4 * r) * k + j];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) Mw = fmaxf(Mw, t8[r]);
+    }
+    for (; q < n; q += 4) Mw = fmaxf(Mw, pm[(b0 + q) * k + j]);
+    redm[wave][lane] = Mw;
+    __syncthreads();
+    M = fmaxf(fmaxf(redm[0][lane], redm[1][lane]), fmaxf(redm[2][lane], redm[3][lane]));
+  }
+  if (work) {
     int q = wave;
     for (; q + 28 < n; q += 32) {
       f32x4 v[8];
