@@ -76,3 +76,22 @@ def test_action_fusion_backward_is_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("n_types", [1, 16])
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)])
+def test_action_fusion_backward_type_counts(n_types, dtype, tol):
+    # the per-type sums behind dA and the action rows of dW1, dW3, at one type
+    # and at the largest table (16 types), on a ragged event count
+    say(f"case action fusion backward n_types={n_types} dtype={dtype}")
+    d, T = 64, 2077
+    e, types, A, W1, W3, W2 = _inputs(50 + n_types, T, d, n_types, dtype)
+    dx = torch.randn(T, d, generator=torch.Generator().manual_seed(n_types))
+    grads = sa.action_fusion_backward(*(t.cuda() for t in (e, types, A, W1, W3, W2)), dx.cuda())
+    torch.cuda.synchronize()
+    rg = action_fusion_backward_ref(e.double().numpy(), types.numpy(), A.double().numpy(),
+                                    W1.double().numpy(), W3.double().numpy(), W2.double().numpy(),
+                                    dx.double().numpy())
+    for name, a, b in zip(("de", "dA", "dW1", "dW3", "dW2"), grads, rg):
+        eg = rel_err(a.cpu().numpy(), b)
+        assert eg <= tol, f"{name} rel err {eg:.3e}"
