@@ -275,33 +275,36 @@ __global__ __launch_bounds__(256) void sa_action_build_v(const ET* __restrict__ 
 // rows T? = A W?a, and every sum over the action half of V becomes a sum over
 // the events of each type (rank n_types).
 
-// E32 = fp32(e), 8 values per thread.
-__global__ __launch_bounds__(256) void sa_action_e32(const bf16* __restrict__ e, int64_t n8,
-                                                     float* __restrict__ E32) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const bf16x8 v = *(const bf16x8*)(e + 8 * i);
-  *(f32x4*)(E32 + 8 * i) = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-  *(f32x4*)(E32 + 8 * i + 4) = f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
-}
-
 __device__ __forceinline__ float act_logistic(float u) {
   return __builtin_amdgcn_rcpf(1.0f + exp2_fast(u * -kLog2e));
+}
+
+// Four consecutive values of an fp32 or bf16 intermediate.
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 ld4(const bf16* p) {
+  const bf16x4 v = *(const bf16x4*)p;
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *(f32x4*)p = v; }
+__device__ __forceinline__ void st4(bf16* p, f32x4 v) {
+  bf16x4 b;
+  b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+  *(bf16x4*)p = b;
 }
 
 // a1 = U1' + T1[type], a3 = U3' + T3[type] (4 columns per thread, H columns
 // per row).  fwd: G = silu(a1) a3.  bwd: dU1 = dG a3 s (1 + a1 (1 - s)),
 // dU3 = dG a1 s, s = logistic(a1).
-template <bool BWD>
-__global__ __launch_bounds__(256) void sa_action_swiglu_t(const float* __restrict__ dG,
-                                                          const float* __restrict__ U1,
-                                                          const float* __restrict__ U3,
+template <bool BWD, typename IT>
+__global__ __launch_bounds__(256) void sa_action_swiglu_t(const IT* __restrict__ dG,
+                                                          const IT* __restrict__ U1,
+                                                          const IT* __restrict__ U3,
                                                           const int32_t* __restrict__ types,
                                                           const float* __restrict__ T1,
                                                           const float* __restrict__ T3,
                                                           int n_types, int H, int64_t n4,
-                                                          float* __restrict__ out1,
-                                                          float* __restrict__ out3) {
+                                                          IT* __restrict__ out1,
+                                                          IT* __restrict__ out3) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   const int q = H / 4;
@@ -309,17 +312,17 @@ __global__ __launch_bounds__(256) void sa_action_swiglu_t(const float* __restric
   const int c = (int)(i % q) * 4;
   int t = types[ev];
   t = t < 0 ? 0 : (t >= n_types ? n_types - 1 : t);
-  const f32x4 a1 = *(const f32x4*)(U1 + 4 * i) + *(const f32x4*)(T1 + t * H + c);
-  const f32x4 a3 = *(const f32x4*)(U3 + 4 * i) + *(const f32x4*)(T3 + t * H + c);
+  const f32x4 a1 = ld4(U1 + 4 * i) + *(const f32x4*)(T1 + t * H + c);
+  const f32x4 a3 = ld4(U3 + 4 * i) + *(const f32x4*)(T3 + t * H + c);
   f32x4 s;
 #pragma unroll
   for (int r = 0; r < 4; ++r) s[r] = act_logistic(a1[r]);
   if (!BWD) {
-    *(f32x4*)(out1 + 4 * i) = a1 * s * a3;
+    st4(out1 + 4 * i, a1 * s * a3);
   } else {
-    const f32x4 g = *(const f32x4*)(dG + 4 * i);
-    *(f32x4*)(out1 + 4 * i) = g * a3 * s * (1.0f + a1 * (1.0f - s));
-    *(f32x4*)(out3 + 4 * i) = g * a1 * s;
+    const f32x4 g = ld4(dG + 4 * i);
+    st4(out1 + 4 * i, g * a3 * s * (1.0f + a1 * (1.0f - s)));
+    st4(out3 + 4 * i, g * a1 * s);
   }
 }
 
@@ -327,7 +330,8 @@ __global__ __launch_bounds__(256) void sa_action_swiglu_t(const float* __restric
 // 1024}): this block's events, part[(blk n_types + t) ncol + c].  Sub-rows of
 // ncol / 4 threads take events e0 + r, e0 + r + SR, ... in order into their
 // own LDS accumulators, added in sub-row order (deterministic).
-__global__ __launch_bounds__(256) void sa_action_type_sums(const float* __restrict__ X,
+template <typename IT>
+__global__ __launch_bounds__(256) void sa_action_type_sums(const IT* __restrict__ X,
                                                            const int32_t* __restrict__ types,
                                                            int n_types, int ncol, int64_t T,
                                                            int64_t epb, float* __restrict__ part) {
@@ -345,13 +349,13 @@ __global__ __launch_bounds__(256) void sa_action_type_sums(const float* __restri
     int t[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      g[j] = *(const f32x4*)(X + (ev + j * sr_n) * ncol + 4 * q);
+      g[j] = ld4(X + (ev + j * sr_n) * ncol + 4 * q);
       t[j] = types[ev + j * sr_n];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) mine[clampt(t[j]) * qpr] += g[j];
   }
-  for (; ev < e1; ev += sr_n) mine[clampt(types[ev]) * qpr] += *(const f32x4*)(X + ev * ncol + 4 * q);
+  for (; ev < e1; ev += sr_n) mine[clampt(types[ev]) * qpr] += ld4(X + ev * ncol + 4 * q);
   __syncthreads();
   for (int o = tid; o < n_types * qpr; o += 256) {
     f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -432,38 +436,40 @@ hipError_t launch_action_small(int mode, int d, int n_types, const float* A, con
   return hipGetLastError();
 }
 
-hipError_t launch_action_e32(const void* e, int64_t n, float* E32, hipStream_t st) {
-  const int64_t n8 = n / 8;                      // n = T d, d % 8 == 0
-  if (n8 <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sa_action_e32, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
-                     (const bf16*)e, n8, E32);
-  return hipGetLastError();
-}
-
-hipError_t launch_action_swiglu(bool bwd, const float* dG, const float* U1, const float* U3,
-                                const int32_t* types, const float* T1, const float* T3,
-                                int n_types, int H, int64_t T, float* out1, float* out3,
-                                hipStream_t st) {
+hipError_t launch_action_swiglu(bool bwd, bool bf16_io, const void* dG, const void* U1,
+                                const void* U3, const int32_t* types, const float* T1,
+                                const float* T3, int n_types, int H, int64_t T, void* out1,
+                                void* out3, hipStream_t st) {
   const int64_t n4 = T * (H / 4);
   if (n4 <= 0) return hipSuccess;
   const unsigned nb = (unsigned)((n4 + 255) / 256);
-  if (bwd)
-    hipLaunchKernelGGL(sa_action_swiglu_t<true>, dim3(nb), dim3(256), 0, st, dG, U1, U3, types, T1,
-                       T3, n_types, H, n4, out1, out3);
-  else
-    hipLaunchKernelGGL(sa_action_swiglu_t<false>, dim3(nb), dim3(256), 0, st, dG, U1, U3, types,
-                       T1, T3, n_types, H, n4, out1, out3);
+#define SA_SWIGLU(B_, IT_)                                                                       \
+  hipLaunchKernelGGL((sa_action_swiglu_t<B_, IT_>), dim3(nb), dim3(256), 0, st, (const IT_*)dG, \
+                     (const IT_*)U1, (const IT_*)U3, types, T1, T3, n_types, H, n4, (IT_*)out1,  \
+                     (IT_*)out3)
+  if (bf16_io) {
+    if (bwd) SA_SWIGLU(true, bf16);
+    else SA_SWIGLU(false, bf16);
+  } else {
+    if (bwd) SA_SWIGLU(true, float);
+    else SA_SWIGLU(false, float);
+  }
+#undef SA_SWIGLU
   return hipGetLastError();
 }
 
-hipError_t launch_action_type_sums(const float* X, const int32_t* types, int n_types, int ncol,
-                                   int64_t T, float* part, int nblk, hipStream_t st) {
+hipError_t launch_action_type_sums(bool bf16_in, const void* X, const int32_t* types, int n_types,
+                                   int ncol, int64_t T, float* part, int nblk, hipStream_t st) {
   if (n_types < 1 || n_types > kActionMaxTypes || ncol % 4 != 0 || ncol > 1024 ||
       256 % (ncol / 4) != 0)
     return hipErrorInvalidValue;
   const int64_t epb = (T + nblk - 1) / nblk;
-  hipLaunchKernelGGL(sa_action_type_sums, dim3(nblk), dim3(256), 0, st, X, types, n_types, ncol, T,
-                     epb > 0 ? epb : 1, part);
+  if (bf16_in)
+    hipLaunchKernelGGL(sa_action_type_sums<bf16>, dim3(nblk), dim3(256), 0, st, (const bf16*)X,
+                       types, n_types, ncol, T, epb > 0 ? epb : 1, part);
+  else
+    hipLaunchKernelGGL(sa_action_type_sums<float>, dim3(nblk), dim3(256), 0, st, (const float*)X,
+                       types, n_types, ncol, T, epb > 0 ? epb : 1, part);
   return hipGetLastError();
 }
 

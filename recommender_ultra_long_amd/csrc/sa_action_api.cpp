@@ -33,15 +33,16 @@ int slices_for(int64_t T) {
 }
 
 // Forward workspace (fp32 histories): V [T, 2d], U1, U3, G [T, H] (H = 2d), F
-// [T, d].  Backward: E (fp32 e, bf16 histories), U1' = E W1e, U3' = E W3e,
-// G, dG, dU1, dU3 [T, H], the weight-gradient slices, the per-type partial
-// sums, S1, S3 (per-type sums of dU1, dU3) and T1, T3 (= A W1a, A W3a).
+// [T, d].  Backward: U1' = e W1e, U3' = e W3e, G, dG, dU1, dU3 [T, H] (bf16
+// for bf16 histories, fp32 otherwise), the weight-gradient slices, the
+// per-type partial sums, S1, S3 (per-type sums of dU1, dU3) and T1, T3
+// (= A W1a, A W3a).
 struct ActionPlan {
   size_t prep, V, U1, U3, G, F, fwd_bf16, fwd_f32;
-  size_t bE, bU1, bU3, bG, bdG, bdU1, bdU3, bparts, btparts, bS1, bS3, bT1, bT3, bwd;
+  size_t bU1, bU3, bG, bdG, bdU1, bdU3, bparts, btparts, bS1, bS3, bT1, bT3, bwd;
 };
 
-ActionPlan action_plan(int d, int64_t T, int n_types) {
+ActionPlan action_plan(int d, int64_t T, int n_types, int dtype) {
   ActionPlan p;
   memset(&p, 0, sizeof(p));
   const size_t Tn = (size_t)T, H = 2 * (size_t)d, nt = (size_t)n_types;
@@ -56,13 +57,13 @@ ActionPlan action_plan(int d, int64_t T, int n_types) {
   p.F = off; off = a256(off + Tn * d * 4);
   p.fwd_f32 = off;
   off = base;
-  p.bE = off; off = a256(off + Tn * d * 4);
-  p.bU1 = off; off = a256(off + Tn * H * 4);
-  p.bU3 = off; off = a256(off + Tn * H * 4);
-  p.bG = off; off = a256(off + Tn * H * 4);
-  p.bdG = off; off = a256(off + Tn * H * 4);
-  p.bdU1 = off; off = a256(off + Tn * H * 4);
-  p.bdU3 = off; off = a256(off + Tn * H * 4);
+  const size_t es = dtype == SA_BF16 ? 2 : 4;     // intermediates' element size
+  p.bU1 = off; off = a256(off + Tn * H * es);
+  p.bU3 = off; off = a256(off + Tn * H * es);
+  p.bG = off; off = a256(off + Tn * H * es);
+  p.bdG = off; off = a256(off + Tn * H * es);
+  p.bdU1 = off; off = a256(off + Tn * H * es);
+  p.bdU3 = off; off = a256(off + Tn * H * es);
   p.bparts = off; off = a256(off + (size_t)slices_for(T) * d * H * 4);
   p.btparts = off; off = a256(off + (size_t)kTypeBlocks * nt * H * 4);
   p.bS1 = off; off = a256(off + nt * H * 4);
@@ -117,7 +118,7 @@ extern "C" {
 
 size_t sa_action_fusion_workspace_size(int d, sa_dtype dtype, int64_t T, int n_types, int op) {
   if (!shape_ok(d, T, n_types) || (dtype != SA_F32 && dtype != SA_BF16)) return 0;
-  const ActionPlan p = action_plan(d, T, n_types);
+  const ActionPlan p = action_plan(d, T, n_types, (int)dtype);
   if (op == SA_OP_FORWARD) return dtype == SA_BF16 ? p.fwd_bf16 : p.fwd_f32;
   if (op == SA_OP_BACKWARD) return p.bwd;
   return 0;
@@ -137,7 +138,7 @@ sa_status sa_action_fusion_forward(int d, sa_dtype dtype, int64_t T, int n_types
     return SA_ERR_MISALIGNED;
   if (ws_bytes < sa_action_fusion_workspace_size(d, dtype, T, n_types, SA_OP_FORWARD))
     return SA_ERR_WORKSPACE_TOO_SMALL;
-  const ActionPlan p = action_plan(d, T, n_types);
+  const ActionPlan p = action_plan(d, T, n_types, (int)dtype);
   char* w = (char*)ws;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == SA_BF16) {
@@ -174,7 +175,7 @@ sa_status sa_action_fusion_backward(int d, sa_dtype dtype, int64_t T, int n_type
     return SA_ERR_MISALIGNED;
   if (ws_bytes < sa_action_fusion_workspace_size(d, dtype, T, n_types, SA_OP_BACKWARD))
     return SA_ERR_WORKSPACE_TOO_SMALL;
-  const ActionPlan p = action_plan(d, T, n_types);
+  const ActionPlan p = action_plan(d, T, n_types, (int)dtype);
   char* w = (char*)ws;
   hipStream_t st = (hipStream_t)stream;
   const int H = 2 * d, dt = (int)dtype, nt = n_types;
@@ -182,53 +183,66 @@ sa_status sa_action_fusion_backward(int d, sa_dtype dtype, int64_t T, int n_type
   // With V = [e | A[type]]: U1 = e W1e + T1[type] (T1 = A W1a), likewise U3;
   // de = dx + dU1 W1e^T + dU3 W3e^T; dA = S1 W1a^T + S3 W3a^T and
   // dW1 = [e^T dU1 ; A^T S1], dW3 likewise, with S1[t], S3[t] the sums of the
-  // rows of dU1, dU3 over the events of type t.  V is never formed.
-  const float* E = dtype == SA_BF16 ? (const float*)(w + p.bE) : (const float*)e;
-  float* U1 = (float*)(w + p.bU1);
-  float* U3 = (float*)(w + p.bU3);
-  float* G = (float*)(w + p.bG);
-  float* dG = (float*)(w + p.bdG);
-  float* dU1 = (float*)(w + p.bdU1);
-  float* dU3 = (float*)(w + p.bdU3);
+  // rows of dU1, dU3 over the events of type t.  V is never formed.  bf16
+  // histories keep the [T, H] intermediates in bf16 and run every product on
+  // the matrix cores; fp32 histories are fp32 throughout.
+  const bool bf = dtype == SA_BF16;
+  void* U1 = w + p.bU1;
+  void* U3 = w + p.bU3;
+  void* G = w + p.bG;
+  void* dG = w + p.bdG;
+  void* dU1 = w + p.bdU1;
+  void* dU3 = w + p.bdU3;
   float* parts = (float*)(w + p.bparts);
   float* tparts = (float*)(w + p.btparts);
   float* S1 = (float*)(w + p.bS1);
   float* S3 = (float*)(w + p.bS3);
   float* T1 = (float*)(w + p.bT1);
   float* T3 = (float*)(w + p.bT3);
+  // C (+)= op(A) op(B): typed matrix-core products for bf16 histories, fp32
+  // vector-ALU products otherwise.
+  auto prod = [&](bool ta, bool tb, bool abf, bool bbf, bool obf, const void* A_, int lda,
+                  const void* B_, int ldb, void* C_, int ldc, int M, int N, int K, int sl,
+                  int accumulate, const float* init) -> hipError_t {
+    if (bf)
+      return launch_gemm_mx_typed(ta, tb, abf, bbf, obf, A_, lda, B_, ldb, C_, ldc, M, N, K, sl,
+                                  accumulate, init, st);
+    if (init != nullptr) {
+      const hipError_t e_ = launch_sum_slices(init, 1, (int64_t)M * N, nullptr, (float*)C_, st);
+      if (e_ != hipSuccess) return e_;
+      accumulate = 1;
+    }
+    return launch_gemm(ta, tb, (const float*)A_, lda, (const float*)B_, ldb, (float*)C_, ldc, M,
+                       N, K, sl, accumulate, st);
+  };
   SA_TRY(launch_action_small(0, d, nt, A, W1, W3, nullptr, nullptr, T1, T3, nullptr, nullptr,
                              nullptr, st));
   if (T > 0) {
-    if (dtype == SA_BF16) SA_TRY(launch_action_e32(e, T * d, (float*)(w + p.bE), st));
-    SA_TRY(product(dt, false, false, E, d, W1, H, U1, H, (int)T, H, d, 1, 0, st));
-    SA_TRY(product(dt, false, false, E, d, W3, H, U3, H, (int)T, H, d, 1, 0, st));
-    SA_TRY(launch_action_swiglu(false, nullptr, U1, U3, types, T1, T3, nt, H, T, G, nullptr, st));
-    // dG = dx W2^T.
-    SA_TRY(product(dt, false, true, dx, d, W2, d, dG, H, (int)T, H, d, 1, 0, st));
-    SA_TRY(launch_action_swiglu(true, dG, U1, U3, types, T1, T3, nt, H, T, dU1, dU3, st));
+    // U1' = e W1e, U3' = e W3e (rows 0 .. d-1 of W1, W3); G.
+    SA_TRY(prod(false, false, bf, false, bf, e, d, W1, H, U1, H, (int)T, H, d, 1, 0, nullptr));
+    SA_TRY(prod(false, false, bf, false, bf, e, d, W3, H, U3, H, (int)T, H, d, 1, 0, nullptr));
+    SA_TRY(launch_action_swiglu(false, bf, nullptr, U1, U3, types, T1, T3, nt, H, T, G, nullptr,
+                                st));
+    // dG = dx W2^T; dU1, dU3.
+    SA_TRY(prod(false, true, false, false, bf, dx, d, W2, d, dG, H, (int)T, H, d, 1, 0, nullptr));
+    SA_TRY(launch_action_swiglu(true, bf, dG, U1, U3, types, T1, T3, nt, H, T, dU1, dU3, st));
     // de = dx + dU1 W1e^T + dU3 W3e^T.
-    if (dtype == SA_BF16) {
-      SA_TRY(launch_gemm_mx_sliced(false, true, dU1, H, W1, H, de, d, (int)T, d, H, 1, 0, st, dx));
-    } else {
-      SA_TRY(launch_sum_slices(dx, 1, T * d, nullptr, de, st));
-      SA_TRY(launch_gemm(false, true, dU1, H, W1, H, de, d, (int)T, d, H, 1, 1, st));
-    }
-    SA_TRY(product(dt, false, true, dU3, H, W3, H, de, d, (int)T, d, H, 1, 1, st));
+    SA_TRY(prod(false, true, bf, false, false, dU1, H, W1, H, de, d, (int)T, d, H, 1, 0, dx));
+    SA_TRY(prod(false, true, bf, false, false, dU3, H, W3, H, de, d, (int)T, d, H, 1, 1, nullptr));
   }
   // dW2 = G^T dx (zero without events).
-  SA_TRY(product(dt, true, false, G, H, dx, d, parts, d, H, d, (int)T, ns, 0, st));
+  SA_TRY(prod(true, false, bf, false, false, G, H, dx, d, parts, d, H, d, (int)T, ns, 0, nullptr));
   SA_TRY(launch_sum_slices(parts, ns, (int64_t)H * d, nullptr, dW2, st));
-  // S1, S3; dA = S1 W1a^T + S3 W3a^T.
-  SA_TRY(launch_action_type_sums(dU1, types, nt, H, T, tparts, kTypeBlocks, st));
+  // S1, S3; dA and the action rows of dW1, dW3 (A^T S1, A^T S3).
+  SA_TRY(launch_action_type_sums(bf, dU1, types, nt, H, T, tparts, kTypeBlocks, st));
   SA_TRY(launch_sum_slices(tparts, kTypeBlocks, (int64_t)nt * H, nullptr, S1, st));
-  SA_TRY(launch_action_type_sums(dU3, types, nt, H, T, tparts, kTypeBlocks, st));
+  SA_TRY(launch_action_type_sums(bf, dU3, types, nt, H, T, tparts, kTypeBlocks, st));
   SA_TRY(launch_sum_slices(tparts, kTypeBlocks, (int64_t)nt * H, nullptr, S3, st));
-  // dA and the action rows of dW1, dW3 (A^T S1, A^T S3); then their event rows
-  // E^T dU1, E^T dU3.
   SA_TRY(launch_action_small(1, d, nt, A, W1, W3, S1, S3, nullptr, nullptr, dA, dW1, dW3, st));
-  SA_TRY(product(dt, true, false, E, d, dU1, H, parts, H, d, H, (int)T, ns, 0, st));
+  // The event rows of dW1, dW3: e^T dU1, e^T dU3.
+  SA_TRY(prod(true, false, bf, bf, false, e, d, dU1, H, parts, H, d, H, (int)T, ns, 0, nullptr));
   SA_TRY(launch_sum_slices(parts, ns, (int64_t)d * H, nullptr, dW1, st));
-  SA_TRY(product(dt, true, false, E, d, dU3, H, parts, H, d, H, (int)T, ns, 0, st));
+  SA_TRY(prod(true, false, bf, bf, false, e, d, dU3, H, parts, H, d, H, (int)T, ns, 0, nullptr));
   SA_TRY(launch_sum_slices(parts, ns, (int64_t)d * H, nullptr, dW3, st));
   return SA_OK;
 }

@@ -41,17 +41,21 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float4 a, const float4 b) {
   return r;
 }
 
-// One operand tile (64 rows x 32 k) of an fp32 matrix, staged into LDS as
-// [row][k] bf16.  KROW: the matrix is stored [k][row] (ld between k rows);
-// otherwise [row][k] (ld between rows).  `rows` bounds the row index.
-template <bool KROW>
+// One operand tile (64 rows x 32 k) of an fp32 (ST = float) or bf16 (ST =
+// bf16) matrix, staged into LDS as [row][k] bf16.  KROW: the matrix is stored
+// [k][row] (ld between k rows); otherwise [row][k] (ld between rows).  `rows`
+// bounds the row index.
+template <bool KROW, typename ST>
 struct MxOperand {
-  const float* base;   // this thread's first element (row clamped)
+  static constexpr bool B16 = sizeof(ST) == 2;
+  const ST* base;      // this thread's first element (row clamped)
   int ld;
   int row_s, k_s;      // staging position: LDS row and first k of this thread
-  float4 r[kMxPf][2];
+  float4 r[kMxPf][2];  // fp32 source
+  bf16x4 rb[kMxPf][2]; // bf16 source, [k][row]: two k rows of 4 values
+  bf16x8 rr[kMxPf];    // bf16 source, [row][k]: 8 k values
 
-  __device__ void init(const float* m, int ldm, int row0, int rows, int tid) {
+  __device__ void init(const ST* m, int ldm, int row0, int rows, int tid) {
     ld = ldm;
     if (KROW) {
       k_s = (tid >> 4) * 2;
@@ -70,38 +74,55 @@ struct MxOperand {
     if (KROW) {
       const int ka = k0 + k_s, kb = ka + 1;
       const int kac = ka < k1 ? ka : k1 - 1, kbc = kb < k1 ? kb : k1 - 1;
-      const float4 va = *(const float4*)(base + (int64_t)kac * ld);
-      const float4 vb = *(const float4*)(base + (int64_t)kbc * ld);
-      const float4 z = {0.f, 0.f, 0.f, 0.f};
-      r[s][0] = ka < k1 ? va : z;
-      r[s][1] = kb < k1 ? vb : z;
+      if constexpr (B16) {
+        const bf16x4 va = *(const bf16x4*)(base + (int64_t)kac * ld);
+        const bf16x4 vb = *(const bf16x4*)(base + (int64_t)kbc * ld);
+        rb[s][0] = ka < k1 ? va : bf16x4{};
+        rb[s][1] = kb < k1 ? vb : bf16x4{};
+      } else {
+        const float4 va = *(const float4*)(base + (int64_t)kac * ld);
+        const float4 vb = *(const float4*)(base + (int64_t)kbc * ld);
+        const float4 z = {0.f, 0.f, 0.f, 0.f};
+        r[s][0] = ka < k1 ? va : z;
+        r[s][1] = kb < k1 ? vb : z;
+      }
     } else {
-      r[s][0] = *(const float4*)(base + k0);
-      r[s][1] = *(const float4*)(base + k0 + 4);
+      if constexpr (B16) {
+        rr[s] = *(const bf16x8*)(base + k0);
+      } else {
+        r[s][0] = *(const float4*)(base + k0);
+        r[s][1] = *(const float4*)(base + k0 + 4);
+      }
     }
   }
   __device__ void store(int s, bf16* S) const {
     if (KROW) {
-      const float x0[4] = {r[s][0].x, r[s][0].y, r[s][0].z, r[s][0].w};
-      const float x1[4] = {r[s][1].x, r[s][1].y, r[s][1].z, r[s][1].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         bf16x2 v;
-        v[0] = (bf16)x0[i];
-        v[1] = (bf16)x1[i];
+        if constexpr (B16) {
+          v[0] = rb[s][0][i];
+          v[1] = rb[s][1][i];
+        } else {
+          const float x0[4] = {r[s][0].x, r[s][0].y, r[s][0].z, r[s][0].w};
+          const float x1[4] = {r[s][1].x, r[s][1].y, r[s][1].z, r[s][1].w};
+          v[0] = (bf16)x0[i];
+          v[1] = (bf16)x1[i];
+        }
         *(bf16x2*)&S[(row_s + i) * kMxStride + k_s] = v;
       }
     } else {
-      *(bf16x8*)&S[row_s * kMxStride + k_s] = to_bf16x8(r[s][0], r[s][1]);
+      if constexpr (B16) *(bf16x8*)&S[row_s * kMxStride + k_s] = rr[s];
+      else *(bf16x8*)&S[row_s * kMxStride + k_s] = to_bf16x8(r[s][0], r[s][1]);
     }
   }
 };
 
 }  // namespace
 
-template <bool TA, bool TB, bool OBF>
-__global__ __launch_bounds__(256) void sa_gemm_mx(const float* __restrict__ A, int lda, int64_t sA,
-                                                  const float* __restrict__ B, int ldb, int64_t sB,
+template <bool TA, bool TB, bool OBF, typename AT = float, typename BT = float>
+__global__ __launch_bounds__(256) void sa_gemm_mx(const AT* __restrict__ A, int lda, int64_t sA,
+                                                  const BT* __restrict__ B, int ldb, int64_t sB,
                                                   void* __restrict__ Cv, int ldc, int64_t sC, int M,
                                                   int N, int K, int kc, int zk, int accumulate,
                                                   const float* __restrict__ C0) {
@@ -120,8 +141,8 @@ __global__ __launch_bounds__(256) void sa_gemm_mx(const float* __restrict__ A, i
     B += (int64_t)z * sB;
   }
 
-  MxOperand<TA> a;     // A stored [k][m] when TA
-  MxOperand<!TB> b;    // B stored [k][n] when !TB
+  MxOperand<TA, AT> a;     // A stored [k][m] when TA
+  MxOperand<!TB, BT> b;    // B stored [k][n] when !TB
   a.init(A, lda, m0, M, tid);
   b.init(B, ldb, n0, N, tid);
 
@@ -236,6 +257,52 @@ hipError_t launch_gemm_mx_sliced(bool ta, bool tb, const float* A, int lda, cons
                   (unsigned)slices);
   return mx_dispatch(ta, tb, false, grid, A, lda, 0, B, ldb, 0, C, ldc, (int64_t)M * ldc, M, N, K,
                      kc, 1, accumulate, init, st);
+}
+
+// Operands in bf16 as well as fp32 (a_bf16, b_bf16) and a bf16 output
+// (out_bf16), for the intermediates of the action-fusion backward; only the
+// combinations it uses are built.  bf16 operands stored [row][k] need
+// 16-byte aligned rows (ld % 8 == 0), those stored [k][row] 8-byte aligned
+// rows.
+hipError_t launch_gemm_mx_typed(bool ta, bool tb, bool a_bf16, bool b_bf16, bool out_bf16,
+                                const void* A, int lda, const void* B, int ldb, void* C, int ldc,
+                                int M, int N, int K, int slices, int accumulate, const float* init,
+                                hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (slices < 1) slices = 1;
+  int kc = (K + slices - 1) / slices;
+  kc = (kc + kMxK - 1) / kMxK * kMxK;
+  if (kc < kMxK) kc = kMxK;
+  const int kcheck = slices > 1 ? kc : K;
+  const bool rowk_a = !ta, rowk_b = tb;
+  bool ok = slices <= 65535 && ((uintptr_t)A & 7u) == 0 && ((uintptr_t)B & 7u) == 0;
+  if ((rowk_a || rowk_b) && (K % kMxK != 0 || kcheck % kMxK != 0)) ok = false;
+  if (ta && M % 4 != 0) ok = false;
+  if (!tb && N % 4 != 0) ok = false;
+  if (lda % (a_bf16 && rowk_a ? 8 : 4) != 0 || ldb % (b_bf16 && rowk_b ? 8 : 4) != 0) ok = false;
+  if ((!a_bf16 || rowk_a) && ((uintptr_t)A & 15u) != 0) ok = false;
+  if ((!b_bf16 || rowk_b) && ((uintptr_t)B & 15u) != 0) ok = false;
+  if (init != nullptr && (slices != 1 || accumulate || out_bf16)) ok = false;
+  if (out_bf16 && (slices != 1 || accumulate)) ok = false;
+  if (!ok) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((M + kMxTile - 1) / kMxTile), (unsigned)((N + kMxTile - 1) / kMxTile),
+                  (unsigned)slices);
+  const int64_t sC = (int64_t)M * ldc;
+#define SA_MXT(TA_, TB_, OBF_, AT_, BT_)                                                         \
+  hipLaunchKernelGGL((sa_gemm_mx<TA_, TB_, OBF_, AT_, BT_>), grid, dim3(256), 0, st,             \
+                     (const AT_*)A, lda, 0, (const BT_*)B, ldb, 0, C, ldc, sC, M, N, K, kc, 1,     \
+                     accumulate, init)
+  if (!a_bf16 && !b_bf16 && !out_bf16)
+    return mx_dispatch(ta, tb, false, grid, (const float*)A, lda, 0, (const float*)B, ldb, 0, C,
+                       ldc, sC, M, N, K, kc, 1, accumulate, init, st);
+  if (!ta && !tb && a_bf16 && !b_bf16 && out_bf16) SA_MXT(false, false, true, bf16, float);
+  else if (!ta && tb && !a_bf16 && !b_bf16 && out_bf16) SA_MXT(false, true, true, float, float);
+  else if (!ta && tb && a_bf16 && !b_bf16 && !out_bf16) SA_MXT(false, true, false, bf16, float);
+  else if (ta && !tb && a_bf16 && !b_bf16 && !out_bf16) SA_MXT(true, false, false, bf16, float);
+  else if (ta && !tb && a_bf16 && b_bf16 && !out_bf16) SA_MXT(true, false, false, bf16, bf16);
+  else return hipErrorInvalidValue;
+#undef SA_MXT
+  return hipGetLastError();
 }
 
 }  // namespace sa

@@ -153,6 +153,13 @@ hipError_t launch_gemm_mx(bool tb, bool out_bf16, const float* A, int lda, int64
 hipError_t launch_gemm_mx_sliced(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,
                                  float* C, int ldc, int M, int N, int K, int slices, int accumulate,
                                  hipStream_t st, const float* init = nullptr);
+// bf16 operands (a_bf16, b_bf16) and a bf16 output (out_bf16) for the
+// action-fusion backward's intermediates (sa_gemm_mx.hip); the combinations
+// it does not use return hipErrorInvalidValue.
+hipError_t launch_gemm_mx_typed(bool ta, bool tb, bool a_bf16, bool b_bf16, bool out_bf16,
+                                const void* A, int lda, const void* B, int ldb, void* C, int ldc,
+                                int M, int N, int K, int slices, int accumulate, const float* init,
+                                hipStream_t st);
 // Batch z of the product: A + z sA, B + z sB -> C + z sC, over all of K.
 hipError_t launch_gemm_batched(bool ta, bool tb, const float* A, int lda, int64_t sA,
                                const float* B, int ldb, int64_t sB, float* C, int ldc, int64_t sC,
@@ -180,16 +187,16 @@ hipError_t launch_action_fwd(int d, int dtype, int64_t T, int n_types, const voi
 size_t action_prep_bytes(int d);
 hipError_t launch_action_build_v(int d, int dtype, int64_t T, int n_types, const void* e,
                                  const int32_t* types, const float* A, float* V, hipStream_t st);
-// Backward without V: E32 = fp32(e) (bf16 e, T d values); the SwiGLU with the
-// type rows added on the fly (bwd: dU1, dU3 from dG; fwd: G into out1); the
-// per-type row sums of X [T, ncol] per block (part [nblk, n_types, ncol]).
-hipError_t launch_action_e32(const void* e, int64_t n, float* E32, hipStream_t st);
-hipError_t launch_action_swiglu(bool bwd, const float* dG, const float* U1, const float* U3,
-                                const int32_t* types, const float* T1, const float* T3,
-                                int n_types, int H, int64_t T, float* out1, float* out3,
-                                hipStream_t st);
-hipError_t launch_action_type_sums(const float* X, const int32_t* types, int n_types, int ncol,
-                                   int64_t T, float* part, int nblk, hipStream_t st);
+// Backward without V: the SwiGLU with the type rows added on the fly (bwd:
+// dU1, dU3 from dG; fwd: G into out1), its intermediates fp32 or bf16
+// (bf16_io); the per-type row sums of X [T, ncol] per block (part [nblk,
+// n_types, ncol]).
+hipError_t launch_action_swiglu(bool bwd, bool bf16_io, const void* dG, const void* U1,
+                                const void* U3, const int32_t* types, const float* T1,
+                                const float* T3, int n_types, int H, int64_t T, void* out1,
+                                void* out3, hipStream_t st);
+hipError_t launch_action_type_sums(bool bf16_in, const void* X, const int32_t* types, int n_types,
+                                   int ncol, int64_t T, float* part, int nblk, hipStream_t st);
 // mode 0: T1 = A W1a, T3 = A W3a; mode 1: dA = S1 W1a^T + S3 W3a^T and the
 // action rows of dW1, dW3 (A^T S1, A^T S3).
 hipError_t launch_action_small(int mode, int d, int n_types, const float* A, const float* W1,
