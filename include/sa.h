@@ -337,9 +337,10 @@ sa_status sa_block_backward(const sa_problem* problem, int n_layers, const int64
  * Backward: given dx = dL/dx (float [T, d], e.g. sa_backward's dX), writes
  * de (float [T, d]), dA (float [n_types, d]), dW1, dW3 (float [2d, 2d]) and
  * dW2 (float [2d, d]), all overwritten; the weight and table gradients sum
- * over events in a fixed order.  With SA_BF16 the backward's products round
- * their fp32 operands to bf16 on the matrix cores (fp32 accumulation); with
- * SA_F32 it is fp32 throughout.  Errors as for the fold.
+ * over events in a fixed order.  With SA_BF16 the backward keeps its
+ * per-event intermediates in bf16 and runs its products on the matrix cores
+ * (bf16 operands, fp32 accumulation); with SA_F32 it is fp32 throughout.
+ * Errors as for the fold.
  */
 size_t sa_action_fusion_workspace_size(int d, sa_dtype dtype, int64_t T, int n_types, int op);
 sa_status sa_action_fusion_forward(int d, sa_dtype dtype, int64_t T, int n_types, const void* e,
