@@ -230,16 +230,27 @@ bool mx_shape_ok(bool ta, bool tb, const float* A, int lda, int64_t sA, const fl
 
 }  // namespace
 
-hipError_t launch_gemm_mx(bool tb, bool out_bf16, const float* A, int lda, int64_t sA,
+hipError_t launch_gemm_mx(bool tb, bool out_bf16, bool a_bf16, const void* A, int lda, int64_t sA,
                           const float* B, int ldb, int64_t sB, void* C, int ldc, int64_t sC, int M,
                           int N, int K, int batch, hipStream_t st) {
   if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
-  if (batch > 65535 || !mx_shape_ok(false, tb, A, lda, sA, B, ldb, sB, M, N, K, K))
-    return hipErrorInvalidValue;
+  if (batch > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((M + kMxTile - 1) / kMxTile), (unsigned)((N + kMxTile - 1) / kMxTile),
                   (unsigned)batch);
-  return mx_dispatch(false, tb, out_bf16, grid, A, lda, sA, B, ldb, sB, C, ldc, sC, M, N, K, K, 0, 0,
-                     nullptr, st);
+  if (a_bf16) {
+    // bf16 A stored [row][k] (the STCA context): 16-byte aligned rows.
+    if (tb || out_bf16 || K % kMxK != 0 || lda % 8 != 0 || sA % 8 != 0 ||
+        ((uintptr_t)A & 15u) != 0 || N % 4 != 0 || ldb % 4 != 0 || sB % 4 != 0 ||
+        ((uintptr_t)B & 15u) != 0)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((sa_gemm_mx<false, false, false, bf16, float>), grid, dim3(256), 0, st,
+                       (const bf16*)A, lda, sA, B, ldb, sB, C, ldc, sC, M, N, K, K, 0, 0, nullptr);
+    return hipGetLastError();
+  }
+  const float* Af = (const float*)A;
+  if (!mx_shape_ok(false, tb, Af, lda, sA, B, ldb, sB, M, N, K, K)) return hipErrorInvalidValue;
+  return mx_dispatch(false, tb, out_bf16, grid, Af, lda, sA, B, ldb, sB, C, ldc, sC, M, N, K, K, 0,
+                     0, nullptr, st);
 }
 
 hipError_t launch_gemm_mx_sliced(bool ta, bool tb, const float* A, int lda, const float* B, int ldb,

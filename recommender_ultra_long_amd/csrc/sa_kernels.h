@@ -142,8 +142,9 @@ hipError_t launch_gemm(bool ta, bool tb, const float* A, int lda, const float* B
 // fp32 operands rounded to bf16 on the matrix cores, fp32 accumulation
 // (sa_gemm_mx.hip): C (fp32, or bf16 when out_bf16) = A B(k, n) per batch z,
 // A row-major, B(k, n) = tb ? B[n ldb + k] : B[k ldb + n].  K % 32 == 0 and
-// 16-byte aligned rows, else hipErrorInvalidValue.
-hipError_t launch_gemm_mx(bool tb, bool out_bf16, const float* A, int lda, int64_t sA,
+// 16-byte aligned rows, else hipErrorInvalidValue.  a_bf16: A is bf16 (then
+// tb and out_bf16 must be false).
+hipError_t launch_gemm_mx(bool tb, bool out_bf16, bool a_bf16, const void* A, int lda, int64_t sA,
                           const float* B, int ldb, int64_t sB, void* C, int ldc, int64_t sC, int M,
                           int N, int K, int batch, hipStream_t st);
 // The same with A(m, k) = ta ? A[k lda + m] : A[m lda + k] and the
@@ -204,10 +205,10 @@ hipError_t launch_action_small(int mode, int d, int n_types, const float* A, con
                                float* T3, float* dA, float* dW1, float* dW3, hipStream_t st);
 
 // Reordered single-query STCA attention core (sa_stca.hip).
-// U, X: bf16 device arrays.
+// U, X: bf16 device arrays; C fp32, or bf16 when c_bf16.
 hipError_t launch_stca_core(int D, int h, int B, const int64_t* x_off, const int64_t* t_off,
-                            const void* U, const void* X, int64_t L, int64_t rows, float* C,
-                            float* lse, hipStream_t st);
+                            const void* U, const void* X, int64_t L, int64_t rows, void* C,
+                            int c_bf16, float* lse, hipStream_t st);
 hipError_t launch_to_bf16(const float* a, int64_t n, void* b, hipStream_t st);
 
 // Argument blocks of the sketch kernels for a plan and a workspace (sa_api.cpp).

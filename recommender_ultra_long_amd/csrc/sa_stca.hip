@@ -69,15 +69,16 @@ __device__ __forceinline__ int user_of_target(const int64_t* t_off, int B, int64
 
 // grid = ceil(rows / 32), rows = R h; block 512 (8 waves).
 // U: [rows, D] bf16 (row r h + j), X: [L_total, D] bf16, C: [rows, D] fp32,
-// lse: [rows] (natural log; -inf for a user without history rows).
-template <int DW>
+// lse: [rows] (natural log; -inf for a user without history rows).  C is
+// written in bf16 when CBF (the value product rounds it to bf16 anyway).
+template <int DW, bool CBF>
 __global__ __launch_bounds__(512, 1) void sa_stca_core(const int64_t* __restrict__ x_off,
                                                       const int64_t* __restrict__ t_off, int B,
                                                       int h, const bf16* __restrict__ U,
                                                       const bf16* __restrict__ X,
                                                       int64_t nrows_x, int64_t rows,
                                                       float alpha, float scale,
-                                                      float* __restrict__ C,
+                                                      void* __restrict__ Cv,
                                                       float* __restrict__ lse) {
   constexpr int NW = 8;
   constexpr int D = DW * NW;
@@ -302,14 +303,21 @@ __global__ __launch_bounds__(512, 1) void sa_stca_core(const int64_t* __restrict
       for (int g = 0; g < 4; ++g) {
         const f32x4 v = {acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv,
                          acc[db][4 * g + 3] * inv};
-        *(f32x4*)(C + q * D + c0 + 32 * db + 8 * g + 4 * h2) = v;
+        const int64_t o = q * D + c0 + 32 * db + 8 * g + 4 * h2;
+        if constexpr (CBF) {
+          bf16x4 b;
+          b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+          *(bf16x4*)((bf16*)Cv + o) = b;
+        } else {
+          *(f32x4*)((float*)Cv + o) = v;
+        }
       }
   }
 }
 
 hipError_t launch_stca_core(int D, int h, int B, const int64_t* x_off, const int64_t* t_off,
-                            const void* Uv, const void* Xv, int64_t L, int64_t rows, float* C,
-                            float* lse, hipStream_t st) {
+                            const void* Uv, const void* Xv, int64_t L, int64_t rows, void* C,
+                            int c_bf16, float* lse, hipStream_t st) {
   const bf16* U = (const bf16*)Uv;
   const bf16* X = (const bf16*)Xv;
   if (rows <= 0) return hipSuccess;
@@ -317,12 +325,16 @@ hipError_t launch_stca_core(int D, int h, int B, const int64_t* x_off, const int
   const float scale = 1.0f / sqrtf((float)dh);
   const float alpha = scale * kLog2e;
   const dim3 grid((unsigned)((rows + 31) / 32));
+#define SA_STCA(DW_, CBF_)                                                                       \
+  hipLaunchKernelGGL((sa_stca_core<DW_, CBF_>), grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, \
+                     L, rows, alpha, scale, C, lse)
   switch (D) {
-    case 256: hipLaunchKernelGGL(sa_stca_core<32>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, L, rows, alpha, scale, C, lse); break;
-    case 512: hipLaunchKernelGGL(sa_stca_core<64>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, L, rows, alpha, scale, C, lse); break;
-    case 1024: hipLaunchKernelGGL(sa_stca_core<128>, grid, dim3(512), 0, st, x_off, t_off, B, h, U, X, L, rows, alpha, scale, C, lse); break;
+    case 256: if (c_bf16) SA_STCA(32, true); else SA_STCA(32, false); break;
+    case 512: if (c_bf16) SA_STCA(64, true); else SA_STCA(64, false); break;
+    case 1024: if (c_bf16) SA_STCA(128, true); else SA_STCA(128, false); break;
     default: return hipErrorInvalidValue;
   }
+#undef SA_STCA
   return hipGetLastError();
 }
 

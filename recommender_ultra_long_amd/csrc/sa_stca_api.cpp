@@ -18,7 +18,8 @@ bool stca_shape_ok(int B, int D, int h, int64_t L, int64_t R) {
          L < ((int64_t)1 << 34) && R >= 0 && (int64_t)R * h < ((int64_t)1 << 31) / 32 * 32;
 }
 
-// Qp [R, D] fp32 | Uf [R h, D] fp32 | U [R h, D] bf16 | C [R h, D] fp32 | lse [R h]
+// Qp [R, D] fp32 | Uf [R h, D] fp32 | U [R h, D] bf16 | C [R h, D] fp32 (or
+// bf16) | lse [R h]
 struct StcaPlan {
   size_t Qp, Uf, U, C, lse, total;
 };
@@ -86,19 +87,22 @@ sa_status sa_stca_attention(int B, int D, int h, int64_t L, int64_t R, const int
   // operands rounded to bf16 (the precision the core consumes them in); other
   // widths use the fp32 products.
   if (dh % 32 == 0) {
-    SA_TRY(launch_gemm_mx(false, false, Q, D, 0, Wq, D, 0, Qp, D, 0, (int)R, D, D, 1, st));
-    SA_TRY(launch_gemm_mx(true, true, Qp, D, dh, Wk, D, dh, w + p.U, h * D, D, (int)R, D, dh, h,
-                          st));
+    SA_TRY(launch_gemm_mx(false, false, false, Q, D, 0, Wq, D, 0, Qp, D, 0, (int)R, D, D, 1, st));
+    SA_TRY(launch_gemm_mx(true, true, false, Qp, D, dh, Wk, D, dh, w + p.U, h * D, D, (int)R, D,
+                          dh, h, st));
   } else {
     SA_TRY(launch_gemm(false, false, Q, D, Wq, D, Qp, D, (int)R, D, D, 1, 0, st));
     SA_TRY(launch_gemm_batched(false, true, Qp, D, dh, Wk, D, dh, Uf, h * D, D, (int)R, D, dh, h,
                                0, st));
     SA_TRY(launch_to_bf16(Uf, rows * D, w + p.U, st));
   }
-  // The length-dependent core: C[r, j] = softmax(X_u u_j / sqrt(d_h)) X_u.
-  SA_TRY(launch_stca_core(D, h, B, x_off, t_off, w + p.U, X, L, rows, C, l, st));
-  if (dh % 32 == 0)
-    SA_TRY(launch_gemm_mx(false, false, C, h * D, D, Wv, D, dh, o, D, dh, (int)R, dh, D, h, st));
+  // The length-dependent core: C[r, j] = softmax(X_u u_j / sqrt(d_h)) X_u,
+  // written in bf16 when the value product consumes it on the matrix cores.
+  const bool mx = dh % 32 == 0;
+  SA_TRY(launch_stca_core(D, h, B, x_off, t_off, w + p.U, X, L, rows, C, mx ? 1 : 0, l, st));
+  if (mx)
+    SA_TRY(launch_gemm_mx(false, false, true, C, h * D, D, Wv, D, dh, o, D, dh, (int)R, dh, D, h,
+                          st));
   else
     SA_TRY(launch_gemm_batched(false, false, C, h * D, D, Wv, D, dh, o, D, dh, (int)R, dh, D, h,
                                0, st));
