@@ -25,7 +25,8 @@ def _case(seed, x_lens, t_lens, D, h):
     return x_off, X, t_off, Q, W
 
 
-@pytest.mark.parametrize("D,h", [(256, 4), (256, 16), (512, 8), (1024, 16)])
+@pytest.mark.parametrize("D,h", [(256, 4), (256, 8), (256, 16), (512, 8), (512, 64), (1024, 1),
+                                 (1024, 8), (1024, 16)])
 def test_stca_attention(D, h):
     x_lens = [700, 0, 1, 33, 1024, 90]
     t_lens = [3, 2, 1, 0, 5, 4]
