@@ -40,9 +40,12 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=("all", "block", "stca"), default="all",
-                    help="block: time only the stacked block on the 32-user batch and print "
-                         "its JSON (for profiling the block's kernels alone)")
+    ap.add_argument("--part", choices=("all", "block", "stca", "token_wise", "action_fusion"),
+                    default="all",
+                    help="time one component alone and print its JSON (for profiling its "
+                         "kernels alone): the stacked block or the action-side fusion on the "
+                         "32-user batch, the STCA attention, or the token-wise variant on the "
+                         "step's workload")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step only: skip the token-wise, per-user, stacked-block and "
                          "action-fusion timings (profiling runs use this, so that the kernel "
@@ -370,15 +373,16 @@ def _stca_timing(sa, timed, dev, D=1024, h=16):
     return res
 
 
-def _extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop):
-    """Timings beside the step (not part of it): the token-wise normalised
-    variant on the step's workload, shared vs per-user tables and the stacked
-    block on the 32-user batch, and the action-side fusion."""
+def _tokenwise_timing(sa, timed, dev, prob, off, reps, dX=None, dP=None):
+    """The token-wise normalised variant (the vanilla-attention baseline of
+    Table 1) on the step's own workload: one pass forward (4 k d matrix flops
+    per token, no statistics pass), single-stage dX pass backward."""
     import torch
-    ex = {}
-    # The token-wise normalised variant (the vanilla-attention baseline of
-    # Table 1) on the step's own workload: one pass forward (4 k d matrix
-    # flops per token, no statistics pass), single-stage dX pass backward.
+    B, T = len(prob.offsets) - 1, prob.total_tokens
+    k, d = prob.workload.k, prob.workload.d
+    if dX is None:
+        dX = torch.empty((T, d), dtype=torch.float32, device=dev)
+        dP = torch.empty((k, d), dtype=torch.float32, device=dev)
     Stw = torch.empty((B, k, d), dtype=torch.float32, device=dev)
     lsetw = torch.empty((B, k), dtype=torch.float32, device=dev)
     prt = sa.make_problem(B, k, d, T, prob.X.dtype, token_wise=True)
@@ -391,10 +395,18 @@ def _extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop
     tw_bwd()
     ms_tf = timed(tw_fwd, reps)
     ms_tb = timed(tw_bwd, reps)
-    ex["token_wise"] = {
+    fwd_flop = 4.0 * k * d * T
+    return {
         "forward_ms": round(ms_tf, 5), "backward_ms": round(ms_tb, 5),
         "forward_frac_bf16_peak": round(fwd_flop / (ms_tf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(T / ((ms_tf + ms_tb) * 1e-3), 1)}
+
+
+def _extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop):
+    """Timings beside the step (not part of it): the token-wise normalised
+    variant on the step's workload, shared vs per-user tables and the stacked
+    block on the 32-user batch, and the action-side fusion."""
+    ex = {"token_wise": _tokenwise_timing(sa, timed, dev, prob, off, reps, dX, dP)}
     ex["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
     ex["block"] = _block_timing(sa, synth, timed, dev)
     ex["action_fusion"] = _action_timing(sa, timed, dev)
@@ -416,7 +428,7 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    if args.part in ("block", "stca"):
+    if args.part != "all":
         def timed_block(fn, reps):
             st = torch.cuda.current_stream()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -429,8 +441,15 @@ def main():
             return a.elapsed_time(b) / reps
         if args.part == "block":
             print(json.dumps({"block": _block_timing(sa, synth, timed_block, dev)}))
-        else:
+        elif args.part == "stca":
             print(json.dumps({"stca": _stca_timing(sa, timed_block, dev)}))
+        elif args.part == "action_fusion":
+            print(json.dumps({"action_fusion": _action_timing(sa, timed_block, dev)}))
+        else:
+            pw = synth.make_workload(args.workload, device=dev, with_dS=True)
+            pw_off = torch.as_tensor(pw.offsets, device=dev)
+            print(json.dumps({"token_wise": _tokenwise_timing(sa, timed_block, dev, pw, pw_off,
+                                                              args.steps)}))
         return
     prob = synth.make_workload(args.workload, device=dev, with_dS=True)
     w = prob.workload
