@@ -48,3 +48,35 @@ def test_history_row_order_does_not_matter():
     a, la = stca_attention_ref(x_off, X, t_off, Q, Wq, Wk, Wv, 2)
     b, lb = stca_attention_ref(x_off, X[perm], t_off, Q, Wq, Wk, Wv, 2)
     assert np.allclose(a, b, atol=1e-13) and np.allclose(la, lb, atol=1e-13)
+
+
+def test_lse_two_rows_closed_form():
+    # One head (d_h = D = 2), W_Q = W_K = I: the scores of rows a e1 and b e1
+    # for query c e1 are a c / sqrt(2) and b c / sqrt(2).  Their log-sum-exp
+    # is s_max + log(1 + exp(-delta)), delta = |s1 - s2|.
+    a, b, c = 3.0, -1.5, 2.0
+    X = np.array([[a, 0.0], [b, 0.0]])
+    Q = np.array([[c, 0.0]])
+    eye = np.eye(2)
+    _, lse = stca_attention_ref(np.array([0, 2]), X, np.array([0, 1]), Q, eye, eye, eye, 1)
+    s1, s2 = a * c / math.sqrt(2), b * c / math.sqrt(2)
+    want = max(s1, s2) + math.log1p(math.exp(-abs(s1 - s2)))
+    assert abs(max(s1, s2)) > 4.0          # the maximum is far from zero
+    assert abs(lse[0, 0] - want) < 1e-13
+
+
+def test_lse_matches_library_logsumexp_per_head():
+    from scipy.special import logsumexp
+
+    x_off, X, t_off, Q, (Wq, Wk, Wv) = _case(4, [9, 3], [2, 2], D=8, h=4)
+    Q = Q * 3.0                            # scores of several units
+    _, lse = stca_attention_ref(x_off, X, t_off, Q, Wq, Wk, Wv, 4)
+    # standard (unreordered) scores K q / sqrt(d_h) with K = X W_K per head
+    for r in range(4):
+        u = 0 if r < 2 else 1
+        Xu = X[x_off[u]:x_off[u + 1]]
+        for j in range(4):
+            cols = slice(2 * j, 2 * j + 2)
+            s = (Xu @ Wk[:, cols]) @ (Q[r] @ Wq[:, cols]) / math.sqrt(2)
+            assert abs(np.max(s)) > 0.5
+            assert abs(lse[r, j] - logsumexp(s)) < 1e-12
