@@ -12,23 +12,32 @@ item embedding plus an action-type embedding (reading notes Eq. (20); the
 additive form here is a stand-in for the SwiGLU fusion).
 
 Conventions
+  * Every tensor comes from numpy's PCG64 seeded with
+    SeedSequence(seed, spawn_key=(workload id, tensor tag, index)), where the
+    index is the user for per-user tensors (history rows, action ids, dS, a
+    per-user prototype table) and 0 for shared ones.  Any user's rows can be
+    regenerated on the host alone, without the rest of the batch and without
+    a GPU.
   * N(0, s2) means variance s2 (so P ~ N(0, 1/d) has standard deviation
-    d**-0.5).
-  * Floating-point samples are drawn in float32 by torch, then rounded to
-    bfloat16 (round-to-nearest-even) for bf16 workloads.
-  * Lengths come from numpy's PCG64 seeded with SeedSequence(seed,
-    spawn_key=(workload id, 0)); tensors from torch generators seeded with a
-    value derived from (seed, workload id, tensor tag), so every tensor is
-    independent and reproducible on a given device type.
+    d**-0.5).  Samples are drawn in float64, cast to float32, then rounded
+    to bfloat16 (round to nearest, ties to even) for bf16 workloads.
+  * Lengths come from PCG64 seeded with SeedSequence(seed, spawn_key=(workload
+    id, 0)).
+
+The numpy half (``user_rows``, ``prototype_table``, ``user_dS``) imports no
+torch, so worker processes of the test-suite oracle can regenerate a user's
+inputs cheaply; ``make_inputs`` and ``make_workload`` assemble torch tensors
+from it.
 """
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
-import torch
 
 
 @dataclasses.dataclass(frozen=True)
@@ -81,11 +90,64 @@ LOGNORMAL_MU = 11.514
 LOGNORMAL_SIGMA = 0.5
 N_ACTION_TYPES = 8
 
-_TAGS = {"X": 1, "P": 2, "dS": 3, "act_table": 4, "act_ids": 5}
+TAGS = {"X": 1, "P": 2, "dS": 3, "act_table": 4, "act_ids": 5}
+
+# Host threads drawing a batch's rows (numpy's generators release the GIL
+# while filling arrays).
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
-def _seed_for(seed, wid, tag):
-    return (int(seed) * 1_000_003 + int(wid) * 10_007 + _TAGS[tag] * 101) & 0x7FFFFFFFFFFFFFFF
+def rng_for(seed, wid, tag, index=0):
+    """The generator of one tensor (tag) of workload wid, for one user or
+    shared (index 0)."""
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence(int(seed), spawn_key=(int(wid), TAGS[tag], int(index)))))
+
+
+def round_bf16(a):
+    """float32 array -> float32 array of the nearest bfloat16 values (ties to
+    even).  Finite inputs only (normal samples never hold NaN or inf)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _to_dtype_values(a32, dtype):
+    return round_bf16(a32) if dtype == "bf16" else a32
+
+
+def action_table(seed, wid, d):
+    """8 x d action-type embeddings, N(0, 0.5), float32."""
+    g = rng_for(seed, wid, "act_table", 0)
+    return (g.standard_normal((N_ACTION_TYPES, d)) * math.sqrt(0.5)).astype(np.float32)
+
+
+def user_rows(seed, wid, u, n, d, dtype, x_kind="normal"):
+    """History rows of user u: float32 values exactly representable in dtype.
+
+    x_kind "normal": x_i ~ N(0, I).  "item_action": x_i = e_i + a[t_i] with
+    e_i ~ N(0, I), t_i ~ U{0..7} and the action table of ``action_table``,
+    summed in float32 and then rounded to dtype."""
+    g = rng_for(seed, wid, "X", u)
+    e = g.standard_normal((int(n), d)).astype(np.float32)
+    if x_kind == "item_action":
+        ids = rng_for(seed, wid, "act_ids", u).integers(0, N_ACTION_TYPES, size=int(n))
+        e += action_table(seed, wid, d)[ids]
+    elif x_kind != "normal":
+        raise ValueError(x_kind)
+    return _to_dtype_values(e, dtype)
+
+
+def prototype_table(seed, wid, k, d, dtype, p_std, index=0):
+    """k x d prototypes ~ N(0, p_std^2): the shared table (index 0) or user
+    index - 1's own table (index = u + 1)."""
+    g = rng_for(seed, wid, "P", index)
+    return _to_dtype_values((g.standard_normal((k, d)) * p_std).astype(np.float32), dtype)
+
+
+def user_dS(seed, wid, u, k, d):
+    """Upstream gradient of user u's sketch, k x d, N(0, 1), float32."""
+    return rng_for(seed, wid, "dS", u).standard_normal((k, d)).astype(np.float32)
 
 
 def workload_lengths(w: Workload, seed: int = 0) -> np.ndarray:
@@ -107,42 +169,48 @@ def offsets_from_lengths(lengths) -> np.ndarray:
     return off
 
 
-def _torch_dtype(name):
-    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+@dataclasses.dataclass(frozen=True)
+class GenSpec:
+    """Everything needed to regenerate a problem's tensors user by user."""
+    seed: int
+    wid: int
+    k: int
+    d: int
+    dtype: str
+    x_kind: str
+    p_std: float
+    per_user_p: bool
 
+    def rows(self, u, n):
+        return user_rows(self.seed, self.wid, u, n, self.d, self.dtype, self.x_kind)
 
-def _gen(device, seed):
-    g = torch.Generator(device=device)
-    g.manual_seed(seed)
-    return g
+    def table(self, u=None):
+        """The shared table (u None) or user u's own table."""
+        return prototype_table(self.seed, self.wid, self.k, self.d, self.dtype, self.p_std,
+                               0 if u is None else u + 1)
 
-
-def _normal_rows(T, d, std, dtype, device, seed, chunk_rows=1 << 22):
-    """T x d samples of N(0, std^2), drawn in float32 and cast to dtype in
-    row chunks so that the float32 staging stays bounded."""
-    out = torch.empty((T, d), dtype=dtype, device=device)
-    g = _gen(device, seed)
-    for r0 in range(0, T, chunk_rows):
-        r1 = min(T, r0 + chunk_rows)
-        tmp = torch.randn((r1 - r0, d), generator=g, device=device, dtype=torch.float32)
-        if std != 1.0:
-            tmp.mul_(std)
-        out[r0:r1] = tmp.to(dtype)
-    return out
+    def dS(self, u):
+        return user_dS(self.seed, self.wid, u, self.k, self.d)
 
 
 @dataclasses.dataclass
 class Problem:
     workload: Workload
     offsets: np.ndarray          # int64 [B+1], host
-    X: torch.Tensor              # [T, d] f32 or bf16
-    P: torch.Tensor              # [k, d] (or [B, k, d] per user), same dtype as X
-    dS: torch.Tensor | None      # [B, k, d] f32
+    X: "torch.Tensor"            # [T, d] f32 or bf16
+    P: "torch.Tensor"            # [k, d] (or [B, k, d] per user), same dtype as X
+    dS: "torch.Tensor | None"    # [B, k, d] f32
     mass_norm: bool
+    gen: GenSpec | None = None
 
     @property
     def total_tokens(self):
         return int(self.offsets[-1])
+
+
+def _torch_dtype(name):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
 
 
 def make_inputs(lengths, k, d, dtype="bf16", device="cpu", seed=0, wid=0,
@@ -154,41 +222,39 @@ def make_inputs(lengths, k, d, dtype="bf16", device="cpu", seed=0, wid=0,
     logits (the standard deviation of each affinity is p_std when X ~ N(0, 1)).
     per_user_p draws one k x d table per user (P is then [B, k, d]).
     """
+    import torch
+
     lengths = np.asarray(lengths, dtype=np.int64)
     off = offsets_from_lengths(lengths)
     T = int(off[-1])
+    B = int(lengths.size)
     tdt = _torch_dtype(dtype)
     if p_std is None:
         p_std = 1.0 / math.sqrt(d)
-    if x_kind == "normal":
-        X = _normal_rows(T, d, 1.0, tdt, device, _seed_for(seed, wid, "X"))
-    elif x_kind == "item_action":
-        g = _gen(device, _seed_for(seed, wid, "act_table"))
-        table = torch.randn((N_ACTION_TYPES, d), generator=g, device=device,
-                            dtype=torch.float32) * math.sqrt(0.5)
-        gi = _gen(device, _seed_for(seed, wid, "act_ids"))
-        X = torch.empty((T, d), dtype=tdt, device=device)
-        gx = _gen(device, _seed_for(seed, wid, "X"))
-        step = 1 << 22
-        for r0 in range(0, T, step):
-            r1 = min(T, r0 + step)
-            ids = torch.randint(0, N_ACTION_TYPES, (r1 - r0,), generator=gi, device=device)
-            e = torch.randn((r1 - r0, d), generator=gx, device=device, dtype=torch.float32)
-            X[r0:r1] = (e + table[ids]).to(tdt)
+    spec = GenSpec(int(seed), int(wid), int(k), int(d), dtype, x_kind, float(p_std),
+                   bool(per_user_p))
+    X = torch.empty((T, d), dtype=tdt, device=device)
+    # Users are drawn in parallel host threads and copied in user order.
+    with concurrent.futures.ThreadPoolExecutor(_THREADS) as ex:
+        futs = [ex.submit(spec.rows, u, int(lengths[u])) for u in range(B)]
+        for u, f in enumerate(futs):
+            lo, hi = int(off[u]), int(off[u + 1])
+            rows = f.result()
+            futs[u] = None
+            if hi > lo:
+                X[lo:hi].copy_(torch.from_numpy(rows).to(tdt))
+    if per_user_p:
+        P = torch.from_numpy(np.stack([spec.table(u) for u in range(B)])).to(tdt).to(device)
     else:
-        raise ValueError(x_kind)
-    gp = _gen(device, _seed_for(seed, wid, "P"))
-    pshape = (int(lengths.size), k, d) if per_user_p else (k, d)
-    P = (torch.randn(pshape, generator=gp, device=device, dtype=torch.float32) * p_std).to(tdt)
+        P = torch.from_numpy(spec.table()).to(tdt).to(device)
     dS = None
     if with_dS:
-        gd = _gen(device, _seed_for(seed, wid, "dS"))
-        dS = torch.randn((lengths.size, k, d), generator=gd, device=device, dtype=torch.float32)
+        dS = torch.from_numpy(np.stack([spec.dS(u) for u in range(B)]).reshape(B, k, d)).to(device)
     if workload is None:
-        workload = Workload(wid, "custom", int(lengths.size), k, d, dtype, mass_norm,
+        workload = Workload(wid, "custom", B, k, d, dtype, mass_norm,
                             "custom", int(lengths.min()) if lengths.size else 0,
                             int(lengths.max()) if lengths.size else 0, x_kind, with_dS)
-    return Problem(workload, off, X, P, dS, mass_norm)
+    return Problem(workload, off, X, P, dS, mass_norm, spec)
 
 
 def make_workload(name: str, device="cpu", seed=0, with_dS=None) -> Problem:
@@ -200,6 +266,7 @@ def make_workload(name: str, device="cpu", seed=0, with_dS=None) -> Problem:
                        None, with_dS, w.mass_norm, w)
 
 
-def to_f64(t: torch.Tensor) -> np.ndarray:
+def to_f64(t) -> np.ndarray:
     """Exact upcast of a float32 / bfloat16 tensor to a float64 numpy array."""
+    import torch
     return t.detach().to("cpu").to(torch.float64).numpy()

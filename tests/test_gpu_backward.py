@@ -9,7 +9,7 @@ import torch
 
 from oracle.sa_ref import sa_backward_ref
 from recommender_ultra_long_amd import sa, synth
-from sa_testutil import TOL_BF16, TOL_F32, rel_err, say
+from sa_testutil import TOL_BF16, TOL_F32, check_backward_all_users, record, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -83,40 +83,26 @@ def test_uniform_dS_gives_zero_dP():
     assert rel_err(dX.cpu().numpy(), v.expand(2500, 128).cpu().numpy()) <= 2e-2
 
 
-def test_backward32_workload_full_size():
-    """The 32-user backward workload at full size.  dX is checked against the
-    oracle on sampled users (each user's dX depends only on its own tokens);
-    dP, which sums over all users, is checked (i) against the oracle on two
-    single-user sub-batches and (ii) for additivity: the full-batch dP equals
-    the sum of the per-user dPs computed by separate GPU calls."""
+def test_backward32_workload_every_user():
+    """The 32-user backward workload at full size: dX of every user and the
+    batch's dP (summed over users, the table is shared) against the oracle,
+    which runs user by user in worker processes.  A single-user call also
+    reproduces the batch call's dX bit for bit."""
     prob = synth.make_workload("backward32_k1024", device="cuda")
     say(f"case backward32_k1024 T={prob.total_tokens}")
     off = torch.as_tensor(prob.offsets, device="cuda")
     S, lse, mass = sa.sa_forward(off, prob.X, prob.P)
     dX, dP = sa.sa_backward(off, prob.X, prob.P, prob.dS, lse)
     torch.cuda.synchronize()
-    lens = np.diff(prob.offsets)
-    users = sorted({0, 31, int(np.argmin(lens)), int(np.argmax(lens))})
-    P64 = synth.to_f64(prob.P)
-    dP_sum = torch.zeros_like(dP, dtype=torch.float64)
-    for u in range(32):
-        lo, hi = int(prob.offsets[u]), int(prob.offsets[u + 1])
-        Xu, dSu = prob.X[lo:hi].contiguous(), prob.dS[u:u + 1].contiguous()
-        offu = torch.tensor([0, hi - lo], device="cuda")
-        dXu, dPu = sa.sa_backward(offu, Xu, prob.P, dSu, lse[lo:hi].clone())
-        dP_sum += dPu.double()
-        if u in users:
-            dXr, dPr = sa_backward_ref(np.array([0, hi - lo]), synth.to_f64(Xu), P64,
-                                       synth.to_f64(dSu))
-            e1 = rel_err(dX[lo:hi].cpu().numpy(), dXr)
-            e2 = rel_err(dPu.cpu().numpy(), dPr)
-            say(f"  user {u} n={hi - lo}: dX {e1:.2e} dP_u {e2:.2e}")
-            assert e1 <= TOL_BF16 and e2 <= TOL_BF16
-            # the single-user call reproduces the batch call's dX bit for bit
-            assert torch.equal(dXu, dX[lo:hi])
-    e = rel_err(dP.double().cpu().numpy(), dP_sum.cpu().numpy())
-    say(f"  dP additivity {e:.2e}")
-    assert e <= 1e-5
+    edx, edp = check_backward_all_users(prob, dX, dP, TOL_BF16)
+    record("backward32_k1024, all 32 users", dX=edx, dP=edp)
+    u = int(np.argmax(np.diff(prob.offsets)))
+    lo, hi = int(prob.offsets[u]), int(prob.offsets[u + 1])
+    offu = torch.tensor([0, hi - lo], device="cuda")
+    dXu, _ = sa.sa_backward(offu, prob.X[lo:hi].contiguous(), prob.P, prob.dS[u:u + 1].contiguous(),
+                            lse[lo:hi].clone())
+    torch.cuda.synchronize()
+    assert torch.equal(dXu, dX[lo:hi])
 
 
 def test_bitwise_deterministic():

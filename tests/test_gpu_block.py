@@ -11,7 +11,7 @@ import torch
 
 from oracle.block import block_backward_ref, block_forward_ref
 from recommender_ultra_long_amd import sa, synth
-from sa_testutil import TOL_BF16, TOL_F32, rel_err, say
+from sa_testutil import TOL_BF16, TOL_F32, record, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +91,33 @@ def test_block_backward_is_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a, b)
+
+
+def test_block_two_layers_k1024_long_user():
+    """The configuration the benchmark times (k = 1024, d = 128, bf16, two
+    layers) with users of 12,000 and 3,000 tokens and an empty one."""
+    lengths = [12000, 0, 3000]
+    say("case block k=1024 d=128 bf16 2 layers, users 12000/0/3000")
+    prob, out, dX, dP0, grads, X64, P064, ref_layers, dout = _run(lengths, 1024, 128, "bf16", 2,
+                                                                  seed=31)
+    ref_out, _ = block_forward_ref(prob.offsets, X64, P064, ref_layers)
+    rdX, rdP0, rgrads = block_backward_ref(prob.offsets, X64, P064, ref_layers, dout)
+    worst = {"out": 0.0, "dX": 0.0}
+    for u in range(len(lengths)):
+        e = rel_err(out[u].cpu().numpy(), ref_out[u])
+        assert e <= TOL_BF16, f"user {u}: out rel err {e:.3e}"
+        worst["out"] = max(worst["out"], e)
+        lo, hi = int(prob.offsets[u]), int(prob.offsets[u + 1])
+        if hi > lo:
+            e = rel_err(dX[lo:hi].cpu().numpy(), rdX[lo:hi])
+            assert e <= TOL_BF16, f"user {u}: dX rel err {e:.3e}"
+            worst["dX"] = max(worst["dX"], e)
+    worst["dP0"] = rel_err(dP0.cpu().numpy(), rdP0)
+    assert worst["dP0"] <= TOL_BF16
+    wg = 0.0
+    for li in range(2):
+        for ok, ck in KEYMAP.items():
+            e = rel_err(grads[li][ck].cpu().numpy(), rgrads[li][ok])
+            assert e <= TOL_BF16, f"layer {li} d{ck} rel err {e:.3e}"
+            wg = max(wg, e)
+    record("stacked block, 2 layers, k=1024, users 12000/0/3000", **worst, params=wg)

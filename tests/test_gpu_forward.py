@@ -12,7 +12,8 @@ import torch
 
 from oracle.sa_ref import sa_forward_ref
 from recommender_ultra_long_amd import sa, synth
-from sa_testutil import (TOL_BF16, TOL_F32, check_forward_users, gpu_forward, rel_err, say)
+from sa_testutil import (TOL_BF16, TOL_F32, check_forward_all_users, check_forward_users,
+                         gpu_forward, record, rel_err, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,8 +27,8 @@ def test_fp32_workload_n4096_k64_d32():
     prob = synth.make_workload("fp32_n4096_k64_d32", device="cuda")
     say("case fp32_n4096_k64_d32")
     S, lse, mass = gpu_forward(prob)
-    e = check_forward_users(prob, S, lse, mass, [0], TOL_F32)
-    say(f"  S rel err {e:.2e}")
+    eS, em, el = check_forward_all_users(prob, S, lse, mass, TOL_F32)
+    record("fp32_n4096_k64_d32", S=eS, mass=em, lse_abs=el)
 
 
 @pytest.mark.parametrize("dtype,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
@@ -69,32 +70,31 @@ def test_bf16_workload_n100k_k1024_d128():
     prob = synth.make_workload("bf16_n100k_k1024_d128", device="cuda")
     say("case bf16_n100k_k1024_d128")
     S, lse, mass = gpu_forward(prob)
-    e = check_forward_users(prob, S, lse, mass, [0], TOL_BF16)
-    say(f"  S rel err {e:.2e}")
+    eS, em, el = check_forward_all_users(prob, S, lse, mass, TOL_BF16)
+    record("bf16_n100k_k1024_d128", S=eS, mass=em, lse_abs=el)
 
 
-def test_ragged64_massnorm_sampled_users():
+def test_ragged64_massnorm_every_user():
+    """The 64-user mass-normalised batch: every user against the oracle."""
     prob = synth.make_workload("ragged64_k1024_massnorm", device="cuda")
     say(f"case ragged64_k1024_massnorm T={prob.total_tokens}")
     S, lse, mass = gpu_forward(prob)
-    lens = np.diff(prob.offsets)
-    users = sorted({0, 63, int(np.argmin(lens)), int(np.argmax(lens)), 17})
-    e = check_forward_users(prob, S, lse, mass, users, TOL_BF16)
-    say(f"  S rel err {e:.2e} on users {users}")
+    eS, em, el = check_forward_all_users(prob, S, lse, mass, TOL_BF16)
+    record("ragged64_k1024_massnorm, all 64 users", S=eS, mass=em, lse_abs=el)
 
 
-def test_ragged256_lognormal_sampled_users():
+def test_ragged256_lognormal_every_user():
+    """The 256-user lognormal batch (k = 512, item + action rows): every user
+    against the oracle, plus a property that holds at any size: each user's
+    masses add up to its token count (the columns of A sum to one)."""
     prob = synth.make_workload("ragged256_lognormal_k512", device="cuda")
     say(f"case ragged256_lognormal_k512 T={prob.total_tokens}")
     S, lse, mass = gpu_forward(prob)
     lens = np.diff(prob.offsets)
-    users = sorted({0, 255, int(np.argmin(lens)), 100})
-    e = check_forward_users(prob, S, lse, mass, users, TOL_BF16)
-    say(f"  S rel err {e:.2e} on users {users}")
-    # every user, via properties that hold at any size: masses add up to the
-    # user's token count (column sums of A are one).
     tot = mass.double().sum(dim=1).cpu().numpy()
     np.testing.assert_allclose(tot, lens, rtol=1e-3)
+    eS, em, el = check_forward_all_users(prob, S, lse, mass, TOL_BF16)
+    record("ragged256_lognormal_k512, all 256 users", S=eS, mass=em, lse_abs=el)
 
 
 def test_sum_over_prototypes_is_sum_of_tokens():
