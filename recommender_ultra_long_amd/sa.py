@@ -16,7 +16,10 @@ import os
 import numpy as np
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsa.so")
+# SA_LIBRARY_PATH selects another build of the same library (the host-side
+# AddressSanitizer build of the CPU checks).
+_LIB_PATH = os.environ.get("SA_LIBRARY_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libsa.so")
 _lib = None
 
 SA_OK = 0
@@ -176,6 +179,74 @@ def workspace_size(problem, op=SA_OP_FORWARD):
     return int(load().sa_workspace_size(ctypes.byref(problem), int(op)))
 
 
+
+# ---------------------------------------------------------------------------
+# Argument checks.  Every public call checks its tensors before the first
+# library call: the kernels take raw pointers and sizes, so a wrong dtype,
+# shape or stride would otherwise be read as something else.  Mismatches raise
+# ValueError; device placement is checked last, so that the dtype and shape
+# checks also run on tensors that live on the host.
+
+_FLOATS = (torch.float32, torch.bfloat16)
+
+
+def _expect(name, t, dtype=None, shape=None, dtypes=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(device, **tensors):
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_offsets_tensor(offsets):
+    if isinstance(offsets, torch.Tensor):
+        if offsets.dim() != 1 or offsets.numel() < 2:
+            raise ValueError(f"offsets must be 1-D with at least 2 entries, got {tuple(offsets.shape)}")
+        if offsets.dtype not in (torch.int64, torch.int32):
+            raise ValueError(f"offsets must be an integer tensor, got {offsets.dtype}")
+    else:
+        arr = np.asarray(offsets)
+        if arr.ndim != 1 or arr.size < 2 or not np.issubdtype(arr.dtype, np.integer):
+            raise ValueError("offsets must be a 1-D integer array with at least 2 entries")
+
+
+def _check_workspace(workspace, device):
+    if workspace is not None:
+        _expect("workspace", workspace, dtype=torch.uint8)
+        _on_device(device, workspace=workspace)
+
+
+def _check_sketch_args(offsets, X, P):
+    """Shared checks of sa_forward / sa_backward: returns (B, T, d, k, per_user)."""
+    _check_offsets_tensor(offsets)
+    B = (offsets.numel() if isinstance(offsets, torch.Tensor) else len(offsets)) - 1
+    _expect("X", X, dtypes=_FLOATS)
+    if X.dim() != 2:
+        raise ValueError(f"X must be [T, d], got {tuple(X.shape)}")
+    _expect("P", P, dtype=X.dtype)
+    T, d = X.shape
+    if P.shape[-1] != d:
+        raise ValueError(f"P's last dimension must equal X's width {d}, got {tuple(P.shape)}")
+    k, per_user = _tables(P, B)
+    return B, T, d, k, per_user
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -226,12 +297,15 @@ def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, work
     copied to X's device); X [T, d] and P float32 or bfloat16 on the GPU, P
     either [k, d] (shared) or [B, k, d] (one table per user).  Returns
     (S [B, k, d] f32, lse [T] f32 or None, mass [B, k] f32 or None)."""
-    lib = load()
+    B, T, d, k, per_user = _check_sketch_args(offsets, X, P)
+    _expect("S", S, torch.float32, (B, k, d), optional=True)
+    _expect("lse", lse, torch.float32, (T,), optional=True)
+    _expect("mass", mass, torch.float32, (B, k), optional=True)
     dev = P.device
+    _check_workspace(workspace, dev)
+    _on_device(dev, X=X, S=S, lse=lse, mass=mass)
+    lib = load()
     off = _device_offsets(offsets, dev)
-    B = off.numel() - 1
-    T, d = X.shape
-    k, per_user = _tables(P, B)
     pr = make_problem(B, k, d, T, X.dtype, mass_norm, per_user)
     if S is None:
         S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
@@ -255,12 +329,16 @@ def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, work
 def tokenwise_forward(offsets, X, P, S=None, lse=None, workspace=None, stream=None):
     """Calls sa_forward with SA_FLAG_TOKEN_WISE (the vanilla-attention baseline:
     softmax over each user's tokens).  Returns (S [B, k, d] f32, lse [B, k] f32)."""
-    lib = load()
+    B, T, d, k, per_user = _check_sketch_args(offsets, X, P)
+    if per_user:
+        raise ValueError("the token-wise variant takes one shared [k, d] table")
+    _expect("S", S, torch.float32, (B, k, d), optional=True)
+    _expect("lse", lse, torch.float32, (B, k), optional=True)
     dev = P.device
+    _check_workspace(workspace, dev)
+    _on_device(dev, X=X, S=S, lse=lse)
+    lib = load()
     off = _device_offsets(offsets, dev)
-    B = off.numel() - 1
-    T, d = X.shape
-    k = P.shape[0]
     pr = make_problem(B, k, d, T, X.dtype, token_wise=True)
     if S is None:
         S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
@@ -278,12 +356,19 @@ def tokenwise_forward(offsets, X, P, S=None, lse=None, workspace=None, stream=No
 def tokenwise_backward(offsets, X, P, dS, S, lse, dX=None, dP=None, workspace=None, stream=None):
     """Calls sa_backward with SA_FLAG_TOKEN_WISE, given the token-wise
     forward's S [B, k, d] and lse [B, k].  Returns (dX [T, d], dP [k, d])."""
-    lib = load()
+    B, T, d, k, per_user = _check_sketch_args(offsets, X, P)
+    if per_user:
+        raise ValueError("the token-wise variant takes one shared [k, d] table")
+    _expect("dS", dS, torch.float32, (B, k, d))
+    _expect("S", S, torch.float32, (B, k, d))
+    _expect("lse", lse, torch.float32, (B, k))
+    _expect("dX", dX, torch.float32, (T, d), optional=True)
+    _expect("dP", dP, torch.float32, (k, d), optional=True)
     dev = P.device
+    _check_workspace(workspace, dev)
+    _on_device(dev, X=X, dS=dS, S=S, lse=lse, dX=dX, dP=dP)
+    lib = load()
     off = _device_offsets(offsets, dev)
-    B = off.numel() - 1
-    T, d = X.shape
-    k = P.shape[0]
     pr = make_problem(B, k, d, T, X.dtype, token_wise=True)
     if dX is None:
         dX = torch.empty((T, d), dtype=torch.float32, device=dev)
@@ -302,12 +387,18 @@ def sa_backward(offsets, X, P, dS, lse=None, S=None, mass=None, mass_norm=False,
                 dP=None, workspace=None, stream=None, timer=None):
     """Calls sa_backward.  Returns (dX [T, d] f32, dP f32 shaped like P:
     [k, d] summed over users, or [B, k, d] per user)."""
-    lib = load()
+    B, T, d, k, per_user = _check_sketch_args(offsets, X, P)
+    _expect("dS", dS, torch.float32, (B, k, d))
+    _expect("lse", lse, torch.float32, (T,), optional=True)
+    _expect("S", S, torch.float32, (B, k, d), optional=not mass_norm)
+    _expect("mass", mass, torch.float32, (B, k), optional=not mass_norm)
+    _expect("dX", dX, torch.float32, (T, d), optional=True)
+    _expect("dP", dP, torch.float32, tuple(P.shape), optional=True)
     dev = P.device
+    _check_workspace(workspace, dev)
+    _on_device(dev, X=X, dS=dS, lse=lse, S=S, mass=mass, dX=dX, dP=dP)
+    lib = load()
     off = _device_offsets(offsets, dev)
-    B = off.numel() - 1
-    T, d = X.shape
-    k, per_user = _tables(P, B)
     pr = make_problem(B, k, d, T, X.dtype, mass_norm, per_user)
     if dX is None:
         dX = torch.empty((T, d), dtype=torch.float32, device=dev)
@@ -334,8 +425,15 @@ def _dtype_code(dtype):
 def fold_prototypes(P, Wq, Wk, P_eff=None, stream=None):
     """Calls sa_fold_prototypes: P_eff = P W_Q W_K^T ([k, d], P's dtype), the
     prototype table whose affinities are Eq. (6)'s projected ones."""
-    lib = load()
+    _expect("P", P, dtypes=_FLOATS)
+    if P.dim() != 2:
+        raise ValueError(f"P must be [k, d], got {tuple(P.shape)}")
     k, d = P.shape
+    _expect("Wq", Wq, torch.float32, (d, d))
+    _expect("Wk", Wk, torch.float32, (d, d))
+    _expect("P_eff", P_eff, P.dtype, (k, d), optional=True)
+    _on_device(P.device, Wq=Wq, Wk=Wk, P_eff=P_eff)
+    lib = load()
     if P_eff is None:
         P_eff = torch.empty_like(P)
     st = lib.sa_fold_prototypes(int(k), int(d), _dtype_code(P.dtype), _ptr(P), _ptr(Wq), _ptr(Wk),
@@ -348,9 +446,17 @@ def fold_prototypes(P, Wq, Wk, P_eff=None, stream=None):
 def fold_prototypes_backward(P, Wq, Wk, dP_eff, workspace=None, stream=None):
     """Calls sa_fold_prototypes_backward.  Returns (dP [k, d], dW_Q [d, d],
     dW_K [d, d]), all float32."""
-    lib = load()
+    _expect("P", P, dtypes=_FLOATS)
+    if P.dim() != 2:
+        raise ValueError(f"P must be [k, d], got {tuple(P.shape)}")
     k, d = P.shape
+    _expect("Wq", Wq, torch.float32, (d, d))
+    _expect("Wk", Wk, torch.float32, (d, d))
+    _expect("dP_eff", dP_eff, torch.float32, (k, d))
     dev = P.device
+    _check_workspace(workspace, dev)
+    _on_device(dev, Wq=Wq, Wk=Wk, dP_eff=dP_eff)
+    lib = load()
     dP = torch.empty((k, d), dtype=torch.float32, device=dev)
     dWq = torch.empty((d, d), dtype=torch.float32, device=dev)
     dWk = torch.empty((d, d), dtype=torch.float32, device=dev)
@@ -363,6 +469,21 @@ def fold_prototypes_backward(P, Wq, Wk, dP_eff, workspace=None, stream=None):
     if st != SA_OK:
         raise SAError(st, "sa_fold_prototypes_backward")
     return dP, dWq, dWk
+
+
+def _layer_shapes(d):
+    return {"Wq": (d, d), "Wk": (d, d), "ln1_g": (d,), "ln1_b": (d,), "W1": (d, 2 * d),
+            "W3": (d, 2 * d), "W2": (2 * d, d), "ln2_g": (d,), "ln2_b": (d,)}
+
+
+def _check_layers(name, layers, d, device):
+    shapes = _layer_shapes(d)
+    for i, L in enumerate(layers):
+        for key in BLOCK_LAYER_KEYS:
+            t = L.get(key) if isinstance(L, dict) else None
+            _expect(f"{name}[{i}]['{key}']", t, torch.float32, shapes[key])
+    for L in layers:
+        _on_device(device, **L)
 
 
 def _layer_array(layers):
@@ -386,12 +507,24 @@ def block_forward(offsets, X, P0, layers, out=None, workspace=None, stream=None)
     X [T, d] (f32 or bf16), P0 [k, d] f32, layers: list of dicts of f32 device
     tensors keyed by BLOCK_LAYER_KEYS.  Returns (out [B, k, d] f32, workspace);
     pass the same workspace to block_backward."""
-    lib = load()
+    _check_offsets_tensor(offsets)
+    _expect("X", X, dtypes=_FLOATS)
+    if X.dim() != 2:
+        raise ValueError(f"X must be [T, d], got {tuple(X.shape)}")
+    T, d = X.shape
+    _expect("P0", P0, torch.float32)
+    if P0.dim() != 2 or P0.shape[1] != d:
+        raise ValueError(f"P0 must be [k, {d}], got {tuple(P0.shape)}")
+    k = P0.shape[0]
     dev = P0.device
+    _check_layers("layers", layers, d, dev)
+    _on_device(dev, X=X)
+    _check_workspace(workspace, dev)
+    lib = load()
     off = _device_offsets(offsets, dev)
     B = off.numel() - 1
-    T, d = X.shape
-    k = P0.shape[0]
+    _expect("out", out, torch.float32, (B, k, d), optional=True)
+    _on_device(dev, out=out)
     pr = make_problem(B, k, d, T, X.dtype)
     if out is None:
         out = torch.empty((B, k, d), dtype=torch.float32, device=dev)
@@ -411,12 +544,29 @@ def block_backward(offsets, X, P0, layers, dout, workspace, dX=None, dP0=None, g
     """Calls sa_block_backward with the workspace of the matching
     block_forward.  Returns (dX [T, d], dP0 [k, d], grads: list of dicts like
     layers), all f32."""
-    lib = load()
+    _check_offsets_tensor(offsets)
+    _expect("X", X, dtypes=_FLOATS)
+    if X.dim() != 2:
+        raise ValueError(f"X must be [T, d], got {tuple(X.shape)}")
+    T, d = X.shape
+    _expect("P0", P0, torch.float32)
+    if P0.dim() != 2 or P0.shape[1] != d:
+        raise ValueError(f"P0 must be [k, {d}], got {tuple(P0.shape)}")
+    k = P0.shape[0]
     dev = P0.device
+    _check_layers("layers", layers, d, dev)
+    _on_device(dev, X=X)
+    if grads is not None:
+        _check_layers("grads", grads, d, dev)
+    _expect("workspace", workspace, torch.uint8)
+    _on_device(dev, workspace=workspace)
+    lib = load()
     off = _device_offsets(offsets, dev)
     B = off.numel() - 1
-    T, d = X.shape
-    k = P0.shape[0]
+    _expect("dout", dout, torch.float32, (B, k, d))
+    _expect("dX", dX, torch.float32, (T, d), optional=True)
+    _expect("dP0", dP0, torch.float32, (k, d), optional=True)
+    _on_device(dev, dout=dout, dX=dX, dP0=dP0)
     pr = make_problem(B, k, d, T, X.dtype)
     if dX is None:
         dX = torch.empty((T, d), dtype=torch.float32, device=dev)
@@ -440,13 +590,31 @@ def _action_ws(d, dtype, T, n_types, op, device, workspace):
     return _workspace(n, device, workspace)
 
 
+def _check_action_args(e, types, A, W1, W3, W2, workspace):
+    _expect("e", e, dtypes=_FLOATS)
+    if e.dim() != 2:
+        raise ValueError(f"e must be [T, d], got {tuple(e.shape)}")
+    T, d = e.shape
+    _expect("types", types, torch.int32, (T,))
+    _expect("A", A, torch.float32)
+    if A.dim() != 2 or A.shape[1] != d:
+        raise ValueError(f"A must be [n_types, {d}], got {tuple(A.shape)}")
+    _expect("W1", W1, torch.float32, (2 * d, 2 * d))
+    _expect("W3", W3, torch.float32, (2 * d, 2 * d))
+    _expect("W2", W2, torch.float32, (2 * d, d))
+    _on_device(e.device, types=types, A=A, W1=W1, W3=W3, W2=W2)
+    _check_workspace(workspace, e.device)
+    return T, d, A.shape[0]
+
+
 def action_fusion_forward(e, types, A, W1, W3, W2, x=None, workspace=None, stream=None):
     """Calls sa_action_fusion_forward: x = e + SwiGLU([e; A[types]]) (Eq. 20).
     e [T, d] f32 or bf16, types int32 [T], A [n_types, d], W1, W3 [2d, 2d],
     W2 [2d, d] f32.  Returns x [T, d] in e's dtype."""
+    T, d, n_types = _check_action_args(e, types, A, W1, W3, W2, workspace)
+    _expect("x", x, e.dtype, (T, d), optional=True)
+    _on_device(e.device, x=x)
     lib = load()
-    T, d = e.shape
-    n_types = A.shape[0]
     if x is None:
         x = torch.empty_like(e)
     ws = _action_ws(d, e.dtype, T, n_types, SA_OP_FORWARD, e.device, workspace)
@@ -462,9 +630,10 @@ def action_fusion_forward(e, types, A, W1, W3, W2, x=None, workspace=None, strea
 def action_fusion_backward(e, types, A, W1, W3, W2, dx, workspace=None, stream=None):
     """Calls sa_action_fusion_backward.  Returns (de [T, d], dA, dW1, dW3,
     dW2), all f32."""
+    T, d, n_types = _check_action_args(e, types, A, W1, W3, W2, workspace)
+    _expect("dx", dx, torch.float32, (T, d))
+    _on_device(e.device, dx=dx)
     lib = load()
-    T, d = e.shape
-    n_types = A.shape[0]
     dev = e.device
     de = torch.empty((T, d), dtype=torch.float32, device=dev)
     dA, dW1, dW3, dW2 = (torch.empty_like(t) for t in (A, W1, W3, W2))
@@ -485,8 +654,23 @@ def stca_attention(x_off, X, t_off, Q, Wq, Wk, Wv, h, o=None, lse=None, workspac
     """Calls sa_stca_attention (Eq. 24): per target and head, softmax over the
     target's user's rows of X.  x_off, t_off: int64 [B+1] (device); X bf16
     [L, D]; Q, Wq, Wk, Wv f32.  Returns (o [R, D], lse [R, h])."""
-    lib = load()
+    _check_offsets_tensor(x_off)
+    _check_offsets_tensor(t_off)
+    _expect("X", X, torch.bfloat16)
+    if X.dim() != 2:
+        raise ValueError(f"X must be [L, D], got {tuple(X.shape)}")
+    D = X.shape[1]
+    _expect("Q", Q, torch.float32)
+    if Q.dim() != 2 or Q.shape[1] != D:
+        raise ValueError(f"Q must be [R, {D}], got {tuple(Q.shape)}")
+    for name, w in (("Wq", Wq), ("Wk", Wk), ("Wv", Wv)):
+        _expect(name, w, torch.float32, (D, D))
+    _expect("o", o, torch.float32, (Q.shape[0], D), optional=True)
+    _expect("lse", lse, torch.float32, (Q.shape[0], int(h)), optional=True)
     dev = Q.device
+    _check_workspace(workspace, dev)
+    _on_device(dev, X=X, Wq=Wq, Wk=Wk, Wv=Wv, o=o, lse=lse)
+    lib = load()
     xo = _device_offsets(x_off, dev)
     to = _device_offsets(t_off, dev)
     B = xo.numel() - 1
