@@ -50,6 +50,55 @@ def _compile(src, hipcc):
     return out
 
 
+def _objects_for(sources):
+    return [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in sources]
+
+
+def build_host_asan(verbose=False) -> str:
+    """A copy of the library whose host code (the C-ABI layer: argument
+    validation, plans, workspace layout) is built with AddressSanitizer, for
+    CPU-only checks of the validation paths.  Device code is unchanged (the
+    kernel objects of ``build``); the sanitizer applies to the host pass only.
+    The library leaves the sanitizer's runtime unresolved: load it into a
+    process started with that runtime preloaded (``asan_runtime()``)."""
+    if not all(os.path.exists(o) for o in _objects_for(SOURCES)):
+        build(verbose)
+    hipcc = _hipcc()
+    out_dir = os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    api = [s for s in SOURCES if s.endswith(".cpp")]
+    objs = []
+    for src in api:
+        out = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc, "-x", "hip", "--offload-arch=gfx950", "-O1", "-g", "-fPIC", "-std=c++17",
+               "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+               "-Wno-unused-command-line-argument", "-I", CSRC, "-I", os.path.join(ROOT, "include"),
+               "-c", os.path.join(CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        objs.append(out)
+    lib = os.path.join(out_dir, "libsa_asan.so")
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib, *objs,
+           *_objects_for([s for s in SOURCES if not s.endswith(".cpp")])]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print("built", lib)
+    return lib
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return path
+
+
 def build(verbose=False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()

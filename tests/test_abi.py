@@ -226,3 +226,94 @@ def test_stca_argument_errors_are_synchronous():
     assert call(ws_bytes=16) == sa.SA_ERR_WORKSPACE_TOO_SMALL
     # no targets: nothing to compute, nothing enqueued
     assert call(R=0, Q=nul, o=nul) == sa.SA_OK
+
+
+def test_loaded_library_is_the_selected_build():
+    # SA_LIBRARY_PATH selects the host-side AddressSanitizer build in
+    # test_abi_asan.py; otherwise the in-tree library is loaded.
+    want = os.environ.get("SA_LIBRARY_PATH") or os.path.join(ROOT, "recommender_ultra_long_amd",
+                                                              "libsa.so")
+    assert os.path.samefile(sa.lib_path(), want)
+
+
+def test_block_argument_errors_are_synchronous():
+    lib = sa.load()
+    buf = ctypes.create_string_buffer(1024)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    vp = ctypes.c_void_p
+    ok, nul = vp(al), vp(None)
+    layer = sa.SaBlockLayer(*([al] * len(sa.BLOCK_LAYER_KEYS)))
+    layers = (sa.SaBlockLayer * 2)(layer, layer)
+    grads = (sa.SaBlockLayer * 2)(layer, layer)
+    pr = _p(dtype=sa.SA_BF16, d=128, k=256)
+    ws = lib.sa_block_workspace_size(ctypes.byref(pr), 2)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.sa_block_workspace_size(ctypes.byref(pr), 9) == 0      # at most 8 layers
+    pm = _p(mass_norm=True)
+    assert lib.sa_block_workspace_size(ctypes.byref(pm), 2) == 0      # flags unsupported
+
+    def fwd(pr=pr, L=2, off=ok, X=ok, P0=ok, lay=layers, out=ok, w=ok, wb=1 << 40):
+        return lib.sa_block_forward(ctypes.byref(pr), L, off, X, P0, lay, out, w,
+                                    ctypes.c_size_t(wb), nul)
+
+    def bwd(pr=pr, L=2, off=ok, X=ok, P0=ok, lay=layers, dout=ok, dX=ok, dP0=ok, g=grads, w=ok,
+            wb=1 << 40):
+        return lib.sa_block_backward(ctypes.byref(pr), L, off, X, P0, lay, dout, dX, dP0, g, w,
+                                     ctypes.c_size_t(wb), nul)
+
+    assert fwd(L=0) == sa.SA_ERR_UNSUPPORTED
+    assert fwd(L=9) == sa.SA_ERR_UNSUPPORTED
+    assert fwd(pr=pm) == sa.SA_ERR_UNSUPPORTED
+    assert fwd(pr=_p(k=0)) == sa.SA_ERR_BAD_SHAPE
+    assert fwd(off=nul) == sa.SA_ERR_NULL_ARG
+    assert fwd(out=nul) == sa.SA_ERR_NULL_ARG
+    bad = (sa.SaBlockLayer * 2)(layer, layer)
+    bad[1].W2 = None
+    assert fwd(lay=bad) == sa.SA_ERR_NULL_ARG
+    bad[1].W2 = al + 4
+    assert fwd(lay=bad) == sa.SA_ERR_MISALIGNED
+    assert fwd(X=vp(al + 8)) == sa.SA_ERR_MISALIGNED
+    assert fwd(wb=256) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(dout=nul) == sa.SA_ERR_NULL_ARG
+    assert bwd(g=None) == sa.SA_ERR_NULL_ARG
+    assert bwd(dX=nul) == sa.SA_ERR_NULL_ARG
+    assert bwd(dP0=vp(al + 4)) == sa.SA_ERR_MISALIGNED
+    assert bwd(wb=256) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_action_fusion_argument_errors_are_synchronous():
+    lib = sa.load()
+    buf = ctypes.create_string_buffer(512)
+    al = (ctypes.addressof(buf) + 255) & ~255
+    vp = ctypes.c_void_p
+    ok, nul = vp(al), vp(None)
+    for dt in (sa.SA_F32, sa.SA_BF16):
+        for op in (sa.SA_OP_FORWARD, sa.SA_OP_BACKWARD):
+            assert lib.sa_action_fusion_workspace_size(128, dt, 1000, 8, op) > 0
+    assert lib.sa_action_fusion_workspace_size(96, sa.SA_F32, 1000, 8, 0) == 0
+    assert lib.sa_action_fusion_workspace_size(128, sa.SA_F32, 1000, 17, 0) == 0
+    assert lib.sa_action_fusion_workspace_size(128, sa.SA_F32, 1000, 0, 0) == 0
+    assert lib.sa_action_fusion_workspace_size(128, 7, 1000, 8, 0) == 0
+
+    def fwd(d=128, dt=sa.SA_BF16, T=1000, nt=8, e=ok, types=ok, A=ok, W1=ok, W3=ok, W2=ok, x=ok,
+            w=ok, wb=1 << 40):
+        return lib.sa_action_fusion_forward(d, dt, T, nt, e, types, A, W1, W3, W2, x, w,
+                                            ctypes.c_size_t(wb), nul)
+
+    def bwd(e=ok, types=ok, dx=ok, de=ok, dA=ok, dW2=ok, wb=1 << 40):
+        return lib.sa_action_fusion_backward(128, sa.SA_BF16, 1000, 8, e, types, ok, ok, ok, ok, dx,
+                                             de, dA, ok, ok, dW2, ok, ctypes.c_size_t(wb), nul)
+
+    assert fwd(dt=3) == sa.SA_ERR_BAD_DTYPE
+    assert fwd(d=48) == sa.SA_ERR_BAD_SHAPE
+    assert fwd(nt=17) == sa.SA_ERR_BAD_SHAPE
+    assert fwd(W3=nul) == sa.SA_ERR_NULL_ARG
+    assert fwd(types=nul) == sa.SA_ERR_NULL_ARG
+    assert fwd(types=vp(al + 2)) == sa.SA_ERR_MISALIGNED
+    assert fwd(W1=vp(al + 8)) == sa.SA_ERR_MISALIGNED
+    assert fwd(wb=16) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+    assert bwd(dA=nul) == sa.SA_ERR_NULL_ARG
+    assert bwd(de=nul) == sa.SA_ERR_NULL_ARG
+    assert bwd(dW2=vp(al + 4)) == sa.SA_ERR_MISALIGNED
+    assert bwd(dx=vp(al + 4)) == sa.SA_ERR_MISALIGNED
+    assert bwd(wb=16) == sa.SA_ERR_WORKSPACE_TOO_SMALL
