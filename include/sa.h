@@ -393,6 +393,33 @@ sa_status sa_stca_attention(int B, int D, int h, int64_t L, int64_t R, const int
  * (SA_OK).  SA_ERR_HIP if the wait or the read fails. */
 sa_status sa_get_device_status(const void* ws, void* stream);
 
+/*
+ * sa_forward without a caller workspace, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  The caller still owns every input and
+ * output (same arguments and meaning as sa_forward); the workspace is a
+ * device array of SA_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * per GPU, which that GPU holds until the process ends.  The call allocates
+ * and frees nothing.  The first call on a device (the current device, which
+ * must be the stream's) looks the array's device address up once.
+ *
+ * Returns SA_ERR_WORKSPACE_TOO_SMALL, with nothing enqueued, when the
+ * problem's sa_workspace_size(problem, SA_OP_FORWARD) exceeds
+ * SA_NOALLOC_SCRATCH_BYTES (64 MiB: for k = 1024, d = 128 that holds about
+ * 100 partial sketches, e.g. one user of any length, or a few tens of users
+ * of 100K tokens when lse is passed); SA_ERR_HIP if the lookup fails; other
+ * errors as sa_forward.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (two streams, two threads) race and
+ * give wrong results; serialize them.  Each call rewrites every byte of the
+ * array it reads, so nothing carries over from the previous call.  Offsets
+ * errors are flagged in the library's array, which the caller cannot read:
+ * validate offsets on the host (sa_validate) where that matters.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sa_status sa_forward_noalloc(const sa_problem* problem, const int64_t* offsets_dev,
+                             const void* X, const void* P, float* S, float* lse, float* mass,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

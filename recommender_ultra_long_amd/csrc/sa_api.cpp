@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sa.h"
 #include "sa_kernels.h"
 
@@ -326,6 +328,47 @@ sa_status sa_fold_prototypes_backward(int k, int d, sa_dtype dtype, const void* 
   const hipError_t e = launch_fold_backward(k, d, (int)dtype, P, Wq, Wk, dP_eff, dP, dWq, dWk,
                                             (float*)ws, (hipStream_t)stream);
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // extern "C"
+
+// Workspace of sa_forward_noalloc: one array per GPU, placed by the loader
+// with the code object.  On the host, `scratch` only names the symbol; its
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, or null
+
+// The device address of `scratch` on the current device (looked up on the
+// first call for that device), or null if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+sa_status sa_forward_noalloc(const sa_problem* pr, const int64_t* offsets_dev, const void* X,
+                             const void* P, float* S, float* lse, float* mass, void* stream) {
+  const sa_status v = sa_validate(pr, nullptr);
+  if (v != SA_OK) return v;
+  if (sa_workspace_size(pr, SA_OP_FORWARD) > SA_NOALLOC_SCRATCH_BYTES)
+    return SA_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return SA_ERR_HIP;
+  return forward_impl(pr, offsets_dev, X, P, S, lse, mass, ws, SA_NOALLOC_SCRATCH_BYTES, stream,
+                      nullptr);
 }
 
 sa_status sa_get_device_status(const void* ws, void* stream) {

@@ -47,7 +47,11 @@ EXPORTED = ("sa_version", "sa_status_string", "sa_validate", "sa_workspace_size"
             "sa_get_device_status", "sa_fold_workspace_size", "sa_fold_prototypes",
             "sa_fold_prototypes_backward", "sa_block_workspace_size", "sa_block_forward",
             "sa_block_backward", "sa_action_fusion_workspace_size", "sa_action_fusion_forward",
-            "sa_action_fusion_backward", "sa_stca_workspace_size", "sa_stca_attention")
+            "sa_action_fusion_backward", "sa_stca_workspace_size", "sa_stca_attention",
+            "sa_forward_noalloc")
+
+# Bytes of the library's own workspace array used by sa_forward_noalloc.
+SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Parameter names of one layer of the stacked block, in sa_block_layer order.
 BLOCK_LAYER_KEYS = ("Wq", "Wk", "ln1_g", "ln1_b", "W1", "W3", "W2", "ln2_g", "ln2_b")
@@ -136,6 +140,8 @@ def load():
     lib.sa_stca_workspace_size.argtypes = [i32, i32, i64]
     lib.sa_stca_attention.restype = i32
     lib.sa_stca_attention.argtypes = [i32, i32, i32, i64, i64] + [vp] * 9 + [vp, sz, vp]
+    lib.sa_forward_noalloc.restype = i32
+    lib.sa_forward_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -323,6 +329,29 @@ def sa_forward(offsets, X, P, mass_norm=False, S=None, lse=None, mass=None, work
         st = lib.sa_forward_profiled(*args, ctypes.byref(timer.prof))
     if st != SA_OK:
         raise SAError(st, "sa_forward")
+    return S, lse, mass
+
+
+def sa_forward_noalloc(offsets, X, P, S, lse=None, mass=None, mass_norm=False, stream=None):
+    """Calls sa_forward_noalloc: sa_forward with the library's own workspace
+    array instead of a caller workspace.  Outputs are the caller's: S
+    [B, k, d], and optionally lse [T] and mass [B, k] (float32, on the GPU).
+    offsets must already be an int64 device tensor.  Returns (S, lse, mass)."""
+    B, T, d, k, per_user = _check_sketch_args(offsets, X, P)
+    _expect("S", S, torch.float32, (B, k, d))
+    _expect("lse", lse, torch.float32, (T,), optional=True)
+    _expect("mass", mass, torch.float32, (B, k), optional=True)
+    if not isinstance(offsets, torch.Tensor) or offsets.dtype != torch.int64:
+        raise ValueError("offsets must be an int64 device tensor")
+    _expect("offsets", offsets)
+    dev = P.device
+    _on_device(dev, X=X, S=S, lse=lse, mass=mass, offsets=offsets)
+    lib = load()
+    pr = make_problem(B, k, d, T, X.dtype, mass_norm, per_user)
+    st = lib.sa_forward_noalloc(ctypes.byref(pr), _ptr(offsets), _ptr(X), _ptr(P), _ptr(S),
+                                _ptr(lse), _ptr(mass), _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_forward_noalloc")
     return S, lse, mass
 
 
