@@ -19,8 +19,20 @@ output projection W_O and the FFN that follow are outside the attention).
 Each target attends over its own user's rows (a ragged batch: targets are
 grouped by user); a user without rows gives o = 0.
 
+The whole layer of Eq. (26) adds the output projection W_O (2 D^2 per
+target) and the query-side SwiGLU FFN (12 D^2 per target: Eq. (23) with
+hidden width w_f = 2 D).  The page counts their flops only; it prints no
+residual connections or normalisation.  Reading taken (stca_layer_ref): the
+two sublayers are residual, as in a standard transformer layer, with no
+normalisation (the page lists none; its FLOP convention leaves out layer
+norms anyway):
+    a = q + o W_O,        y = a + (silu(a W1) * (a W3)) W2,
+W_O: D x D, W1, W3: D x 2D, W2: 2D x D, no biases.
+
 Pins: tests/test_oracle_stca.py (the unreordered form with X W_K and X W_V
-materialised, closed forms, finite properties).
+materialised, closed forms, finite properties; for the layer, torch's
+scaled_dot_product_attention and silu on the unreordered form, W2 = 0 and
+W_O = 0 special cases).
 """
 
 from __future__ import annotations
@@ -80,3 +92,20 @@ def stca_attention_unreordered(x_off, X, t_off, Q, Wq, Wk, Wv, h):
                 a = np.exp(s - s.max())
                 o[r, cols] = (a / a.sum()) @ V
     return o
+
+
+def _silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def stca_layer_ref(x_off, X, t_off, Q, Wq, Wk, Wv, Wo, W1, W3, W2, h):
+    """One STCA layer for every target (reading notes section 5.1, Eq. (26)):
+    the reordered attention of stca_attention_ref, then the output projection
+    and the query-side SwiGLU FFN, each as a residual sublayer.  Returns
+    (y [R, D], o [R, D], lse [R, h])."""
+    o, lse = stca_attention_ref(x_off, X, t_off, Q, Wq, Wk, Wv, h)
+    Q = np.asarray(Q, dtype=np.float64)
+    Wo, W1, W3, W2 = (np.asarray(w, dtype=np.float64) for w in (Wo, W1, W3, W2))
+    a = Q + o @ Wo
+    y = a + (_silu(a @ W1) * (a @ W3)) @ W2
+    return y, o, lse

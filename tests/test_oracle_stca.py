@@ -5,7 +5,7 @@ import math
 
 import numpy as np
 
-from oracle.stca import stca_attention_ref, stca_attention_unreordered
+from oracle.stca import stca_attention_ref, stca_attention_unreordered, stca_layer_ref
 
 
 def _case(seed, x_lens, t_lens, D=8, h=2):
@@ -80,3 +80,62 @@ def test_lse_matches_library_logsumexp_per_head():
             s = (Xu @ Wk[:, cols]) @ (Q[r] @ Wq[:, cols]) / math.sqrt(2)
             assert abs(np.max(s)) > 0.5
             assert abs(lse[r, j] - logsumexp(s)) < 1e-12
+
+
+def _layer_weights(seed, D):
+    rng = np.random.default_rng(seed)
+    Wo = rng.standard_normal((D, D)) * 0.4
+    W1 = rng.standard_normal((D, 2 * D)) * 0.4
+    W3 = rng.standard_normal((D, 2 * D)) * 0.4
+    W2 = rng.standard_normal((2 * D, D)) * 0.4
+    return Wo, W1, W3, W2
+
+
+def test_layer_against_torch_attention_and_silu():
+    # Independent form of Eq. (26): K = X W_K and V = X W_V materialised per
+    # head, torch's scaled_dot_product_attention (scale 1/sqrt(d_h)), torch's
+    # silu, float64 on the CPU.
+    import torch
+    import torch.nn.functional as F
+
+    x_off, X, t_off, Q, (Wq, Wk, Wv) = _case(5, [6, 0, 9], [2, 1, 3], D=8, h=2)
+    Wo, W1, W3, W2 = _layer_weights(6, 8)
+    y, o, _ = stca_layer_ref(x_off, X, t_off, Q, Wq, Wk, Wv, Wo, W1, W3, W2, 2)
+    t = lambda a: torch.as_tensor(a, dtype=torch.float64)
+    yt = torch.zeros(Q.shape[0], 8, dtype=torch.float64)
+    for u in range(3):
+        Xu = t(X[x_off[u]:x_off[u + 1]])
+        for r in range(t_off[u], t_off[u + 1]):
+            heads = []
+            for j in range(2):
+                cols = slice(4 * j, 4 * j + 4)
+                if Xu.shape[0] == 0:
+                    heads.append(torch.zeros(4, dtype=torch.float64))
+                    continue
+                q = (t(Q[r]) @ t(Wq)[:, cols])[None, None]
+                k = (Xu @ t(Wk)[:, cols])[None]
+                v = (Xu @ t(Wv)[:, cols])[None]
+                heads.append(F.scaled_dot_product_attention(q, k, v)[0, 0])
+            a = t(Q[r]) + torch.cat(heads) @ t(Wo)
+            yt[r] = a + (F.silu(a @ t(W1)) * (a @ t(W3))) @ t(W2)
+    assert np.max(np.abs(y - yt.numpy())) < 1e-12
+
+
+def test_layer_special_cases():
+    x_off, X, t_off, Q, (Wq, Wk, Wv) = _case(7, [5, 3], [2, 2], D=8, h=4)
+    Wo, W1, W3, W2 = _layer_weights(8, 8)
+    _, o, _ = stca_layer_ref(x_off, X, t_off, Q, Wq, Wk, Wv, Wo, W1, W3, W2, 4)
+    # W2 = 0: the FFN adds nothing, y = q + o W_O (the attention path alone)
+    y0, _, _ = stca_layer_ref(x_off, X, t_off, Q, Wq, Wk, Wv, Wo, W1, W3, np.zeros((16, 8)), 4)
+    assert np.max(np.abs(y0 - (Q + o @ Wo))) < 1e-12
+    # W_O = 0: the FFN acts on q itself, y = q + FFN(q), FFN by scipy's expit
+    from scipy.special import expit
+
+    yq, _, _ = stca_layer_ref(x_off, X, t_off, Q, Wq, Wk, Wv, np.zeros((8, 8)), W1, W3, W2, 4)
+    u1 = Q @ W1
+    want = Q + (u1 * expit(u1) * (Q @ W3)) @ W2
+    assert np.max(np.abs(yq - want)) < 1e-12
+    # both zero: y = q
+    yz, _, _ = stca_layer_ref(x_off, X, t_off, Q, Wq, Wk, Wv, np.zeros((8, 8)), W1, W3,
+                              np.zeros((16, 8)), 4)
+    assert np.array_equal(yz, Q)
