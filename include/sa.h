@@ -363,7 +363,7 @@ sa_status sa_action_fusion_backward(int d, sa_dtype dtype, int64_t T, int n_type
  * so X W_K and X W_V are never formed; the length-dependent work is the two
  * reductions, 4 L D flops per head and target, on the matrix cores (X and u
  * in bf16, fp32 accumulation).  The output projection and the FFN that
- * follow in the pages' STCA are outside this call.
+ * follow in the pages' STCA layer are added by sa_stca_layer below.
  *
  *  B           : users; x_off: int64 [B+1] device, rows of X per user;
  *                t_off: int64 [B+1] device, targets (rows of Q and o) per user.
@@ -387,6 +387,31 @@ sa_status sa_stca_attention(int B, int D, int h, int64_t L, int64_t R, const int
                             const int64_t* t_off, const void* X, const float* Q, const float* Wq,
                             const float* Wk, const float* Wv, float* o, float* lse, void* ws,
                             size_t ws_bytes, void* stream);
+
+/*
+ * One whole STCA layer per target (reading notes section 5.1, Eq. (26)): the
+ * reordered attention above, then the output projection W_O (2 D^2 flops
+ * per target) and the query-side SwiGLU FFN of hidden width 2D (12 D^2, the
+ * pages' Eq. (23) with w_f = 2w).  The page counts their flops and prints no
+ * residual connection or normalisation; they are read as residual sublayers
+ * without normalisation:
+ *     a = q + o W_O,     y = a + (silu(a W1) * (a W3)) W2.
+ *
+ *  Wo : float [D, D];  W1, W3 : float [D, 2D];  W2 : float [2D, D]; no biases.
+ *  y  : float [R, D], written.
+ *  o  : float [R, D] or NULL: the attention output, also written when given.
+ *  lse, and every other argument: as for sa_stca_attention.
+ *  ws : sa_stca_layer_workspace_size(D, h, R) bytes.
+ * The four products round their fp32 operands to bf16 on the matrix cores
+ * with fp32 accumulation; the SwiGLU is fp32.  Errors as for
+ * sa_stca_attention, checked before anything is enqueued.
+ */
+size_t sa_stca_layer_workspace_size(int D, int h, int64_t R);
+sa_status sa_stca_layer(int B, int D, int h, int64_t L, int64_t R, const int64_t* x_off,
+                        const int64_t* t_off, const void* X, const float* Q, const float* Wq,
+                        const float* Wk, const float* Wv, const float* Wo, const float* W1,
+                        const float* W3, const float* W2, float* y, float* o, float* lse,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Waits for `stream`, then reports whether a kernel of the last call that
  * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS) or not

@@ -1,7 +1,8 @@
 // sa_stca_api.cpp — the reordered single-query STCA attention of include/sa.h
-// (SequenceO1 reading notes, section 5.1, Eq. (24)): validation, workspace
-// layout and the launch sequence (query projections, the length-dependent
-// core, value projections).  Host code only.
+// (SequenceO1 reading notes, section 5.1, Eq. (24)) and the whole STCA layer
+// of Eq. (26) around it: validation, workspace layout and the launch sequence
+// (query projections, the length-dependent core, value projections; then the
+// output projection and the query-side SwiGLU FFN).  Host code only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -106,6 +107,68 @@ sa_status sa_stca_attention(int B, int D, int h, int64_t L, int64_t R, const int
   else
     SA_TRY(launch_gemm_batched(false, false, C, h * D, D, Wv, D, dh, o, D, dh, (int)R, dh, D, h,
                                0, st));
+  return SA_OK;
+}
+
+// Workspace of the whole layer: the attention's, then o [R, D] (when the
+// caller passes none), a [R, D], U1, U3, G [R, 2D], all fp32.
+struct StcaLayerPlan {
+  size_t attn, o, a, U1, U3, G, total;
+};
+
+static StcaLayerPlan stca_layer_plan(int D, int h, int64_t R) {
+  StcaLayerPlan p;
+  size_t off = 0;
+  p.attn = off; off = a256(off + stca_plan(D, h, R).total);
+  p.o = off; off = a256(off + (size_t)R * D * 4);
+  p.a = off; off = a256(off + (size_t)R * D * 4);
+  p.U1 = off; off = a256(off + (size_t)R * 2 * D * 4);
+  p.U3 = off; off = a256(off + (size_t)R * 2 * D * 4);
+  p.G = off; off = a256(off + (size_t)R * 2 * D * 4);
+  p.total = off;
+  return p;
+}
+
+size_t sa_stca_layer_workspace_size(int D, int h, int64_t R) {
+  if (!stca_shape_ok(1, D, h, 0, R)) return 0;
+  return stca_layer_plan(D, h, R).total;
+}
+
+sa_status sa_stca_layer(int B, int D, int h, int64_t L, int64_t R, const int64_t* x_off,
+                        const int64_t* t_off, const void* X, const float* Q, const float* Wq,
+                        const float* Wk, const float* Wv, const float* Wo, const float* W1,
+                        const float* W3, const float* W2, float* y, float* o, float* lse,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!stca_shape_ok(B, D, h, L, R)) return SA_ERR_BAD_SHAPE;
+  if (Wo == nullptr || W1 == nullptr || W3 == nullptr || W2 == nullptr || ws == nullptr)
+    return SA_ERR_NULL_ARG;
+  if (R > 0 && y == nullptr) return SA_ERR_NULL_ARG;
+  if (!a16(Wo) || !a16(W1) || !a16(W3) || !a16(W2) || !a16(ws) || (y && !a16(y)) ||
+      (o && !a16(o)))
+    return SA_ERR_MISALIGNED;
+  const StcaLayerPlan p = stca_layer_plan(D, h, R);
+  if (ws_bytes < p.total) return SA_ERR_WORKSPACE_TOO_SMALL;
+  char* w = (char*)ws;
+  float* ob = o ? o : (float*)(w + p.o);
+  // The attention validates its own arguments (x_off, t_off, X, Q, W_Q, W_K,
+  // W_V) before enqueueing anything.
+  const sa_status v = sa_stca_attention(B, D, h, L, R, x_off, t_off, X, Q, Wq, Wk, Wv, ob, lse,
+                                        w + p.attn, stca_plan(D, h, R).total, stream);
+  if (v != SA_OK || R == 0) return v;
+  hipStream_t st = (hipStream_t)stream;
+  float* a = (float*)(w + p.a);
+  float* U1 = (float*)(w + p.U1);
+  float* U3 = (float*)(w + p.U3);
+  float* G = (float*)(w + p.G);
+  const int M = (int)R;
+  // a = q + o W_O; U1 = a W1, U3 = a W3; G = silu(U1) * U3; y = a + G W2.
+  // The products round their fp32 operands to bf16 on the matrix cores with
+  // fp32 accumulation, as the attention's projections do.
+  SA_TRY(launch_gemm_mx_sliced(false, false, ob, D, Wo, D, a, D, M, D, D, 1, 0, st, Q));
+  SA_TRY(launch_gemm_mx_sliced(false, false, a, D, W1, 2 * D, U1, 2 * D, M, 2 * D, D, 1, 0, st));
+  SA_TRY(launch_gemm_mx_sliced(false, false, a, D, W3, 2 * D, U3, 2 * D, M, 2 * D, D, 1, 0, st));
+  SA_TRY(launch_swiglu_fwd(U1, U3, (int64_t)R * 2 * D, G, st));
+  SA_TRY(launch_gemm_mx_sliced(false, false, G, 2 * D, W2, D, y, D, M, D, 2 * D, 1, 0, st, a));
   return SA_OK;
 }
 

@@ -48,7 +48,7 @@ EXPORTED = ("sa_version", "sa_status_string", "sa_validate", "sa_workspace_size"
             "sa_fold_prototypes_backward", "sa_block_workspace_size", "sa_block_forward",
             "sa_block_backward", "sa_action_fusion_workspace_size", "sa_action_fusion_forward",
             "sa_action_fusion_backward", "sa_stca_workspace_size", "sa_stca_attention",
-            "sa_forward_noalloc")
+            "sa_forward_noalloc", "sa_stca_layer_workspace_size", "sa_stca_layer")
 
 # Bytes of the library's own workspace array used by sa_forward_noalloc.
 SA_NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -140,6 +140,10 @@ def load():
     lib.sa_stca_workspace_size.argtypes = [i32, i32, i64]
     lib.sa_stca_attention.restype = i32
     lib.sa_stca_attention.argtypes = [i32, i32, i32, i64, i64] + [vp] * 9 + [vp, sz, vp]
+    lib.sa_stca_layer_workspace_size.restype = sz
+    lib.sa_stca_layer_workspace_size.argtypes = [i32, i32, i64]
+    lib.sa_stca_layer.restype = i32
+    lib.sa_stca_layer.argtypes = [i32, i32, i32, i64, i64] + [vp] * 14 + [vp, sz, vp]
     lib.sa_forward_noalloc.restype = i32
     lib.sa_forward_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib
@@ -718,6 +722,53 @@ def stca_attention(x_off, X, t_off, Q, Wq, Wk, Wv, h, o=None, lse=None, workspac
     if st != SA_OK:
         raise SAError(st, "sa_stca_attention")
     return o, lse
+
+
+def stca_layer(x_off, X, t_off, Q, Wq, Wk, Wv, Wo, W1, W3, W2, h, y=None, o=None, lse=None,
+               workspace=None, stream=None):
+    """Calls sa_stca_layer (Eq. 26): the attention of stca_attention, then
+    a = q + o W_O and y = a + SwiGLU(a) with hidden width 2D.  Wo [D, D],
+    W1, W3 [D, 2D], W2 [2D, D] f32.  Returns (y [R, D], o [R, D], lse [R, h])."""
+    _check_offsets_tensor(x_off)
+    _check_offsets_tensor(t_off)
+    _expect("X", X, torch.bfloat16)
+    if X.dim() != 2:
+        raise ValueError(f"X must be [L, D], got {tuple(X.shape)}")
+    D = X.shape[1]
+    _expect("Q", Q, torch.float32)
+    if Q.dim() != 2 or Q.shape[1] != D:
+        raise ValueError(f"Q must be [R, {D}], got {tuple(Q.shape)}")
+    R = Q.shape[0]
+    for name, w, shape in (("Wq", Wq, (D, D)), ("Wk", Wk, (D, D)), ("Wv", Wv, (D, D)),
+                           ("Wo", Wo, (D, D)), ("W1", W1, (D, 2 * D)), ("W3", W3, (D, 2 * D)),
+                           ("W2", W2, (2 * D, D))):
+        _expect(name, w, torch.float32, shape)
+    _expect("y", y, torch.float32, (R, D), optional=True)
+    _expect("o", o, torch.float32, (R, D), optional=True)
+    _expect("lse", lse, torch.float32, (R, int(h)), optional=True)
+    dev = Q.device
+    _check_workspace(workspace, dev)
+    _on_device(dev, X=X, Wq=Wq, Wk=Wk, Wv=Wv, Wo=Wo, W1=W1, W3=W3, W2=W2, y=y, o=o, lse=lse)
+    lib = load()
+    xo = _device_offsets(x_off, dev)
+    to = _device_offsets(t_off, dev)
+    B = xo.numel() - 1
+    L = X.shape[0]
+    if y is None:
+        y = torch.empty((R, D), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((R, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((R, h), dtype=torch.float32, device=dev)
+    n = int(lib.sa_stca_layer_workspace_size(int(D), int(h), int(R)))
+    ws = _workspace(n, dev, workspace)
+    st = lib.sa_stca_layer(int(B), int(D), int(h), int(L), int(R), _ptr(xo), _ptr(to), _ptr(X),
+                           _ptr(Q), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo), _ptr(W1), _ptr(W3),
+                           _ptr(W2), _ptr(y), _ptr(o), _ptr(lse), _ptr(ws),
+                           ctypes.c_size_t(ws.numel() * ws.element_size()), _stream_handle(stream))
+    if st != SA_OK:
+        raise SAError(st, "sa_stca_layer")
+    return y, o, lse
 
 
 def sa_get_device_status(workspace, stream=None):

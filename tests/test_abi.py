@@ -317,3 +317,31 @@ def test_action_fusion_argument_errors_are_synchronous():
     assert bwd(dW2=vp(al + 4)) == sa.SA_ERR_MISALIGNED
     assert bwd(dx=vp(al + 4)) == sa.SA_ERR_MISALIGNED
     assert bwd(wb=16) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_stca_layer_argument_errors_are_synchronous():
+    lib = sa.load()
+    D, h, R = 512, 8, 7
+    base = lib.sa_stca_workspace_size(D, h, R)
+    a256 = lambda v: (v + 255) // 256 * 256
+    want = a256(base) + 2 * a256(R * D * 4) + 3 * a256(R * 2 * D * 4)
+    assert lib.sa_stca_layer_workspace_size(D, h, R) == want
+    assert lib.sa_stca_layer_workspace_size(128, 4, R) == 0
+    buf = ctypes.create_string_buffer(256)
+    al = (ctypes.addressof(buf) + 15) & ~15
+    vp = ctypes.c_void_p
+    ok, nul = vp(al), vp(None)
+
+    def call(D=256, h=4, R=3, Wo=ok, W1=ok, W3=ok, W2=ok, y=ok, o=nul, x_off=ok, ws=ok,
+             ws_bytes=1 << 40):
+        return lib.sa_stca_layer(2, D, h, 10, R, x_off, ok, ok, ok, ok, ok, ok, Wo, W1, W3, W2, y,
+                                 o, nul, ws, ctypes.c_size_t(ws_bytes), nul)
+
+    assert call(D=128) == sa.SA_ERR_BAD_SHAPE
+    assert call(W1=nul) == sa.SA_ERR_NULL_ARG
+    assert call(y=nul) == sa.SA_ERR_NULL_ARG
+    assert call(x_off=nul) == sa.SA_ERR_NULL_ARG          # the attention's own checks
+    assert call(W2=vp(al + 4)) == sa.SA_ERR_MISALIGNED
+    assert call(o=vp(al + 8)) == sa.SA_ERR_MISALIGNED
+    assert call(ws_bytes=16) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+    assert call(R=0, y=nul) == sa.SA_OK                   # nothing to compute

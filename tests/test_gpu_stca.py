@@ -9,7 +9,7 @@ import torch
 
 from oracle.stca import stca_attention_ref
 from recommender_ultra_long_amd import sa, synth
-from sa_testutil import TOL_BF16, TOL_LSE_ABS, rel_err, say
+from sa_testutil import TOL_BF16, TOL_LSE_ABS, record, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -98,3 +98,43 @@ def test_stca_is_deterministic():
     o2, l2 = sa.stca_attention(*args)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("D,h", [(256, 4), (256, 16), (1024, 16)])
+def test_stca_layer_eq26(D, h):
+    """The whole layer of Eq. (26): attention, a = q + o W_O, y = a + SwiGLU(a)
+    (hidden width 2D).  Checked per target on y and on y - q (the part the
+    products make), and on o."""
+    from oracle.stca import stca_layer_ref
+
+    x_lens = [700, 0, 33, 1024, 5]
+    t_lens = [3, 2, 0, 5, 4]
+    say(f"case stca layer D={D} h={h}")
+    x_off, X, t_off, Q, (Wq, Wk, Wv) = _case(3 * D + h, x_lens, t_lens, D, h)
+    g = torch.Generator().manual_seed(D + 7 * h)
+    Wo = torch.randn(D, D, generator=g) * D ** -0.5
+    W1 = torch.randn(D, 2 * D, generator=g) * D ** -0.5
+    W3 = torch.randn(D, 2 * D, generator=g) * D ** -0.5
+    W2 = torch.randn(2 * D, D, generator=g) * (2 * D) ** -0.5
+    c = lambda t: t.cuda()
+    y, o, lse = sa.stca_layer(torch.as_tensor(x_off, device="cuda"), c(X),
+                              torch.as_tensor(t_off, device="cuda"), c(Q), c(Wq), c(Wk), c(Wv),
+                              c(Wo), c(W1), c(W3), c(W2), h)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.double().numpy()
+    ry, ro, rl = stca_layer_ref(x_off, synth.to_f64(X), t_off, f64(Q), f64(Wq), f64(Wk), f64(Wv),
+                                f64(Wo), f64(W1), f64(W3), f64(W2), h)
+    yg, og, q = y.cpu().numpy(), o.cpu().numpy(), f64(Q)
+    worst = {"y": 0.0, "y_minus_q": 0.0, "o": 0.0}
+    for r in range(ry.shape[0]):
+        for name, got, ref in (("y", yg[r], ry[r]), ("y_minus_q", yg[r] - q[r], ry[r] - q[r])):
+            e = rel_err(got, ref)
+            assert e <= TOL_BF16, f"target {r}: {name} rel err {e:.3e}"
+            worst[name] = max(worst[name], e)
+        if np.any(ro[r] != 0):
+            e = rel_err(og[r], ro[r])
+            assert e <= TOL_BF16, f"target {r}: o rel err {e:.3e}"
+            worst["o"] = max(worst["o"], e)
+        else:
+            assert not np.any(og[r])
+    record(f"stca layer (Eq. 26) D={D} h={h}", **worst)
