@@ -66,7 +66,9 @@ typedef enum {
   SA_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes < sa_workspace_size()          */
   SA_ERR_BAD_OFFSETS = 6,         /* host-checked or device-detected offsets */
   SA_ERR_MISALIGNED = 7,          /* a pointer is not 16-byte aligned        */
-  SA_ERR_HIP = 8                  /* a HIP runtime call failed               */
+  SA_ERR_HIP = 8,                 /* a HIP runtime call failed               */
+  SA_ERR_DEVICE_TIMEOUT = 9       /* device-detected: the single-pass forward's
+                                     statistics exchange gave up waiting     */
 } sa_status;
 
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
@@ -414,8 +416,11 @@ sa_status sa_stca_layer(int B, int D, int h, int64_t L, int64_t R, const int64_t
                         void* ws, size_t ws_bytes, void* stream);
 
 /* Waits for `stream`, then reports whether a kernel of the last call that
- * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS) or not
- * (SA_OK).  SA_ERR_HIP if the wait or the read fails. */
+ * used this workspace found inconsistent offsets (SA_ERR_BAD_OFFSETS), or the
+ * single-pass forward's statistics exchange between workgroups gave up
+ * waiting (SA_ERR_DEVICE_TIMEOUT: every wait is bounded, so the kernel ends,
+ * but that call's results are wrong), or neither (SA_OK).  SA_ERR_HIP if the
+ * wait or the read fails. */
 sa_status sa_get_device_status(const void* ws, void* stream);
 
 /*

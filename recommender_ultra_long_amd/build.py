@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsa.so")
 
 SOURCES = ["sa_api.cpp", "sa_block_api.cpp", "sa_action_api.cpp", "sa_action.hip",
-           "sa_stca_api.cpp", "sa_stca.hip", "sa_gemm_mx.hip", "sa_fwd_bf16.hip", "sa_fwd_f32.hip", "sa_reduce.hip", "sa_tok.hip",
+           "sa_stca_api.cpp", "sa_stca.hip", "sa_gemm_mx.hip", "sa_fwd_bf16.hip", "sa_fused_bf16.hip", "sa_fwd_f32.hip", "sa_reduce.hip", "sa_tok.hip",
            "sa_bwd.hip", "sa_fold.hip", "sa_block.hip"]
 
 COMMON = [

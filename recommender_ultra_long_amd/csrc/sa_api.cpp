@@ -49,6 +49,8 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, bool p
   p->off_pmass = off; off = align256(off + (size_t)p->nslots * k * 4);
   p->off_pl = off; off = align256(off + (size_t)p->nslots * k * 4);
   p->off_tlse = off; off = align256(off + (size_t)B * k * 4);
+  // exchange words of the single-pass forward: one per (chunk, token)
+  p->off_xchg = off; off = align256(off + (dtype == 1 ? (size_t)p->nchunks * Tn * 8 : 0));
   p->fwd_bytes = off;
 
   const size_t esz = dtype == 1 ? 2 : 4;
@@ -82,6 +84,7 @@ FwdArgs fwd_args(const Plan& p, char* w, const int64_t* offsets, const void* X, 
   a.pmass = (float*)(w + p.off_pmass);
   a.pl = (float*)(w + p.off_pl);
   a.status = (uint32_t*)(w + p.off_status);
+  a.xchg = (uint64_t*)(w + p.off_xchg);
   a.G = p.G; a.nchunks = p.nchunks;
   a.mass_norm = p.mass_norm ? 1 : 0;
   return a;
@@ -137,6 +140,7 @@ const char* sa_status_string(sa_status s) {
     case SA_ERR_BAD_OFFSETS: return "SA_ERR_BAD_OFFSETS: offsets not 0-based, non-decreasing and ending at total_tokens";
     case SA_ERR_MISALIGNED: return "SA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
     case SA_ERR_HIP: return "SA_ERR_HIP: a HIP runtime call failed";
+    case SA_ERR_DEVICE_TIMEOUT: return "SA_ERR_DEVICE_TIMEOUT: the single-pass forward's statistics exchange gave up waiting (results are wrong)";
   }
   return "SA_ERR_UNKNOWN";
 }
@@ -374,11 +378,12 @@ sa_status sa_forward_noalloc(const sa_problem* pr, const int64_t* offsets_dev, c
 sa_status sa_get_device_status(const void* ws, void* stream) {
   if (ws == nullptr) return SA_ERR_NULL_ARG;
   hipStream_t st = (hipStream_t)stream;
-  uint32_t word = 0;
-  if (hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess)
+  uint32_t word[2] = {0u, 0u};
+  if (hipMemcpyAsync(word, ws, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess)
     return SA_ERR_HIP;
   if (hipStreamSynchronize(st) != hipSuccess) return SA_ERR_HIP;
-  return word == kStatusOk ? SA_OK : SA_ERR_BAD_OFFSETS;
+  if (word[0] != kStatusOk) return SA_ERR_BAD_OFFSETS;
+  return word[1] == kStatusExchangeTimeout ? SA_ERR_DEVICE_TIMEOUT : SA_OK;
 }
 
 }  // extern "C"

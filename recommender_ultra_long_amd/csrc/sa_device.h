@@ -151,17 +151,22 @@ __device__ __forceinline__ int first_user_after(const int64_t* offsets, int B, i
 }
 
 // Block-wide check of the CSR offsets (offsets[0] = 0, non-decreasing,
-// offsets[B] = T); thread 0 writes the status word.  Every thread of the block
-// must call it.
+// offsets[B] = T); thread 0 writes the status word and, unless keep2, clears
+// the second status word (the single-pass forward's exchange status, which
+// its reduce keeps).  Every thread of the block must call it.
 __device__ __forceinline__ void check_offsets_block(const int64_t* offsets, int B, int64_t T,
-                                                    uint32_t* status, uint32_t ok, uint32_t bad_code) {
+                                                    uint32_t* status, uint32_t ok, uint32_t bad_code,
+                                                    bool keep2 = false) {
   __shared__ int bad;
   if (threadIdx.x == 0) bad = (offsets[0] != 0 || offsets[B] != T) ? 1 : 0;
   __syncthreads();
   for (int i = threadIdx.x; i < B; i += blockDim.x)
     if (offsets[i + 1] < offsets[i]) bad = 1;
   __syncthreads();
-  if (threadIdx.x == 0) *status = bad ? bad_code : ok;
+  if (threadIdx.x == 0) {
+    *status = bad ? bad_code : ok;
+    if (!keep2) status[1] = ok;
+  }
 }
 
 // LDS layout of a 32-token x D tile without padding: row r holds D/8 units of

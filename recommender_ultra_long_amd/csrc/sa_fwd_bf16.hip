@@ -23,6 +23,9 @@
 //     operand (X^T) is read from the LDS tile with the gfx950 transpose read.
 //     Partial sketches go to a workspace slot per (segment, user) piece;
 //     sa_reduce sums them in segment order.
+#include <stdlib.h>
+#include <string.h>
+
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -579,7 +582,23 @@ hipError_t launch_stats_bf16(const FwdArgs& a, hipStream_t st, Prof* prof) {
   return hipErrorInvalidValue;
 }
 
+// This file's two-pass forward is the default.  SA_FORWARD_PATH=single_pass
+// in the environment (read at every call) selects the single-pass forward
+// of sa_fused_bf16.hip where it applies (a shared table, a non-empty batch);
+// a refused cooperative launch falls back to the two-pass forward.  On
+// MI355X the single-pass kernel is the slower of the two (its per-tile
+// statistics exchange and barrier serialise the waves; the two-pass form
+// spends 2 k d more matrix flops, which are not the bottleneck).
+static bool single_pass_enabled() {
+  const char* v = getenv("SA_FORWARD_PATH");
+  return v != nullptr && strcmp(v, "single_pass") == 0;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st, Prof* prof) {
+  if (a.T > 0 && a.pstride == 0 && single_pass_enabled()) {
+    if (launch_fwd_fused_bf16(a, st, prof) == hipSuccess) return hipSuccess;
+    (void)hipGetLastError();   // clear the error of the refused launch
+  }
   switch (a.d) {
     case 32: return launch_fwd_bf16_t<32>(a, st, prof);
     case 64: return launch_fwd_bf16_t<64>(a, st, prof);

@@ -22,6 +22,10 @@ constexpr int kBwdpWaves = 8;         // waves of a bf16 dP workgroup (32 protot
 // Device status word values written into the first bytes of the workspace.
 constexpr uint32_t kStatusOk = 0u;
 constexpr uint32_t kStatusBadOffsets = 1u;
+// Second status word (byte 4 of the workspace): the single-pass forward's
+// exchange gave up waiting.  A distinctive value, so that an unwritten word
+// is not mistaken for it.
+constexpr uint32_t kStatusExchangeTimeout = 0x7E4C7105u;
 
 struct Plan {
   int B, k, d;
@@ -37,7 +41,7 @@ struct Plan {
   int64_t bslots;       // dP partial slots: Gb, or Gb + B - 1 with per-user tables
   int kp;               // row stride of G and cv: k rounded up to the dX chunk (bf16), else k
   // forward workspace layout (byte offsets)
-  size_t off_status, off_lse, off_lse2, off_part, off_pmass, off_pl, off_tlse, fwd_bytes;
+  size_t off_status, off_lse, off_lse2, off_part, off_pmass, off_pl, off_tlse, off_xchg, fwd_bytes;
   // backward workspace layout (byte offsets)
   size_t off_G, off_cv, off_cvs, off_Pq, off_delta, off_dpp, off_blse, off_blse2, off_tlse2,
       bwd_bytes;
@@ -61,7 +65,8 @@ struct FwdArgs {
   float* part;         // [nslots, k, d]
   float* pmass;        // [nslots, k] (token-wise: per-slot running maxima)
   float* pl;           // [nslots, k] token-wise: per-slot sums of weights
-  uint32_t* status;    // device status word
+  uint32_t* status;    // device status words: [0] offsets, [1] exchange
+  uint64_t* xchg;      // [nchunks, T] exchange words of the single-pass forward
   int G, nchunks;
   int mass_norm;
 };
@@ -219,8 +224,15 @@ BwdArgs bwd_args(const Plan& p, char* ws, const int64_t* offsets, const void* X,
                  const float* mass, float* dX, float* dP);
 hipError_t launch_stats_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
+// Single-pass forward (sa_fused_bf16.hip): the exchange clear, the fused
+// kernel (cooperative launch) and the reduce.  An error means the fused
+// kernel did not run.
+hipError_t launch_fwd_fused_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
-hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof);
+// keep_exchange_status: leave the second status word as the single-pass
+// forward's kernel left it.
+hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof,
+                         bool keep_exchange_status = false);
 // Token-wise normalisation (sa_tok.hip): S [B, k, d] and lse [B, k].
 hipError_t launch_tok_fwd(const FwdArgs& a, int dtype, hipStream_t st, Prof* prof);
 // out[u] = scale * sum of user u's piece partials (slot s + u of segment s of

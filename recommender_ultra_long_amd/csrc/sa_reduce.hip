@@ -19,12 +19,13 @@ __global__ __launch_bounds__(256) void sa_reduce_kernel(
     const int64_t* __restrict__ offsets, int B, int k, int d, int64_t T, int G,
     const float* __restrict__ part, const float* __restrict__ pmass, int use_mass,
     float* __restrict__ S, float* __restrict__ mass, int mass_norm, float out_scale,
-    uint32_t* __restrict__ status) {
+    uint32_t* __restrict__ status, int keep2) {
   __shared__ f32x4 red[4][64];
   __shared__ float redm[4][64];
   const int u = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (blockIdx.y == 0 && u == 0) check_offsets_block(offsets, B, T, status, kStatusOk, kStatusBadOffsets);
+  if (blockIdx.y == 0 && u == 0)
+    check_offsets_block(offsets, B, T, status, kStatusOk, kStatusBadOffsets, keep2 != 0);
   const int64_t kd = (int64_t)k * d;
   const int64_t e = ((int64_t)blockIdx.y * 64 + lane) * 4;
   const bool live = e < kd;
@@ -76,14 +77,14 @@ __global__ __launch_bounds__(256) void sa_reduce_kernel(
   if (mass != nullptr && (e % d) == 0) mass[(int64_t)u * k + j] = mu;
 }
 
-hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof) {
+hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof, bool keep_exchange_status) {
   const int64_t kd = (int64_t)a.k * a.d;
   const unsigned gy = (unsigned)((kd + 255) / 256);
   const int use_mass = (a.mass_norm || a.mass != nullptr) ? 1 : 0;
   prof_begin(prof, "sa_reduce", st);
   hipLaunchKernelGGL(sa_reduce_kernel, dim3(a.B, gy), dim3(256), 0, st, a.offsets, a.B, a.k, a.d,
                      a.T, a.G, a.part, a.pmass, use_mass, a.S, a.mass, a.mass_norm, 1.0f,
-                     a.status);
+                     a.status, keep_exchange_status ? 1 : 0);
   const hipError_t e = hipGetLastError();
   prof_end(prof, st);
   return e;
@@ -96,7 +97,7 @@ hipError_t launch_piece_sum(const int64_t* offsets, int B, int k, int d, int64_t
   const unsigned gy = (unsigned)((kd + 255) / 256);
   prof_begin(prof, "sa_reduce", st);
   hipLaunchKernelGGL(sa_reduce_kernel, dim3(B, gy), dim3(256), 0, st, offsets, B, k, d, T, G,
-                     parts, (const float*)nullptr, 0, out, (float*)nullptr, 0, scale, status);
+                     parts, (const float*)nullptr, 0, out, (float*)nullptr, 0, scale, status, 0);
   const hipError_t e = hipGetLastError();
   prof_end(prof, st);
   return e;

@@ -31,6 +31,7 @@ SA_ERR_WORKSPACE_TOO_SMALL = 5
 SA_ERR_BAD_OFFSETS = 6
 SA_ERR_MISALIGNED = 7
 SA_ERR_HIP = 8
+SA_ERR_DEVICE_TIMEOUT = 9
 
 SA_F32 = 0
 SA_BF16 = 1

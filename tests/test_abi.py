@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     assert sa.version() == 10000
-    for code in range(9):
+    for code in range(10):
         s = sa.status_string(code)
         assert s.startswith("SA_")
     assert sa.status_string(123) == "SA_ERR_UNKNOWN"
