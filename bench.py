@@ -40,6 +40,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload lines (every workload at full size)")
     ap.add_argument("--part", choices=("all", "block", "stca", "token_wise", "action_fusion"),
                     default="all",
                     help="time one component alone and print its JSON (for profiling its "
@@ -63,14 +65,15 @@ def _parse():
 def _kernel_algorithmic(name, k, d, T):
     """Algorithmic work credited to each kernel (flop, HBM bytes).
 
-    Forward: 4 k d flop per token, all of it done by the aggregation kernel
-    (both products); the statistics pass is recomputation and is not credited.
+    Forward: 4 k d flop per token (both products), all of it done by the
+    single-pass kernel, or in the two-pass forward by the aggregation kernel
+    (its statistics pass is recomputation and is not credited).
     Backward: 10 k d per token = recomputed affinities (2) + dA (2) + g (2)
     + the dZ P product (2), all in the dX kernel, + dZ X (2) in the dP kernel.
     Bytes: each pass's compulsory traffic (X read, per-token statistics,
     outputs)."""
     bx = 2 * d           # bf16 X row
-    if name == "sa_agg_bf16":
+    if name in ("sa_agg_bf16", "sa_fused_bf16"):
         return 4.0 * k * d * T, T * (bx + 4)
     if name == "sa_stats_bf16":
         return 0.0, T * (bx + 4)
@@ -157,6 +160,7 @@ def _parse_traffic(fetch_csv, write_csv):
 # and the kernel declarations) are unchanged.
 KERNEL_SOURCES = {
     "sa_stats_bf16": "sa_fwd_bf16.hip", "sa_agg_bf16": "sa_fwd_bf16.hip",
+    "sa_fused_bf16": "sa_fused_bf16.hip", "sa_fused_clear": "sa_fused_bf16.hip",
     "sa_stats_f32": "sa_fwd_f32.hip", "sa_agg_f32": "sa_fwd_f32.hip",
     "sa_reduce_kernel": "sa_reduce.hip",
     "sa_bwd_prep": "sa_bwd.hip", "sa_bwdx_bf16": "sa_bwd.hip", "sa_bwdp_bf16": "sa_bwd.hip",
@@ -348,7 +352,9 @@ def _stca_timing(sa, timed, dev, D=1024, h=16):
     import torch
     g = torch.Generator(device=dev).manual_seed(17)
     s = D ** -0.5
-    Wq, Wk, Wv = (torch.randn(D, D, generator=g, device=dev) * s for _ in range(3))
+    Wq, Wk, Wv, Wo = (torch.randn(D, D, generator=g, device=dev) * s for _ in range(4))
+    W1, W3 = (torch.randn(D, 2 * D, generator=g, device=dev) * s for _ in range(2))
+    W2 = torch.randn(2 * D, D, generator=g, device=dev) * (2 * D) ** -0.5
     res = {"D": D, "heads": h}
     for name, B, L, R in (("sketch_rows", 32, 1024, 40), ("recent_suffix", 8, 10000, 300)):
         x_off = torch.arange(0, B + 1, device=dev, dtype=torch.int64) * L
@@ -368,7 +374,20 @@ def _stca_timing(sa, timed, dev, D=1024, h=16):
                      "targets_per_s": round(B * R / (ms * 1e-3), 1),
                      "core_gflop": round(core / 1e9, 2), "projection_gflop": round(proj / 1e9, 2),
                      "tflops_all": round((core + proj) / (ms * 1e-3) / 1e12, 1)}
-        del X, Q, o, lse, ws
+        # The whole layer of Eq. 26: + W_O (2 D^2) and the SwiGLU FFN (12 D^2)
+        # per target, 4 L D h + 20 D^2 in all.
+        y = torch.empty((B * R, D), dtype=torch.float32, device=dev)
+        wsl = torch.empty(int(sa.load().sa_stca_layer_workspace_size(D, h, B * R)),
+                          dtype=torch.uint8, device=dev)
+        fl = lambda: sa.stca_layer(x_off, X, t_off, Q, Wq, Wk, Wv, Wo, W1, W3, W2, h, y=y, o=o,
+                                   lse=lse, workspace=wsl)
+        fl()
+        ms_l = timed(fl, 5)
+        layer_flop = core + 20.0 * D * D * B * R
+        res[name]["layer_ms"] = round(ms_l, 4)
+        res[name]["layer_targets_per_s"] = round(B * R / (ms_l * 1e-3), 1)
+        res[name]["layer_tflops"] = round(layer_flop / (ms_l * 1e-3) / 1e12, 1)
+        del X, Q, o, lse, ws, y, wsl
     torch.cuda.empty_cache()
     return res
 
@@ -402,11 +421,195 @@ def _tokenwise_timing(sa, timed, dev, prob, off, reps, dX=None, dP=None):
         "tokens_per_s": round(T / ((ms_tf + ms_tb) * 1e-3), 1)}
 
 
+PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector peak (published): the fp32 path's bound
+NOMINAL_SCLK_MHZ = 2400.0
+
+
+def _gfx_clock_mhz():
+    """Current graphics clock of GPU 0 in MHz, averaged over its XCDs
+    (amdsmi), or None."""
+    try:
+        import amdsmi
+        if not getattr(_gfx_clock_mhz, "ready", False):
+            amdsmi.amdsmi_init()
+            _gfx_clock_mhz.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            _gfx_clock_mhz.ready = True
+        m = amdsmi.amdsmi_get_gpu_metrics_info(_gfx_clock_mhz.handle)
+        v = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float))]
+        if v:
+            return sum(v) / len(v)
+        v = m.get("current_gfxclk")
+        return float(v) if isinstance(v, (int, float)) else None
+    except Exception:
+        return None
+
+
+def _busy_sclk(fn, seconds=3.0):
+    """Median graphics clock while fn runs back to back for about `seconds`
+    (the clock the matrix cores run at under this load), sampled every 50 ms
+    over the second half of the run (the clock takes about a second to ramp
+    up), or None when the clock cannot be read."""
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+    t_start = time.perf_counter()
+
+    def sample():
+        while not stop.is_set():
+            v = _gfx_clock_mhz()
+            if v and time.perf_counter() - t_start > seconds / 2:
+                samples.append(v)
+            time.sleep(0.05)
+
+    if _gfx_clock_mhz() is None:
+        return None
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    while time.perf_counter() - t_start < seconds:
+        for _ in range(100):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    samples.sort()
+    return round(samples[len(samples) // 2], 1)
+
+
+def _oracle_sample(prob, backward, budget_s=3.0):
+    """The float64 oracle, as it stands, on whole users of the same input (in
+    user order, until about budget_s seconds of host work): history tokens/s
+    and the threads it used."""
+    import numpy as np
+    from oracle.sa_ref import sa_backward_ref, sa_forward_ref
+    from recommender_ultra_long_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    P64 = synth.to_f64(prob.P)
+    t = 0.0
+    n_tok = users = 0
+    B = len(prob.offsets) - 1
+    for u in range(B):
+        lo, hi = int(prob.offsets[u]), int(prob.offsets[u + 1])
+        hi = min(hi, lo + 50000)            # at most 50,000 tokens of one user
+        X64 = synth.to_f64(prob.X[lo:hi])
+        off = np.array([0, hi - lo], dtype=np.int64)
+        t0 = time.perf_counter()
+        if backward:
+            sa_backward_ref(off, X64, P64, synth.to_f64(prob.dS[u:u + 1]), prob.mass_norm)
+        else:
+            sa_forward_ref(off, X64, P64, prob.mass_norm)
+        t += time.perf_counter() - t0
+        n_tok += hi - lo
+        users += 1
+        if t >= budget_s:
+            break
+    what = "sa_backward_ref" if backward else "sa_forward_ref"
+    return {"value": round(n_tok / t, 1), "unit": "history tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_tok} tokens of the first {users} users (at most 50,000 per user), "
+                      f"{what} (float64 numpy), {t:.1f} s"}
+
+
+def _config_lines(sa, synth, timed, dev, sclk):
+    """Every workload of the path, each at its full size: forward throughput
+    (or latency, for the small fp32 case) and, for the 32-user batch, backward
+    throughput.  Algorithmic work: 4 k d flop per token forward, 10 k d
+    backward; bytes: X, the statistics and the outputs (inputs resident in
+    GPU memory)."""
+    import torch
+    out = {}
+    for name in synth.WORKLOAD_ORDER:
+        w = synth.WORKLOADS[name]
+        prob = synth.make_workload(name, device=dev, with_dS=w.backward)
+        B = len(prob.offsets) - 1
+        T, k, d = prob.total_tokens, w.k, w.d
+        off = torch.as_tensor(prob.offsets, device=dev)
+        esz = 2 if w.dtype == "bf16" else 4
+        pr = sa.make_problem(B, k, d, T, prob.X.dtype, prob.mass_norm)
+        S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((T,), dtype=torch.float32, device=dev)
+        mass = torch.empty((B, k), dtype=torch.float32, device=dev)
+        wsf = torch.empty(sa.workspace_size(pr, sa.SA_OP_FORWARD), dtype=torch.uint8, device=dev)
+        fwd = lambda: sa.sa_forward(off, prob.X, prob.P, prob.mass_norm, S=S, lse=lse, mass=mass,
+                                    workspace=wsf)
+        fwd()
+        reps = 50 if T < 200000 else (5 if T > 10000000 else 10)
+        if w.backward:
+            dX = torch.empty((T, d), dtype=torch.float32, device=dev)
+            dP = torch.empty((k, d), dtype=torch.float32, device=dev)
+            wsb = torch.empty(sa.workspace_size(pr, sa.SA_OP_BACKWARD), dtype=torch.uint8,
+                              device=dev)
+            fn = lambda: sa.sa_backward(off, prob.X, prob.P, prob.dS, lse, S, mass,
+                                        prob.mass_norm, dX=dX, dP=dP, workspace=wsb)
+            fn()
+            flop = 10.0 * k * d * T
+            byts = T * (esz * d + 4 + 4 * d) + B * k * d * 4 + k * d * (esz + 4)
+            what = "sa_backward (lse from the forward)"
+        else:
+            fn = fwd
+            flop = 4.0 * k * d * T
+            byts = T * (esz * d + 4) + B * k * d * 4 + k * d * esz + B * k * 4
+            what = "sa_forward"
+        ms = min(timed(fn, reps) for _ in range(3))
+        tf = flop / (ms * 1e-3) / 1e12
+        ent = {"workload": w.description, "call": what, "users": B, "tokens": T, "k": k, "d": d,
+               "dtype": w.dtype, "mass_norm": bool(prob.mass_norm), "ms": round(ms, 4),
+               "tokens_per_s": round(T / (ms * 1e-3), 1), "tflops": round(tf, 2),
+               "algorithmic_GBps": round(byts / (ms * 1e-3) / 1e9, 1)}
+        if w.dtype == "bf16":
+            ent["frac_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+            if sclk:
+                ent["frac_bf16_peak_at_measured_sclk"] = round(
+                    tf / (PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_MHZ), 4)
+        else:
+            ent["frac_fp32_valu_peak"] = round(tf / PEAK_FP32_VALU_TFLOPS, 4)
+        ent["cpu_baseline"] = _oracle_sample(prob, w.backward)
+        out[name] = ent
+        del prob, S, lse, mass, wsf
+        torch.cuda.empty_cache()
+    return out
+
+
+def _single_pass_timing(sa, timed, dev, prob, off, reps, fwd_flop):
+    """The single-pass forward (SA_FORWARD_PATH=single_pass: affinities once,
+    per-token statistics exchanged between the workgroups of a segment) on
+    the step's workload, beside the default two-pass forward."""
+    import torch
+    B, T = len(prob.offsets) - 1, prob.total_tokens
+    k, d = prob.workload.k, prob.workload.d
+    pr = sa.make_problem(B, k, d, T, prob.X.dtype, prob.mass_norm)
+    ws = torch.empty(sa.workspace_size(pr, sa.SA_OP_FORWARD), dtype=torch.uint8, device=dev)
+    S = torch.empty((B, k, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((T,), dtype=torch.float32, device=dev)
+    fn = lambda timer=None: sa.sa_forward(off, prob.X, prob.P, prob.mass_norm, S=S, lse=lse,
+                                          workspace=ws, want_mass=False, timer=timer)
+    os.environ["SA_FORWARD_PATH"] = "single_pass"
+    try:
+        fn()
+        ms = timed(fn, reps)
+        tm = sa.KernelTimer()
+        fn(tm)
+        torch.cuda.synchronize()
+        kern = {n: round(v, 5) for n, v in tm.times()}
+        status = sa.sa_get_device_status(ws)
+    finally:
+        del os.environ["SA_FORWARD_PATH"]
+    return {"forward_ms": round(ms, 5), "kernel_ms": kern,
+            "frac_bf16_peak": round(fwd_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "device_status": int(status)}
+
+
 def _extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop):
     """Timings beside the step (not part of it): the token-wise normalised
     variant on the step's workload, shared vs per-user tables and the stacked
     block on the 32-user batch, and the action-side fusion."""
     ex = {"token_wise": _tokenwise_timing(sa, timed, dev, prob, off, reps, dX, dP)}
+    ex["single_pass_forward"] = _single_pass_timing(sa, timed, dev, prob, off, reps, fwd_flop)
     ex["per_user_tables"] = _per_user_timing(sa, synth, timed, dev)
     ex["block"] = _block_timing(sa, synth, timed, dev)
     ex["action_fusion"] = _action_timing(sa, timed, dev)
@@ -526,6 +729,9 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": _traffic_for(name),
+                "traffic_counts": "L2-to-fabric bytes per launch (rocprofv3 FETCH_SIZE + "
+                                  "WRITE_SIZE, Infinity Cache hits included), scaled by the "
+                                  "readings of a plain 1 GiB copy",
                 "avg_launch_ms": round(ms, 5), "algorithmic_flop": fl,
                 "algorithmic_bytes": by,
                 "algorithmic_GBps": round(by / (ms * 1e-3) / 1e9, 1)}
@@ -554,7 +760,8 @@ def main():
         "forward": {"ms": round(ms_fwd, 5), "tokens_per_s": round(T / (ms_fwd * 1e-3), 1),
                     "tflops": round(fwd_flop / (ms_fwd * 1e-3) / 1e12, 2),
                     "frac_bf16_peak": round(fwd_flop / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                    "roofline_aggregation_kernel": roofline("sa_agg_bf16")},
+                    "roofline_aggregation_kernel": roofline(
+                        "sa_fused_bf16" if "sa_fused_bf16" in kern_ms else "sa_agg_bf16")},
         "backward": {"ms": round(ms_bwd, 5), "tokens_per_s": round(T / (ms_bwd * 1e-3), 1),
                      "tflops": round(bwd_flop / (ms_bwd * 1e-3) / 1e12, 2),
                      "frac_bf16_peak": round(bwd_flop / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
@@ -596,8 +803,17 @@ def main():
         "fold_us": round(ms_fold * 1e3, 2), "fold_backward_us": round(ms_fold_bwd * 1e3, 2),
         "fold_gflops": round(fold_flop / (ms_fold * 1e-3) / 1e9, 1),
         "fold_backward_gflops": round(fold_bwd_flop / (ms_fold_bwd * 1e-3) / 1e9, 1)}
+    sclk = _busy_sclk(step)
+    out["sclk_mhz_under_load"] = sclk
+    if sclk:
+        out["forward"]["frac_bf16_peak_at_measured_sclk"] = round(
+            out["forward"]["frac_bf16_peak"] * NOMINAL_SCLK_MHZ / sclk, 4)
+        out["roofline"]["frac_at_measured_sclk"] = round(
+            out["roofline"]["frac"] * NOMINAL_SCLK_MHZ / sclk, 4)
     if not args.step_only:
         out.update(_extras(sa, synth, timed, dev, prob, off, B, T, k, d, reps, dX, dP, fwd_flop))
+    if not args.step_only and not args.no_configs:
+        out["configs"] = _config_lines(sa, synth, timed, dev, sclk)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
