@@ -16,10 +16,10 @@
 // Kernels
 //  sa_bwd_prep:   G (input dtype) and cv per user and prototype.
 //  sa_bwdx_bf16:  token-stationary, one pass over all prototypes per token
-//                 tile: Z and dA' on the matrix cores (Z = P X^T orientation,
-//                 token per lane), then g^T, a^T, b^T += {G,P}^T {A,w} with
-//                 the A operands read transposed from LDS.  Writes dX and
-//                 delta.  10 k d MFMA flops per token.
+//                 tile, twice: Z and g^T = G^T A, giving delta, then Z, dA'
+//                 and dX^T += P^T dZ (Z = P X^T orientation, token per lane;
+//                 the accumulation operands read transposed from LDS).
+//                 Writes dX and delta.  10 k d MFMA flops per token.
 //  sa_bwdp_bf16:  prototype-stationary (256 prototypes per workgroup, like
 //                 the forward aggregation): Z^T, dA'^T, dZ, then
 //                 dP^T += X^T dZ^T.  One partial per token segment.  6 k d.
@@ -124,17 +124,17 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(
 // the user.
 //
 // With w'_ji = c A_ji (dA'_ji - cv_j) and s_i = sum_j w'_ji (= c delta_i),
-//   dX_i = sum_j (A_ji G_j + w'_ji p_j) - s_i sum_j A_ji p_j.
-// Holding both sums would need two 32 x d fp32 accumulators per wave, which
-// does not fit two waves per SIMD, so the pass runs over the prototypes twice:
-//   stage 1: Z, dA' - cv (the product starts from -cv), A, w';
-//            acc^T += G^T A + P^T w', s += w';
-//   stage 2: Z, A;  acc^T += P^T (-s A).
-// Stage 2 recomputes Z (and adds P^T A) for 16 of the 48 matrix products
-// per tile.
+//   dX_i = g_i + sum_j (w'_ji - s_i A_ji) p_j,   g_i = sum_j A_ji G_j,
+// and, since dA'_ji = G_j . x_i,  s_i = c (x_i . g_i - sum_j A_ji cv_j).
+// s_i needs every prototype before any w' - s A can be formed, so the pass
+// runs over the prototypes twice:
+//   stage 1: Z, A;  acc^T = G^T A (= g^T), e += A (-cv);  s = c (x . g + e);
+//   stage 2: Z, dA' - cv, A;  acc^T += P^T (c A (dA' - cv) - s A).
+// 4 + 6 = 10 k d matrix flops per token; the weight of stage 2 is c dZ
+// itself, rounded to bf16 once.
 //
-// Prototypes stream through LDS in chunks of 64 rows: P, G and -cv in stage 1,
-// P alone in stage 2, copied global -> LDS by the direct-to-LDS loads three
+// Prototypes stream through LDS in chunks of 64 rows: P, G and -cv in both
+// stages, copied global -> LDS by the direct-to-LDS loads three
 // chunks ahead into four buffers (rows stored with the tile swizzle of
 // sa_device.h), one barrier per chunk.  P, G and cv are padded with zero rows
 // to a whole number of chunks: a padded prototype's weight is at most 1 and
@@ -145,8 +145,9 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(
 //
 // Token-wise normalisation (TW): the weights A_ji = exp(z_ji - lse_j) use the
 // prototype's statistic, streamed with each chunk beside -cv (= -D_j); with
-// w'_ji = c A_ji (dA'_ji - D_j) = c dZ_ji there is no per-token coupling, so
-// stage 1 alone gives dX_i = sum_j (A_ji G_j + w'_ji p_j), and no delta.
+// w'_ji = c A_ji (dA'_ji - D_j) = c dZ_ji there is no per-token coupling:
+// one round (stage 2 with s = 0, also adding G^T A) gives
+// dX_i = sum_j (A_ji G_j + w'_ji p_j), 8 k d, and no delta.
 template <int D, bool TW>
 __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
@@ -164,8 +165,8 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
   constexpr int UPW = CU / NW;            // units per wave per matrix
   static_assert(UPW < 64 || UPW % 64 == 0, "");
   constexpr int XI = (UPW + 63) / 64;     // copy instructions per wave per matrix
-  constexpr int L1 = 2 * XI + 1 + (TW ? 1 : 0);   // loads per wave per stage-1 chunk
-  constexpr int L2 = XI;                  // loads per wave per stage-2 chunk
+  constexpr int LC = 2 * XI + 1 + (TW ? 1 : 0);   // loads per wave per chunk copy
+  constexpr int NST = TW ? 1 : 2;         // rounds over the prototypes
   constexpr int CW = PCH / NW;            // cv entries copied per wave
   constexpr uint32_t MB = PCH * D * 2;    // bytes of one matrix chunk
   constexpr uint32_t GOFF = MB;           // G follows P in a buffer
@@ -229,38 +230,33 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const float* cvu = cvn + (int64_t)u * kp;
     const float* lqu = TW ? lq2 + (int64_t)u * kp : nullptr;
 
-    // Chunk q of the stream: q < nch is stage-1 chunk q (P, G, -cv), then
-    // stage-2 chunk q - nch (P), then copies of chunk 0 that are never read.
-    // Into buffer q % NB.
+    // Chunk q of the stream is prototype chunk q mod nch (P, G, -cv) while
+    // q < NST nch (one round per stage), then copies of chunk 0 that are
+    // never read, so that every copy is the same number of loads.  Into
+    // buffer q % NB.
     auto copy_chunk = [&](int q) {
       const uint32_t dst = sb0 + (uint32_t)(q & (NB - 1)) * CB + (uint32_t)(wave * UPW) * 16;
-      if (q < nch) {
-        const uint32_t goff = (uint32_t)q * MB;
+      const int c = q < nch ? q : (q < NST * nch ? q - nch : 0);
+      const uint32_t goff = (uint32_t)c * MB;
 #pragma unroll
-        for (int j = 0; j < XI; ++j) {
-          if (UPW >= 64 || lane < UPW) {
-            lds_copy16(Pu, goff + cgo[j], dst + j * 1024);
-            lds_copy16(Gu, goff + cgo[j], dst + GOFF + j * 1024);
-          }
+      for (int j = 0; j < XI; ++j) {
+        if (UPW >= 64 || lane < UPW) {
+          lds_copy16(Pu, goff + cgo[j], dst + j * 1024);
+          lds_copy16(Gu, goff + cgo[j], dst + GOFF + j * 1024);
         }
+      }
+      if (lane < CW)
+        lds_copy4v(cvu + c * PCH + wave * CW + lane, sc0 + ((q & (NB - 1)) * PCH + wave * CW) * 4);
+      if constexpr (TW) {
         if (lane < CW)
-          lds_copy4v(cvu + q * PCH + wave * CW + lane, sc0 + ((q & (NB - 1)) * PCH + wave * CW) * 4);
-        if constexpr (TW) {
-          if (lane < CW)
-            lds_copy4v(lqu + q * PCH + wave * CW + lane, sq0 + ((q & (NB - 1)) * PCH + wave * CW) * 4);
-        }
-      } else {
-        const uint32_t goff = (uint32_t)(q < 2 * nch ? q - nch : 0) * MB;
-#pragma unroll
-        for (int j = 0; j < XI; ++j)
-          if (UPW >= 64 || lane < UPW) lds_copy16(Pu, goff + cgo[j], dst + j * 1024);
+          lds_copy4v(lqu + c * PCH + wave * CW + lane, sq0 + ((q & (NB - 1)) * PCH + wave * CW) * 4);
       }
     };
     // After chunk q: wait until chunk q + 1 has landed (q + 2 may still be in
     // flight); after the barrier no wave reads chunk q - 1 any more, and its
     // buffer takes chunk q + 3.
     auto advance = [&](int q) {
-      if (q + 2 < nch) wait_vmcnt<L1>(); else wait_vmcnt<L2>();
+      wait_vmcnt<LC>();
       barrier_lds();
       copy_chunk(q + 3);
     };
@@ -268,14 +264,11 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-    float ssum = 0.f;
 
     __syncthreads();   // the previous user's buffers are no longer read
 #pragma unroll
     for (int q = 0; q < 3; ++q) copy_chunk(q);
-    if (nch > 2) wait_vmcnt<2 * L1>();
-    else if (nch == 2) wait_vmcnt<L1 + L2>();
-    else wait_vmcnt<2 * L2>();
+    wait_vmcnt<2 * LC>();
     __syncthreads();   // chunk 0 has landed
 
     // The loops below are written in the order the instructions should
@@ -283,10 +276,10 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     // scheduling fences keep the compiler from moving the reads back next to
     // the products (where each product would wait for its read).
     constexpr int NS = 2 * DB;               // accumulation steps (db, kb) per tile
-    constexpr int ZA = KS < 3 ? KS : 3;      // stage-1 Z / dA' operand look-ahead (products)
-    constexpr int ZB = KS < 4 ? KS : 4;      // stage-2 Z operand look-ahead
-    constexpr int TA = NS < 2 ? NS : 2;      // stage-1 accumulation operand look-ahead (steps)
-    constexpr int TB2 = NS < 3 ? NS : 3;     // stage-2 accumulation operand look-ahead
+    constexpr int ZA = KS < 3 ? KS : 3;      // Z / dA' operand look-ahead (products)
+    constexpr int ZB = KS < 4 ? KS : 4;      // Z operand look-ahead when Z is alone
+    constexpr int TA = NS < 2 ? NS : 2;      // look-ahead of two accumulation operands (steps)
+    constexpr int TB2 = NS < 3 ? NS : 3;     // look-ahead of one accumulation operand
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
     auto rd16 = [&](uint32_t a) { return *(const SA_LDS bf16x8*)(lds + a); };
     auto rdtr = [&](uint32_t a0, uint32_t a1) {
@@ -297,9 +290,96 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     auto tra = [&](uint32_t base, int st, int e) {
       return base + toff[st >> 1][e] + (uint32_t)((st & 1) * KB);
     };
+    // -cv of prototypes crow(i, h) of tile pt, as register i.
+    auto cv_regs = [&](uint32_t cb, int pt) {
+      f32x16 c;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 c4 = *(const SA_LDS f32x4*)(lds + cb + pt * 128 + 32 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[4 * g4 + r] = c4[r];
+      }
+      return c;
+    };
 
-    // Stage 1.
-    for (int q = 0; q < nch; ++q) {
+    // Stage 1 (softmax weights only): acc^T = g^T = G^T A and
+    // e = sum_j A_ji (-cv_j); then s = c (x_i . g_i + e) = c delta_i.
+    float s = 0.f;
+    if constexpr (!TW) {
+      float eneg = 0.f;
+      for (int q = 0; q < nch; ++q) {
+        const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
+        const uint32_t cb = sc0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const uint32_t tbuf = buf + pt * TB;
+          f32x16 z = f32x16{};
+          bf16x8 pa[KS];
+#pragma unroll
+          for (int ks = 0; ks < ZB; ++ks) pa[ks] = rd16(tbuf + aoff[ks]);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            fence();
+            if (ks + ZB < KS) pa[ks + ZB] = rd16(tbuf + aoff[ks + ZB]);
+            z = mfma32(pa[ks], xb[ks], z);
+          }
+          fence();
+          bf16x8 gt[NS];
+#pragma unroll
+          for (int st = 0; st < TB2; ++st)
+            gt[st] = rdtr(tra(tbuf, st, 0) + GOFF, tra(tbuf, st, 1) + GOFF);
+          const f32x16 cvn = cv_regs(cb, pt);
+          fence();
+          bf16x8 abf[2];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float a = __builtin_amdgcn_fmed3f(exp2_fast(fmaf(z[i], alpha, -lsh)), 0.f, 1.f);
+            eneg = fmaf(a, cvn[i], eneg);
+            abf[i >> 3][i & 7] = (bf16)a;
+          }
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            fence();
+            if (st + TB2 < NS)
+              gt[st + TB2] = rdtr(tra(tbuf, st + TB2, 0) + GOFF, tra(tbuf, st + TB2, 1) + GOFF);
+            acc[st >> 1] = mfma32(gt[st], abf[st & 1], acc[st >> 1]);
+          }
+          fence();
+        }
+        advance(q);
+      }
+      // x_i . g_i.  Register 4 g4 + r of block db is column
+      // 32 db + 8 g4 + 4h + r = 16 ks + 8 (g4 % 2) + 4h + r with ks = 2 db + g4 / 2,
+      // which lane (l32, g4 % 2) holds in xb[ks] at position 4h + r.  Each
+      // lane keeps the positions 4h .. 4h + 3 of its own xb and takes the
+      // others from the partner lane l ^ 32.
+      float dot = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 xv = __builtin_bit_cast(u32x4, xb[ks]);
+        const uint32_t o0 = h ? xv[2] : xv[0], o1 = h ? xv[3] : xv[1];   // own 4h .. 4h + 3
+        const uint32_t p0 = h ? xv[0] : xv[2], p1 = h ? xv[1] : xv[3];   // the partner's
+        const uint32_t r0w = (uint32_t)__shfl_xor((int)p0, 32, 64);
+        const uint32_t r1w = (uint32_t)__shfl_xor((int)p1, 32, 64);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int db = ks >> 1, g4 = 2 * (ks & 1) + half;
+          const bool own = half == h;
+          const uint32_t w0 = own ? o0 : r0w, w1 = own ? o1 : r1w;
+          dot = fmaf(__uint_as_float(w0 << 16), acc[db][4 * g4 + 0], dot);
+          dot = fmaf(__uint_as_float(w0 & 0xFFFF0000u), acc[db][4 * g4 + 1], dot);
+          dot = fmaf(__uint_as_float(w1 << 16), acc[db][4 * g4 + 2], dot);
+          dot = fmaf(__uint_as_float(w1 & 0xFFFF0000u), acc[db][4 * g4 + 3], dot);
+        }
+      }
+      const float part = dot + eneg;
+      s = scale * (part + shfl_xor32(part));
+    }
+
+    // Stage 2 (the only one with token-wise weights): Z, dA' - cv, A and
+    // w_ji = c A_ji (dA'_ji - cv_j) - s_i A_ji = c dZ_ji;  acc^T += P^T w
+    // (+ G^T A with token-wise weights, where s = 0 and acc starts at 0).
+    for (int q = TW ? 0 : nch; q < NST * nch; ++q) {
       const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
       const uint32_t cb = sc0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
       const uint32_t qb = sq0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
@@ -307,14 +387,9 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
       for (int pt = 0; pt < 2; ++pt) {
         const uint32_t tbuf = buf + pt * TB;
         // Z and dA' - cv: rows = prototypes crow(i, h), column = this token.
-        f32x16 z = f32x16{}, da;
+        f32x16 z = f32x16{};
+        f32x16 da = cv_regs(cb, pt);
         bf16x8 pa[KS], ga[KS];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 c4 = *(const SA_LDS f32x4*)(lds + cb + pt * 128 + 32 * g4);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) da[4 * g4 + r] = c4[r];
-        }
 #pragma unroll
         for (int ks = 0; ks < ZA; ++ks) {
           pa[ks] = rd16(tbuf + aoff[ks]);
@@ -332,10 +407,11 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
         }
         fence();
         // The first accumulation operands, read while the weights are formed.
+        constexpr int LA = TA;
         bf16x8 gt[NS], ptr[NS];
 #pragma unroll
-        for (int st = 0; st < TA; ++st) {
-          gt[st] = rdtr(tra(tbuf, st, 0) + GOFF, tra(tbuf, st, 1) + GOFF);
+        for (int st = 0; st < LA; ++st) {
+          if constexpr (TW) gt[st] = rdtr(tra(tbuf, st, 0) + GOFF, tra(tbuf, st, 1) + GOFF);
           ptr[st] = rdtr(tra(tbuf, st, 0), tra(tbuf, st, 1));
         }
         fence();
@@ -349,62 +425,22 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
             const int i = 4 * g4 + r;
             // A <= 1 for real prototypes; the clamp keeps padded ones finite.
             const float a = __builtin_amdgcn_fmed3f(exp2_fast(fmaf(z[i], alpha, -l4[r])), 0.f, 1.f);
-            const float w = a * (da[i] * scale);
-            if constexpr (!TW) ssum += w;
-            abf[i >> 3][i & 7] = (bf16)a;
+            const float w = a * fmaf(da[i], scale, -s);
+            if constexpr (TW) abf[i >> 3][i & 7] = (bf16)a;
             wbf[i >> 3][i & 7] = (bf16)w;
           }
         }
-        // acc^T (d x tokens) += G^T A + P^T w'.  K slot j of half h in block
-        // kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
+        // K slot j of half h in block kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           fence();
-          if (st + TA < NS) {
-            gt[st + TA] = rdtr(tra(tbuf, st + TA, 0) + GOFF, tra(tbuf, st + TA, 1) + GOFF);
-            ptr[st + TA] = rdtr(tra(tbuf, st + TA, 0), tra(tbuf, st + TA, 1));
+          if (st + LA < NS) {
+            if constexpr (TW)
+              gt[st + LA] = rdtr(tra(tbuf, st + LA, 0) + GOFF, tra(tbuf, st + LA, 1) + GOFF);
+            ptr[st + LA] = rdtr(tra(tbuf, st + LA, 0), tra(tbuf, st + LA, 1));
           }
-          acc[st >> 1] = mfma32(gt[st], abf[st & 1], acc[st >> 1]);
+          if constexpr (TW) acc[st >> 1] = mfma32(gt[st], abf[st & 1], acc[st >> 1]);
           acc[st >> 1] = mfma32(ptr[st], wbf[st & 1], acc[st >> 1]);
-        }
-        fence();
-      }
-      advance(q);
-    }
-
-    // Stage 2: acc^T += P^T (-s A) (not with token-wise weights).
-    const float s = ssum + shfl_xor32(ssum);   // c delta of this lane's token
-    for (int q = nch; q < (TW ? nch : 2 * nch); ++q) {
-      const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        const uint32_t tbuf = buf + pt * TB;
-        f32x16 z = f32x16{};
-        bf16x8 pa[KS];
-#pragma unroll
-        for (int ks = 0; ks < ZB; ++ks) pa[ks] = rd16(tbuf + aoff[ks]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          fence();
-          if (ks + ZB < KS) pa[ks + ZB] = rd16(tbuf + aoff[ks + ZB]);
-          z = mfma32(pa[ks], xb[ks], z);
-        }
-        fence();
-        bf16x8 ptr[NS];
-#pragma unroll
-        for (int st = 0; st < TB2; ++st) ptr[st] = rdtr(tra(tbuf, st, 0), tra(tbuf, st, 1));
-        fence();
-        bf16x8 bbf[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float a = __builtin_amdgcn_fmed3f(exp2_fast(fmaf(z[i], alpha, -lsh)), 0.f, 1.f);
-          bbf[i >> 3][i & 7] = (bf16)(-s * a);
-        }
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          fence();
-          if (st + TB2 < NS) ptr[st + TB2] = rdtr(tra(tbuf, st + TB2, 0), tra(tbuf, st + TB2, 1));
-          acc[st >> 1] = mfma32(ptr[st], bbf[st & 1], acc[st >> 1]);
         }
         fence();
       }
