@@ -66,6 +66,12 @@ bool make_plan(int B, int k, int d, int64_t T, int dtype, bool mass_norm, bool p
   p->off_blse = off; off = align256(off + Tn * 4);
   p->off_blse2 = off; off = align256(off + (Tn + 1) * 4);
   p->off_tlse2 = off; off = align256(off + (size_t)B * kp * 4);
+  // c dZ (bf16) per token and prototype, written by the dX pass and read by
+  // the dP pass: 2 KiB per (32-token tile, 32-prototype tile) for
+  // bnchunks x 256 prototypes, and one scratch token tile at the end.
+  p->off_dz = off;
+  if (dtype == 1)
+    off = align256(off + ((Tn + 31) / 32 + 1) * (size_t)p->bnchunks * (kChunkBf16 / 32) * 2048);
   p->bwd_bytes = off;
   return true;
 }
@@ -116,6 +122,8 @@ BwdArgs bwd_args(const Plan& p, char* w, const int64_t* offsets, const void* X, 
   a.mass_norm = p.mass_norm ? 1 : 0;
   a.tokwise = 0;
   a.tlse2 = (float*)(w + p.off_tlse2);
+  a.dz = (void*)(w + p.off_dz);
+  a.kz = p.bnchunks * kChunkBf16;
   return a;
 }
 

@@ -25,6 +25,8 @@
 //                 dP^T += X^T dZ^T.  One partial per token segment.  6 k d.
 //  sa_dp_reduce:  dP = c sum over segments in order (deterministic).
 // The fp32 variants do the same arithmetic on the vector ALU.
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const bf16* __restrict__ Pq, int64_t pq_ustride, const bf16* __restrict__ Gq,
     const float* __restrict__ cvn, int kp, int64_t T, float alpha, float scale,
     const float* __restrict__ lse, const float* __restrict__ lq2, float* __restrict__ dX,
-    int acc_dx, float* __restrict__ delta_out) {
+    int acc_dx, float* __restrict__ delta_out, bf16* __restrict__ wz, int kz) {
   constexpr int NW = 8;                   // waves
   static_assert(NW * 32 == kBwdxTokensBf16, "");
   constexpr int KS = D / 16, DB = D / 32, U = D / 8;
@@ -255,11 +257,15 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     // After chunk q: wait until chunk q + 1 has landed (q + 2 may still be in
     // flight); after the barrier no wave reads chunk q - 1 any more, and its
     // buffer takes chunk q + 3.
-    auto advance = [&](int q) {
-      wait_vmcnt<LC>();
+    // Stage-2 chunks also issued their NZS stores of W after chunk q + 2's copy.
+    constexpr int NZS = 4;                 // stores of W per wave per chunk (2 per tile)
+    auto advance = [&](int q, auto stores) {
+      wait_vmcnt<LC + decltype(stores)::value>();
       barrier_lds();
       copy_chunk(q + 3);
     };
+    using NoStores = std::integral_constant<int, 0>;
+    using WStores = std::integral_constant<int, NZS>;
 
     f32x16 acc[DB];
 #pragma unroll
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
           }
           fence();
         }
-        advance(q);
+        advance(q, NoStores{});
       }
       // x_i . g_i.  Register 4 g4 + r of block db is column
       // 32 db + 8 g4 + 4h + r = 16 ks + 8 (g4 % 2) + 4h + r with ks = 2 db + g4 / 2,
@@ -379,7 +385,8 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     // Stage 2 (the only one with token-wise weights): Z, dA' - cv, A and
     // w_ji = c A_ji (dA'_ji - cv_j) - s_i A_ji = c dZ_ji;  acc^T += P^T w
     // (+ G^T A with token-wise weights, where s = 0 and acc starts at 0).
-    for (int q = TW ? 0 : nch; q < NST * nch; ++q) {
+    const int q0 = TW ? 0 : nch;
+    for (int q = q0; q < NST * nch; ++q) {
       const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
       const uint32_t cb = sc0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
       const uint32_t qb = sq0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
@@ -430,6 +437,18 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
             wbf[i >> 3][i & 7] = (bf16)w;
           }
         }
+        // W = c dZ for the dP pass, in fragment order: block (token tile
+        // tok / 32, prototype tile) of wz holds the 64 lanes' 16 weights
+        // (32 bytes each) as they are here, so each lane writes 32 contiguous
+        // bytes and a wave 2 KiB.  Every lane stores (a token of another user,
+        // or past the end, writes to the scratch tile after the last one), so
+        // that each wave issues exactly NZS stores per chunk.
+        {
+          const int64_t zt = mine ? (tok >> 5) : ((T + 31) >> 5);
+          bf16* zd = wz + ((zt * (kz >> 5) + ((q - q0) * 2 + pt)) * 64 + lane) * 16;
+          *(bf16x8*)zd = wbf[0];
+          *(bf16x8*)(zd + 8) = wbf[1];
+        }
         // K slot j of half h in block kb is prototype 16 kb + 8 (j / 4) + 4h + (j % 4).
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
@@ -444,7 +463,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
         }
         fence();
       }
-      advance(q);
+      advance(q, WStores{});
     }
     wait_vmcnt<0>();
     __syncthreads();   // every wave's copies have landed and every read is done
@@ -485,78 +504,62 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
 }
 
 // ----------------------------------------------------------------------------
-// bf16 dP pass.  grid = (Gb segments, nchunks); block = NW waves x 32
-// prototypes, the tiling and copy pipeline of the forward aggregation:
-// 32-token tiles copied global -> LDS (X, lse2, delta) six tiles ahead into
-// eight buffers, a barrier after every second tile.  Per tile: Z^T and dA'^T
-// (matrix cores), dZ (vector ALU), dP^T += X^T dZ^T (matrix cores).  With a
-// shared P the partial spans the whole segment, across users (slot s).  With
-// one table per user (PU, user u's at P + u pstride) each (segment, user)
-// piece has its own partial (slot s + u), and a user change reloads the
-// prototype rows.
-//
-// lse2 holds the log-sum-exp in log2 units with lse2[T] = +inf, which rows
-// past the end of a tile read (weight 0, so dZ = 0).
-//
-// Token-wise normalisation (TW): the weights use the prototype's statistic,
-// lq2[user][proto] (a lane register, reloaded with G at a user change), dZ =
-// A (dA' - D_j) has no per-token term, and rows past a tile's end are masked
-// by the tile's row count (no per-token copies at all).
-template <int D, int NW, bool PU, bool TW>
+// bf16 dP pass, a product of two stored operands: dP^T (d x prototypes) =
+// X^T (d x tokens) W (tokens x prototypes) with W = c dZ, the bf16 weights the
+// dX pass formed and stored in its fragment order: 2 KiB blocks per (aligned
+// 32-token tile, 32-prototype tile), lane L = 32 h + token % 32 holding the
+// 16 weights of prototypes crow(i, h) (i = 0 .. 15), kz / 32 blocks per token
+// tile.  grid = (Gb segments, nchunks); block = NW waves x 32 prototypes (one
+// 256-prototype chunk).  The segment's token stream is cut into 32-token
+// tiles that never straddle two users (nor align with the stored ones); the X
+// tile and the tile's W entries of this chunk are copied global -> LDS by the
+// direct-to-LDS loads three tiles ahead into four buffers, one barrier per
+// tile.  In LDS, wave w's W is [token row][h][16 weights]: 8 bytes at (row,
+// h, 4 (c / 2)) are the row's prototypes 4c .. 4c + 3 (c % 2 = h), so both
+// operands are transpose-read like a row-major tile (K = tokens, in the same
+// order for both).  Rows of a tile past its end are copies of the tile's
+// first row; their W entries are zeroed in registers.
+// With a shared P the partial spans the whole segment, across users (slot
+// s); with one table per user (PU) each (segment, user) piece has its own
+// partial (slot s + u).
+template <int D, int NW, bool PU>
 __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
-    const bf16* __restrict__ P, int64_t pstride, const bf16* __restrict__ Gq,
-    const float* __restrict__ cv, int k, int kp, int64_t T, int G, float alpha,
-    const float* __restrict__ lse2, const float* __restrict__ delta,
-    const float* __restrict__ lq2, float* __restrict__ dpp) {
-  constexpr int KS = D / 16;             // reduction steps over d
+    const bf16* __restrict__ W, int kz, int k, int64_t T, int G, float* __restrict__ dpp) {
+  // W units (16 bytes) of one tile: 8 prototype tiles x 32 rows x 2 halves x 2.
   constexpr int DB = D / 32;             // 32-row blocks of the transposed partial
-  constexpr int U = D / 8;               // 16-byte units per token row
+  constexpr int U = D / 8;               // 16-byte units per X row
   constexpr int KC = NW * 32;            // prototypes per workgroup
   static_assert(KC == kChunkBf16, "one workgroup covers one prototype chunk");
   constexpr int TILE = 32;
-  constexpr int UNITS = TILE * U;
-  constexpr int UPW = UNITS / NW;        // units copied by each wave
-  static_assert(UNITS % NW == 0 && (UPW <= 64 || UPW % 64 == 0), "");
-  constexpr int XI = (UPW + 63) / 64;    // X copy instructions per wave per tile
-  constexpr int LPW = TILE / NW;         // lse and delta entries copied by each wave
-  constexpr int NBUF = 8, AHEAD = 6;
-  constexpr int L = XI + (TW ? 0 : 2);   // loads per wave per tile
-  constexpr uint32_t XBYTES = TILE * D * 2;
+  constexpr int XUN = TILE * U, ZUN = TILE * (KC / 8);
+  constexpr int XPW = XUN / NW, ZPW = ZUN / NW;   // units copied by each wave
+  static_assert(XUN % NW == 0 && (XPW <= 64 || XPW % 64 == 0), "");
+  static_assert(ZPW % 64 == 0, "");
+  constexpr int XI = (XPW + 63) / 64, ZI = ZPW / 64;   // copy instructions per wave per tile
+  constexpr int L = XI + ZI;             // loads per wave per tile
+  constexpr int NBUF = 4, AHEAD = 3;
+  constexpr uint32_t XBYTES = TILE * D * 2, ZBYTES = TILE * KC * 2;
 
   __shared__ __attribute__((aligned(16))) bf16 sX[NBUF][TILE * D];
-  __shared__ __attribute__((aligned(16))) float sL[NBUF][TILE];
-  __shared__ __attribute__((aligned(16))) float sD[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 sW[NBUF][TILE * KC];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int s = blockIdx.x, chunk = blockIdx.y;
-  const int proto = chunk * KC + wave * 32 + l32;   // this lane's prototype
-  const int prow = proto < k ? proto : k - 1;       // rows past k: results unused
+  const int proto = chunk * KC + wave * 32 + l32;   // this lane's prototype (output column)
   const uint32_t sx0 = lds_addr((const SA_LDS void*)&sX[0][0]);
-  const uint32_t sl0 = lds_addr((const SA_LDS void*)&sL[0][0]);
-  const uint32_t sd0 = lds_addr((const SA_LDS void*)&sD[0][0]);
+  const uint32_t sw0 = lds_addr((const SA_LDS void*)&sW[0][0]);
   const SA_LDS char* lds = (const SA_LDS char*)0;
 
-  // B operands: pw[ks] = P[proto][16 ks + 8h .. +7], gw likewise for the
-  // current user's G (row stride kp); cw = cv[user][proto].
   const int64_t lo = seg_lo(T, G, s), hi = seg_lo(T, G, s + 1);
   TileWalker<TILE> cw_;                // tile being computed
   cw_.start(offsets, B, lo, hi);
 
-  bf16x8 pw[KS], gw[KS];
-  float cw, lj = 0.f;   // cv (or D_j) and, token-wise, lse2 of the lane's prototype
-  auto load_prototype = [&](const bf16* Pu) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      pw[ks] = *(const bf16x8*)(Pu + (int64_t)prow * D + 16 * ks + 8 * h);
-  };
-  load_prototype(PU && cw_.valid ? P + (int64_t)cw_.user * pstride : P);
-
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  // acc[db] register i is dP[proto][d = 32 db + crow(i, h)] / c.
+  // acc[db] register i is dP[proto][d = 32 db + crow(i, h)].
   auto flush = [&](int64_t slot) {
     if (proto < k) {
       float* dst = dpp + (slot * k + proto) * D;
@@ -574,149 +577,115 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_bwdp_bf16(
   if (cw_.valid) {
     TileWalker<TILE> qw = cw_;         // next tile to copy
 
-    int crow_[XI];
-    uint32_t ccol[XI];
+    // Copy geometry.  X: unit v of the tile is row v / U at stored position
+    // v % U, holding global unit (v % U) ^ xswz<D>(row).  W: unit v of wave
+    // w's 128 is (row (v / 4) % 32, half (v / 2) % 2, 16 bytes v % 2) of
+    // prototype tile w of the chunk.
+    int xrow[XI], zrow[ZI];
+    uint32_t xcol[XI], zcol[ZI];
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // uniform: a scalar base
 #pragma unroll
     for (int j = 0; j < XI; ++j) {
-      const int v = wave * UPW + j * 64 + lane;
-      crow_[j] = v / U;
-      ccol[j] = (uint32_t)(((v % U) ^ xswz<D>(v / U)) * 16);
+      const int v = wave * XPW + j * 64 + lane;
+      xrow[j] = v / U;
+      xcol[j] = (uint32_t)(((v % U) ^ xswz<D>(v / U)) * 16);
     }
-    const int lrow = wave * LPW + lane;
+#pragma unroll
+    for (int j = 0; j < ZI; ++j) {
+      const int v = j * 64 + lane;
+      zrow[j] = (v >> 2) & 31;
+      zcol[j] = (uint32_t)((((v >> 1) & 1) * 32) * 32 + (v & 1) * 16);   // + 32 (row % 32) later
+    }
 
     // Every wave issues exactly L loads per tile (also past the end of the
-    // stream), so that vmcnt counts are the same every time.
+    // stream, re-reading the segment's first tile), so that vmcnt counts are
+    // the same every time.
     auto copy_next = [&](uint32_t b) {
       const bool valid = qw.valid;
-      const int64_t base = valid ? qw.t0 : 0;
-      const int nr = valid ? (int)(qw.t1 - qw.t0) : 0;
+      const int64_t base = valid ? qw.t0 : cw_.t0;
+      const int nr = valid ? (int)(qw.t1 - qw.t0) : 1;
       const bf16* xb = X + base * D;
+      // W blocks of the stored token tile holding row 0 of this tile, and of
+      // the next one (rows may run into it).
+      const int64_t tau0 = base >> 5;
+      const bf16* zb = W + (tau0 * (kz >> 5) + chunk * NW + wave_s) * 1024;
+      const uint32_t nextb = (uint32_t)(kz >> 5) * 2048u;
 #pragma unroll
       for (int j = 0; j < XI; ++j) {
-        const int r = crow_[j] < nr ? crow_[j] : 0;
-        if (UPW >= 64 || lane < UPW)
-          lds_copy16(xb, (uint32_t)(r * D * 2) + ccol[j],
-                     sx0 + b * XBYTES + (uint32_t)(wave * UPW + j * 64) * 16);
+        const int r = xrow[j] < nr ? xrow[j] : 0;
+        if (XPW >= 64 || lane < XPW)
+          lds_copy16(xb, (uint32_t)(r * D * 2) + xcol[j],
+                     sx0 + b * XBYTES + (uint32_t)(wave * XPW + j * 64) * 16);
       }
-      if (!TW && lane < LPW) {
-        const bool in = lrow < nr;
-        lds_copy4v(in ? lse2 + base + lrow : lse2 + T, sl0 + (b * TILE + wave * LPW) * 4);
-        lds_copy4v(delta + base + (in ? lrow : 0), sd0 + (b * TILE + wave * LPW) * 4);
+#pragma unroll
+      for (int j = 0; j < ZI; ++j) {
+        const int r = zrow[j] < nr ? zrow[j] : 0;
+        const int tl = (int)(base & 31) + r;              // row within the stored tiles
+        lds_copy16(zb, (tl >> 5) * nextb + (uint32_t)(tl & 31) * 32u + zcol[j],
+                   sw0 + b * ZBYTES + (uint32_t)(wave * ZPW + j * 64) * 16);
       }
       if (valid) qw.advance();
     };
 
     guser = cw_.user;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * kp + prow) * D + 16 * ks + 8 * h);
-    cw = cv[(int64_t)guser * kp + prow];
-    if constexpr (TW) lj = lq2[(int64_t)guser * kp + prow];
-#pragma unroll
     for (int b = 0; b < AHEAD; ++b) copy_next(b);
-    // The compiler must see the waits for the operand loads above here, not
-    // inside the loop (where they would also wait for every copy in flight).
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(pw[ks]), "v"(gw[ks]));
-    asm volatile("" ::"v"(cw), "v"(lj));
-    wait_vmcnt<0>();
-    __syncthreads();
 
+    // Transpose-read offsets: X^T block db (A operand, rows = d) and this
+    // wave's W columns (B operand, columns = its 32 prototypes); token rows
+    // 4h + tr_r + 8e (+ 16 kb), so K slot j of half h in block kb is token
+    // 16 kb + 8 (j / 4) + 4h + (j % 4) for both operands.
     const int tr_r = (lane & 15) >> 2, tr_c = lane & 3, tr_half = (lane >> 4) & 1;
-    uint32_t aoff[KS], toff[DB][2];
+    uint32_t toff[DB][2], woff[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) aoff[ks] = (uint32_t)xoff<D>(l32, 2 * ks + h) * 2;
+    for (int e = 0; e < 2; ++e) {
+      const int r = 4 * h + tr_r + 8 * e;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        toff[db][e] = (uint32_t)(xoff<D>(4 * h + tr_r + 8 * e, 4 * db + 2 * tr_half + (tr_c >> 1)) +
-                                 (tr_c & 1) * 4) * 2;
-    const uint32_t lqoff = (uint32_t)(4 * h) * 4;
+      for (int db = 0; db < DB; ++db)
+        toff[db][e] = (uint32_t)(xoff<D>(r, 4 * db + 2 * tr_half + (tr_c >> 1)) + (tr_c & 1) * 4) * 2;
+      // columns 4c .. 4c + 3, c = 4 tr_half + tr_c: half c % 2, bytes 8 (c / 2)
+      woff[e] = (uint32_t)(wave * 2048 + r * 64 + (tr_c & 1) * 32 + 8 * (2 * tr_half + (tr_c >> 1)));
+    }
 
     uint32_t t = 0;
     while (true) {
       const uint32_t buf = t & (NBUF - 1);
+      // Tile t has landed (t + 1 and t + 2 may be in flight); after the
+      // barrier every wave's copies of it are visible and nobody reads tile
+      // t - 1 any more, whose buffer takes tile t + 3.
+      wait_vmcnt<(AHEAD - 1) * L>();
+      barrier_lds();
       copy_next((t + AHEAD) & (NBUF - 1));
-      if (cw_.user != guser) {
-        // A new user: its G rows and cv (rare; waits for the loads here).
-        if constexpr (PU) {
-          // The finished piece's partial; then nothing stays in flight, so
-          // the vmcnt counts below hold as at the start.
-          flush((int64_t)s + guser);
+      if (PU && cw_.user != guser) {
+        // The finished piece's partial (its stores only make later vmcnt
+        // waits stricter).
+        flush((int64_t)s + guser);
 #pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-          wait_vmem_all();
-        }
+        for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
         guser = cw_.user;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          gw[ks] = *(const bf16x8*)(Gq + ((int64_t)guser * kp + prow) * D + 16 * ks + 8 * h);
-        cw = cv[(int64_t)guser * kp + prow];
-        if constexpr (TW) lj = lq2[(int64_t)guser * kp + prow];
-        if constexpr (PU) {
-          load_prototype(P + (int64_t)guser * pstride);
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(pw[ks]));
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(gw[ks]));
-        asm volatile("" ::"v"(cw), "v"(lj));
       }
-
+      const int nr = (int)(cw_.t1 - cw_.t0);   // valid rows of this tile
       const SA_LDS char* xs = lds + sx0 + buf * XBYTES;
-      // Z^T and dA'^T (tokens x prototypes) of this tile.
-      f32x16 z = f32x16{}, da = f32x16{};
+      const SA_LDS char* ws = lds + sw0 + buf * ZBYTES;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const SA_LDS bf16x8*)(xs + aoff[ks]);
-        z = mfma32(a, pw[ks], z);
-        da = mfma32(a, gw[ks], da);
-      }
-      // dZ = A (dA' - cv - delta); register i of a lane is token crow(i, h).
-      bf16x8 zbf[2];
-      if constexpr (TW) {
-        const int nr = (int)(cw_.t1 - cw_.t0);   // valid rows of this tile
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 wt = concat4(lds_read_tr16((const SA_LDS bf16*)(ws + woff[0] + kb * 16 * 64)),
+                            lds_read_tr16((const SA_LDS bf16*)(ws + woff[1] + kb * 16 * 64)));
+        if (nr < TILE) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float a = crow(i, h) < nr ? exp2_fast(fmaf(z[i], alpha, -lj)) : 0.f;
-          zbf[i >> 3][i & 7] = (bf16)(a * (da[i] - cw));
-        }
-      } else {
-        const SA_LDS char* ls = lds + sl0 + buf * (TILE * 4) + lqoff;
-        const SA_LDS char* ds = lds + sd0 + buf * (TILE * 4) + lqoff;
-        f32x4 lq[4], dq[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          lq[g] = *(const SA_LDS f32x4*)(ls + 32 * g);
-          dq[g] = *(const SA_LDS f32x4*)(ds + 32 * g);
+          for (int j = 0; j < 8; ++j)
+            if (16 * kb + 8 * (j >> 2) + 4 * h + (j & 3) >= nr) wt[j] = (bf16)0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float a = exp2_fast(fmaf(z[i], alpha, -lq[i >> 2][i & 3]));
-          zbf[i >> 3][i & 7] = (bf16)(a * (da[i] - cw - dq[i >> 2][i & 3]));
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 xt =
+              concat4(lds_read_tr16((const SA_LDS bf16*)(xs + toff[db][0] + kb * 16 * D * 2)),
+                      lds_read_tr16((const SA_LDS bf16*)(xs + toff[db][1] + kb * 16 * D * 2)));
+          acc[db] = mfma32(xt, wt, acc[db]);
         }
       }
-      // dP^T (d x prototypes) += X^T (d x tokens) dZ^T (tokens x prototypes).
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const SA_LDS char* p0 = xs + toff[db][0];
-        const SA_LDS char* p1 = xs + toff[db][1];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 xt = concat4(lds_read_tr16((const SA_LDS bf16*)(p0 + kb * 32 * D)),
-                                    lds_read_tr16((const SA_LDS bf16*)(p1 + kb * 32 * D)));
-          acc[db] = mfma32(xt, zbf[kb], acc[db]);
-        }
-      }
-
       cw_.advance();
       if (!cw_.valid) break;
-      if (t & 1) {
-        // The next two steps read tiles up to t+2; t+3 .. t+6 may be in flight.
-        wait_vmcnt<4 * L>();
-        barrier_lds();
-      }
       ++t;
     }
     wait_vmcnt<0>();   // no copy left in flight
@@ -965,20 +934,19 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
     FwdArgs f = {};
     f.offsets = a.offsets; f.B = a.B; f.pstride = a.pstride;
     f.X = a.X; f.P = a.P; f.k = a.k; f.d = a.d; f.T = a.T; f.lse = a.lse_ws;
-    f.lse2 = dtype == 1 ? a.lse2 : nullptr;
+    f.lse2 = nullptr;
     e = dtype == 1 ? launch_stats_bf16(f, st, prof) : launch_stats_f32(f, st, prof);
     if (e != hipSuccess) return e;
   }
   // G and cv rows (padded to kp per user), the zero-padded copy of P (bf16),
-  // and, when the caller supplied lse (not recomputed above), lse2 for the
-  // bf16 dP pass.
+  // and, token-wise, lse2 per (user, prototype) for the bf16 dX pass.
   const int64_t rows = (int64_t)a.B * a.kp;
   const unsigned nbg = (unsigned)((rows * (D / 4) + 255) / 256);
   const bool bf = dtype == 1;
   const int pq_users = pu ? a.B : 1;
   const unsigned nbq =
       bf ? (unsigned)(((int64_t)pq_users * a.kp * (D / 8) + 255) / 256) : 0u;
-  const bool lse2 = bf && a.T > 0 && (tw || !a.recompute_lse);
+  const bool lse2 = bf && a.T > 0 && tw;
   const int64_t nl = tw ? (int64_t)a.B * a.kp : a.T + 1;
   const unsigned nbl = lse2 ? (unsigned)((nl + 255) / 256) : 0u;
   const int mode = tw ? 2 : (a.mass_norm ? 1 : 0);
@@ -1005,33 +973,24 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
         hipLaunchKernelGGL((sa_bwdx_bf16<D, true>), dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st,
                            a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.Pq, (int64_t)0,
                            (const bf16*)a.Gq, a.cvs, a.kp, a.T, alpha, scale, a.lse,
-                           (const float*)a.tlse2, a.dX, a.acc_dx, a.delta);
+                           (const float*)a.tlse2, a.dX, a.acc_dx, a.delta, (bf16*)a.dz, a.kz);
       else
         hipLaunchKernelGGL((sa_bwdx_bf16<D, false>), dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st,
                            a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.Pq,
                            pu ? (int64_t)a.kp * D : (int64_t)0, (const bf16*)a.Gq, a.cvs, a.kp,
                            a.T, alpha, scale, a.lse, (const float*)nullptr, a.dX, a.acc_dx,
-                           a.delta);
+                           a.delta, (bf16*)a.dz, a.kz);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
       prof_begin(prof, "sa_bwdp_bf16", st);
       const dim3 pg(a.Gb, a.bnchunks), pb(64 * kBwdpWaves);
-      if (tw)
-        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, false, true>), pg, pb, 0, st, a.offsets,
-                           a.B, (const bf16*)a.X, (const bf16*)a.P, (int64_t)0, (const bf16*)a.Gq,
-                           a.cv, a.k, a.kp, a.T, a.Gb, alpha, a.lse2, a.delta,
-                           (const float*)a.tlse2, a.dpp);
-      else if (pu)
-        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, true, false>), pg, pb, 0, st, a.offsets,
-                           a.B, (const bf16*)a.X, (const bf16*)a.P, a.pstride, (const bf16*)a.Gq,
-                           a.cv, a.k, a.kp, a.T, a.Gb, alpha, a.lse2, a.delta,
-                           (const float*)nullptr, a.dpp);
+      if (pu && !tw)
+        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, true>), pg, pb, 0, st, a.offsets, a.B,
+                           (const bf16*)a.X, (const bf16*)a.dz, a.kz, a.k, a.T, a.Gb, a.dpp);
       else
-        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, false, false>), pg, pb, 0, st, a.offsets,
-                           a.B, (const bf16*)a.X, (const bf16*)a.P, (int64_t)0, (const bf16*)a.Gq,
-                           a.cv, a.k, a.kp, a.T, a.Gb, alpha, a.lse2, a.delta,
-                           (const float*)nullptr, a.dpp);
+        hipLaunchKernelGGL((sa_bwdp_bf16<D, kBwdpWaves, false>), pg, pb, 0, st, a.offsets, a.B,
+                           (const bf16*)a.X, (const bf16*)a.dz, a.kz, a.k, a.T, a.Gb, a.dpp);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
@@ -1054,13 +1013,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
       if (e != hipSuccess) return e;
     }
   }
-  if (pu)   // dP[u] = c (sum of user u's pieces), like the forward's sketch
-    return launch_piece_sum(a.offsets, a.B, a.k, a.d, a.T, a.Gb, a.dpp, scale, a.dP, a.status, st,
+  // The bf16 partials already hold c dZ; the fp32 ones dZ.
+  const float rscale = bf ? 1.0f : scale;
+  if (pu)   // dP[u] = sum of user u's pieces, like the forward's sketch
+    return launch_piece_sum(a.offsets, a.B, a.k, a.d, a.T, a.Gb, a.dpp, rscale, a.dP, a.status, st,
                             prof);
   const int64_t kd = (int64_t)a.k * a.d;
   prof_begin(prof, "sa_dp_reduce", st);
   hipLaunchKernelGGL(sa_dp_reduce, dim3((unsigned)((kd + 255) / 256)), dim3(256), 0, st,
-                     a.offsets, a.B, a.T, a.k, a.d, a.Gb, scale, a.dpp, a.dP, a.status);
+                     a.offsets, a.B, a.T, a.k, a.d, a.Gb, rscale, a.dpp, a.dP, a.status);
   e = hipGetLastError();
   prof_end(prof, st);
   return e;

@@ -44,7 +44,7 @@ struct Plan {
   size_t off_status, off_lse, off_lse2, off_part, off_pmass, off_pl, off_tlse, off_xchg, fwd_bytes;
   // backward workspace layout (byte offsets)
   size_t off_G, off_cv, off_cvs, off_Pq, off_delta, off_dpp, off_blse, off_blse2, off_tlse2,
-      bwd_bytes;
+      off_dz, bwd_bytes;
 };
 
 // Fills the plan; returns false for an unsupported problem.
@@ -101,6 +101,9 @@ struct BwdArgs {
   int recompute_lse;
   int tokwise;         // token-wise normalisation: lse is [B, k] and S is required
   float* tlse2;        // [B, kp] token-wise: log2-unit lse per prototype (bf16 path)
+  void* dz;            // bf16 c dZ from the dX pass for the dP pass, in MFMA fragment order:
+                       // [ceil(T / 32) + 1 token tiles][kz / 32 prototype tiles][64 lanes][16]
+  int kz;              // prototypes per token tile of dz: bnchunks x kChunkBf16 (>= kp)
 };
 
 // Optional per-kernel timing: when ev is non-null, the launchers record
