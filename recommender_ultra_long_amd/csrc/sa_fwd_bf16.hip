@@ -26,6 +26,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -92,18 +94,19 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
     for (int e = 0; e < PPT; ++e) sP[buf][tid + 256 * e] = reg[e];
   };
 
-  float m[2] = {-INFINITY, -INFINITY};   // running max of raw dot products
-  float l[2] = {0.f, 0.f};               // running sum of exp2((z - m) alpha)
+  // Per-token statistics of one pass, per lane (its token, half h of the
+  // prototypes): ref = reference maximum, l = sum of exp2((z - ref) alpha).
+  float ref[2], l[2];
 
-  // Folds one 32-prototype x 32-token product tile (register i of a lane is
-  // prototype crow(i, h) of the tile, the lane's token is tt 32 + l32) into
-  // the running max and sum of token tile tt.
-  auto fold = [&](const f32x16& v, int tt) {
+  // Exact form (running maximum, the sum rescaled whenever it grows).  Folds
+  // one 32-prototype x 32-token product tile (register i of a lane is
+  // prototype crow(i, h) of the tile, the lane's token is tt 32 + l32).
+  auto fold_exact = [&](const f32x16& v, int tt) {
     float t0 = fmaxf(fmaxf(v[0], v[1]), v[2]), t1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
     float t2 = fmaxf(fmaxf(v[6], v[7]), v[8]), t3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
     float t4 = fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15]));
     const float tmax = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(t3, t4));
-    const float mnew = fmaxf(m[tt], tmax);
+    const float mnew = fmaxf(ref[tt], tmax);
     // A lane whose prototypes are all padding so far keeps m = -inf; a zero
     // shift then keeps every term at exp2(-inf) = 0 instead of NaN.
     const float ma = mnew == -INFINITY ? 0.f : mnew * alpha;
@@ -115,8 +118,33 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       s2 += exp2_fast(fmaf(v[i + 2], alpha, -ma));
       s3 += exp2_fast(fmaf(v[i + 3], alpha, -ma));
     }
-    l[tt] = fmaf(l[tt], exp2_fast(fmaf(m[tt], alpha, -ma)), (s0 + s1) + (s2 + s3));
-    m[tt] = mnew;
+    l[tt] = fmaf(l[tt], exp2_fast(fmaf(ref[tt], alpha, -ma)), (s0 + s1) + (s2 + s3));
+    ref[tt] = mnew;
+  };
+  // Fast form: the reference is the maximum over the first tile and stays
+  // fixed, so a fold is one fma, one exp2 and one add per product.  A term
+  // overflows only when a later product exceeds the reference by more than
+  // 128 / alpha; the pass then ends with a non-finite sum and is redone in
+  // the exact form.
+  auto fold_fast = [&](const f32x16& v, int tt) {
+    const float ma = ref[tt] * alpha;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      s0 += exp2_fast(fmaf(v[i], alpha, -ma));
+      s1 += exp2_fast(fmaf(v[i + 1], alpha, -ma));
+      s2 += exp2_fast(fmaf(v[i + 2], alpha, -ma));
+      s3 += exp2_fast(fmaf(v[i + 3], alpha, -ma));
+    }
+    l[tt] += (s0 + s1) + (s2 + s3);
+  };
+  auto set_ref = [&](const f32x16& v, int tt) {
+    float t0 = fmaxf(fmaxf(v[0], v[1]), v[2]), t1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+    float t2 = fmaxf(fmaxf(v[6], v[7]), v[8]), t3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+    float t4 = fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15]));
+    const float tmax = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(t3, t4));
+    // all padding (k < 32): any finite reference; the lane's sum stays 0
+    ref[tt] = tmax == -INFINITY ? 0.f : tmax;
   };
 
   // Products of prototype tile pt of the chunk in LDS buffer buf.
@@ -135,22 +163,36 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
   };
 
   // One pass over all prototypes of table Pu; writes the statistics of the
-  // tokens in [ulo, uhi).
-  auto run_pass = [&](int64_t ulo, int64_t uhi) {
-    m[0] = m[1] = -INFINITY;
-    l[0] = l[1] = 0.f;
+  // tokens in [ulo, uhi).  Returns false (block-uniform) when the fast form
+  // overflowed and nothing was written.
+  auto run_pass = [&](int64_t ulo, int64_t uhi, auto exact_tag) -> bool {
+    constexpr bool EXACT = decltype(exact_tag)::value;
+    auto fold = [&](const f32x16& v, int tt) {
+      if constexpr (EXACT) fold_exact(v, tt);
+      else fold_fast(v, tt);
+    };
+    // Tiles folded so far (block-uniform); the first real tile sets the
+    // reference in the fast form.
+    int nfold = 0;
+    auto consume = [&](const f32x16& v0, const f32x16& v1) {
+      if (!EXACT && nfold == 0) { set_ref(v0, 0); set_ref(v1, 1); }
+      fold(v0, 0);
+      fold(v1, 1);
+      ++nfold;
+    };
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) { ref[tt] = -INFINITY; l[tt] = 0.f; }
     // Software pipeline over prototype tiles: the products of tile p are
     // issued in the same straight-line block as the vector work on tile p - 1,
     // so the matrix cores and the vector ALU overlap.  All chunks but the last
-    // are full; q starts as an all -inf tile, whose fold changes nothing.
+    // are full.
     bf16x8 pre[PPT];
     load_chunk(0, pre);
     store_chunk(0, pre);
     __syncthreads();
     const int nch = (k + PCH - 1) / PCH;
-    f32x16 q0, q1;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
+    f32x16 q0, q1;                       // the tile whose fold is pending
+    bool qreal = false;
     static_assert(PCH == 64, "two prototype tiles per chunk");
     for (int ci = 0; ci + 1 < nch; ++ci) {
       load_chunk((ci + 1) * PCH, pre);
@@ -158,11 +200,10 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       // The two tiles of the chunk swap roles with q, so nothing is copied.
       f32x16 c0, c1;
       products(buf, 0, c0, c1);
-      fold(q0, 0);
-      fold(q1, 1);
+      if (ci > 0) consume(q0, q1);
       products(buf, 1, q0, q1);
-      fold(c0, 0);
-      fold(c1, 1);
+      consume(c0, c1);
+      qreal = true;
       store_chunk(buf ^ 1, pre);
       __syncthreads();
     }
@@ -176,37 +217,49 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
         if (pbase >= k) break;             // uniform across the block
         f32x16 c0, c1;
         products(buf, pt, c0, c1);
-        fold(q0, 0);
-        fold(q1, 1);
+        if (qreal) consume(q0, q1);
         q0 = c0;
         q1 = c1;
+        qreal = true;
         if (pbase + 32 > k) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (pbase + crow(i, h) >= k) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
         }
       }
-      fold(q0, 0);
-      fold(q1, 1);
+      consume(q0, q1);
     }
 
+    if constexpr (!EXACT) {
+      // Redo in the exact form if any lane's sum overflowed.
+      const bool bad = !(__builtin_isfinite(l[0]) && __builtin_isfinite(l[1]));
+      if (__syncthreads_or(bad)) return false;
+    }
     // Lanes l and l ^ 32 saw disjoint halves of the prototypes of one token.
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const float mo = shfl_xor32(m[tt]), lo = shfl_xor32(l[tt]);
-      const float M = fmaxf(m[tt], mo);
+      const float m = l[tt] > 0.f ? ref[tt] : -INFINITY;   // a lane with no terms
+      const float mo = shfl_xor32(m), lo = shfl_xor32(l[tt]);
+      const float M = fmaxf(m, mo);
       const float Ma = M * alpha;
-      const float L = l[tt] * exp2_fast(fmaf(m[tt], alpha, -Ma)) + lo * exp2_fast(fmaf(mo, alpha, -Ma));
+      const float L = l[tt] * exp2_fast(fmaf(m, alpha, -Ma)) + lo * exp2_fast(fmaf(mo, alpha, -Ma));
       const int64_t tok = tok0 + tt * 32 + l32;
       if (h == 0 && tok >= ulo && tok < uhi) {
         lse_out[tok] = M * scale + __logf(L);
         if (lse2_out != nullptr) lse2_out[tok] = Ma + __log2f(L);
       }
     }
+    return true;
+  };
+  auto pass = [&](int64_t ulo, int64_t uhi) {
+    if (!run_pass(ulo, uhi, std::false_type{})) {
+      __syncthreads();   // the fast pass's LDS reads are done before the next store
+      run_pass(ulo, uhi, std::true_type{});
+    }
   };
 
   if constexpr (!PU) {
-    run_pass(0, T);
+    pass(0, T);
   } else {
     // One pass per user among this block's tokens, with that user's table.
     const int64_t b0 = (int64_t)blockIdx.x * 256;
@@ -216,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       const int64_t uhi = clamp64(uload64(offsets + u + 1), ulo, b1);
       if (uhi > ulo) {
         Pu = P + (int64_t)u * pstride;
-        run_pass(ulo, uhi);
+        pass(ulo, uhi);
       }
       if (uhi >= b1 || u + 1 >= B) break;
       __syncthreads();   // the last pass's LDS reads are done before the next store

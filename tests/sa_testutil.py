@@ -56,7 +56,8 @@ def check_forward_users(prob, S, lse, mass, users, tol, mass_norm=None):
     for u in users:
         lo, hi = int(prob.offsets[u]), int(prob.offsets[u + 1])
         X64 = synth.to_f64(prob.X[lo:hi])
-        Sr, lr, mr = sa_forward_ref(np.array([0, hi - lo]), X64, P64, mn)
+        Pu = P64[u] if P64.ndim == 3 else P64          # one table per user, or shared
+        Sr, lr, mr = sa_forward_ref(np.array([0, hi - lo]), X64, Pu, mn)
         e = rel_err(S[u].cpu().numpy(), Sr[0])
         assert e <= tol, f"user {u} (n={hi - lo}): S rel err {e:.3e} > {tol}"
         em = rel_err(mass[u].cpu().numpy(), mr[0])

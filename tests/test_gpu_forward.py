@@ -58,6 +58,29 @@ def test_sharp_logits_exercise_max_shift(dtype, tol):
     check_forward_users(prob, S, lse, mass, [0, 1], tol)
 
 
+@pytest.mark.parametrize("per_user", [False, True])
+def test_bf16_stats_reference_overflow_takes_exact_path(per_user):
+    # The bf16 statistics pass keeps each token's first-tile maximum as a fixed
+    # reference; a later affinity more than 128 / alpha above it (here ~800
+    # against ~0, with 128 / alpha ~ 710 at d = 64) overflows the fast sum and
+    # the block redoes its pass with the running maximum.
+    prob = _small([300, 45, 0, 200], 300, 64, "bf16", seed=21)
+    X = prob.X.float()
+    P = prob.P.float().clone()
+    P[:32] *= 0.01                                   # the first tile: z ~ 0
+    for j, t in ((200, 7), (299, 320)):              # one huge affinity per chosen token
+        P[j] = 100.0 * X[t] / X[t].norm()
+    if per_user:
+        P = P.unsqueeze(0).repeat(4, 1, 1)
+        P[2:] *= -1.0                                # users 2 and 3: a different table
+    prob.P = P.to(torch.bfloat16)
+    say(f"case stats overflow per_user={per_user}")
+    S, lse, mass = gpu_forward(prob)
+    assert float(lse.max()) > 90.0                   # z / sqrt(d) of the aligned tokens
+    assert bool(torch.isfinite(lse).all()) and bool(torch.isfinite(S).all())
+    check_forward_users(prob, S, lse, mass, [0, 1, 2, 3], TOL_BF16)
+
+
 @pytest.mark.parametrize("k", [512, 1000, 1024, 2048])
 def test_bf16_large_k(k):
     prob = _small([4000, 2500, 1], k, 128, "bf16", seed=k)
