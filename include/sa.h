@@ -328,7 +328,9 @@ sa_status sa_block_backward(const sa_problem* problem, int n_layers, const int64
  * from item embeddings e (the history's dtype) and action types t_i that
  * index an action table A (float [n_types, d]).  W1, W3: float [2d, 2d]
  * (rows 0 .. d-1 act on e, rows d .. 2d-1 on the action row), W2: float
- * [2d, d]; hidden width 2d, no biases.
+ * [2d, d]; hidden width 2d, no biases.  The page leaves the FFN's sizes
+ * open; the hidden width 2d (twice the width of e_i, half of what Eq. (23)'s
+ * rule would give for the 2d-wide v_i) is this library's choice.
  *
  *  d       : 32, 64 or 128;  T: events, 0 <= T <= 2^30;  1 <= n_types <= 16.
  *  dtype   : of e and x.  SA_BF16 runs the fused matrix-core kernel (bf16

@@ -12,8 +12,10 @@ the sketch consumes is
 where the FFN maps the concatenation back to e_i's width.  Readings where the
 page is silent: e_i, a_i in R^d (a_i is row t_i of an action table A with
 one row per action type); FFN_SwiGLU(v) = (silu(v W1) * (v W3)) W2 with
-W1, W3 in R^{2d x 2d} (hidden width 2d, twice the row width, the convention
-of Eq. 23 and Eq. 27) and W2 in R^{2d x d}; no biases.
+W1, W3 in R^{2d x 2d} and W2 in R^{2d x d}; no biases.  The hidden width
+is a choice, not something the page fixes: Eq. 23's rule (hidden width twice
+the FFN's input width) would give 4d for the 2d-wide [e_i; a_i]; 2d, twice the
+row width d of e_i, is used instead and is fixed in the library.
 
 Backward (L = sum(dx * x)):  with v = [e; a], U1 = v W1, U3 = v W3,
 G = silu(U1) U3, s = logistic(U1):
