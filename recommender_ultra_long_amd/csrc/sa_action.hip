@@ -244,8 +244,9 @@ hipError_t launch_action_fwd(int d, int dtype, int64_t T, int n_types, const voi
 }
 
 // ----------------------------------------------------------------------------
-// Backward helpers (the products themselves are sa_gemm_f32).
-// V = [e; A[t]] as fp32 rows of width 2D.
+// Helpers of the backward and of the fp32 path (the products themselves run
+// in sa_gemm_mx, or in sa_gemm_f32 for fp32 histories).
+// V = [e; A[t]] as fp32 rows of width 2D (the fp32 path's hidden layer).
 template <typename ET>
 __global__ __launch_bounds__(256) void sa_action_build_v(const ET* __restrict__ e,
                                                          const int32_t* __restrict__ types,

@@ -1,9 +1,11 @@
 // sa_stca.hip — the length-dependent core of the reordered single-query STCA
 // attention (SequenceO1 reading notes, section 5.1, Eq. (24)-(25)).  For every
 // (target r, head j) query row u = (q_r W_Q[:, j]) W_K[:, j]^T (width D, formed
-// by sa_gemm_f32 beforehand), over the rows X_u of the target's user:
+// by the projection products beforehand: sa_gemm_mx on the matrix cores, or
+// the fp32 sa_gemm_f32 when d_h is not a multiple of 32), over the rows X_u
+// of the target's user:
 //     alpha = softmax(X_u u / sqrt(d_h)),   C[r, j] = alpha X_u   (width D)
-// and then o[r, j] = C[r, j] W_V[:, j] (sa_gemm_f32 again).  The two
+// and then o[r, j] = C[r, j] W_V[:, j] (a projection product again).  The two
 // reductions are 4 L D flops per query row, the whole length-dependent cost.
 //
 // sa_stca_core<DW>: one workgroup per 32 query rows, 8 waves; wave w owns the
