@@ -142,6 +142,13 @@ size_t sa_workspace_size(const sa_problem* problem, int op);
  * Errors: SA_ERR_NULL_ARG, SA_ERR_BAD_SHAPE, SA_ERR_BAD_DTYPE,
  * SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE_TOO_SMALL, SA_ERR_MISALIGNED
  * (nothing enqueued); SA_ERR_HIP if a launch fails.
+ * Two forms compute the same values (up to rounding order): the default
+ * two-pass form (per-token statistics, then the aggregation) and, for bf16
+ * with a shared table when the environment variable SA_FORWARD_PATH is
+ * "single_pass", a single pass whose workgroups exchange per-token
+ * statistics (cooperative launch; if that launch is refused the two-pass
+ * form runs instead).  The single pass reports a given-up wait through
+ * sa_get_device_status (SA_ERR_DEVICE_TIMEOUT).
  */
 sa_status sa_forward(const sa_problem* problem, const int64_t* offsets_dev,
                      const void* X, const void* P, float* S, float* lse,
