@@ -7,6 +7,11 @@ single-user workload n = 100,000 history tokens, k = 1024 prototypes,
 d = 128, bf16 inputs with fp32 accumulation, seeded synthetic data
 (X ~ N(0,1), P ~ N(0,1/d), dS ~ N(0,1)) already resident in GPU memory.
 
+Order: W warm-up + K timed steps on the GPU fresh from input generation
+(reported as first_steps), then 3 s of steps back to back while the graphics
+clock is read, then the timed region of the value: W warm-up steps and exactly
+K steps between two events, synchronized on both sides.
+
 Prints one JSON line: history tokens/s of the whole step, the roofline of
 the dominant kernel (per-kernel durations measured with HIP events recorded
 on the launch stream by the library's profiled entry points), the forward
@@ -445,10 +450,11 @@ def _gfx_clock_mhz():
 
 
 def _busy_sclk(fn, seconds=3.0):
-    """Median graphics clock while fn runs back to back for about `seconds`
-    (the clock the matrix cores run at under this load), sampled every 50 ms
-    over the second half of the run (the clock takes about a second to ramp
-    up), or None when the clock cannot be read."""
+    """Runs fn back to back for about `seconds` and returns the median
+    graphics clock meanwhile (the clock the matrix cores run at under this
+    load), sampled every 50 ms over the second half of the run (the clock
+    takes about a second to settle), or None when the clock cannot be read
+    (the load runs either way)."""
     import threading
     import torch
     samples, stop = [], threading.Event()
@@ -461,16 +467,17 @@ def _busy_sclk(fn, seconds=3.0):
                 samples.append(v)
             time.sleep(0.05)
 
-    if _gfx_clock_mhz() is None:
-        return None
-    th = threading.Thread(target=sample, daemon=True)
-    th.start()
+    th = None
+    if _gfx_clock_mhz() is not None:
+        th = threading.Thread(target=sample, daemon=True)
+        th.start()
     while time.perf_counter() - t_start < seconds:
         for _ in range(100):
             fn()
         torch.cuda.synchronize()
     stop.set()
-    th.join()
+    if th is not None:
+        th.join()
     if not samples:
         return None
     samples.sort()
@@ -634,11 +641,23 @@ def _short_history_timing(sa, synth, timed, dev, long_ms_per_token):
 
     step()
     ms = timed(step, 5)
+    kern = {}
+    for which in ("forward", "backward"):
+        tm = sa.KernelTimer()
+        if which == "forward":
+            sa.sa_forward(off, prob.X, prob.P, False, S=S, lse=lse, mass=None, workspace=wsf,
+                          want_mass=False, timer=tm)
+        else:
+            sa.sa_backward(off, prob.X, prob.P, prob.dS, lse, dX=dX, dP=dP, workspace=wsb, timer=tm)
+        torch.cuda.synchronize()
+        for name, t in tm.times():
+            kern[name] = round(t, 4)
     users_per_block = B / max(1, (T + 255) // 256)
     res = {"workload": "2048 users, lengths uniform[16, 256], k=1024, d=128, bf16",
            "tokens": T, "mean_users_per_256_token_block": round(users_per_block, 2),
            "ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
-           "cost_per_token_over_long_history": round((ms / T) / long_ms_per_token, 2)}
+           "cost_per_token_over_long_history": round((ms / T) / long_ms_per_token, 2),
+           "kernel_ms": kern}
     del prob, wsf, wsb, S, lse, dX, dP
     torch.cuda.empty_cache()
     return res
@@ -721,21 +740,35 @@ def main():
         fwd()
         bwd()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    e0.record(st)
-    for _ in range(args.steps):
-        step()
-    e1.record(st)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall0
-    ms_step = e0.elapsed_time(e1) / args.steps
+
+    def timed_steps():
+        """W untimed warm-up steps, then exactly K steps between two events,
+        with a synchronize on both sides: (ms per step, wall seconds)."""
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall0 = time.perf_counter()
+        e0.record(st)
+        for _ in range(args.steps):
+            step()
+        e1.record(st)
+        timed_steps.enqueue_s = time.perf_counter() - t_wall0   # host time to launch them
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - t_wall0
+
+    # First, the same measurement on the GPU as it comes out of input
+    # generation (idle before): reported beside the value, not as it.  The
+    # kernels get 5-10 % faster over the first ~150 ms of load, and this
+    # region has shown occasional multi-millisecond stalls.
+    ms_first, _ = timed_steps()
+    enqueue_first = timed_steps.enqueue_s
+    # The graphics clock under sustained load: 3 s of steps back to back.
+    sclk = _busy_sclk(step)
+    # The timed region of the value: W warm-up steps, then exactly K steps.
+    ms_step, wall = timed_steps()
 
     def timed(fn, reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -809,6 +842,7 @@ def main():
         "step_tflops": round((fwd_flop + bwd_flop) / (ms_step * 1e-3) / 1e12, 2),
         "kernel_avg_ms": {n: round(v, 5) for n, v in kern_ms.items()},
         "wall_s_timed_region": round(wall, 4),
+        "host_launch_ms_per_step": round(timed_steps.enqueue_s * 1e3 / args.steps, 4),
     }
     # Query/key projections of Eq. (6) folded into the prototype table: the
     # fold and its backward for this workload's k and d (not part of the step:
@@ -844,16 +878,13 @@ def main():
         "fold_us": round(ms_fold * 1e3, 2), "fold_backward_us": round(ms_fold_bwd * 1e3, 2),
         "fold_gflops": round(fold_flop / (ms_fold * 1e-3) / 1e9, 1),
         "fold_backward_gflops": round(fold_bwd_flop / (ms_fold_bwd * 1e-3) / 1e9, 1)}
-    sclk = _busy_sclk(step)
     out["sclk_mhz_under_load"] = sclk
+    out["first_steps"] = {"ms_per_step": round(ms_first, 5),
+                          "tokens_per_s": round(T / (ms_first * 1e-3), 1),
+                          "host_launch_ms_per_step": round(enqueue_first * 1e3 / args.steps, 4),
+                          "when": "W warm-up + K timed steps right after input generation, "
+                                  "before the 3 s sustained run that precedes the timed region"}
     if sclk:
-        # The same K steps again right after the 3 s sustained run: the kernels
-        # run 5-10 % faster once the GPU has been busy for ~150 ms.  Reported
-        # beside the timed region's number above, never instead of it.
-        ms_steady = timed(step, args.steps)
-        out["steady_state"] = {"ms_per_step": round(ms_steady, 5),
-                               "tokens_per_s": round(T / (ms_steady * 1e-3), 1),
-                               "after_seconds_of_load": 3.0}
         out["forward"]["frac_bf16_peak_at_measured_sclk"] = round(
             out["forward"]["frac_bf16_peak"] * NOMINAL_SCLK_MHZ / sclk, 4)
         out["roofline"]["frac_at_measured_sclk"] = round(
