@@ -36,8 +36,12 @@ namespace sa {
 // ----------------------------------------------------------------------------
 // Pass 1: per-token log-sum-exp over all k prototypes.
 // Block: 256 threads = 4 waves; wave w handles tokens blk*256 + 64w .. +63 as
-// two 32-token MFMA tiles.  Prototypes are streamed in chunks of 64 rows
-// through LDS in MFMA fragment order, double buffered via registers.
+// two 32-token MFMA tiles.  Prototypes stream through LDS in chunks of 64
+// rows, stored in MFMA fragment order and copied global -> LDS by the
+// direct-to-LDS loads three chunks ahead into four buffers, one barrier per
+// chunk.  Every block reads the same chunk at about the same time, so the
+// first request for a chunk's lines usually goes past the L2; the copies are
+// issued early enough to cover that latency.
 // With one table per user (PU), the block makes one pass over the prototypes
 // per user among its tokens, with that user's table, and each pass writes the
 // statistics of its user's tokens only.
@@ -51,14 +55,54 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
                                                      int64_t pstride) {
   constexpr int KS = D / 16;            // 16-wide reduction steps over d
   constexpr int PCH = 64;               // prototypes per LDS chunk
-  constexpr int NPIECE = PCH * D / 8;   // 16-byte pieces per chunk
-  constexpr int PPT = NPIECE / 256;     // pieces per thread
-  static_assert(PPT >= 1, "");
-  __shared__ bf16x8 sP[2][NPIECE];
+  constexpr int NPIECE = PCH * D / 8;   // 16-byte slots per chunk
+  constexpr int SPW = NPIECE / 4;       // slots copied by each wave
+  constexpr int XI = SPW / 64;          // copy instructions per wave per chunk
+  static_assert(SPW % 64 == 0 && XI >= 1, "");
+  constexpr int NB = 4;                 // chunk buffers
+  constexpr uint32_t CBYTES = NPIECE * 16;
+  __shared__ __attribute__((aligned(16))) bf16x8 sP[NB][NPIECE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int64_t tok0 = (int64_t)blockIdx.x * 256 + wave * 64;
+  const uint32_t sp0 = lds_addr((const SA_LDS void*)&sP[0][0]);
+  const int nch = (k + PCH - 1) / PCH;
+
+  // Copy geometry.  Slot (pt KS + ks) 64 + L of a chunk buffer is lane L's A
+  // operand for prototype tile pt and step ks: chunk row 32 pt + L % 32,
+  // 16-byte unit 2 ks + L / 32.  Copy instruction j of this wave fills the
+  // slots wave SPW + 64 j + lane (consecutive lanes, consecutive slots: the
+  // reads below are free of bank conflicts).
+  int crow_[XI];
+  uint32_t cunit[XI];
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int slot = wave * SPW + 64 * j + lane;
+    crow_[j] = (slot / (KS * 64)) * 32 + l32;
+    cunit[j] = (uint32_t)(2 * ((slot / 64) % KS) + h) * 16;
+  }
+  const bf16* Pu = P;                    // the current user's table
+  // Copy chunk q of the stream into buffer q % NB: prototype chunk q while
+  // q < nch, afterwards chunk 0 again (never read), so that every chunk is
+  // the same number of loads.  Rows past k copy row k - 1; the last chunk
+  // masks them.
+  auto copy_chunk = [&](int q) {
+    const int c = q < nch ? q : 0;
+    const uint32_t dst = sp0 + (uint32_t)(q & (NB - 1)) * CBYTES + (uint32_t)(wave * SPW) * 16;
+#pragma unroll
+    for (int j = 0; j < XI; ++j) {
+      const int row = c * PCH + crow_[j] < k ? c * PCH + crow_[j] : k - 1;
+      lds_copy16(Pu, (uint32_t)row * (uint32_t)(D * 2) + cunit[j], dst + 1024 * j);
+    }
+  };
+
+  // The first pass's chunks are requested before the token rows, so that
+  // both streams are in flight together.
+  if constexpr (PU) Pu = P + (int64_t)first_user_after(offsets, B, (int64_t)blockIdx.x * 256) * pstride;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) copy_chunk(q);
+  bool primed = true;
 
   // This lane's token rows as B operands: xb[tt][ks] = X[tok][16 ks + 8h .. +7].
   bf16x8 xb[2][KS];
@@ -71,28 +115,12 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       else xb[tt][ks] = bf16x8{};
     }
   }
-
-  // Thread t fills fragment-order slots t, t + 256, ...: slot
-  // ((pt KS + ks) 64 + L) is lane L's A operand for prototype tile pt and
-  // step ks, i.e. P[p0 + 32 pt + L % 32][16 ks + 8 (L / 32) .. +7].  Consecutive
-  // lanes write consecutive 16-byte slots (no LDS bank conflicts).
-  const bf16* Pu = P;                    // the current user's table
-  auto load_chunk = [&](int p0, bf16x8 (&reg)[PPT]) {
+  // The compiler waits for the rows here, where it also sees the wait, and
+  // adds none inside the loops (where it would hold up every copy in flight).
 #pragma unroll
-    for (int e = 0; e < PPT; ++e) {
-      const int slot = tid + 256 * e;
-      const int pt = slot / (KS * 64), rem = slot % (KS * 64);
-      const int ks = rem / 64, L = rem % 64;
-      const int row = p0 + pt * 32 + (L & 31);
-      const int cp = 2 * ks + (L >> 5);
-      if (row < k) reg[e] = *(const bf16x8*)(Pu + (int64_t)row * D + 8 * cp);
-      else reg[e] = bf16x8{};
-    }
-  };
-  auto store_chunk = [&](int buf, const bf16x8 (&reg)[PPT]) {
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int e = 0; e < PPT; ++e) sP[buf][tid + 256 * e] = reg[e];
-  };
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(xb[tt][ks]));
 
   // Per-token statistics of one pass, per lane (its token, half h of the
   // prototypes): ref = reference maximum, l = sum of exp2((z - ref) alpha).
@@ -182,21 +210,24 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
     };
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) { ref[tt] = -INFINITY; l[tt] = 0.f; }
+    // The chunk stream: chunks 0 .. 2 in flight (the first pass requested
+    // them before the token rows), then wait for chunk 0.
+    if (!primed) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) copy_chunk(q);
+    }
+    primed = false;
+    wait_vmcnt<2 * XI>();
+    barrier_lds();
     // Software pipeline over prototype tiles: the products of tile p are
     // issued in the same straight-line block as the vector work on tile p - 1,
     // so the matrix cores and the vector ALU overlap.  All chunks but the last
     // are full.
-    bf16x8 pre[PPT];
-    load_chunk(0, pre);
-    store_chunk(0, pre);
-    __syncthreads();
-    const int nch = (k + PCH - 1) / PCH;
     f32x16 q0, q1;                       // the tile whose fold is pending
     bool qreal = false;
     static_assert(PCH == 64, "two prototype tiles per chunk");
     for (int ci = 0; ci + 1 < nch; ++ci) {
-      load_chunk((ci + 1) * PCH, pre);
-      const int buf = ci & 1;
+      const int buf = ci & (NB - 1);
       // The two tiles of the chunk swap roles with q, so nothing is copied.
       f32x16 c0, c1;
       products(buf, 0, c0, c1);
@@ -204,13 +235,17 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       products(buf, 1, q0, q1);
       consume(c0, c1);
       qreal = true;
-      store_chunk(buf ^ 1, pre);
-      __syncthreads();
+      // Chunk ci + 1 has landed (ci + 2 may still be in flight); after the
+      // barrier no wave reads chunk ci any more, and chunk ci + 3 goes into
+      // the buffer of chunk ci - 1.
+      wait_vmcnt<XI>();
+      barrier_lds();
+      copy_chunk(ci + 3);
     }
     {
       // Last chunk: tiles may be partial or past k; padding rows drop out as
       // -inf.
-      const int ci = nch - 1, buf = ci & 1;
+      const int ci = nch - 1, buf = ci & (NB - 1);
 #pragma unroll
       for (int pt = 0; pt < PCH / 32; ++pt) {
         const int pbase = ci * PCH + pt * 32;
@@ -229,6 +264,7 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       }
       consume(q0, q1);
     }
+    wait_vmcnt<0>();   // the copies past the end have landed: none is in flight after the pass
 
     if constexpr (!EXACT) {
       // Redo in the exact form if any lane's sum overflowed.
@@ -268,7 +304,12 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       const int64_t ulo = clamp64(uload64(offsets + u), b0, b1);
       const int64_t uhi = clamp64(uload64(offsets + u + 1), ulo, b1);
       if (uhi > ulo) {
-        Pu = P + (int64_t)u * pstride;
+        const bf16* tab = P + (int64_t)u * pstride;
+        if (primed && tab != Pu) {   // only with corrupt offsets: drop the early copies
+          wait_vmcnt<0>();
+          primed = false;
+        }
+        Pu = tab;
         pass(ulo, uhi);
       }
       if (uhi >= b1 || u + 1 >= B) break;
@@ -277,6 +318,7 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
   }
   // Sentinel read by the aggregation pass for rows past the end of a tile.
   if (lse2_out != nullptr && blockIdx.x == 0 && tid == 0) lse2_out[T] = INFINITY;
+  wait_vmcnt<0>();   // no copy into this block's LDS is left in flight at exit
 }
 
 // ----------------------------------------------------------------------------
