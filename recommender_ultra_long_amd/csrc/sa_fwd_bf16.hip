@@ -328,10 +328,12 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
 // fp32 partial sketch as MFMA accumulators (AGPRs).
 //
 // The token stream of the segment is cut into 32-token tiles that never
-// straddle two users.  Tile t + 6 is copied global -> LDS by the
-// direct-to-LDS loads while tile t is computed, into eight rotating buffers;
-// a barrier after every second tile publishes the copies (waits are explicit
-// vmcnt counts and the barrier carries no fence).  Step t computes the
+// straddle two users.  Tile t + 8 is copied global -> LDS by the
+// direct-to-LDS loads while tile t is computed, into sixteen rotating
+// buffers; a barrier after every fourth tile publishes the copies (waits are
+// explicit vmcnt counts and the barrier carries no fence).  Fewer barriers
+// leave the waves less time waiting for the slowest one (a barrier every
+// second tile was 2-3 % slower).  Step t computes the
 // affinities of tile t+1 on the matrix cores while the vector ALU turns those
 // of tile t into softmax weights, then the sketch update of tile t.
 //
@@ -358,8 +360,9 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
   static_assert(UNITS % NW == 0 && (UPW <= 64 || UPW % 64 == 0), "");
   constexpr int XI = (UPW + 63) / 64;    // copy instructions per wave per tile
   constexpr int LPW = TILE / NW;         // lse entries copied by each wave
-  constexpr int NBUF = 8;                // tiles t-1 .. t+6
-  constexpr int AHEAD = 6;               // copy distance in tiles
+  constexpr int NBUF = 16;               // tile buffers (a power of two)
+  constexpr int AHEAD = 8;               // copy distance in tiles
+  static_assert((NBUF & (NBUF - 1)) == 0 && AHEAD >= 6 && AHEAD + 4 <= NBUF, "");
   constexpr int L = XI + 1;              // loads per wave per tile
   constexpr uint32_t XBYTES = TILE * D * 2;
 
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     bool last;
     do {
       const uint32_t buf = t & (NBUF - 1), b1 = (t + 1) & (NBUF - 1);
-      copy_next((t + AHEAD) & (NBUF - 1));        // into the buffer of tile t-2
+      copy_next((t + AHEAD) & (NBUF - 1));        // into the buffer of tile t-8
 
       const SA_LDS char* xs = lds + sx0 + buf * XBYTES;
       const SA_LDS char* xs1 = lds + sx0 + b1 * XBYTES;
@@ -570,10 +573,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[pt][db] = mfma32(xt[kb][db], abf[pt][kb], acc[pt][db]);
 
-      if (t & 1) {
-        // Tiles up to t+3 must be complete before the barrier (the next two
-        // steps read up to tile t+3); those of t+4 .. t+6 may be in flight.
-        wait_vmcnt<3 * L>();
+      if ((t & 3) == 3) {
+        // Tiles up to t+5 must be complete before the barrier (the next four
+        // steps read up to tile t+5); those of t+6 .. t+AHEAD may be in flight.
+        // The buffer a step copies into held tile t-8 or later, which every
+        // wave finished before the previous barrier (at most four steps ago).
+        wait_vmcnt<(AHEAD - 5) * L>();
         barrier_lds();
       }
       last = cw.last_in_piece();
