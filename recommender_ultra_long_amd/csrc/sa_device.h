@@ -59,19 +59,22 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Written as assembly so that the compiler does not turn every later LDS read
 // into a wait for all copies in flight: the caller orders them with explicit
 // vmcnt waits.  The instructions write no register.  Every call sets M0, and
-// no compiler-generated code in these kernels keeps a value in M0.
+// no compiler-generated code in these kernels keeps a value in M0.  An LDS DMA
+// reads M0 one wait state after an SALU write to it at the earliest (the
+// compiler's own global_load_lds code keeps that gap), hence the s_nop 0:
+// without it the copy can take the previous M0 and write another LDS address.
 __device__ __forceinline__ uint32_t lds_addr(const SA_LDS void* p) {
   return (uint32_t)(uintptr_t)p;
 }
 __device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 // Lane i copies the 4 bytes at its own address src_i to LDS byte address
 // lds + 4 i.
 __device__ __forceinline__ void lds_copy4v(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src),
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
