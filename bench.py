@@ -9,8 +9,10 @@ d = 128, bf16 inputs with fp32 accumulation, seeded synthetic data
 
 Order: W warm-up + K timed steps on the GPU fresh from input generation
 (reported as first_steps), then 3 s of steps back to back while the graphics
-clock is read, then the timed region of the value: W warm-up steps and exactly
-K steps between two events, synchronized on both sides.
+clock is read, then the timed region of the value: 0.3 s of steps and W warm-up
+steps back to back (the clock drops within tens of milliseconds of idle and
+needs 100-150 ms of load to recover), then exactly K steps between two events,
+synchronized on both sides.
 
 Prints one JSON line: history tokens/s of the whole step, the roofline of
 the dominant kernel (per-kernel durations measured with HIP events recorded
@@ -742,9 +744,24 @@ def main():
 
     st = torch.cuda.current_stream()
 
-    def timed_steps():
-        """W untimed warm-up steps, then exactly K steps between two events,
-        with a synchronize on both sides: (ms per step, wall seconds)."""
+    def warm(seconds=0.3):
+        """Steps back to back for about `seconds` (untimed).  The graphics clock
+        drops within tens of milliseconds of idle (here: the clock reader's
+        thread ends) and takes 100-150 ms of load to come back, so W warm-up
+        steps alone (a few milliseconds) would start the timed region on a
+        clock that is still rising."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+
+    def timed_steps(warm_s=0.0):
+        """warm_s seconds and W untimed warm-up steps, then exactly K steps
+        between two events, with a synchronize on both sides: (ms per step,
+        wall seconds)."""
+        if warm_s > 0:
+            warm(warm_s)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -767,8 +784,9 @@ def main():
     enqueue_first = timed_steps.enqueue_s
     # The graphics clock under sustained load: 3 s of steps back to back.
     sclk = _busy_sclk(step)
-    # The timed region of the value: W warm-up steps, then exactly K steps.
-    ms_step, wall = timed_steps()
+    # The timed region of the value: 0.3 s of steps and W warm-up steps back to
+    # back (the clock back at its sustained level), then exactly K steps.
+    ms_step, wall = timed_steps(warm_s=0.3)
 
     def timed(fn, reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
