@@ -344,11 +344,19 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
 // after the segment's first reloads the prototype rows and recomputes the
 // affinities of its first tile (the step before computed them with the
 // previous user's table).
-template <int D, bool MASS, int NW, int PT, bool PU>
+//
+// DIRECT (batches of many short users): a user whose tokens all lie
+// in this segment has this one piece, and its sketch (normalised by its mass
+// with mass_norm) and its mass go straight to S and mass_out, which sa_reduce
+// then leaves alone; this saves the k x d partial and its read-back per short
+// user.  Without DIRECT every piece goes to its partial (the extra per-piece
+// state costs the main loop about 2 % when pieces are long).
+template <int D, bool MASS, int NW, int PT, bool PU, bool DIRECT>
 __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ P, int64_t pstride, int k, int64_t T, int G, float alpha,
-    const float* __restrict__ lse2, float* __restrict__ part, float* __restrict__ pmass) {
+    const float* __restrict__ lse2, float* __restrict__ part, float* __restrict__ pmass,
+    float* __restrict__ S, float* __restrict__ mass_out, int mass_norm) {
   constexpr int KS = D / 16;             // reduction steps of the affinity product
   constexpr int DB = D / 32;             // 32-row blocks of the transposed sketch
   constexpr int U = D / 8;               // 16-byte units per token row
@@ -503,6 +511,13 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
       }
     }
     const int64_t slot = (int64_t)s + cw.user;
+    bool whole = false;                          // the user's only piece
+    if constexpr (DIRECT) {
+      const int64_t ulo = clamp64(uload64(offsets + cw.user), 0, T);
+      const int64_t uhi = clamp64(uload64(offsets + cw.user + 1), ulo, T);
+      whole = ulo >= lo && uhi <= hi;
+    }
+    const int64_t urow = (int64_t)cw.user;
     f32x16 acc[PT][DB];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt)
@@ -593,16 +608,25 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
       const int proto = pw0 + pt * 32 + l32;
       const float mo = MASS ? shfl_xor32(mass[pt]) : 0.f;
       if (proto < k) {
-        float* dst = part + (slot * k + proto) * D;
+        const float mu = mass[pt] + mo;
+        // The direct row is what sa_reduce forms from a single piece: the
+        // partial, divided by the mass when normalised (zero mass: zero row).
+        const bool nz = !(MASS && mass_norm) || mu > 0.f;
+        const float inv = (MASS && mass_norm && mu > 0.f) ? 1.0f / mu : 1.0f;
+        float* dst = whole ? S + (urow * k + proto) * D : part + (slot * k + proto) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             f32x4 v = {acc[pt][db][4 * g], acc[pt][db][4 * g + 1], acc[pt][db][4 * g + 2],
                        acc[pt][db][4 * g + 3]};
+            if (whole && MASS && mass_norm) v = nz ? v * inv : f32x4{0.f, 0.f, 0.f, 0.f};
             *(f32x4*)(dst + 32 * db + 8 * g + 4 * h) = v;
           }
-        if (MASS && h == 0) pmass[slot * k + proto] = mass[pt] + mo;
+        if (MASS && h == 0) {
+          if (!whole) pmass[slot * k + proto] = mu;
+          else if (mass_out != nullptr) mass_out[urow * k + proto] = mu;
+        }
       }
     }
     wait_vmem_all();   // once per piece: the stores above are complete
@@ -636,40 +660,44 @@ static hipError_t launch_stats_bf16_t(const FwdArgs& a, hipStream_t st, Prof* pr
   return e;
 }
 
+template <int D, bool MASS, int PT, bool PU>
+static void launch_agg_bf16(const FwdArgs& a, bool direct, float alpha, hipStream_t st) {
+  const dim3 grid(a.G, a.nchunks), block(64 * kAggWaves);
+  const bf16* X = (const bf16*)a.X;
+  const bf16* P = (const bf16*)a.P;
+  if (direct)
+    hipLaunchKernelGGL((sa_agg_bf16<D, MASS, kAggWaves, PT, PU, true>), grid, block, 0, st,
+                       a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
+                       a.pmass, a.S, a.mass, a.mass_norm);
+  else
+    hipLaunchKernelGGL((sa_agg_bf16<D, MASS, kAggWaves, PT, PU, false>), grid, block, 0, st,
+                       a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
+                       a.pmass, a.S, a.mass, a.mass_norm);
+}
+
 template <int D>
 static hipError_t launch_fwd_bf16_t(const FwdArgs& a, hipStream_t st, Prof* prof) {
   const float scale = 1.0f / sqrtf((float)D);
   const float alpha = scale * kLog2e;
   constexpr int PT = kChunkBf16 / (32 * kAggWaves);
+  // Single-piece users write S directly when users outnumber segments four
+  // to one (most users then lie inside one segment).  With fewer, longer
+  // users the partials saved do not pay for the slower main loop.
+  const bool direct = (int64_t)a.B >= 4 * (int64_t)a.G;
   if (a.T > 0) {
     hipError_t e = launch_stats_bf16_t<D>(a, st, prof);
     if (e != hipSuccess) return e;
     prof_begin(prof, "sa_agg_bf16", st);
     const bool ms = a.mass_norm || a.mass != nullptr, pu = a.pstride != 0;
-    const dim3 grid(a.G, a.nchunks), block(64 * kAggWaves);
-    const bf16* X = (const bf16*)a.X;
-    const bf16* P = (const bf16*)a.P;
-    if (ms && pu)
-      hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, PT, true>), grid, block, 0, st,
-                         a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
-                         a.pmass);
-    else if (ms)
-      hipLaunchKernelGGL((sa_agg_bf16<D, true, kAggWaves, PT, false>), grid, block, 0, st,
-                         a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
-                         a.pmass);
-    else if (pu)
-      hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, PT, true>), grid, block, 0, st,
-                         a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
-                         a.pmass);
-    else
-      hipLaunchKernelGGL((sa_agg_bf16<D, false, kAggWaves, PT, false>), grid, block, 0, st,
-                         a.offsets, a.B, X, P, a.pstride, a.k, a.T, a.G, alpha, a.lse2, a.part,
-                         a.pmass);
+    if (ms && pu) launch_agg_bf16<D, true, PT, true>(a, direct, alpha, st);
+    else if (ms) launch_agg_bf16<D, true, PT, false>(a, direct, alpha, st);
+    else if (pu) launch_agg_bf16<D, false, PT, true>(a, direct, alpha, st);
+    else launch_agg_bf16<D, false, PT, false>(a, direct, alpha, st);
     e = hipGetLastError();
     prof_end(prof, st);
     if (e != hipSuccess) return e;
   }
-  return launch_reduce(a, st, prof);
+  return launch_reduce(a, st, prof, false, direct);
 }
 
 hipError_t launch_stats_bf16(const FwdArgs& a, hipStream_t st, Prof* prof) {

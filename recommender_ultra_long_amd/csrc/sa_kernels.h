@@ -233,9 +233,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_fused_bf16(const FwdArgs& a, hipStream_t st, Prof* prof);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st, Prof* prof);
 // keep_exchange_status: leave the second status word as the single-pass
-// forward's kernel left it.
+// forward's kernel left it.  skip_single: users that lie in one segment were
+// written to S (and mass) by the aggregation pass; leave them.
 hipError_t launch_reduce(const FwdArgs& a, hipStream_t st, Prof* prof,
-                         bool keep_exchange_status = false);
+                         bool keep_exchange_status = false, bool skip_single = false);
 // Token-wise normalisation (sa_tok.hip): S [B, k, d] and lse [B, k].
 hipError_t launch_tok_fwd(const FwdArgs& a, int dtype, hipStream_t st, Prof* prof);
 // out[u] = scale * sum of user u's piece partials (slot s + u of segment s of

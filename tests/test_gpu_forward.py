@@ -47,6 +47,36 @@ def test_ragged_edge_lengths(dtype, tol, d, mass_norm):
             assert torch.all(S[u] == 0) and torch.all(mass[u] == 0)
 
 
+@pytest.mark.parametrize("k,mass_norm,per_user", [(1024, False, False), (1024, True, False),
+                                                  (1024, True, True), (256, True, False)])
+def test_many_short_users_stale_workspace(k, mass_norm, per_user):
+    """300 short users (up to 200 tokens).  k=1024: 64 segments of about 470
+    tokens, users outnumber them four to one, so a user inside one segment
+    has its row of S written by the aggregation pass and skipped by the
+    reduction; k=256: 256 segments, every row goes through a partial.  About
+    one user per segment boundary crosses it; three users are empty.  The
+    workspace starts as all-ones bytes (NaN as float32), so a row of S or
+    mass taken from a partial that this call did not write shows."""
+    rng = np.random.default_rng(11)
+    lengths = rng.integers(0, 200, size=300)
+    lengths[[0, 7, 299]] = 0
+    prob = synth.make_inputs([int(x) for x in lengths], k, 64, "bf16", device="cuda", seed=11,
+                             wid=101, mass_norm=mass_norm, per_user_p=per_user)
+    pr = sa.make_problem(len(lengths), k, 64, prob.total_tokens, sa.SA_BF16, mass_norm,
+                         per_user)
+    ws = torch.full((sa.workspace_size(pr, sa.SA_OP_FORWARD),), 255, dtype=torch.uint8,
+                    device="cuda")
+    off = torch.as_tensor(prob.offsets, device="cuda")
+    say(f"case many_short_users k={k} mass_norm={mass_norm} per_user={per_user}")
+    S, lse, mass = sa.sa_forward(off, prob.X, prob.P, mass_norm, workspace=ws)
+    torch.cuda.synchronize()
+    assert sa.sa_get_device_status(ws) == sa.SA_OK
+    assert bool(torch.isfinite(S).all()) and bool(torch.isfinite(mass).all())
+    check_forward_users(prob, S, lse, mass, range(len(lengths)), TOL_BF16)
+    for u in (0, 7, 299):
+        assert torch.all(S[u] == 0) and torch.all(mass[u] == 0)
+
+
 @pytest.mark.parametrize("dtype,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
 def test_sharp_logits_exercise_max_shift(dtype, tol):
     # P scaled so that affinities reach |z| ~ 30: exp without the max shift
