@@ -233,6 +233,10 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     if (uhi <= ulo) continue;
     const bool mine = tok >= ulo && tok < uhi;
     const float lsh = mine ? l2 : INFINITY;
+    // A wave none of whose tokens belong to user u only copies its share of
+    // the chunks and meets the barriers: its products would all get weight 0.
+    const int64_t wt0 = r0 + (int64_t)__builtin_amdgcn_readfirstlane(wave) * 32;
+    const bool active = wt0 < uhi && wt0 + 32 > ulo;
     const bf16* Gu = Gq + (int64_t)u * kp * D;
     const bf16* Pu = Pq + (int64_t)u * pq_ustride;   // the user's table (or the shared one)
     const float* cvu = cvn + (int64_t)u * kp;
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
         const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
         const uint32_t cb = sc0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
+        for (int pt = 0; pt < 2 && active; ++pt) {
           const uint32_t tbuf = buf + pt * TB;
           f32x16 z = f32x16{};
           bf16x8 pa[KS];
@@ -398,6 +402,10 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
       const uint32_t buf = sb0 + (uint32_t)(q & (NB - 1)) * CB;
       const uint32_t cb = sc0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
       const uint32_t qb = sq0 + (uint32_t)((q & (NB - 1)) * PCH * 4 + 16 * h);
+      if (!active) {
+        advance(q, NoStores{});   // no stores of W issued
+        continue;
+      }
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         const uint32_t tbuf = buf + pt * TB;

@@ -57,6 +57,21 @@ def test_ragged_edges(dtype, tol, d, mass_norm):
         _check(prob, dX, dP, tol)
 
 
+@pytest.mark.parametrize("mass_norm", [False, True])
+def test_many_short_users(mass_norm):
+    """160 users of 0-120 tokens (bf16, k=1024, d=64): most 256-token blocks of
+    the dX pass hold three or more users, so in each user's round over the
+    prototypes most waves hold none of its tokens and only copy and wait."""
+    rng = np.random.default_rng(21)
+    lengths = [int(x) for x in rng.integers(0, 121, size=160)]
+    lengths[5] = 0
+    prob = _prob(lengths, 1024, 64, "bf16", seed=21, mass_norm=mass_norm)
+    say(f"case bwd many short users mass_norm={mass_norm}")
+    dX, dP = _gpu_bwd(prob)
+    worst = _check(prob, dX, dP, TOL_BF16)
+    say(f"many short users mass_norm={mass_norm}: worst rel err {worst:.2e}")
+
+
 @pytest.mark.parametrize("dtype,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
 def test_recomputed_lse_and_sharp_logits(dtype, tol):
     prob = _prob([700, 90], 96, 64, dtype, seed=4, p_std=8.0)
