@@ -134,12 +134,16 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
-// Load of a value that is the same for every lane, kept in scalar registers.
+// Load of a value that is the same for every lane (offsets, which no kernel
+// writes), as a scalar load: it is waited for with lgkmcnt, so its wait does
+// not also wait for the vector loads and direct-to-LDS copies in flight, as a
+// vector load's vmcnt wait would.
 __device__ __forceinline__ int64_t uload64(const int64_t* p) {
-  const uint64_t v = (uint64_t)*p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  typedef const __attribute__((address_space(4))) int64_t* const_i64_ptr;
+  return *(const_i64_ptr)(((uint64_t)hi << 32) | lo);
 }
 
 // First user whose row range ends after token t (offsets[u+1] > t).

@@ -629,7 +629,11 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
         }
       }
     }
-    wait_vmem_all();   // once per piece: the stores above are complete
+    // With one table per user the next piece reloads the prototype rows and
+    // waits for them (and so for everything in flight) anyway.  With a shared
+    // table the stores stay in flight: the copy waits of the tile loop count
+    // them among the newer operations, which only makes those waits longer.
+    if constexpr (PU) wait_vmem_all();
   }
   wait_vmcnt<0>();   // no copy left in flight at exit
 }
