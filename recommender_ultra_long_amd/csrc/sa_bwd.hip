@@ -123,7 +123,8 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(
 // waves per SIMD so that one wave's vector work overlaps the other's matrix
 // products.  Tokens of the workgroup that belong to different users are
 // handled one user at a time (the others get weight 0), because G depends on
-// the user.
+// the user; in a user's round, waves that hold none of its tokens only copy
+// their share of the chunks and meet the barriers.
 //
 // With w'_ji = c A_ji (dA'_ji - cv_j) and s_i = sum_j w'_ji (= c delta_i),
 //   dX_i = g_i + sum_j (w'_ji - s_i A_ji) p_j,   g_i = sum_j A_ji G_j,

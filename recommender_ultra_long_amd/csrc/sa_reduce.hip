@@ -5,8 +5,10 @@
 // user u) that cover its tokens.  The pieces of one user are split over the
 // waves that share an output slice by a fixed rule (wave sub takes pieces
 // sub, sub + WPS, ...) and the wave sums are added in wave order, so the
-// result does not depend on scheduling.  Mass normalisation divides row j by the prototype mass
-// mu_j = sum_i A[j,i] (a zero mass gives a zero row).
+// result does not depend on scheduling.  Mass normalisation divides row j by
+// the prototype mass mu_j = sum_i A[j,i] (a zero mass gives a zero row).  A
+// user with one piece whose row the aggregation pass already wrote (skip_single)
+// is left alone; an empty user gets zero rows here.
 #include "sa_device.h"
 #include "sa_kernels.h"
 
