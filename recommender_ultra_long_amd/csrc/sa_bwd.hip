@@ -157,7 +157,10 @@ __global__ __launch_bounds__(256) void sa_bwd_prep(
 // w'_ji = c A_ji (dA'_ji - D_j) = c dZ_ji there is no per-token coupling:
 // one round (stage 2 with s = 0, also adding G^T A) gives
 // dX_i = sum_j (A_ji G_j + w'_ji p_j), 8 k d, and no delta.
-template <int D, bool TW>
+//
+// CV: cv is not zero (mass normalisation, token-wise); without it (the plain
+// sum) the -cv terms are left out.
+template <int D, bool TW, bool CV>
 __global__ __launch_bounds__(512) void sa_bwdx_bf16(
     const int64_t* __restrict__ offsets, int B, const bf16* __restrict__ X,
     const bf16* __restrict__ Pq, int64_t pq_ustride, const bf16* __restrict__ Gq,
@@ -345,14 +348,14 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
 #pragma unroll
           for (int st = 0; st < TB2; ++st)
             gt[st] = rdtr(tra(tbuf, st, 0) + GOFF, tra(tbuf, st, 1) + GOFF);
-          const f32x16 cvn = cv_regs(cb, pt);
+          const f32x16 cvn = CV ? cv_regs(cb, pt) : f32x16{};
           fence();
           __builtin_amdgcn_s_setprio(0);
           bf16x8 abf[2];
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float a = __builtin_amdgcn_fmed3f(exp2_fast(fmaf(z[i], alpha, -lsh)), 0.f, 1.f);
-            eneg = fmaf(a, cvn[i], eneg);
+            if constexpr (CV) eneg = fmaf(a, cvn[i], eneg);
             abf[i >> 3][i & 7] = (bf16)a;
           }
           __builtin_amdgcn_s_setprio(1);
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(512) void sa_bwdx_bf16(
         const uint32_t tbuf = buf + pt * TB;
         // Z and dA' - cv: rows = prototypes crow(i, h), column = this token.
         f32x16 z = f32x16{};
-        f32x16 da = cv_regs(cb, pt);
+        f32x16 da = CV ? cv_regs(cb, pt) : f32x16{};
         bf16x8 pa[KS], ga[KS];
 #pragma unroll
         for (int ks = 0; ks < ZA; ++ks) {
@@ -942,6 +945,16 @@ __global__ __launch_bounds__(256) void sa_dp_reduce(const int64_t* __restrict__ 
 }
 
 // ----------------------------------------------------------------------------
+template <int D, bool TW, bool CV>
+static void launch_bwdx_bf16(const BwdArgs& a, unsigned nbx, bool pu, float alpha, float scale,
+                             hipStream_t st) {
+  hipLaunchKernelGGL((sa_bwdx_bf16<D, TW, CV>), dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st,
+                     a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.Pq,
+                     (!TW && pu) ? (int64_t)a.kp * D : (int64_t)0, (const bf16*)a.Gq, a.cvs, a.kp,
+                     a.T, alpha, scale, a.lse, TW ? (const float*)a.tlse2 : (const float*)nullptr,
+                     a.dX, a.acc_dx, a.delta, (bf16*)a.dz, a.kz);
+}
+
 template <int D>
 static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof* prof) {
   const float scale = 1.0f / sqrtf((float)D);
@@ -988,17 +1001,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int dtype, hipStream_t st, Prof
     if (bf) {
       const unsigned nbx = (unsigned)((a.T + kBwdxTokensBf16 - 1) / kBwdxTokensBf16);
       prof_begin(prof, "sa_bwdx_bf16", st);
-      if (tw)
-        hipLaunchKernelGGL((sa_bwdx_bf16<D, true>), dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st,
-                           a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.Pq, (int64_t)0,
-                           (const bf16*)a.Gq, a.cvs, a.kp, a.T, alpha, scale, a.lse,
-                           (const float*)a.tlse2, a.dX, a.acc_dx, a.delta, (bf16*)a.dz, a.kz);
-      else
-        hipLaunchKernelGGL((sa_bwdx_bf16<D, false>), dim3(nbx), dim3(kBwdxTokensBf16 * 2), 0, st,
-                           a.offsets, a.B, (const bf16*)a.X, (const bf16*)a.Pq,
-                           pu ? (int64_t)a.kp * D : (int64_t)0, (const bf16*)a.Gq, a.cvs, a.kp,
-                           a.T, alpha, scale, a.lse, (const float*)nullptr, a.dX, a.acc_dx,
-                           a.delta, (bf16*)a.dz, a.kz);
+      // cv is zero for the plain sum.
+      if (tw) launch_bwdx_bf16<D, true, true>(a, nbx, pu, alpha, scale, st);
+      else if (a.mass_norm) launch_bwdx_bf16<D, false, true>(a, nbx, pu, alpha, scale, st);
+      else launch_bwdx_bf16<D, false, false>(a, nbx, pu, alpha, scale, st);
       e = hipGetLastError();
       prof_end(prof, st);
       if (e != hipSuccess) return e;
