@@ -80,27 +80,37 @@ __global__ __launch_bounds__(256) void sa_reduce_kernel(
       if (hi > lo && live) {
         const int n = s1 - s0 + 1;                     // pieces of user u
         const float* pp = part + ((int64_t)s0 + u) * kd + e;
-        // Eight loads in flight at a time.
+        const float* pm = use_mass ? pmass + ((int64_t)s0 + u) * k + j : nullptr;
+        // Eight pieces in flight at a time; the masses in the same rounds.
         int q = sub;
-        for (; q + 7 * WPS < n; q += 8 * WPS) {
-          f32x4 v[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) v[r] = *(const f32x4*)(pp + (int64_t)(q + WPS * r) * kd);
-#pragma unroll
-          for (int r = 0; r < 8; ++r) acc += v[r];
-        }
-        for (; q < n; q += WPS) acc += *(const f32x4*)(pp + (int64_t)q * kd);
         if (use_mass) {
-          const float* pm = pmass + ((int64_t)s0 + u) * k + j;
-          int r = sub;
-          for (; r + 7 * WPS < n; r += 8 * WPS) {
+          for (; q + 7 * WPS < n; q += 8 * WPS) {
+            f32x4 v[8];
             float m8[8];
 #pragma unroll
-            for (int q8 = 0; q8 < 8; ++q8) m8[q8] = pm[(int64_t)(r + WPS * q8) * k];
+            for (int r = 0; r < 8; ++r) {
+              v[r] = *(const f32x4*)(pp + (int64_t)(q + WPS * r) * kd);
+              m8[r] = pm[(int64_t)(q + WPS * r) * k];
+            }
 #pragma unroll
-            for (int q8 = 0; q8 < 8; ++q8) mu += m8[q8];
+            for (int r = 0; r < 8; ++r) {
+              acc += v[r];
+              mu += m8[r];
+            }
           }
-          for (; r < n; r += WPS) mu += pm[(int64_t)r * k];
+          for (; q < n; q += WPS) {
+            acc += *(const f32x4*)(pp + (int64_t)q * kd);
+            mu += pm[(int64_t)q * k];
+          }
+        } else {
+          for (; q + 7 * WPS < n; q += 8 * WPS) {
+            f32x4 v[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) v[r] = *(const f32x4*)(pp + (int64_t)(q + WPS * r) * kd);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc += v[r];
+          }
+          for (; q < n; q += WPS) acc += *(const f32x4*)(pp + (int64_t)q * kd);
         }
       }
       if constexpr (WPS > 1) {
