@@ -77,6 +77,26 @@ def test_many_short_users_stale_workspace(k, mass_norm, per_user):
         assert torch.all(S[u] == 0) and torch.all(mass[u] == 0)
 
 
+@pytest.mark.parametrize("dtype,mass_norm", [("bf16", False), ("bf16", True), ("f32", True)])
+def test_three_thousand_users(dtype, mass_norm):
+    """3000 users of 0-40 tokens at k=256, d=32: each block row of the
+    reduction walks about 190 users, three 64-user votes, and with bf16 most
+    rows come straight from the aggregation pass (users outnumber the 256
+    segments four to one); the fp32 path reduces every user."""
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(0, 41, size=3000)]
+    lengths[0] = lengths[1500] = lengths[2999] = 0
+    prob = synth.make_inputs(lengths, 256, 32, dtype, device="cuda", seed=31, wid=131,
+                             mass_norm=mass_norm)
+    say(f"case 3000 users dtype={dtype} mass_norm={mass_norm}")
+    S, lse, mass = gpu_forward(prob)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    worst = check_forward_users(prob, S, lse, mass, range(len(lengths)), tol)
+    for u in (0, 1500, 2999):
+        assert torch.all(S[u] == 0) and torch.all(mass[u] == 0)
+    say(f"3000 users dtype={dtype} mass_norm={mass_norm}: worst S rel err {worst:.2e}")
+
+
 @pytest.mark.parametrize("dtype,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
 def test_sharp_logits_exercise_max_shift(dtype, tol):
     # P scaled so that affinities reach |z| ~ 30: exp without the max shift
