@@ -129,16 +129,40 @@ __global__ __launch_bounds__(256, 1) void sa_action_fwd(const ET* __restrict__ e
   __syncthreads();
 
   const int64_t ntiles = (T + 31) / 32;
+  // The next tile's event rows and type are loaded one tile ahead, and this
+  // tile's residual rows at its start, so that the loads overlap the products
+  // (one workgroup per CU: nothing else hides their latency).
+  auto load_rows = [&](int64_t tl, bf16x8* eb, int& ty) {
+    const int64_t ev = tl * 32 + l32;
+    const bool valid = tl < ntiles && ev < T;
+    ty = valid ? types[ev] : 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      eb[ks] = valid ? load8_bf16(e + ev * D + 16 * ks + 8 * h) : bf16x8{};
+  };
+  bf16x8 ebn[KS];
+  int tyn;
+  load_rows(blockIdx.x, ebn, tyn);
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t ev = tile * 32 + l32;            // this lane's event
     const bool valid = ev < T;
-    const int ty = valid ? types[ev] : 0;
+    const int ty = tyn;
     const int tcl = ty < 0 ? 0 : (ty >= n_types ? n_types - 1 : ty);   // clamped type
     // e^T as B operands: eb[ks] = e[ev][16 ks + 8h .. +7].
     bf16x8 eb[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      eb[ks] = valid ? load8_bf16(e + ev * D + 16 * ks + 8 * h) : bf16x8{};
+    for (int ks = 0; ks < KS; ++ks) eb[ks] = ebn[ks];
+    // Residual: columns 32 wave + 8 g4 + 4h .. +3 of this lane's event.
+    float res[4][4];
+    if (wave < OT) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const ET* src = e + (valid ? ev : 0) * D + 32 * wave + 8 * g4 + 4 * h;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) res[g4][r] = (float)src[r];
+      }
+    }
+    load_rows(tile + gridDim.x, ebn, tyn);
     if (has_hidden) {
 #pragma unroll
       for (int m = 0; m < TPW; ++m) {
@@ -195,9 +219,8 @@ __global__ __launch_bounds__(256, 1) void sa_action_fwd(const ET* __restrict__ e
         for (int g4 = 0; g4 < 4; ++g4) {
           const int c = 32 * wave + 8 * g4 + 4 * h;
           ET* dst = x + ev * D + c;
-          const ET* src = e + ev * D + c;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dst[r] = (ET)((float)src[r] + xo[4 * g4 + r]);
+          for (int r = 0; r < 4; ++r) dst[r] = (ET)(res[g4][r] + xo[4 * g4 + r]);
         }
       }
     }
