@@ -80,6 +80,19 @@ __device__ __forceinline__ bf16x8 load8_bf16(const ET* p) {
   }
 }
 
+// Four consecutive values of an fp32 or bf16 row (one 16- or 8-byte access).
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 ld4(const bf16* p) {
+  const bf16x4 v = *(const bf16x4*)p;
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *(f32x4*)p = v; }
+__device__ __forceinline__ void st4(bf16* p, f32x4 v) {
+  bf16x4 b;
+  b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+  *(bf16x4*)p = b;
+}
+
 // grid: persistent, ntiles = ceil(T / 32) tiles of 32 events; block 256.
 template <int D, typename ET>
 __global__ __launch_bounds__(256, 1) void sa_action_fwd(const ET* __restrict__ e,
@@ -152,15 +165,13 @@ __global__ __launch_bounds__(256, 1) void sa_action_fwd(const ET* __restrict__ e
     bf16x8 eb[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) eb[ks] = ebn[ks];
-    // Residual: columns 32 wave + 8 g4 + 4h .. +3 of this lane's event.
-    float res[4][4];
+    // Residual: columns 32 wave + 8 g4 + 4h .. +3 of this lane's event (one
+    // 4-element load each).
+    f32x4 res[4];
     if (wave < OT) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const ET* src = e + (valid ? ev : 0) * D + 32 * wave + 8 * g4 + 4 * h;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) res[g4][r] = (float)src[r];
-      }
+      for (int g4 = 0; g4 < 4; ++g4)
+        res[g4] = ld4(e + (valid ? ev : 0) * D + 32 * wave + 8 * g4 + 4 * h);
     }
     load_rows(tile + gridDim.x, ebn, tyn);
     if (has_hidden) {
@@ -218,9 +229,9 @@ __global__ __launch_bounds__(256, 1) void sa_action_fwd(const ET* __restrict__ e
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int c = 32 * wave + 8 * g4 + 4 * h;
-          ET* dst = x + ev * D + c;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[r] = (ET)(res[g4][r] + xo[4 * g4 + r]);
+          const f32x4 v = {res[g4][0] + xo[4 * g4], res[g4][1] + xo[4 * g4 + 1],
+                           res[g4][2] + xo[4 * g4 + 2], res[g4][3] + xo[4 * g4 + 3]};
+          st4(x + ev * D + c, v);
         }
       }
     }
@@ -303,18 +314,6 @@ __device__ __forceinline__ float act_logistic(float u) {
   return __builtin_amdgcn_rcpf(1.0f + exp2_fast(u * -kLog2e));
 }
 
-// Four consecutive values of an fp32 or bf16 intermediate.
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *(const f32x4*)p; }
-__device__ __forceinline__ f32x4 ld4(const bf16* p) {
-  const bf16x4 v = *(const bf16x4*)p;
-  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-__device__ __forceinline__ void st4(float* p, f32x4 v) { *(f32x4*)p = v; }
-__device__ __forceinline__ void st4(bf16* p, f32x4 v) {
-  bf16x4 b;
-  b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
-  *(bf16x4*)p = b;
-}
 
 // a1 = U1' + T1[type], a3 = U3' + T3[type] (4 columns per thread, H columns
 // per row).  fwd: G = silu(a1) a3.  bwd: dU1 = dG a3 s (1 + a1 (1 - s)),
