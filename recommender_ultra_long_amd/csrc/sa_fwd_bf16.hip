@@ -9,8 +9,10 @@
 // prototypes of a token while one compute unit cannot hold the k x d fp32
 // accumulator for k = 1024 (512 KiB, the whole register file):
 //
-//  1. sa_stats_bf16: token-stationary.  Each wave keeps 64 tokens' rows in
-//     registers as MFMA B operands, streams every prototype through LDS, and
+//  1. sa_stats_bf16: token-stationary.  Each wave keeps 32 tokens' rows in
+//     registers as MFMA B operands (four waves per SIMD, so that one wave's
+//     products overlap another's exponentials), streams every prototype
+//     through LDS, and
 //     reduces the per-token max and sum of exponentials inside each lane
 //     (orientation Z = P X^T puts a token in each lane and prototypes in the
 //     registers).  Writes lse (natural log) per token.
@@ -35,9 +37,13 @@ namespace sa {
 
 // ----------------------------------------------------------------------------
 // Pass 1: per-token log-sum-exp over all k prototypes.
-// Block: 256 threads = 4 waves; wave w handles tokens blk*256 + 64w .. +63 as
-// two 32-token MFMA tiles.  Prototypes stream through LDS in chunks of 64
-// rows, stored in MFMA fragment order and copied global -> LDS by the
+// Block: 256 tokens in NW = 8 / NT waves; wave w handles tokens
+// blk*256 + 32 NT w .. +32 NT - 1 as NT 32-token MFMA tiles.  With NT = 1 (the
+// shared table at d >= 64) two blocks give every SIMD four waves, which keeps
+// the matrix cores fed while other waves exponentiate (measured 38.4 -> 36.6
+// us at 100,000 tokens, k = 1024, d = 128, against NT = 2 with two waves per
+// SIMD); each prototype fragment read from LDS then feeds one product instead
+// of two.  Prototypes stream through LDS in chunks of 64 rows, stored in MFMA fragment order and copied global -> LDS by the
 // direct-to-LDS loads three chunks ahead into four buffers, one barrier per
 // chunk.  Every block reads the same chunk at about the same time, so the
 // first request for a chunk's lines usually goes past the L2; the copies are
@@ -45,8 +51,11 @@ namespace sa {
 // With one table per user (PU), the block makes one pass over the prototypes
 // per user among its tokens, with that user's table, and each pass writes the
 // statistics of its user's tokens only.
-template <int D, bool PU>
-__global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__ X,
+#ifndef SA_STATS_TILES
+#define SA_STATS_TILES 1
+#endif
+template <int D, bool PU, int NT>
+__global__ __launch_bounds__(512 / NT, 2) void sa_stats_bf16(const bf16* __restrict__ X,
                                                      const bf16* __restrict__ P, int k,
                                                      int64_t T, float alpha, float scale,
                                                      float* __restrict__ lse_out,
@@ -56,7 +65,9 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
   constexpr int KS = D / 16;            // 16-wide reduction steps over d
   constexpr int PCH = 64;               // prototypes per LDS chunk
   constexpr int NPIECE = PCH * D / 8;   // 16-byte slots per chunk
-  constexpr int SPW = NPIECE / 4;       // slots copied by each wave
+  constexpr int NW = 8 / NT;            // waves per block
+  static_assert(NT == 1 || NT == 2, "");
+  constexpr int SPW = NPIECE / NW;      // slots copied by each wave
   constexpr int XI = SPW / 64;          // copy instructions per wave per chunk
   static_assert(SPW % 64 == 0 && XI >= 1, "");
   constexpr int NB = 4;                 // chunk buffers
@@ -65,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-  const int64_t tok0 = (int64_t)blockIdx.x * 256 + wave * 64;
+  const int64_t tok0 = (int64_t)blockIdx.x * 256 + wave * 32 * NT;
   const uint32_t sp0 = lds_addr((const SA_LDS void*)&sP[0][0]);
   const int nch = (k + PCH - 1) / PCH;
 
@@ -105,9 +116,9 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
   bool primed = true;
 
   // This lane's token rows as B operands: xb[tt][ks] = X[tok][16 ks + 8h .. +7].
-  bf16x8 xb[2][KS];
+  bf16x8 xb[NT][KS];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < NT; ++tt) {
     const int64_t tok = tok0 + tt * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -118,13 +129,13 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
   // The compiler waits for the rows here, where it also sees the wait, and
   // adds none inside the loops (where it would hold up every copy in flight).
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(xb[tt][ks]));
 
   // Per-token statistics of one pass, per lane (its token, half h of the
   // prototypes): ref = reference maximum, l = sum of exp2((z - ref) alpha).
-  float ref[2], l[2];
+  float ref[NT], l[NT];
 
   // Exact form (running maximum, the sum rescaled whenever it grows).  Folds
   // one 32-prototype x 32-token product tile (register i of a lane is
@@ -176,17 +187,18 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
   };
 
   // Products of prototype tile pt of the chunk in LDS buffer buf.
-  auto products = [&](int buf, int pt, f32x16& c0, f32x16& c1) {
+  using Tiles = f32x16[NT];
+  auto products = [&](int buf, int pt, Tiles& c) {
     {
       const bf16x8 a = sP[buf][(pt * KS) * 64 + lane];
-      c0 = mfma32(a, xb[0][0], f32x16{});
-      c1 = mfma32(a, xb[1][0], f32x16{});
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) c[tt] = mfma32(a, xb[tt][0], f32x16{});
     }
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks) {
       const bf16x8 a = sP[buf][(pt * KS + ks) * 64 + lane];
-      c0 = mfma32(a, xb[0][ks], c0);
-      c1 = mfma32(a, xb[1][ks], c1);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) c[tt] = mfma32(a, xb[tt][ks], c[tt]);
     }
   };
 
@@ -202,14 +214,17 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
     // Tiles folded so far (block-uniform); the first real tile sets the
     // reference in the fast form.
     int nfold = 0;
-    auto consume = [&](const f32x16& v0, const f32x16& v1) {
-      if (!EXACT && nfold == 0) { set_ref(v0, 0); set_ref(v1, 1); }
-      fold(v0, 0);
-      fold(v1, 1);
+    auto consume = [&](const Tiles& v) {
+      if (!EXACT && nfold == 0) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) set_ref(v[tt], tt);
+      }
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) fold(v[tt], tt);
       ++nfold;
     };
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) { ref[tt] = -INFINITY; l[tt] = 0.f; }
+    for (int tt = 0; tt < NT; ++tt) { ref[tt] = -INFINITY; l[tt] = 0.f; }
     // The chunk stream: chunks 0 .. 2 in flight (the first pass requested
     // them before the token rows), then wait for chunk 0.
     if (!primed) {
@@ -223,17 +238,17 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
     // issued in the same straight-line block as the vector work on tile p - 1,
     // so the matrix cores and the vector ALU overlap.  All chunks but the last
     // are full.
-    f32x16 q0, q1;                       // the tile whose fold is pending
+    Tiles q;                             // the tiles whose fold is pending
     bool qreal = false;
     static_assert(PCH == 64, "two prototype tiles per chunk");
     for (int ci = 0; ci + 1 < nch; ++ci) {
       const int buf = ci & (NB - 1);
       // The two tiles of the chunk swap roles with q, so nothing is copied.
-      f32x16 c0, c1;
-      products(buf, 0, c0, c1);
-      if (ci > 0) consume(q0, q1);
-      products(buf, 1, q0, q1);
-      consume(c0, c1);
+      Tiles c;
+      products(buf, 0, c);
+      if (ci > 0) consume(q);
+      products(buf, 1, q);
+      consume(c);
       qreal = true;
       // Chunk ci + 1 has landed (ci + 2 may still be in flight); after the
       // barrier no wave reads chunk ci any more, and chunk ci + 3 goes into
@@ -250,30 +265,35 @@ __global__ __launch_bounds__(256, 2) void sa_stats_bf16(const bf16* __restrict__
       for (int pt = 0; pt < PCH / 32; ++pt) {
         const int pbase = ci * PCH + pt * 32;
         if (pbase >= k) break;             // uniform across the block
-        f32x16 c0, c1;
-        products(buf, pt, c0, c1);
-        if (qreal) consume(q0, q1);
-        q0 = c0;
-        q1 = c1;
+        Tiles c;
+        products(buf, pt, c);
+        if (qreal) consume(q);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) q[tt] = c[tt];
         qreal = true;
         if (pbase + 32 > k) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (pbase + crow(i, h) >= k) { q0[i] = -INFINITY; q1[i] = -INFINITY; }
+            if (pbase + crow(i, h) >= k) {
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt) q[tt][i] = -INFINITY;
+            }
         }
       }
-      consume(q0, q1);
+      consume(q);
     }
     wait_vmcnt<0>();   // the copies past the end have landed: none is in flight after the pass
 
     if constexpr (!EXACT) {
       // Redo in the exact form if any lane's sum overflowed.
-      const bool bad = !(__builtin_isfinite(l[0]) && __builtin_isfinite(l[1]));
+      bool bad = false;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) bad = bad || !__builtin_isfinite(l[tt]);
       if (__syncthreads_or(bad)) return false;
     }
     // Lanes l and l ^ 32 saw disjoint halves of the prototypes of one token.
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < NT; ++tt) {
       const float m = l[tt] > 0.f ? ref[tt] : -INFINITY;   // a lane with no terms
       const float mo = shfl_xor32(m), lo = shfl_xor32(l[tt]);
       const float M = fmaxf(m, mo);
@@ -644,19 +664,26 @@ __global__ __launch_bounds__(NW * 64, 1) void sa_agg_bf16(
 #define SA_AGG_WAVES 8
 #endif
 constexpr int kAggWaves = SA_AGG_WAVES;   // waves per aggregation workgroup
+constexpr int kStatsTiles = SA_STATS_TILES;   // 32-token tiles per statistics wave
 
 template <int D>
 static hipError_t launch_stats_bf16_t(const FwdArgs& a, hipStream_t st, Prof* prof) {
   const float scale = 1.0f / sqrtf((float)D);
   const float alpha = scale * kLog2e;
   const unsigned nb = (unsigned)((a.T + 255) / 256);
+  // Eight single-tile waves need at least 64 copy slots per wave (d >= 64).
+  // With one table per user the block keeps two tiles per wave: its extra
+  // per-user state would not fit the 128 registers of four waves per SIMD.
+  constexpr int NT = D >= 64 ? kStatsTiles : 2;
   prof_begin(prof, "sa_stats_bf16", st);
   if (a.pstride != 0)
-    hipLaunchKernelGGL((sa_stats_bf16<D, true>), dim3(nb), dim3(256), 0, st, (const bf16*)a.X,
+    hipLaunchKernelGGL((sa_stats_bf16<D, true, 2>), dim3(nb), dim3(256), 0, st,
+                       (const bf16*)a.X,
                        (const bf16*)a.P, a.k, a.T, alpha, scale, a.lse, a.lse2, a.offsets, a.B,
                        a.pstride);
   else
-    hipLaunchKernelGGL((sa_stats_bf16<D, false>), dim3(nb), dim3(256), 0, st, (const bf16*)a.X,
+    hipLaunchKernelGGL((sa_stats_bf16<D, false, NT>), dim3(nb), dim3(512 / NT), 0, st,
+                       (const bf16*)a.X,
                        (const bf16*)a.P, a.k, a.T, alpha, scale, a.lse, a.lse2, a.offsets, a.B,
                        (int64_t)0);
   const hipError_t e = hipGetLastError();
